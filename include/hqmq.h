@@ -1,0 +1,185 @@
+/*
+ * hqmq.h -- C ABI of the HQMQ KV-cache codec for AMD Instinct MI355X (gfx950).
+ *
+ * HQMQ (Hurwitz Quaternion Multiplicative Quantization, arXiv 2605.27646)
+ * treats every 4 consecutive elements of a K or V head vector as a
+ * quaternion x, keeps its norm r = |x| and quantises its direction x / r to
+ * the nearest of the 24 S products q_p * q_s, q_p in the binary tetrahedral
+ * group 2T (the 24 unit Hurwitz quaternions) and q_s in a seeded codebook of S
+ * random unit quaternions per (layer, head, role).  A per-batch Med3x step
+ * first keeps every chunk with r > C * median(r) (C = 3) in fp16 on a side
+ * list, flagged by one bit.  Sources: the paper's abstract (paperdance.org and
+ * thelatestinai.com pages for 2605.27646); gist.science/nl/paper/2605.27646,
+ * "Technische Samenvatting", Methodologie 1-3; signal-ia-rouge.vercel.app
+ * article, sections "La mecanique" and "Le probleme des outliers : Med3x".
+ *
+ * Tensor layout.  x and y are contiguous [layers][kv_heads][tokens][head_dim]
+ * (fp16 or fp32).  Chunk c of token t of slice (layer, head) is elements
+ * 4c .. 4c+3 of that token's head vector; element 4c is the real part, then
+ * i, j, k.  A (layer, head) pair is a "slice" of tokens * head_dim / 4 chunks.
+ *
+ * Encoded records (all caller-allocated device memory; sizes from hqmq_sizes):
+ *   idx    [layers][kv_heads][tokens][words_per_token] u32.  Code k = 24 s + p
+ *          of each chunk, b = ceil(log2(24 S)) bits, packed little-endian
+ *          along the token row: bit i of code c is bit (c b + i) of the row,
+ *          row bit j is bit j % 32 of word j / 32; unused high bits are 0.
+ *          2T order p: +1, -1, +i, -i, +j, -j, +k, -k, then (s0,s1,s2,s3)/2
+ *          with s_m = -1 iff bit m of p - 8 is set.  The record always holds
+ *          the nearest codeword, also for an outlier chunk.
+ *   hnorm  [layers][kv_heads][tokens][head_dim / 4] u16.  binary16 of
+ *          sqrt_rn(s2) / 2 with s2 = fma(x3,x3, fma(x2,x2, fma(x1,x1, x0*x0)))
+ *          in fp32; bit 15 (the sign bit, free since norms are >= 0) is the
+ *          Med3x outlier flag.
+ *   side list (Med3x only): out_pos[e] u32 = t * head_dim / 4 + c (position
+ *          in its slice), out_val[4e..4e+3] = the chunk's values as binary16
+ *          (fp32 inputs rounded to nearest even).  Ordered by (slice, batch,
+ *          position); batch_offsets[b] .. batch_offsets[b+1] is batch b's
+ *          range, batches numbered slice-major (slice * batches_per_slice +
+ *          token_block).
+ *   status [2] u64: status[0] = outliers found, status[1] = 1 when they did
+ *          not fit out_capacity (entries past the capacity are dropped).
+ *
+ * Decoding: bulk chunk y = (2 * hnorm) * (q_p * q_s) in fp32, rounded to the
+ * output type; outlier chunk y = its side-list values.
+ *
+ * Threading: every entry point is stateless and re-entrant; device work is
+ * enqueued on the caller's stream and nothing is allocated.  Calls on
+ * different streams that share output buffers race.
+ */
+#ifndef HQMQ_H_
+#define HQMQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    HQMQ_OK = 0,
+    HQMQ_EINVAL = -1,    /* bad descriptor, pointer, size or alignment */
+    HQMQ_ENOTSUP = -2,   /* valid request outside this build's limits */
+    HQMQ_ECAPACITY = -3, /* side list did not fit out_capacity */
+    HQMQ_EHIP = -4       /* a HIP runtime call or kernel launch failed */
+};
+
+/* Element types of x and y. */
+enum { HQMQ_F16 = 0, HQMQ_F32 = 1 };
+
+/* Roles: which cache tensor a codebook belongs to. */
+enum { HQMQ_ROLE_K = 0, HQMQ_ROLE_V = 1 };
+
+/* Problem descriptor (a plain value, read only during the call).
+ *   layers, kv_heads, tokens >= 0 (any of them 0 = empty input)
+ *   head_dim in {16, 32, 64, 128, 256}
+ *   S in [1, 1024]: secondary codewords per (layer, head)
+ *   med_batch_tokens: Med3x batch length in tokens, 0 = Med3x off.  Batches
+ *       start at token multiples of it within each slice; a final partial
+ *       block is its own batch.  Median over the batch's chunks ("the
+ *       current batch", gist.science/nl Methodologie 3).
+ *   med_C: Med3x multiplier, the pages fix 3 (finite, > 0 when Med3x is on)
+ *   dtype: HQMQ_F16 or HQMQ_F32 for x (and y). */
+typedef struct hqmq_desc {
+    int64_t layers;
+    int64_t kv_heads;
+    int64_t tokens;
+    int64_t head_dim;
+    int32_t S;
+    int32_t dtype;
+    int64_t med_batch_tokens;
+    float med_C;
+    int32_t reserved;
+} hqmq_desc;
+
+/* Sizes of every buffer a call needs, in bytes (hqmq_sizes). */
+typedef struct hqmq_sizes_t {
+    int32_t code_bits;          /* b = ceil(log2(24 S)) */
+    int32_t words_per_token;    /* ceil(b * head_dim / 4 / 32) */
+    int64_t chunks;             /* layers * kv_heads * tokens * head_dim / 4 */
+    int64_t batches;            /* Med3x batches (0 when Med3x is off) */
+    int64_t max_outliers;       /* sum over batches of floor(n_batch / 2) */
+    uint64_t input_bytes;       /* x (and y) */
+    uint64_t idx_bytes;
+    uint64_t hnorm_bytes;
+    uint64_t offsets_bytes;     /* (batches + 1) * 8, 0 when Med3x is off */
+    uint64_t side_entry_bytes;  /* 12 bytes per outlier (4 pos + 8 values) */
+    uint64_t workspace_bytes;   /* encode scratch, 0 when Med3x is off */
+    uint64_t codebook_bytes;    /* layers * kv_heads * S * 16 */
+} hqmq_sizes_t;
+
+/* Encoded records: device pointers owned by the caller (see layout above).
+ * batch_offsets, out_pos, out_val and status may be NULL when Med3x is off;
+ * out_pos/out_val may be NULL when out_capacity is 0. */
+typedef struct hqmq_enc {
+    uint32_t *idx;
+    uint16_t *hnorm;
+    uint64_t *batch_offsets;
+    uint32_t *out_pos;
+    uint16_t *out_val;
+    uint64_t out_capacity;
+    uint64_t *status;
+} hqmq_enc;
+
+/* Message for a status code; never NULL. */
+const char *hqmq_strerror(int code);
+
+/* Buffer sizes for descriptor d.  Host only, no device work.
+ * Errors: HQMQ_EINVAL for a NULL pointer or invalid descriptor. */
+int hqmq_sizes(const hqmq_desc *d, hqmq_sizes_t *out);
+
+/* Seeded secondary codebook ("S random unit quaternions" per (layer, head),
+ * no calibration: the abstract; drawn per (layer, head, role): gist.science
+ * Methodologie 1).  Writes [layers][kv_heads][S][4] fp32 into the caller's
+ * HOST buffer out_host.  Uniform on S^3: Philox4x64-10 (Salmon et al., SC'11)
+ * keyed (seed, layer << 32 | head << 8 | role), candidate j from counter
+ * (j, 0, 0, 0), coordinates v_m = (2 (w_m >> 40) - 2^24 + 1) 2^-24, kept when
+ * sum v^2 <= 1, q = v / sqrt(sum v^2) in fp64 rounded to fp32.  Bit-identical
+ * on every IEEE-754 host.  Host only.
+ * Errors: HQMQ_EINVAL if out_host is NULL, layers or kv_heads < 0 or
+ * >= 2^24, role not 0/1, or S outside [1, 1024]. */
+int hqmq_make_codebook(uint64_t seed, int32_t layers, int32_t kv_heads, int32_t role,
+                       int32_t S, float *out_host);
+
+/* Encode x (device, [layers][kv_heads][tokens][head_dim] in d->dtype,
+ * 16-byte aligned) with codebook (device, [layers][kv_heads][S][4] fp32)
+ * into enc.  Steps: per chunk the fp32 norm and its binary16 half-norm code,
+ * the nearest of the 24 S codewords <x, q_p q_s> (gist.science Methodologie
+ * 1; the identity <x, q_p q_s> = <conj(q_p) x, q_s> of the isometry argument,
+ * abstract), then, when Med3x is on, the exact lower median of s2 per batch,
+ * outliers s2 > fl(fl(C*C) * median) flagged in hnorm and copied to the side
+ * list in order.  workspace: device scratch of at least
+ * hqmq_sizes().workspace_bytes, 256-byte aligned (may be NULL when that is 0).
+ * Asynchronous on stream; nothing is enqueued when validation fails.  Ties
+ * between exactly equal fp32 scores keep the smallest code.
+ * Errors (synchronous): HQMQ_EINVAL (descriptor, NULL or misaligned pointer,
+ * workspace too small), HQMQ_EHIP (launch failure).  Side-list overflow is
+ * reported through status and hqmq_encode_result. */
+int hqmq_encode(const hqmq_desc *d, const void *x, const float *codebook, const hqmq_enc *enc,
+                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Wait for stream, read enc->status (16 bytes device to host) and return the
+ * outlier count in *n_outliers.  Returns HQMQ_ECAPACITY (with the count
+ * needed in *n_outliers) when the side list overflowed: re-allocate and
+ * encode again.  Returns HQMQ_OK with 0 when Med3x was off (status NULL).
+ * Errors: HQMQ_EINVAL (NULL enc or n_outliers), HQMQ_EHIP. */
+int hqmq_encode_result(const hqmq_enc *enc, hipStream_t stream, uint64_t *n_outliers);
+
+/* Decode enc into y (device, same shape as x, d->dtype, 16-byte aligned):
+ * bulk chunks r^ (q_p q_s) with r^ = 2 hnorm, computed in fp32 and rounded
+ * to nearest even; outlier chunks take their side-list values (the decoder
+ * the pages run before or inside attention: gist.science "Memory en
+ * Latentie").  enc must come from a successful hqmq_encode with the same
+ * descriptor and codebook.  Asynchronous on stream.
+ * Errors: HQMQ_EINVAL, HQMQ_EHIP. */
+int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, void *y,
+                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQMQ_H_ */

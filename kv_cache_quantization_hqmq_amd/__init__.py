@@ -1,0 +1,16 @@
+"""HQMQ KV-cache codec for AMD Instinct MI355X (gfx950).
+
+The codec runs in the HIP kernels of ``libhqmq.so`` behind the C ABI declared
+in ``include/hqmq.h``; ``kv_cache_quantization_hqmq_amd.hqmq`` is its ctypes
+binding (same function names).  Build with
+``python -m kv_cache_quantization_hqmq_amd.build``.
+"""
+from .hqmq import (CapacityError, Desc, HQMQError, Records, Sizes, allocate_records, decode,
+                   encode, hqmq_decode, hqmq_encode, hqmq_encode_result, hqmq_make_codebook,
+                   hqmq_sizes, hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_ROLE_K,
+                   HQMQ_ROLE_V)
+
+__all__ = ["CapacityError", "Desc", "HQMQError", "Records", "Sizes", "allocate_records",
+           "decode", "encode", "hqmq_decode", "hqmq_encode", "hqmq_encode_result",
+           "hqmq_make_codebook", "hqmq_sizes", "hqmq_strerror", "workspace", "HQMQ_F16",
+           "HQMQ_F32", "HQMQ_ROLE_K", "HQMQ_ROLE_V"]

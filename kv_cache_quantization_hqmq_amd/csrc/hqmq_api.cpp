@@ -1,0 +1,281 @@
+// C-ABI entry points of the HQMQ codec (declared in include/hqmq.h):
+// argument validation, buffer sizes, the seeded codebook generator and the
+// kernel launch sequence.  No device memory is allocated here.
+#include "hqmq.h"
+
+#include <cmath>
+#include <cstring>
+
+#include "hqmq_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxS = 1024;
+constexpr uint64_t kWsAlign = 256;
+
+bool head_dim_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+int code_bits(int64_t S) {
+    int b = 0;
+    while ((int64_t{1} << b) < 24 * S) ++b;
+    return b;
+}
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validate a descriptor and derive the launch geometry.
+int make_geometry(const hqmq_desc *d, hqmq::Geometry *g) {
+    if (!d) return HQMQ_EINVAL;
+    if (d->layers < 0 || d->kv_heads < 0 || d->tokens < 0) return HQMQ_EINVAL;
+    if (!head_dim_ok(d->head_dim)) return HQMQ_EINVAL;
+    if (d->S < 1 || d->S > kMaxS) return HQMQ_EINVAL;
+    if (d->dtype != HQMQ_F16 && d->dtype != HQMQ_F32) return HQMQ_EINVAL;
+    if (d->med_batch_tokens < 0) return HQMQ_EINVAL;
+    if (d->med_batch_tokens > 0 && !(std::isfinite(d->med_C) && d->med_C > 0.0f)) return HQMQ_EINVAL;
+    const int64_t cpt = d->head_dim / 4;
+    // side-list positions are u32 chunk offsets within a slice
+    if (d->tokens > (int64_t{1} << 32) / cpt - 1) return HQMQ_ENOTSUP;
+    if (d->layers > (int64_t{1} << 31) || d->kv_heads > (int64_t{1} << 31)) return HQMQ_ENOTSUP;
+    g->slices = d->layers * d->kv_heads;
+    g->tokens = d->tokens;
+    g->cpt = static_cast<int32_t>(cpt);
+    g->n_slice = d->tokens * cpt;
+    g->S = d->S;
+    g->bits = code_bits(d->S);
+    g->words = static_cast<int32_t>((static_cast<int64_t>(g->bits) * cpt + 31) / 32);
+    g->f32 = d->dtype == HQMQ_F32 ? 1 : 0;
+    if (d->med_batch_tokens > 0) {
+        const int64_t B = d->med_batch_tokens < d->tokens ? d->med_batch_tokens : d->tokens;
+        g->batch_chunks = (B > 0 ? B : 1) * cpt;
+        g->batches_per_slice = d->tokens > 0 ? (d->tokens + B - 1) / B : 0;
+    } else {
+        g->batch_chunks = 0;
+        g->batches_per_slice = 0;
+    }
+    g->med_C = d->med_C;
+    // grids are one-dimensional: keep the block count well inside 2^31
+    if (g->slices > 0 && g->n_slice / 256 + 1 > (int64_t{1} << 31) / g->slices) return HQMQ_ENOTSUP;
+    return HQMQ_OK;
+}
+
+struct Workspace {
+    float *s2;
+    float *thr;
+    uint32_t *counts;
+};
+
+uint64_t workspace_layout(const hqmq::Geometry &g, void *base, Workspace *w) {
+    if (g.batch_chunks == 0) {
+        if (w) *w = Workspace{nullptr, nullptr, nullptr};
+        return 0;
+    }
+    const uint64_t chunks = static_cast<uint64_t>(g.slices * g.n_slice);
+    const uint64_t nb = static_cast<uint64_t>(g.slices * g.batches_per_slice);
+    uint64_t off = 0;
+    const uint64_t o_s2 = off;
+    off = align_up(off + chunks * 4, kWsAlign);
+    const uint64_t o_thr = off;
+    off = align_up(off + nb * 4, kWsAlign);
+    const uint64_t o_cnt = off;
+    off = align_up(off + nb * 4, kWsAlign);
+    if (w) {
+        char *b = static_cast<char *>(base);
+        w->s2 = reinterpret_cast<float *>(b + o_s2);
+        w->thr = reinterpret_cast<float *>(b + o_thr);
+        w->counts = reinterpret_cast<uint32_t *>(b + o_cnt);
+    }
+    return off;
+}
+
+// ----------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds; each round
+// multiplies counter words 0 and 2 by the two round constants (full 128-bit
+// products), and mixes the high halves with the other two words and the key;
+// the key is bumped by two Weyl increments between rounds.
+// ----------------------------------------------------------------------------
+struct Philox4x64 {
+    static constexpr uint64_t kMul0 = 0xD2E7470EE14C6C93ull;
+    static constexpr uint64_t kMul1 = 0xCA5A826395121157ull;
+    static constexpr uint64_t kWeyl0 = 0x9E3779B97F4A7C15ull;
+    static constexpr uint64_t kWeyl1 = 0xBB67AE8584CAA73Bull;
+
+    static void block(const uint64_t in[4], uint64_t k0, uint64_t k1, uint64_t out[4]) {
+        uint64_t c[4] = {in[0], in[1], in[2], in[3]};
+        for (int r = 0; r < 10; ++r) {
+            if (r) {
+                k0 += kWeyl0;
+                k1 += kWeyl1;
+            }
+            const unsigned __int128 p0 = static_cast<unsigned __int128>(kMul0) * c[0];
+            const unsigned __int128 p1 = static_cast<unsigned __int128>(kMul1) * c[2];
+            const uint64_t hi0 = static_cast<uint64_t>(p0 >> 64), lo0 = static_cast<uint64_t>(p0);
+            const uint64_t hi1 = static_cast<uint64_t>(p1 >> 64), lo1 = static_cast<uint64_t>(p1);
+            c[0] = hi1 ^ c[1] ^ k0;
+            c[1] = lo1;
+            c[2] = hi0 ^ c[3] ^ k1;
+            c[3] = lo0;
+        }
+        std::memcpy(out, c, sizeof(c));
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *hqmq_strerror(int code) {
+    switch (code) {
+        case HQMQ_OK: return "ok";
+        case HQMQ_EINVAL: return "invalid argument (descriptor, pointer, size or alignment)";
+        case HQMQ_ENOTSUP: return "request outside the supported limits";
+        case HQMQ_ECAPACITY: return "Med3x side list exceeded out_capacity";
+        case HQMQ_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int hqmq_sizes(const hqmq_desc *d, hqmq_sizes_t *out) {
+    if (!out) return HQMQ_EINVAL;
+    hqmq::Geometry g;
+    const int rc = make_geometry(d, &g);
+    if (rc != HQMQ_OK) return rc;
+    std::memset(out, 0, sizeof(*out));
+    out->code_bits = g.bits;
+    out->words_per_token = g.words;
+    out->chunks = g.slices * g.n_slice;
+    out->batches = g.slices * g.batches_per_slice;
+    int64_t mo = 0;
+    if (g.batch_chunks > 0) {
+        const int64_t full = g.n_slice / g.batch_chunks;
+        const int64_t tail = g.n_slice - full * g.batch_chunks;
+        mo = g.slices * (full * (g.batch_chunks / 2) + tail / 2);
+    }
+    out->max_outliers = mo;
+    out->input_bytes = static_cast<uint64_t>(out->chunks) * 4 * (g.f32 ? 4 : 2);
+    out->idx_bytes = static_cast<uint64_t>(g.slices * g.tokens) * g.words * 4;
+    out->hnorm_bytes = static_cast<uint64_t>(out->chunks) * 2;
+    out->offsets_bytes = g.batch_chunks > 0 ? static_cast<uint64_t>(out->batches + 1) * 8 : 0;
+    out->side_entry_bytes = 12;
+    out->workspace_bytes = workspace_layout(g, nullptr, nullptr);
+    out->codebook_bytes = static_cast<uint64_t>(g.slices) * g.S * 16;
+    return HQMQ_OK;
+}
+
+int hqmq_make_codebook(uint64_t seed, int32_t layers, int32_t kv_heads, int32_t role, int32_t S,
+                       float *out_host) {
+    if (!out_host || layers < 0 || kv_heads < 0 || layers >= (1 << 24) || kv_heads >= (1 << 24) ||
+        (role != HQMQ_ROLE_K && role != HQMQ_ROLE_V) || S < 1 || S > kMaxS)
+        return HQMQ_EINVAL;
+    for (int32_t l = 0; l < layers; ++l) {
+        for (int32_t h = 0; h < kv_heads; ++h) {
+            const uint64_t k1 = (static_cast<uint64_t>(l) << 32) | (static_cast<uint64_t>(h) << 8) |
+                                static_cast<uint64_t>(role);
+            float *q = out_host + (static_cast<int64_t>(l) * kv_heads + h) * S * 4;
+            uint64_t ctr = 0;
+            for (int32_t s = 0; s < S;) {
+                const uint64_t in[4] = {ctr++, 0, 0, 0};
+                uint64_t w[4];
+                Philox4x64::block(in, seed, k1, w);
+                double v[4];
+                double n2 = 0.0;
+                for (int m = 0; m < 4; ++m) {
+                    // odd multiple of 2^-24 in (-1, 1) from the top 24 bits
+                    v[m] = std::ldexp(static_cast<double>(static_cast<int64_t>(w[m] >> 40) * 2 - (int64_t{1} << 24) + 1), -24);
+                    n2 += v[m] * v[m];
+                }
+                if (!(n2 <= 1.0)) continue;  // rejection: uniform in the ball
+                const double r = std::sqrt(n2);
+                for (int m = 0; m < 4; ++m) q[4 * s + m] = static_cast<float>(v[m] / r);
+                ++s;
+            }
+        }
+    }
+    return HQMQ_OK;
+}
+
+int hqmq_encode(const hqmq_desc *d, const void *x, const float *codebook, const hqmq_enc *enc,
+                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    hqmq::Geometry g;
+    int rc = make_geometry(d, &g);
+    if (rc != HQMQ_OK) return rc;
+    if (!enc) return HQMQ_EINVAL;
+    const int64_t chunks = g.slices * g.n_slice;
+    const bool med = g.batch_chunks > 0;
+    const int64_t nb = g.slices * g.batches_per_slice;
+    if (chunks > 0) {
+        if (!x || !codebook || !enc->idx || !enc->hnorm) return HQMQ_EINVAL;
+        if (!aligned(x, 16) || !aligned(codebook, 16) || !aligned(enc->idx, 4) || !aligned(enc->hnorm, 8))
+            return HQMQ_EINVAL;
+    }
+    Workspace ws{nullptr, nullptr, nullptr};
+    if (med) {
+        if (!enc->batch_offsets || !enc->status || !aligned(enc->batch_offsets, 8) || !aligned(enc->status, 8))
+            return HQMQ_EINVAL;
+        if (enc->out_capacity > 0 && (!enc->out_pos || !enc->out_val || !aligned(enc->out_val, 8)))
+            return HQMQ_EINVAL;
+        const uint64_t need = workspace_layout(g, nullptr, nullptr);
+        if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign)))
+            return HQMQ_EINVAL;
+        workspace_layout(g, workspace, &ws);
+    }
+
+    hipError_t e = hipSuccess;
+    if (chunks > 0) {
+        e = hqmq::launch_encode_search(g, x, codebook, enc->idx, enc->hnorm, ws.s2, stream);
+        if (e != hipSuccess) return HQMQ_EHIP;
+    }
+    if (med) {
+        if (nb > 0) {
+            e = hqmq::launch_med3_select(g, ws.s2, ws.thr, ws.counts, stream);
+            if (e == hipSuccess)
+                e = hqmq::launch_med3_scan(nb, ws.counts, enc->batch_offsets, enc->out_capacity, enc->status, stream);
+            if (e == hipSuccess)
+                e = hqmq::launch_med3_flag(g, x, ws.s2, ws.thr, enc->batch_offsets, enc->hnorm, enc->out_pos,
+                                           enc->out_val, enc->out_capacity, stream);
+        } else {
+            e = hqmq::launch_fill_u64(enc->batch_offsets, 1, 0, stream);
+            if (e == hipSuccess) e = hqmq::launch_fill_u64(enc->status, 2, 0, stream);
+        }
+    } else if (enc->status) {
+        if (!aligned(enc->status, 8)) return HQMQ_EINVAL;
+        e = hqmq::launch_fill_u64(enc->status, 2, 0, stream);
+    }
+    return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
+}
+
+int hqmq_encode_result(const hqmq_enc *enc, hipStream_t stream, uint64_t *n_outliers) {
+    if (!enc || !n_outliers) return HQMQ_EINVAL;
+    *n_outliers = 0;
+    if (hipStreamSynchronize(stream) != hipSuccess) return HQMQ_EHIP;
+    if (!enc->status) return HQMQ_OK;
+    uint64_t st[2] = {0, 0};
+    if (hipMemcpy(st, enc->status, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return HQMQ_EHIP;
+    *n_outliers = st[0];
+    return st[1] ? HQMQ_ECAPACITY : HQMQ_OK;
+}
+
+int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, void *y,
+                hipStream_t stream) {
+    hqmq::Geometry g;
+    int rc = make_geometry(d, &g);
+    if (rc != HQMQ_OK) return rc;
+    if (!enc) return HQMQ_EINVAL;
+    const int64_t chunks = g.slices * g.n_slice;
+    if (chunks == 0) return HQMQ_OK;
+    if (!y || !codebook || !enc->idx || !enc->hnorm) return HQMQ_EINVAL;
+    if (!aligned(y, 16) || !aligned(codebook, 16) || !aligned(enc->idx, 4) || !aligned(enc->hnorm, 8))
+        return HQMQ_EINVAL;
+    if (g.batch_chunks > 0) {
+        if (!enc->batch_offsets) return HQMQ_EINVAL;
+        if (enc->out_capacity > 0 && (!enc->out_pos || !enc->out_val || !aligned(enc->out_val, 8)))
+            return HQMQ_EINVAL;
+    }
+    const hipError_t e = hqmq::launch_decode(g, enc->idx, enc->hnorm,
+                                             g.batch_chunks > 0 ? enc->batch_offsets : nullptr, enc->out_pos,
+                                             enc->out_val, enc->out_capacity, codebook, y, stream);
+    return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
+}
+
+}  // extern "C"

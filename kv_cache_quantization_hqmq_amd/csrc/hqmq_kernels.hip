@@ -1,0 +1,840 @@
+// HQMQ encode / Med3x / decode kernels for AMD Instinct MI355X (gfx950).
+//
+// Method (arXiv 2605.27646; the abstract as shown on paperdance.org and
+// thelatestinai.com; gist.science/nl "Technische Samenvatting",
+// Methodologie 1-3): every 4-element chunk x of a K or V head vector is a
+// quaternion; its norm is kept and its direction goes to the codeword
+// q_p * q_s (q_p in 2T, q_s in the slice's S-entry codebook) of largest inner
+// product; a per-batch Med3x step keeps chunks with r > C r_med in fp16.
+//
+// Encode search.  By linearity in q_p, <x, q_p q_s> = sum_m a_pm t_m(s) with
+// t_m(s) = <x, e_m q_s> (e = 1, i, j, k), which is the conj(q_p) identity of
+// the isometry argument (abstract) applied to the four basis units.  The best
+// of the 24 primaries for a given s is max(|t|_inf, |t|_1 / 2): a unit +-e_m
+// scores +-t_m, a half-unit (s0..s3)/2 scores sum s_m t_m / 2 (signs chosen
+// to match t).  So the work per (chunk, s) is one 4x4 orthogonal transform
+// (16 FMA) plus a short max/abs epilogue.  The transforms of 16 chunks against
+// 4 secondary codewords are one v_mfma_f32_16x16x4f32: A = the 16 rows
+// e_m q_s (4 s x 4 m) of the slice, B = 16 chunks x 4 components, and lane l
+// of D holds the four t_m of s = 4 tile + l / 16 for chunk l % 16, so the
+// epilogue runs in-lane.  The matrix core does the 16 FMA / (chunk, s), the
+// VALU the epilogue, concurrently.
+//
+// Parity contract: hnorm and the Med3x outlier set are bit-exact with the
+// declared fp32 arithmetic; codes are exact except where two codewords'
+// scores differ by less than fp32 rounding (near ties).
+#include <hip/hip_runtime.h>
+
+#include "hqmq_launch.h"
+
+namespace hqmq {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kEncThreads = 256;   // 4 waves; each wave encodes 64 chunks per step
+constexpr int kMedThreads = 512;
+constexpr int kFlagThreads = 256;
+constexpr int kScanThreads = 1024;
+constexpr int kDecThreads = 256;   // each thread decodes 4 chunks per step
+constexpr int kMaxS = 1024;
+constexpr int kTableMaxS = 64;     // decode keeps the 24 S codewords in LDS up to here
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// (e_m * q)[k] = sign(m, k) q[m ^ k] for e = (1, i, j, k) under the Hamilton
+// product: i q = (-q1, q0, -q3, q2), j q = (-q2, q3, q0, -q1),
+// k q = (-q3, -q2, q1, q0).  Bit (4 m + k) of kNegMask marks a minus sign.
+constexpr uint32_t kNegMask = 0x3950u;
+
+__device__ __forceinline__ float unit_row(const float *q, int m, int k) {
+    const float v = q[m ^ k];
+    return ((kNegMask >> (4 * m + k)) & 1u) ? -v : v;
+}
+
+// binary16 helpers (round to nearest even: the hardware default mode).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Correctly rounded fp32 square root of a >= 0.  v_sqrt_f32 is within one
+// ulp; the result is then moved to the neighbour whose rounding interval
+// holds sqrt(a), decided exactly in fp64: the midpoints between y and its
+// neighbours have at most 25 significant bits, so their squares are exact.
+// Inputs below 2^-100 are scaled by 2^100 first (exact) to stay in the
+// normal range of v_sqrt_f32.
+__device__ __forceinline__ float sqrt_rn(float a) {
+    if (!(a > 0.0f)) return a;  // 0 (and the documented non-finite precondition)
+    const bool tiny = a < 0x1p-100f;
+    const float as = tiny ? a * 0x1p100f : a;
+    float y = __builtin_amdgcn_sqrtf(as);
+    const double ad = static_cast<double>(as);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const float yu = __uint_as_float(__float_as_uint(y) + 1u);
+        const float yd = __uint_as_float(__float_as_uint(y) - 1u);
+        const double hi = (static_cast<double>(y) + static_cast<double>(yu)) * 0.5;
+        const double lo = (static_cast<double>(y) + static_cast<double>(yd)) * 0.5;
+        if (ad > hi * hi) y = yu;
+        else if (ad < lo * lo) y = yd;
+    }
+    return tiny ? y * 0x1p-50f : y;
+}
+
+// Strict order of (score, s) candidates: higher score, then lower s.
+__device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
+    return sa > sb || (sa == sb && ia < ib);
+}
+
+// --------------------------------------------------------------------------
+// Encode search kernel.
+// --------------------------------------------------------------------------
+struct EncArgs {
+    const void *x;
+    const float *cb;
+    uint32_t *idx;
+    uint16_t *hnorm;
+    float *s2;
+    int64_t n_slice;
+    int64_t tiles_per_slice;
+    int64_t tokens;
+    int32_t tile_chunks;
+    int32_t S;
+    int32_t NT;     // ceil(S / 4) tiles of 4 secondary codewords
+    int32_t cpt;
+    int32_t bits;
+    int32_t words;
+};
+
+// NT_REG > 0: S <= 4 NT_REG and the A operands live in registers.
+// NT_REG == 0: any S <= kMaxS, A read from the LDS copy of the codebook.
+template <int NT_REG, bool F32IN, bool WITH_S2>
+__global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
+    constexpr int kQ = NT_REG > 0 ? 16 * NT_REG : 4 * kMaxS;
+    __shared__ __attribute__((aligned(16))) float sq[kQ];
+    __shared__ __attribute__((aligned(16))) float sx[4][64 * 4];
+    __shared__ uint32_t scode[4][64];
+
+    const int64_t tile = blockIdx.x;
+    const int64_t slice = tile / a.tiles_per_slice;
+    const int64_t c_begin = (tile - slice * a.tiles_per_slice) * a.tile_chunks;
+    const int64_t c_end = min(c_begin + static_cast<int64_t>(a.tile_chunks), a.n_slice);
+    const int NT = NT_REG > 0 ? NT_REG : a.NT;
+
+    {
+        const float *q = a.cb + slice * a.S * 4;
+        const int nq = 16 * NT;
+        for (int i = threadIdx.x; i < nq; i += kEncThreads) sq[i] = i < 4 * a.S ? q[i] : 0.0f;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> 4;          // MFMA k (B row / A column) and D row block
+    const int row = lane & 15;          // MFMA A row i = 4 s_local + m, B/D column
+    const int m_row = row & 3;
+    const int s_loc = row >> 2;
+    const bool neg = (kNegMask >> (4 * m_row + grp)) & 1u;
+    const int a_off = 4 * s_loc + (m_row ^ grp);
+
+    float A[NT_REG > 0 ? NT_REG : 1];
+    if constexpr (NT_REG > 0) {
+#pragma unroll
+        for (int t = 0; t < NT_REG; ++t) {
+            const float v = sq[16 * t + a_off];
+            A[t] = neg ? -v : v;
+        }
+    }
+
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int tpg = 64 / a.cpt;
+    const int wpg = tpg * a.words;
+
+    for (int64_t g0 = c_begin + 64 * wave; g0 < c_end; g0 += 64 * 4) {
+        const int64_t c = g0 + lane;
+        const bool valid = c < c_end;
+        const int64_t gc = slice * a.n_slice + c;
+
+        float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
+        if (valid) {
+            if constexpr (F32IN) {
+                const float4 f = static_cast<const float4 *>(a.x)[gc];
+                v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
+            } else {
+                const uint2 r = static_cast<const uint2 *>(a.x)[gc];
+                v0 = f16_bits_to_f32(static_cast<uint16_t>(r.x));
+                v1 = f16_bits_to_f32(static_cast<uint16_t>(r.x >> 16));
+                v2 = f16_bits_to_f32(static_cast<uint16_t>(r.y));
+                v3 = f16_bits_to_f32(static_cast<uint16_t>(r.y >> 16));
+            }
+        }
+
+        // declared fp32 squared norm and its binary16 half-norm code
+        float s2 = v0 * v0;
+        s2 = __builtin_fmaf(v1, v1, s2);
+        s2 = __builtin_fmaf(v2, v2, s2);
+        s2 = __builtin_fmaf(v3, v3, s2);
+        const uint16_t hn = f32_to_f16_bits(sqrt_rn(s2) * 0.5f);
+
+        // exact power-of-two normalisation for the search (argmax is
+        // scale-invariant; keeps every product far from the denormal range)
+        const float mx = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
+        const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+        const float x0 = __builtin_ldexpf(v0, -ex), x1 = __builtin_ldexpf(v1, -ex);
+        const float x2 = __builtin_ldexpf(v2, -ex), x3 = __builtin_ldexpf(v3, -ex);
+        *reinterpret_cast<float4 *>(&sx[wave][4 * lane]) = make_float4(x0, x1, x2, x3);
+        wave_sync();
+
+        float bsc[4];
+        int bsi[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float bv = sx[wave][4 * (16 * b + row) + grp];
+            float best = -1.0f;
+            int bt = 0;
+            if constexpr (NT_REG > 0) {
+#pragma unroll
+                for (int t = 0; t < NT_REG; ++t) {
+                    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(A[t], bv, zero, 0, 0, 0);
+                    const float e0 = fabsf(d[0]), e1 = fabsf(d[1]), e2 = fabsf(d[2]), e3 = fabsf(d[3]);
+                    const float linf = fmaxf(fmaxf(e0, e1), fmaxf(e2, e3));
+                    const float l1 = (e0 + e1) + (e2 + e3);
+                    const float sc = fmaxf(linf + linf, l1);
+                    if (sc > best) { best = sc; bt = t; }
+                }
+            } else {
+                for (int t = 0; t < NT; ++t) {
+                    const float v = sq[16 * t + a_off];
+                    const float at = neg ? -v : v;
+                    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(at, bv, zero, 0, 0, 0);
+                    const float e0 = fabsf(d[0]), e1 = fabsf(d[1]), e2 = fabsf(d[2]), e3 = fabsf(d[3]);
+                    const float linf = fmaxf(fmaxf(e0, e1), fmaxf(e2, e3));
+                    const float l1 = (e0 + e1) + (e2 + e3);
+                    const float sc = fmaxf(linf + linf, l1);
+                    if (sc > best) { best = sc; bt = t; }
+                }
+            }
+            bsc[b] = best;
+            bsi[b] = 4 * bt + grp;
+        }
+
+        // Transposed reduction over the 4 lane groups: afterwards lane l holds
+        // the best (score, s) of chunk g0 + l over all S.
+        float m1s[2];
+        int m1i[2];
+        const bool h1 = (lane >> 5) & 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float ss = h1 ? bsc[j] : bsc[2 + j];
+            const int si = h1 ? bsi[j] : bsi[2 + j];
+            float ks = h1 ? bsc[2 + j] : bsc[j];
+            int ki = h1 ? bsi[2 + j] : bsi[j];
+            const float rs = __shfl_xor(ss, 32);
+            const int ri = __shfl_xor(si, 32);
+            if (better(rs, ri, ks, ki)) { ks = rs; ki = ri; }
+            m1s[j] = ks;
+            m1i[j] = ki;
+        }
+        const bool h0 = (lane >> 4) & 1;
+        int s_best;
+        {
+            const float ss = h0 ? m1s[0] : m1s[1];
+            const int si = h0 ? m1i[0] : m1i[1];
+            float ks = h0 ? m1s[1] : m1s[0];
+            int ki = h0 ? m1i[1] : m1i[0];
+            const float rs = __shfl_xor(ss, 16);
+            const int ri = __shfl_xor(si, 16);
+            if (better(rs, ri, ks, ki)) { ks = rs; ki = ri; }
+            s_best = min(ki, 4 * NT - 1);
+        }
+
+        // Primary index from the winning s: t = (<x, e_m q_s>)_m in fp32.
+        const float *qs = &sq[4 * s_best];
+        const float q0 = qs[0], q1 = qs[1], q2 = qs[2], q3 = qs[3];
+        const float t0 = __builtin_fmaf(q3, x3, __builtin_fmaf(q2, x2, __builtin_fmaf(q1, x1, q0 * x0)));
+        const float t1 = __builtin_fmaf(q2, x3, __builtin_fmaf(-q3, x2, __builtin_fmaf(q0, x1, -q1 * x0)));
+        const float t2 = __builtin_fmaf(-q1, x3, __builtin_fmaf(q0, x2, __builtin_fmaf(q3, x1, -q2 * x0)));
+        const float t3 = __builtin_fmaf(q0, x3, __builtin_fmaf(q1, x2, __builtin_fmaf(-q2, x1, -q3 * x0)));
+        const float e0 = fabsf(t0), e1 = fabsf(t1), e2 = fabsf(t2), e3 = fabsf(t3);
+        float linf = e0;
+        int mi = 0;
+        float tm = t0;
+        if (e1 > linf) { linf = e1; mi = 1; tm = t1; }
+        if (e2 > linf) { linf = e2; mi = 2; tm = t2; }
+        if (e3 > linf) { linf = e3; mi = 3; tm = t3; }
+        const float l1 = (e0 + e1) + (e2 + e3);
+        int p;
+        if (linf + linf >= l1) {
+            p = 2 * mi + (tm < 0.0f ? 1 : 0);
+        } else {
+            p = 8 + (t0 < 0.0f ? 1 : 0) + (t1 < 0.0f ? 2 : 0) + (t2 < 0.0f ? 4 : 0) + (t3 < 0.0f ? 8 : 0);
+        }
+        const uint32_t code = s2 > 0.0f ? static_cast<uint32_t>(24 * s_best + p) : 0u;
+
+        if (valid) {
+            a.hnorm[gc] = hn;
+            if constexpr (WITH_S2) a.s2[gc] = s2;
+        }
+        scode[wave][lane] = code;
+        wave_sync();
+
+        // pack the codes of the group's token rows into 32-bit words
+        if (lane < wpg) {
+            const int tt = lane / a.words;
+            const int ww = lane - tt * a.words;
+            const int64_t tok = g0 / a.cpt + tt;
+            if (tok * a.cpt < c_end) {
+                const int lo = 32 * ww;
+                const int cf = lo / a.bits;
+                const int cl = min(a.cpt - 1, (lo + 31) / a.bits);
+                uint32_t word = 0;
+                for (int cc = cf; cc <= cl; ++cc) {
+                    const uint32_t v = scode[wave][tt * a.cpt + cc];
+                    const int sh = cc * a.bits - lo;
+                    word |= sh >= 0 ? (v << sh) : (v >> (-sh));
+                }
+                a.idx[(slice * a.tokens + tok) * a.words + ww] = word;
+            }
+        }
+        wave_sync();
+    }
+}
+
+// --------------------------------------------------------------------------
+// Block-wide exclusive scan (all threads of the block must call it).
+// --------------------------------------------------------------------------
+template <typename T, int NTHREADS>
+__device__ __forceinline__ T block_exclusive_scan(T v, T *total, T *sh) {
+    constexpr int kWaves = NTHREADS / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    T incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const T o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        T run = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const T t = sh[w];
+            sh[w] = run;
+            run += t;
+        }
+        sh[kWaves] = run;
+    }
+    __syncthreads();
+    const T res = sh[wave] + incl - v;
+    *total = sh[kWaves];
+    __syncthreads();
+    return res;
+}
+
+// --------------------------------------------------------------------------
+// Med3x: exact lower median of s2 per batch (three radix digits of the fp32
+// bit pattern: non-negative floats order like their bits), threshold
+// fl(fl(C*C) * median) and the count of s2 > threshold.
+// --------------------------------------------------------------------------
+struct MedArgs {
+    const float *s2;
+    float *thr;
+    uint32_t *counts;
+    int64_t n_slice;
+    int64_t batch_chunks;
+    int64_t bps;
+    float C;
+};
+
+__global__ __launch_bounds__(kMedThreads) void med3_select_kernel(MedArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t sh[kMedThreads / 64 + 1];
+    __shared__ uint32_t found[2];
+
+    const int64_t bid = blockIdx.x;
+    const int64_t slice = bid / a.bps;
+    const int64_t lo = (bid - slice * a.bps) * a.batch_chunks;
+    const int64_t n = min(a.batch_chunks, a.n_slice - lo);
+    const uint32_t *keys = reinterpret_cast<const uint32_t *>(a.s2 + slice * a.n_slice + lo);
+
+    uint32_t k = static_cast<uint32_t>((n - 1) / 2);
+    uint32_t prefix = 0;
+    const int shifts[3] = {20, 9, 0};
+    const int widths[3] = {11, 11, 9};
+    for (int d = 0; d < 3; ++d) {
+        const int shift = shifts[d];
+        const int width = widths[d];
+        const int nbins = 1 << width;
+        const uint32_t dmask = static_cast<uint32_t>(nbins - 1);
+        const int above = shift + width;
+        for (int i = threadIdx.x; i < nbins; i += kMedThreads) hist[i] = 0;
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < n; i += kMedThreads) {
+            const uint32_t key = keys[i];
+            if ((key >> above) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        const int per = nbins / kMedThreads;
+        uint32_t local = 0;
+        for (int j = 0; j < per; ++j) local += hist[threadIdx.x * per + j];
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan<uint32_t, kMedThreads>(local, &tot, sh);
+        if (k >= ex && k < ex + local) {
+            uint32_t cum = ex;
+            for (int j = 0; j < per; ++j) {
+                const uint32_t h = hist[threadIdx.x * per + j];
+                if (k < cum + h) {
+                    found[0] = static_cast<uint32_t>(threadIdx.x * per + j);
+                    found[1] = k - cum;
+                    break;
+                }
+                cum += h;
+            }
+        }
+        __syncthreads();
+        prefix = (prefix << width) | found[0];
+        k = found[1];
+        __syncthreads();
+    }
+    const float med = __uint_as_float(prefix);
+    const float cc = a.C * a.C;
+    const float thr = cc * med;
+    uint32_t cnt = 0;
+    for (int64_t i = threadIdx.x; i < n; i += kMedThreads) cnt += __uint_as_float(keys[i]) > thr ? 1u : 0u;
+    uint32_t tot;
+    block_exclusive_scan<uint32_t, kMedThreads>(cnt, &tot, sh);
+    if (threadIdx.x == 0) {
+        a.thr[bid] = thr;
+        a.counts[bid] = tot;
+    }
+}
+
+__global__ __launch_bounds__(kScanThreads) void med3_scan_kernel(int64_t nb, const uint32_t *counts,
+                                                                 uint64_t *offsets, uint64_t capacity,
+                                                                 uint64_t *status) {
+    __shared__ uint64_t sh[kScanThreads / 64 + 1];
+    uint64_t carry = 0;
+    for (int64_t base = 0; base < nb; base += kScanThreads) {
+        const int64_t i = base + threadIdx.x;
+        const uint64_t v = i < nb ? counts[i] : 0;
+        uint64_t tot;
+        const uint64_t ex = block_exclusive_scan<uint64_t, kScanThreads>(v, &tot, sh);
+        if (i < nb) offsets[i] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) {
+        offsets[nb] = carry;
+        if (status) {
+            status[0] = carry;
+            status[1] = carry > capacity ? 1u : 0u;
+        }
+    }
+}
+
+struct FlagArgs {
+    const void *x;
+    const float *s2;
+    const float *thr;
+    const uint64_t *offsets;
+    uint16_t *hnorm;
+    uint32_t *out_pos;
+    uint16_t *out_val;
+    uint64_t capacity;
+    int64_t n_slice;
+    int64_t batch_chunks;
+    int64_t bps;
+    int32_t f32;
+};
+
+// Ordered outlier write: one block per batch walks the batch in order, a
+// block scan gives every outlier its rank, and the entry lands at
+// batch_offsets[batch] + rank (dropped past the capacity).
+__global__ __launch_bounds__(kFlagThreads) void med3_flag_kernel(FlagArgs a) {
+    __shared__ uint32_t sh[kFlagThreads / 64 + 1];
+    const int64_t bid = blockIdx.x;
+    const int64_t slice = bid / a.bps;
+    const int64_t lo = (bid - slice * a.bps) * a.batch_chunks;
+    const int64_t n = min(a.batch_chunks, a.n_slice - lo);
+    const int64_t sbase = slice * a.n_slice;
+    const float thr = a.thr[bid];
+    const uint64_t base = a.offsets[bid];
+    const float *keys = a.s2 + sbase + lo;
+
+    uint64_t running = 0;
+    for (int64_t off = 0; off < n; off += 4 * kFlagThreads) {
+        const int64_t i0 = off + 4 * threadIdx.x;
+        bool f[4];
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = (i0 + e < n) && keys[i0 + e] > thr;
+            cnt += f[e] ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan<uint32_t, kFlagThreads>(cnt, &tot, sh);
+        uint64_t pos = base + running + ex;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (!f[e]) continue;
+            const int64_t cs = lo + i0 + e;       // chunk position in the slice
+            const int64_t gc = sbase + cs;
+            if (pos < a.capacity) {
+                a.out_pos[pos] = static_cast<uint32_t>(cs);
+                uint2 v;
+                if (a.f32) {
+                    const float4 xf = static_cast<const float4 *>(a.x)[gc];
+                    v.x = static_cast<uint32_t>(f32_to_f16_bits(xf.x)) | (static_cast<uint32_t>(f32_to_f16_bits(xf.y)) << 16);
+                    v.y = static_cast<uint32_t>(f32_to_f16_bits(xf.z)) | (static_cast<uint32_t>(f32_to_f16_bits(xf.w)) << 16);
+                } else {
+                    v = static_cast<const uint2 *>(a.x)[gc];
+                }
+                reinterpret_cast<uint2 *>(a.out_val)[pos] = v;
+            }
+            a.hnorm[gc] = static_cast<uint16_t>(a.hnorm[gc] | 0x8000u);
+            ++pos;
+        }
+        running += tot;
+    }
+}
+
+__global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// --------------------------------------------------------------------------
+// Decode kernel: one block per contiguous chunk range of one slice.
+// --------------------------------------------------------------------------
+struct DecArgs {
+    const uint32_t *idx;
+    const uint16_t *hnorm;
+    const uint64_t *offsets;
+    const uint32_t *out_pos;
+    const uint16_t *out_val;
+    uint64_t capacity;
+    const float *cb;
+    void *y;
+    int64_t n_slice;
+    int64_t tokens;
+    int64_t wg_per_slice;
+    int64_t wg_chunks;
+    int64_t batch_chunks;
+    int64_t bps;
+    int32_t S;
+    int32_t cpt;
+    int32_t bits;
+    int32_t words;
+};
+
+// Codeword a_p * q_s in fp32 from the four rows e_m * q_s.
+__device__ __forceinline__ f32x4 codeword_f32(const float *q, int p) {
+    f32x4 c;
+    if (p < 8) {
+        const int m = p >> 1;
+        const bool ng = p & 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float v = unit_row(q, m, k);
+            c[k] = ng ? -v : v;
+        }
+    } else {
+        const int bits = p - 8;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float r[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float v = unit_row(q, m, k);
+                r[m] = ((bits >> m) & 1) ? -v : v;
+            }
+            c[k] = ((r[0] + r[1]) + (r[2] + r[3])) * 0.5f;
+        }
+    }
+    return c;
+}
+
+template <bool F32OUT>
+__device__ __forceinline__ void store_chunk(void *y, int64_t gc, f32x4 v) {
+    if constexpr (F32OUT) {
+        reinterpret_cast<float4 *>(y)[gc] = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+        uint2 o;
+        o.x = static_cast<uint32_t>(f32_to_f16_bits(v[0])) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
+        o.y = static_cast<uint32_t>(f32_to_f16_bits(v[2])) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
+        reinterpret_cast<uint2 *>(y)[gc] = o;
+    }
+}
+
+template <bool F32OUT, bool TABLE>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
+    __shared__ f32x4 tab[TABLE ? 24 * kTableMaxS : kMaxS];
+    const int64_t slice = blockIdx.x / a.wg_per_slice;
+    const int64_t r0 = (blockIdx.x - slice * a.wg_per_slice) * a.wg_chunks;
+    const int64_t r1 = min(r0 + a.wg_chunks, a.n_slice);
+    const int64_t sbase = slice * a.n_slice;
+    const float *q = a.cb + slice * a.S * 4;
+    const int ncw = 24 * a.S;
+
+    if constexpr (TABLE) {
+        for (int k = threadIdx.x; k < ncw; k += kDecThreads) {
+            const int s = k / 24;
+            tab[k] = codeword_f32(q + 4 * s, k - 24 * s);
+        }
+    } else {
+        for (int s = threadIdx.x; s < a.S; s += kDecThreads) {
+            f32x4 v = {q[4 * s], q[4 * s + 1], q[4 * s + 2], q[4 * s + 3]};
+            tab[s] = v;
+        }
+    }
+    __syncthreads();
+
+    const uint32_t cmask = (1u << a.bits) - 1u;
+    for (int64_t c = r0 + 4 * threadIdx.x; c < r1; c += 4 * kDecThreads) {
+        const int64_t tok = c / a.cpt;
+        const int j = static_cast<int>(c - tok * a.cpt);
+        const uint32_t *rowp = a.idx + (sbase / a.cpt + tok) * a.words;
+        const int o = j * a.bits;
+        const int w0 = o >> 5;
+        const int sh = o & 31;
+        uint64_t win = rowp[w0];
+        if (w0 + 1 < a.words) win |= static_cast<uint64_t>(rowp[w0 + 1]) << 32;
+        win >>= sh;
+        if (sh + 4 * a.bits > 64) win |= static_cast<uint64_t>(rowp[w0 + 2]) << (64 - sh);
+        const uint2 hr = *reinterpret_cast<const uint2 *>(a.hnorm + sbase + c);
+        const uint16_t h[4] = {static_cast<uint16_t>(hr.x), static_cast<uint16_t>(hr.x >> 16),
+                               static_cast<uint16_t>(hr.y), static_cast<uint16_t>(hr.y >> 16)};
+        f32x4 out[4];
+        bool flagged = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t k = static_cast<uint32_t>(win >> (i * a.bits)) & cmask;
+            k = min(k, static_cast<uint32_t>(ncw - 1));
+            flagged |= (h[i] & 0x8000u) != 0;
+            const float r = 2.0f * f16_bits_to_f32(static_cast<uint16_t>(h[i] & 0x7FFFu));
+            f32x4 cw;
+            if constexpr (TABLE) {
+                cw = tab[k];
+            } else {
+                const int s = static_cast<int>(k / 24u);
+                const f32x4 qv = tab[s];
+                const float qa[4] = {qv[0], qv[1], qv[2], qv[3]};
+                cw = codeword_f32(qa, static_cast<int>(k) - 24 * s);
+            }
+            out[i] = r * cw;
+        }
+        const int64_t gc = sbase + c;
+        if (!flagged) {
+            if constexpr (F32OUT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) store_chunk<true>(a.y, gc + i, out[i]);
+            } else {
+                uint4 o0, o1;
+                o0.x = static_cast<uint32_t>(f32_to_f16_bits(out[0][0])) | (static_cast<uint32_t>(f32_to_f16_bits(out[0][1])) << 16);
+                o0.y = static_cast<uint32_t>(f32_to_f16_bits(out[0][2])) | (static_cast<uint32_t>(f32_to_f16_bits(out[0][3])) << 16);
+                o0.z = static_cast<uint32_t>(f32_to_f16_bits(out[1][0])) | (static_cast<uint32_t>(f32_to_f16_bits(out[1][1])) << 16);
+                o0.w = static_cast<uint32_t>(f32_to_f16_bits(out[1][2])) | (static_cast<uint32_t>(f32_to_f16_bits(out[1][3])) << 16);
+                o1.x = static_cast<uint32_t>(f32_to_f16_bits(out[2][0])) | (static_cast<uint32_t>(f32_to_f16_bits(out[2][1])) << 16);
+                o1.y = static_cast<uint32_t>(f32_to_f16_bits(out[2][2])) | (static_cast<uint32_t>(f32_to_f16_bits(out[2][3])) << 16);
+                o1.z = static_cast<uint32_t>(f32_to_f16_bits(out[3][0])) | (static_cast<uint32_t>(f32_to_f16_bits(out[3][1])) << 16);
+                o1.w = static_cast<uint32_t>(f32_to_f16_bits(out[3][2])) | (static_cast<uint32_t>(f32_to_f16_bits(out[3][3])) << 16);
+                uint4 *yp = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + 4 * gc);
+                yp[0] = o0;
+                yp[1] = o1;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!(h[i] & 0x8000u)) store_chunk<F32OUT>(a.y, gc + i, out[i]);
+        }
+    }
+
+    if (a.bps > 0) {
+        // side-list entries of [r0, r1): the batches covering the range give
+        // an index window; a 256-way search finds the first position >= r0.
+        const int64_t bl = r0 / a.batch_chunks;
+        const int64_t bh = (r1 - 1) / a.batch_chunks;
+        uint64_t e1 = a.offsets[slice * a.bps + bh + 1];
+        uint64_t lo = a.offsets[slice * a.bps + bl];
+        e1 = e1 < a.capacity ? e1 : a.capacity;
+        lo = lo < e1 ? lo : e1;
+        uint64_t hi = e1;
+        while (hi > lo) {
+            const uint64_t len = hi - lo;
+            const uint64_t step = (len + kDecThreads - 1) / kDecThreads;
+            const uint64_t i = lo + static_cast<uint64_t>(threadIdx.x) * step;
+            const bool below = i < hi && static_cast<int64_t>(a.out_pos[i]) < r0;
+            const int cnt = __syncthreads_count(below);
+            if (cnt == 0) break;
+            const uint64_t nlo = lo + static_cast<uint64_t>(cnt - 1) * step + 1;
+            const uint64_t nhi_c = lo + static_cast<uint64_t>(cnt) * step;
+            hi = nhi_c < hi ? nhi_c : hi;
+            lo = nlo;
+        }
+        for (uint64_t e = lo + threadIdx.x; e < e1; e += kDecThreads) {
+            const int64_t p = a.out_pos[e];
+            if (p >= r1) break;
+            const uint2 v = reinterpret_cast<const uint2 *>(a.out_val)[e];
+            if constexpr (F32OUT) {
+                f32x4 f = {f16_bits_to_f32(static_cast<uint16_t>(v.x)), f16_bits_to_f32(static_cast<uint16_t>(v.x >> 16)),
+                           f16_bits_to_f32(static_cast<uint16_t>(v.y)), f16_bits_to_f32(static_cast<uint16_t>(v.y >> 16))};
+                store_chunk<true>(a.y, sbase + p, f);
+            } else {
+                reinterpret_cast<uint2 *>(a.y)[sbase + p] = v;
+            }
+        }
+    }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+// Launchers.
+// --------------------------------------------------------------------------
+hipError_t launch_encode_search(const Geometry &g, const void *x, const float *codebook,
+                                uint32_t *idx, uint16_t *hnorm, float *s2, hipStream_t st) {
+    const int64_t total = g.slices * g.n_slice;
+    if (total == 0) return hipSuccess;
+    // tiles: multiples of 256 chunks (4 waves x 64), enough blocks to fill
+    // 256 CUs several times, at most 8192 chunks so a block's codebook setup
+    // stays amortised
+    int64_t tile = round_up(ceil_div(total, 4096), 256);
+    tile = tile < 256 ? 256 : (tile > 8192 ? 8192 : tile);
+    EncArgs a;
+    a.x = x;
+    a.cb = codebook;
+    a.idx = idx;
+    a.hnorm = hnorm;
+    a.s2 = s2;
+    a.n_slice = g.n_slice;
+    a.tiles_per_slice = ceil_div(g.n_slice, tile);
+    a.tokens = g.tokens;
+    a.tile_chunks = static_cast<int32_t>(tile);
+    a.S = g.S;
+    a.NT = static_cast<int32_t>(ceil_div(g.S, 4));
+    a.cpt = g.cpt;
+    a.bits = g.bits;
+    a.words = g.words;
+    const dim3 grid(static_cast<unsigned>(g.slices * a.tiles_per_slice));
+    const dim3 block(kEncThreads);
+    const bool ws2 = s2 != nullptr;
+#define HQMQ_ENC(NT, F32, WS2) hipLaunchKernelGGL((encode_search_kernel<NT, F32, WS2>), grid, block, 0, st, a)
+#define HQMQ_ENC_NT(NT)                          \
+    do {                                         \
+        if (g.f32) {                             \
+            if (ws2) HQMQ_ENC(NT, true, true);   \
+            else HQMQ_ENC(NT, true, false);      \
+        } else {                                 \
+            if (ws2) HQMQ_ENC(NT, false, true);  \
+            else HQMQ_ENC(NT, false, false);     \
+        }                                        \
+    } while (0)
+    if (a.NT == 2) HQMQ_ENC_NT(2);
+    else if (a.NT == 8) HQMQ_ENC_NT(8);
+    else HQMQ_ENC_NT(0);
+#undef HQMQ_ENC_NT
+#undef HQMQ_ENC
+    return hipGetLastError();
+}
+
+hipError_t launch_med3_select(const Geometry &g, const float *s2, float *thr, uint32_t *counts,
+                              hipStream_t st) {
+    const int64_t nb = g.slices * g.batches_per_slice;
+    if (nb == 0) return hipSuccess;
+    MedArgs a;
+    a.s2 = s2;
+    a.thr = thr;
+    a.counts = counts;
+    a.n_slice = g.n_slice;
+    a.batch_chunks = g.batch_chunks;
+    a.bps = g.batches_per_slice;
+    a.C = g.med_C;
+    hipLaunchKernelGGL(med3_select_kernel, dim3(static_cast<unsigned>(nb)), dim3(kMedThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_med3_scan(int64_t batches, const uint32_t *counts, uint64_t *offsets,
+                            uint64_t capacity, uint64_t *status, hipStream_t st) {
+    hipLaunchKernelGGL(med3_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, batches, counts, offsets,
+                       capacity, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_med3_flag(const Geometry &g, const void *x, const float *s2, const float *thr,
+                            const uint64_t *offsets, uint16_t *hnorm, uint32_t *out_pos,
+                            uint16_t *out_val, uint64_t capacity, hipStream_t st) {
+    const int64_t nb = g.slices * g.batches_per_slice;
+    if (nb == 0) return hipSuccess;
+    FlagArgs a;
+    a.x = x;
+    a.s2 = s2;
+    a.thr = thr;
+    a.offsets = offsets;
+    a.hnorm = hnorm;
+    a.out_pos = out_pos;
+    a.out_val = out_val;
+    a.capacity = capacity;
+    a.n_slice = g.n_slice;
+    a.batch_chunks = g.batch_chunks;
+    a.bps = g.batches_per_slice;
+    a.f32 = g.f32;
+    hipLaunchKernelGGL(med3_flag_kernel, dim3(static_cast<unsigned>(nb)), dim3(kFlagThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t *hnorm,
+                         const uint64_t *offsets, const uint32_t *out_pos, const uint16_t *out_val,
+                         uint64_t capacity, const float *codebook, void *y, hipStream_t st) {
+    const int64_t total = g.slices * g.n_slice;
+    if (total == 0) return hipSuccess;
+    int64_t wgc = round_up(ceil_div(total, 4096), 4 * kDecThreads);
+    wgc = wgc < 4 * kDecThreads ? 4 * kDecThreads : (wgc > 16384 ? 16384 : wgc);
+    DecArgs a;
+    a.idx = idx;
+    a.hnorm = hnorm;
+    a.offsets = offsets;
+    a.out_pos = out_pos;
+    a.out_val = out_val;
+    a.capacity = capacity;
+    a.cb = codebook;
+    a.y = y;
+    a.n_slice = g.n_slice;
+    a.tokens = g.tokens;
+    a.wg_chunks = wgc;
+    a.wg_per_slice = ceil_div(g.n_slice, wgc);
+    a.batch_chunks = g.batch_chunks;
+    a.bps = g.batch_chunks > 0 ? g.batches_per_slice : 0;
+    a.S = g.S;
+    a.cpt = g.cpt;
+    a.bits = g.bits;
+    a.words = g.words;
+    const dim3 grid(static_cast<unsigned>(g.slices * a.wg_per_slice));
+    const dim3 block(kDecThreads);
+    const bool table = g.S <= kTableMaxS;
+    if (g.f32) {
+        if (table) hipLaunchKernelGGL((decode_kernel<true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, 0, st, a);
+    } else {
+        if (table) hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hqmq

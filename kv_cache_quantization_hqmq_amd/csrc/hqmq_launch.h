@@ -1,0 +1,55 @@
+// Internal launch interface between the C-ABI host code (hqmq_api.cpp) and
+// the gfx950 kernels (hqmq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace hqmq {
+
+// Shape of one call after validation.
+struct Geometry {
+    int64_t slices;          // layers * kv_heads
+    int64_t tokens;          // tokens per slice
+    int64_t n_slice;         // chunks per slice = tokens * cpt
+    int32_t cpt;             // chunks per token = head_dim / 4
+    int32_t S;               // secondary codewords per slice
+    int32_t bits;            // code width b
+    int32_t words;           // u32 words per token row
+    int32_t f32;             // 1: fp32 x / y, 0: fp16
+    int64_t batch_chunks;    // Med3x batch length in chunks (0 = off)
+    int64_t batches_per_slice;
+    float med_C;
+};
+
+// Encode: nearest codeword, norm code and (when s2 != nullptr) the fp32
+// squared norms for Med3x.
+hipError_t launch_encode_search(const Geometry &g, const void *x, const float *codebook,
+                                uint32_t *idx, uint16_t *hnorm, float *s2, hipStream_t st);
+
+// Med3x: per-batch exact lower median, threshold and outlier count.
+hipError_t launch_med3_select(const Geometry &g, const float *s2, float *thr, uint32_t *counts,
+                              hipStream_t st);
+
+// Exclusive scan of the per-batch counts into batch_offsets, total and
+// overflow flag into status.
+hipError_t launch_med3_scan(int64_t batches, const uint32_t *counts, uint64_t *offsets,
+                            uint64_t capacity, uint64_t *status, hipStream_t st);
+
+// Ordered side-list write and hnorm flagging.
+hipError_t launch_med3_flag(const Geometry &g, const void *x, const float *s2, const float *thr,
+                            const uint64_t *offsets, uint16_t *hnorm, uint32_t *out_pos,
+                            uint16_t *out_val, uint64_t capacity, hipStream_t st);
+
+// Zero a few u64 words (status / offsets of empty or Med3x-off calls) with a
+// kernel rather than a memset node.
+hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t st);
+
+// Decode: bulk gather-multiply plus outlier re-insertion.
+hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t *hnorm,
+                         const uint64_t *offsets, const uint32_t *out_pos, const uint16_t *out_val,
+                         uint64_t capacity, const float *codebook, void *y, hipStream_t st);
+
+}  // namespace hqmq

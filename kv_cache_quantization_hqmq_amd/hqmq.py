@@ -1,0 +1,235 @@
+"""ctypes binding of the HQMQ C ABI (include/hqmq.h).
+
+Argument marshalling only: every step of the codec runs in the HIP kernels of
+libhqmq.so.  PyTorch supplies device memory (``tensor.data_ptr()``) and the
+stream (``torch.cuda.current_stream().cuda_stream``).  The functions keep the
+C names; ``Desc``/``Records`` are the C structs, and ``allocate_records`` /
+``workspace`` size torch buffers from ``hqmq_sizes``.
+
+There is no fallback: if libhqmq.so is missing or no GPU is visible, calls
+that need the device raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhqmq.so")
+
+HQMQ_OK, HQMQ_EINVAL, HQMQ_ENOTSUP, HQMQ_ECAPACITY, HQMQ_EHIP = 0, -1, -2, -3, -4
+HQMQ_F16, HQMQ_F32 = 0, 1
+HQMQ_ROLE_K, HQMQ_ROLE_V = 0, 1
+
+# every symbol include/hqmq.h declares
+EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
+           "hqmq_encode_result", "hqmq_decode")
+
+
+class HQMQError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {hqmq_strerror(code)} ({code})")
+        self.code = code
+
+
+class CapacityError(HQMQError):
+    def __init__(self, needed: int):
+        super().__init__(HQMQ_ECAPACITY, "hqmq_encode_result")
+        self.needed = needed
+
+
+class Desc(ctypes.Structure):
+    """hqmq_desc."""
+    _fields_ = [("layers", ctypes.c_int64), ("kv_heads", ctypes.c_int64),
+                ("tokens", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("S", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("med_batch_tokens", ctypes.c_int64), ("med_C", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+    @classmethod
+    def make(cls, layers, kv_heads, tokens, head_dim, S, dtype=HQMQ_F16,
+             med_batch_tokens=0, med_C=3.0) -> "Desc":
+        return cls(layers, kv_heads, tokens, head_dim, S, dtype, med_batch_tokens, med_C, 0)
+
+    @property
+    def shape(self):
+        return (self.layers, self.kv_heads, self.tokens, self.head_dim)
+
+
+class Sizes(ctypes.Structure):
+    """hqmq_sizes_t."""
+    _fields_ = [("code_bits", ctypes.c_int32), ("words_per_token", ctypes.c_int32),
+                ("chunks", ctypes.c_int64), ("batches", ctypes.c_int64),
+                ("max_outliers", ctypes.c_int64), ("input_bytes", ctypes.c_uint64),
+                ("idx_bytes", ctypes.c_uint64), ("hnorm_bytes", ctypes.c_uint64),
+                ("offsets_bytes", ctypes.c_uint64), ("side_entry_bytes", ctypes.c_uint64),
+                ("workspace_bytes", ctypes.c_uint64), ("codebook_bytes", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class Enc(ctypes.Structure):
+    """hqmq_enc (device pointers)."""
+    _fields_ = [("idx", ctypes.c_void_p), ("hnorm", ctypes.c_void_p),
+                ("batch_offsets", ctypes.c_void_p), ("out_pos", ctypes.c_void_p),
+                ("out_val", ctypes.c_void_p), ("out_capacity", ctypes.c_uint64),
+                ("status", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libhqmq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_quantization_hqmq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.hqmq_strerror.argtypes = [ctypes.c_int]
+        L.hqmq_strerror.restype = ctypes.c_char_p
+        L.hqmq_sizes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Sizes)]
+        L.hqmq_make_codebook.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_float)]
+        L.hqmq_encode.argtypes = [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.POINTER(Enc), ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]
+        L.hqmq_encode_result.argtypes = [ctypes.POINTER(Enc), ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_uint64)]
+        L.hqmq_decode.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Enc), ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+        for f in ("hqmq_sizes", "hqmq_make_codebook", "hqmq_encode", "hqmq_encode_result",
+                  "hqmq_decode"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str):
+    if rc != HQMQ_OK:
+        raise HQMQError(rc, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+# ------------------------------------------------------------------ C calls
+def hqmq_strerror(code: int) -> str:
+    return lib().hqmq_strerror(int(code)).decode()
+
+
+def hqmq_sizes(desc: Desc) -> Sizes:
+    out = Sizes()
+    _check(lib().hqmq_sizes(ctypes.byref(desc), ctypes.byref(out)), "hqmq_sizes")
+    return out
+
+
+def hqmq_make_codebook(seed: int, layers: int, kv_heads: int, role: int, S: int) -> np.ndarray:
+    """Host codebook [layers, kv_heads, S, 4] float32."""
+    out = np.empty((layers, kv_heads, S, 4), np.float32)
+    _check(lib().hqmq_make_codebook(seed, layers, kv_heads, role, S,
+                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))),
+           "hqmq_make_codebook")
+    return out
+
+
+def hqmq_encode(desc: Desc, x, codebook, rec: "Records", workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().hqmq_encode(ctypes.byref(desc), _ptr(x), _ptr(codebook), ctypes.byref(rec.c),
+                           _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "hqmq_encode")
+
+
+def hqmq_encode_result(rec: "Records", stream=None) -> int:
+    n = ctypes.c_uint64(0)
+    rc = lib().hqmq_encode_result(ctypes.byref(rec.c), _stream(stream), ctypes.byref(n))
+    if rc == HQMQ_ECAPACITY:
+        raise CapacityError(int(n.value))
+    _check(rc, "hqmq_encode_result")
+    return int(n.value)
+
+
+def hqmq_decode(desc: Desc, rec: "Records", codebook, y, stream=None) -> None:
+    rc = lib().hqmq_decode(ctypes.byref(desc), ctypes.byref(rec.c), _ptr(codebook), _ptr(y),
+                           _stream(stream))
+    _check(rc, "hqmq_decode")
+
+
+# ------------------------------------------------------------------ buffers
+@dataclass
+class Records:
+    """Torch buffers of one encoded tensor plus the C struct pointing at them."""
+    idx: object
+    hnorm: object
+    batch_offsets: object
+    out_pos: object
+    out_val: object
+    status: object
+    capacity: int
+    c: Enc
+
+
+def allocate_records(desc: Desc, capacity: int | None = None, device="cuda") -> Records:
+    """Device buffers for ``desc``; ``capacity`` side-list entries (default:
+    the worst case floor(n/2) per batch, capped at 1/8 of the chunks)."""
+    import torch
+    sz = hqmq_sizes(desc)
+    T, W, cpt = desc.tokens, sz.words_per_token, desc.head_dim // 4
+    L, H = desc.layers, desc.kv_heads
+    idx = torch.empty((L, H, T, W), dtype=torch.int32, device=device)
+    hnorm = torch.empty((L, H, T, cpt), dtype=torch.int16, device=device)
+    med = desc.med_batch_tokens > 0
+    if capacity is None:
+        capacity = min(sz.max_outliers, max(1, sz.chunks // 8)) if med else 0
+    capacity = int(capacity) if med else 0
+    offs = torch.empty((sz.batches + 1,), dtype=torch.int64, device=device) if med else None
+    pos = torch.empty((max(capacity, 1),), dtype=torch.int32, device=device) if med else None
+    val = torch.empty((max(capacity, 1), 4), dtype=torch.int16, device=device) if med else None
+    status = torch.zeros((2,), dtype=torch.int64, device=device)
+    c = Enc(_ptr(idx), _ptr(hnorm), _ptr(offs), _ptr(pos), _ptr(val), capacity, _ptr(status))
+    return Records(idx, hnorm, offs, pos, val, status, capacity, c)
+
+
+def workspace(desc: Desc, device="cuda"):
+    import torch
+    n = hqmq_sizes(desc).workspace_bytes
+    return torch.empty((max(int(n), 1),), dtype=torch.uint8, device=device) if n else None
+
+
+def encode(desc: Desc, x, codebook, capacity: int | None = None, ws=None, stream=None) -> Records:
+    """Encode ``x`` and wait for the outlier count; on side-list overflow,
+    re-allocate with the reported size and encode again."""
+    if ws is None:
+        ws = workspace(desc, x.device)
+    rec = allocate_records(desc, capacity, x.device)
+    hqmq_encode(desc, x, codebook, rec, ws, stream)
+    try:
+        rec.n_outliers = hqmq_encode_result(rec, stream)
+    except CapacityError as e:
+        rec = allocate_records(desc, e.needed, x.device)
+        hqmq_encode(desc, x, codebook, rec, ws, stream)
+        rec.n_outliers = hqmq_encode_result(rec, stream)
+    return rec
+
+
+def decode(desc: Desc, rec: Records, codebook, y=None, stream=None):
+    import torch
+    if y is None:
+        dt = torch.float32 if desc.dtype == HQMQ_F32 else torch.float16
+        y = torch.empty(desc.shape, dtype=dt, device=rec.idx.device)
+    hqmq_decode(desc, rec, codebook, y, stream)
+    return y

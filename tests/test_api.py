@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and
+exports every symbol include/hqmq.h declares, descriptors are validated
+before anything is enqueued, buffer sizes follow the record layout, and the
+codebook generator is bit-identical to the oracle's independent one."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import kv_cache_quantization_hqmq_amd as K
+from kv_cache_quantization_hqmq_amd import hqmq as B
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hqmq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hqmq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert declared == sorted(B.EXPORTS)
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Field offsets and sizes of the ctypes structs equal what a C compiler
+    makes of include/hqmq.h."""
+    structs = {"hqmq_desc": B.Desc, "hqmq_sizes_t": B.Sizes, "hqmq_enc": B.Enc}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hqmq.h"', "int main(void){"]
+    for cname, cls in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                  check=True).stdout.splitlines())
+    for cname, cls in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, -4, 7):
+        assert isinstance(K.hqmq_strerror(c), str) and K.hqmq_strerror(c)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("head_dim", 96), ("head_dim", 0), ("head_dim", 512), ("S", 0), ("S", 1025),
+    ("dtype", 2), ("layers", -1), ("tokens", -5), ("med_batch_tokens", -1)])
+def test_descriptor_validation(field, value):
+    d = K.Desc.make(2, 2, 64, 128, 8, K.HQMQ_F16, 16, 3.0)
+    setattr(d, field, value)
+    with pytest.raises(K.HQMQError) as e:
+        K.hqmq_sizes(d)
+    assert e.value.code == B.HQMQ_EINVAL
+
+
+def test_med_C_must_be_positive_when_med3_is_on():
+    d = K.Desc.make(1, 1, 64, 128, 8, K.HQMQ_F16, 16, 0.0)
+    with pytest.raises(K.HQMQError):
+        K.hqmq_sizes(d)
+    d.med_batch_tokens = 0
+    K.hqmq_sizes(d)   # ignored when Med3x is off
+
+
+def test_token_limit_for_u32_positions():
+    d = K.Desc.make(1, 1, 2 ** 27, 128, 8, K.HQMQ_F16, 0, 3.0)
+    with pytest.raises(K.HQMQError) as e:
+        K.hqmq_sizes(d)
+    assert e.value.code == B.HQMQ_ENOTSUP
+    d.tokens = 2 ** 27 - 1
+    K.hqmq_sizes(d)
+
+
+def test_encode_rejects_before_enqueueing():
+    """Validation errors come back synchronously; no device pointer is
+    touched (null pointers here), so this runs without a GPU."""
+    lib = B.lib()
+    d = K.Desc.make(1, 1, 64, 128, 8, K.HQMQ_F16, 0, 3.0)
+    enc = B.Enc()
+    assert lib.hqmq_encode(ctypes.byref(d), None, None, ctypes.byref(enc), None, 0, None) == B.HQMQ_EINVAL
+    assert lib.hqmq_decode(ctypes.byref(d), ctypes.byref(enc), None, None, None) == B.HQMQ_EINVAL
+    assert lib.hqmq_encode(None, None, None, ctypes.byref(enc), None, 0, None) == B.HQMQ_EINVAL
+    n = ctypes.c_uint64(5)
+    assert lib.hqmq_encode_result(None, None, ctypes.byref(n)) == B.HQMQ_EINVAL
+    # misaligned (but non-null) pointers
+    d.med_batch_tokens = 16
+    enc2 = B.Enc(16, 16, 16, 16, 16, 4, 16)
+    assert lib.hqmq_encode(ctypes.byref(d), ctypes.c_void_p(18), ctypes.c_void_p(16),
+                           ctypes.byref(enc2), ctypes.c_void_p(256), 1 << 20, None) == B.HQMQ_EINVAL
+    # workspace too small
+    assert lib.hqmq_encode(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                           ctypes.byref(enc2), ctypes.c_void_p(256), 16, None) == B.HQMQ_EINVAL
+
+
+@pytest.mark.parametrize("L,H,T,D,S,dt,Bt", [
+    (80, 8, 131072, 128, 32, 0, 4096), (32, 8, 32768, 128, 8, 0, 0), (1, 1, 4096, 128, 8, 1, 0),
+    (2, 3, 1001, 64, 13, 0, 256), (1, 1, 0, 128, 8, 0, 64)])
+def test_sizes_follow_the_layout(L, H, T, D, S, dt, Bt):
+    d = K.Desc.make(L, H, T, D, S, dt, Bt, 3.0)
+    s = K.hqmq_sizes(d)
+    cpt = D // 4
+    b = O.code_bits(S)
+    W = (b * cpt + 31) // 32
+    assert s.code_bits == b and s.words_per_token == W
+    assert s.chunks == L * H * T * cpt
+    assert s.idx_bytes == L * H * T * W * 4
+    assert s.hnorm_bytes == s.chunks * 2
+    assert s.input_bytes == s.chunks * 4 * (4 if dt == 1 else 2)
+    assert s.codebook_bytes == L * H * S * 16
+    if Bt > 0 and T > 0:
+        Bc = min(Bt, T)
+        nb = -(-T // Bc)
+        assert s.batches == L * H * nb
+        assert s.offsets_bytes == (s.batches + 1) * 8
+        per = [min(Bc, T - i * Bc) * cpt // 2 for i in range(nb)]
+        assert s.max_outliers == L * H * sum(per)
+        assert s.workspace_bytes >= s.chunks * 4 + s.batches * 8
+    else:
+        assert s.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("seed,L,H,role,S", [(0, 1, 1, 0, 8), (0, 3, 5, 1, 32), (12345, 2, 2, 0, 1024),
+                                             (2 ** 64 - 1, 1, 3, 1, 7)])
+def test_codebook_matches_oracle_bit_for_bit(seed, L, H, role, S):
+    a = K.hqmq_make_codebook(seed, L, H, role, S)
+    b = O.make_codebook(seed, L, H, role, S)
+    assert a.tobytes() == b.tobytes()
+
+
+def test_codebook_validation():
+    with pytest.raises(K.HQMQError):
+        K.hqmq_make_codebook(0, 1, 1, 2, 8)
+    with pytest.raises(K.HQMQError):
+        K.hqmq_make_codebook(0, 1, 1, 0, 0)

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Small shapes are compared element by element on every chunk; they span
+several encode tiles / decode blocks and end on a ragged tail (token counts
+that are not multiples of the tile, Med3x batches with a partial last batch),
+and cover both kernel families (S <= 32 register codebooks, larger S from
+LDS), fp16 and fp32 inputs and every supported head_dim.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_quantization_hqmq_amd as K
+import oracle as O
+import synth
+from tests import gpu_cases as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(shape, dtype, seed, scale=1.0):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device="cuda") * scale
+    return x.clamp(-65504, 65504).to(dtype)
+
+
+def _cb(L, H, S, role=0, seed=0):
+    host = K.hqmq_make_codebook(seed, L, H, role, S)
+    return host, torch.from_numpy(host).cuda()
+
+
+def _check(desc, x, cb_host, cb_dev, capacity=None, picks=None):
+    print(f"case {tuple(desc.shape)} S={desc.S} dtype={desc.dtype} B={desc.med_batch_tokens}", flush=True)
+    rec, y = G.run(desc, x, cb_dev, capacity)
+    rep = G.compare(desc, x, cb_host, rec, y, picks)
+    print(dict(rep), flush=True)
+    return rep, rec, y
+
+
+def test_workload1_full():
+    """Single-head fp32 K, 4096 x 128, S = 8, Med3x off: every chunk."""
+    w = synth.WORKLOADS[1]
+    x = synth.generate(w, 0, "cuda")
+    cb_host, cb = G.codebook(w, 0)
+    rep, _, _ = _check(G.desc_for(w), x, cb_host, cb)
+    assert rep["chunks"] == w.chunks_per_role
+
+
+CASES = [
+    # (layers, heads, tokens, head_dim, S, dtype, med_batch_tokens)
+    (2, 3, 1000, 128, 8, "f16", 0),
+    (2, 3, 1501, 128, 32, "f16", 512),
+    (1, 2, 777, 64, 13, "f16", 256),
+    (1, 2, 333, 256, 1, "f32", 100),
+    (2, 1, 129, 16, 40, "f16", 64),
+    (1, 3, 64, 32, 100, "f32", 0),
+    (1, 1, 97, 128, 1024, "f16", 32),
+    (1, 1, 4100, 128, 32, "f32", 4096),
+    (3, 2, 2051, 128, 8, "f16", 1024),
+]
+
+
+@pytest.mark.parametrize("L,H,T,D,S,dt,B", CASES)
+def test_small_shapes_every_chunk(L, H, T, D, S, dt, B):
+    dtype = torch.float16 if dt == "f16" else torch.float32
+    x = _x((L, H, T, D), dtype, seed=L * 1000 + T + S)
+    if B > 0:
+        # outlier structure: a few hot channels and token spikes
+        x[:, :, :, 5] *= 40
+        x[:, :, ::97, :] *= 9
+    cb_host, cb = _cb(L, H, S)
+    desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F32 if dt == "f32" else K.HQMQ_F16, B, 3.0)
+    rep, rec, _ = _check(desc, x, cb_host, cb)
+    if B > 0:
+        assert rep["outliers"] > 0
+
+
+def test_empty_inputs():
+    cb_host, cb = _cb(1, 1, 8)
+    for T in (0,):
+        desc = K.Desc.make(1, 1, T, 128, 8, K.HQMQ_F16, 64, 3.0)
+        x = torch.empty((1, 1, T, 128), dtype=torch.float16, device="cuda")
+        rec, y = G.run(desc, x, cb)
+        assert rec.n_outliers == 0
+        assert int(rec.batch_offsets[0]) == 0
+    desc = K.Desc.make(0, 4, 16, 128, 8, K.HQMQ_F16, 0, 3.0)
+    x = torch.empty((0, 4, 16, 128), dtype=torch.float16, device="cuda")
+    rec, y = G.run(desc, x, cb)
+    assert y.numel() == 0
+
+
+def test_single_token_and_tiny_batches():
+    for T, B in ((1, 1), (2, 1), (3, 2), (65, 64)):
+        x = _x((1, 2, T, 128), torch.float16, seed=T)
+        cb_host, cb = _cb(1, 2, 32)
+        desc = K.Desc.make(1, 2, T, 128, 32, K.HQMQ_F16, B, 3.0)
+        _check(desc, x, cb_host, cb)
+
+
+def test_zero_and_degenerate_batches():
+    """All-zero slice (median 0, no outlier), half-zero batch (median 0: every
+    nonzero chunk is an outlier), fp16 extremes."""
+    L, H, T, D, S = 1, 3, 256, 128, 32
+    x = _x((L, H, T, D), torch.float16, seed=5)
+    x[0, 0] = 0
+    x[0, 1, : T // 2 + 1] = 0
+    x[0, 2, 7, :8] = 65504
+    x[0, 2, 9, 4:8] = -65504
+    x[0, 2, 11, :4] = torch.tensor([6e-8, 0, 0, 0], dtype=torch.float16)
+    cb_host, cb = _cb(L, H, S)
+    desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F16, T, 3.0)
+    rep, rec, y = _check(desc, x, cb_host, cb)
+    offs = rec.batch_offsets.cpu().numpy()
+    assert offs[1] - offs[0] == 0                       # all-zero slice
+    assert offs[2] - offs[1] == int((x[0, 1].float().reshape(-1, 4).abs().sum(1) > 0).sum())
+    assert torch.all(y[0, 0] == 0)
+
+
+def test_codeword_inputs_round_trip():
+    """x = rho * codeword (fp32): the codeword maps to itself and decodes back
+    within the fp16 rounding of the norm."""
+    S, T, D = 32, 64, 128
+    cb_host, cb = _cb(1, 1, S)
+    rng = np.random.default_rng(3)
+    cw = np.stack([O.codeword(cb_host[0, 0], k) for k in range(24 * S)])
+    ks = rng.integers(0, 24 * S, T * D // 4)
+    rho = rng.uniform(0.5, 20, len(ks))
+    xh = (rho[:, None] * cw[ks]).astype(np.float32).reshape(1, 1, T, D)
+    x = torch.from_numpy(xh).cuda()
+    desc = K.Desc.make(1, 1, T, D, S, K.HQMQ_F32, 0, 3.0)
+    rep, rec, y = _check(desc, x, cb_host, cb)
+    from tests.parity import unpack_words
+    codes = unpack_words(rec.idx.cpu().numpy().view(np.uint32)[0, 0], D // 4, 10).reshape(-1)
+    assert np.array_equal(codes, ks)
+    err = np.abs(y.cpu().numpy() - xh).reshape(-1, 4).max(1)
+    assert np.all(err <= 2.0 ** -10 * rho)
+
+
+def test_deep_hole_tie_takes_smallest_code():
+    """S = 1, q = 1: u = (1,1,0,0)/sqrt2 ties six 2T vertices; smallest k wins
+    (exact fp32 tie on the GPU too)."""
+    q = np.zeros((1, 1, 1, 4), np.float32)
+    q[..., 0] = 1
+    x = torch.zeros((1, 1, 4, 16), dtype=torch.float32, device="cuda")
+    x[0, 0, :, 0] = 1
+    x[0, 0, :, 1] = 1
+    desc = K.Desc.make(1, 1, 4, 16, 1, K.HQMQ_F32, 0, 3.0)
+    rec, y = G.run(desc, x, torch.from_numpy(q).cuda())
+    from tests.parity import unpack_words
+    codes = unpack_words(rec.idx.cpu().numpy().view(np.uint32)[0, 0], 4, 5)
+    assert codes[:, 0].tolist() == [0, 0, 0, 0]
+    assert codes[:, 1:].tolist() == [[0] * 3] * 4       # zero chunks
+
+
+def test_deterministic():
+    x = _x((2, 2, 3000, 128), torch.float16, seed=9)
+    x[:, :, :, 3] *= 50
+    cb_host, cb = _cb(2, 2, 32)
+    desc = K.Desc.make(2, 2, 3000, 128, 32, K.HQMQ_F16, 1024, 3.0)
+    a, ya = G.run(desc, x, cb)
+    b, yb = G.run(desc, x, cb)
+    for f in ("idx", "hnorm", "batch_offsets"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    n = int(a.n_outliers)
+    assert n > 0
+    assert torch.equal(a.out_pos[:n], b.out_pos[:n]) and torch.equal(a.out_val[:n], b.out_val[:n])
+    assert torch.equal(ya, yb)
+
+
+def test_capacity_overflow_reports_needed_count():
+    x = _x((1, 2, 2048, 128), torch.float16, seed=11)
+    x[:, :, :, 7] *= 60
+    cb_host, cb = _cb(1, 2, 8)
+    desc = K.Desc.make(1, 2, 2048, 128, 8, K.HQMQ_F16, 512, 3.0)
+    ws = K.workspace(desc)
+    rec = K.allocate_records(desc, capacity=10)
+    K.hqmq_encode(desc, x, cb, rec, ws)
+    with pytest.raises(K.CapacityError) as ei:
+        K.hqmq_encode_result(rec)
+    need = ei.value.needed
+    assert need > 10
+    rec2, y2 = G.run(desc, x, cb, capacity=need)
+    assert rec2.n_outliers == need
+    G.compare(desc, x, cb_host, rec2, y2)
+
+
+def test_invalid_arguments_enqueue_nothing():
+    x = _x((1, 1, 64, 128), torch.float16, seed=1)
+    cb_host, cb = _cb(1, 1, 8)
+    desc = K.Desc.make(1, 1, 64, 128, 8, K.HQMQ_F16, 16, 3.0)
+    rec = K.allocate_records(desc)
+    with pytest.raises(K.HQMQError):
+        K.hqmq_encode(desc, x, cb, rec, None)          # workspace missing
+    with pytest.raises(K.HQMQError):
+        K.hqmq_encode(desc, x[..., 1:], cb, rec, K.workspace(desc))   # misaligned input
+    bad = K.Desc.make(1, 1, 64, 96, 8, K.HQMQ_F16, 16, 3.0)
+    with pytest.raises(K.HQMQError):
+        K.hqmq_encode(bad, x, cb, rec, K.workspace(desc))
