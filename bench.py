@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""HQMQ encode + decode throughput on one MI355X.
+
+One step is one pass of the whole codec over the resident cache: for K and
+for V, hqmq_encode (norm code, nearest of the 24 S codewords, Med3x median,
+outlier side list) and hqmq_decode (gather-multiply plus outlier
+re-insertion).  The default workload is the Llama-3-70B 128k-context cache
+(80 layers x 8 KV heads x 131072 tokens x 128, K and V fp16, S = 32, Med3x
+C = 3 per 4096-token batch): the pages' storage example and the largest
+single-GPU configuration, and the one that exercises every step.
+
+Prints one JSON line.  ``value`` counts chunks (4-element groups) per second,
+each chunk encoded and decoded once per step.  ``roofline`` is the encode
+search kernel against the fp32 matrix-core peak, timed with HIP events
+recorded by the library around that kernel on the launch stream.
+``cpu_baseline`` is the plain C oracle timed on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HQMQ encode & decode chunks/s and GB/s (fp16 in) on 1 MI355X; % of roofline"
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-70b-kv-128k.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (events on an arbitrary
+    stream; torch.cuda.Event only records on torch's current stream)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream: int):
+        assert self.rt.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b) -> float:
+        t = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        return float(t.value)
+
+    def destroy(self, e):
+        self.rt.hipEventDestroy(e)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per search-kernel launch from the committed counter summary,
+    or None when it is missing or was taken from another kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE))
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("search_bytes_per_launch")
+
+
+def cpu_baseline(w, xs, cbs, seconds: float):
+    """The oracle as it stands, timed on whole Med3x batches of the resident
+    workload (copied to host first) until ``seconds`` of work are done."""
+    import numpy as np
+    import oracle as O
+    B = w.med_batch_tokens or w.tokens
+    rng = np.random.default_rng(12345)
+    cpt = w.head_dim // 4
+    staged = []
+    n_stage = 48
+    for i in range(n_stage):
+        role = w.roles[i % len(w.roles)]
+        l, h = int(rng.integers(w.layers)), int(rng.integers(w.heads))
+        bi = int(rng.integers(max(1, w.tokens // B)))
+        x = xs[role][l, h, bi * B:(bi + 1) * B].float().cpu().numpy()
+        staged.append((x, cbs[role][l, h], bi * B))
+    chunks, t0, i = 0, time.perf_counter(), 0
+    while True:
+        x, q, tok0 = staged[i % n_stage]
+        r = O.encode_range(x, q, tok0, w.med_batch_tokens, w.med_C)
+        O.decode_range(r["codes"], r["hnorm"], x.shape[0], w.head_dim, q,
+                       r["side_pos"] if w.med_batch_tokens else None,
+                       r["side_val"] if w.med_batch_tokens else None, tok0)
+        chunks += x.shape[0] * cpt
+        i += 1
+        if time.perf_counter() - t0 >= seconds and i >= 2:
+            break
+    el = time.perf_counter() - t0
+    return {"value": chunks / el, "unit": "chunks/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{i} Med3x batches of {B * cpt} chunks ({B} tokens) drawn from the "
+                      f"{w.name} K/V tensors, oracle encode + decode each, {el:.1f} s"}
+
+
+def copy_calibration():
+    """A plain copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 31                               # 4 GiB of fp16
+    a = torch.empty(n, dtype=torch.float16, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 2 * n, "launches": 3}))
+
+
+def summarize_rocpd(db: str, match: str = "hqmq"):
+    """Per-kernel table (calls, average / min / max duration) of a rocprofv3
+    kernel-trace database, for the text summaries kept under profiles/."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, count(*), avg(duration), min(duration), max(duration), "
+                     "sum(duration), max(grid_x), max(workgroup_x), max(vgpr_count), "
+                     "max(accum_vgpr_count), max(lds_size) from kernels group by name "
+                     "order by sum(duration) desc").fetchall()
+    total = sum(r[5] for r in rows)
+    print("| kernel | calls | avg ms | min ms | max ms | % of GPU time | grid threads | block | "
+          "arch VGPR | acc VGPR | LDS B |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        if match and match not in r[0]:
+            continue
+        name = r[0].replace("(anonymous namespace)::", "").split("(")[0]
+        print(f"| `{name}` | {r[1]} | {r[2] / 1e6:.4f} | {r[3] / 1e6:.4f} | {r[4] / 1e6:.4f} | "
+              f"{100 * r[5] / total:.1f} | {r[6]} | {r[7]} | {r[8]} | {r[9]} | {r[10]} |")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4, help="1..4 (see synth.WORKLOADS)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize", metavar="ROCPD_DB", help="print a kernel table of a rocprofv3 database")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize_rocpd(args.summarize)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the codec shards by (layer, head) with no "
+              f"exchange, so there is no multi-GPU path to time (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_quantization_hqmq_amd as K
+    import synth
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    if w.sequences > 1:
+        raise SystemExit("the decode-step workload is timed by its own driver")
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    ev = HipEvents()
+
+    desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, w.S,
+                       K.HQMQ_F32 if w.dtype == "f32" else K.HQMQ_F16, w.med_batch_tokens, w.med_C)
+    sz = K.hqmq_sizes(desc)
+    log(f"workload {synth.describe(w)}; {sz.chunks} chunks per role")
+
+    xs, cbs_host, cbs, recs, ys = {}, {}, {}, {}, {}
+    ws = K.workspace(desc, dev)
+    for role in w.roles:
+        t = time.perf_counter()
+        xs[role] = synth.generate(w, role, dev)
+        cbs_host[role] = K.hqmq_make_codebook(w.codebook_seed, w.layers, w.heads, role, w.S)
+        cbs[role] = torch.from_numpy(cbs_host[role]).to(dev)
+        torch.cuda.synchronize()
+        log(f"role {role}: input generated in {time.perf_counter() - t:.1f} s")
+        # size the side list from a first encode (re-allocated on overflow)
+        recs[role] = K.encode(desc, xs[role], cbs[role], ws=ws)
+        if recs[role].capacity > 0 and recs[role].n_outliers > 0:
+            cap = int(recs[role].n_outliers)
+            if cap < recs[role].capacity // 2:
+                recs[role] = K.encode(desc, xs[role], cbs[role], capacity=cap, ws=ws)
+        ys[role] = torch.empty(desc.shape, dtype=w.torch_dtype, device=dev)
+        log(f"role {role}: {recs[role].n_outliers} outliers "
+            f"({recs[role].n_outliers / sz.chunks:.4%})")
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for role in w.roles:
+            e = events[("enc", role)] if events else (None, None, None, None)
+            if events:
+                ev.record(e[0], sh)
+            K.hqmq_encode_timed(desc, xs[role], cbs[role], recs[role], ws, sh,
+                                e[1] if events else None, e[2] if events else None)
+            if events:
+                ev.record(e[3], sh)
+        for role in w.roles:
+            if events:
+                d = events[("dec", role)]
+                ev.record(d[0], sh)
+            K.hqmq_decode(desc, recs[role], cbs[role], ys[role], sh)
+            if events:
+                ev.record(d[1], sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    all_events = [{**{("enc", r): tuple(ev.create() for _ in range(4)) for r in w.roles},
+                   **{("dec", r): tuple(ev.create() for _ in range(2)) for r in w.roles}}
+                  for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(all_events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1000.0 * elapsed / args.steps
+
+    search_ms, enc_ms, dec_ms = [], [], []
+    for evs in all_events:
+        for r in w.roles:
+            a, b, c, d = evs[("enc", r)]
+            search_ms.append(ev.ms(b, c))
+            enc_ms.append(ev.ms(a, d))
+            e0, e1 = evs[("dec", r)]
+            dec_ms.append(ev.ms(e0, e1))
+        for v in evs.values():
+            for e in v:
+                ev.destroy(e)
+    mean = lambda v: sum(v) / len(v)
+
+    # every launch must still be valid after the timed steps
+    n_out = {}
+    for r in w.roles:
+        n_out[r] = K.hqmq_encode_result(recs[r], sh)
+    chunks_role = sz.chunks
+    total_chunks = chunks_role * len(w.roles)
+    f_out = sum(n_out.values()) / total_chunks
+    in_bytes_chunk = 16 if w.dtype == "f32" else 8
+    rec_bytes = sz.idx_bytes + sz.hnorm_bytes
+    comp_bytes = sum(rec_bytes + 12 * n_out[r] + sz.offsets_bytes + sz.codebook_bytes for r in w.roles)
+    fp16_bytes = total_chunks * 8
+
+    flops_launch = 32 * w.S * chunks_role           # 16 S FMA per chunk (the method's minimum)
+    s_ms = mean(search_ms)
+    achieved_tf = flops_launch / (s_ms * 1e-3) / 1e12
+    traffic = traffic_per_launch()
+    d_ms = mean(dec_ms)
+    dec_bytes_launch = rec_bytes + chunks_role * 8 + 12 * (sum(n_out.values()) / len(w.roles)) + \
+        sz.offsets_bytes
+    dec_gbps = dec_bytes_launch / (d_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": total_chunks / (ms_step * 1e-3),
+        "unit": "chunks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.heads,
+                   "tokens": w.tokens, "head_dim": w.head_dim, "roles": "K+V" if len(w.roles) == 2 else "K",
+                   "input": w.dtype, "S": w.S, "med3_batch_tokens": w.med_batch_tokens,
+                   "med3_C": w.med_C, "parallelism": "none"},
+        "roofline": {"bound": "mfma", "kernel": "encode_search", "achieved": achieved_tf,
+                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tf / PEAK_FP32_MFMA_TFLOPS, "traffic": traffic,
+                     "algorithmic_per_launch": flops_launch, "avg_launch_ms": s_ms},
+        "roofline_decode": {"bound": "hbm", "kernel": "decode", "achieved": dec_gbps,
+                            "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
+                            "algorithmic_per_launch": dec_bytes_launch, "avg_launch_ms": d_ms},
+        "encode_chunks_per_s": total_chunks / (sum(enc_ms) / args.steps * 1e-3),
+        "decode_chunks_per_s": total_chunks / (sum(dec_ms) / args.steps * 1e-3),
+        "encode_GBps_fp16_in": total_chunks * 8 / (sum(enc_ms) / args.steps * 1e-3) / 1e9,
+        "decode_GBps_fp16_out": total_chunks * 8 / (sum(dec_ms) / args.steps * 1e-3) / 1e9,
+        "encode_ms_per_role": mean(enc_ms),
+        "med3_ms_per_role": mean(enc_ms) - s_ms,
+        "outlier_fraction": f_out,
+        "fp16_bytes": fp16_bytes,
+        "compressed_bytes": comp_bytes,
+        "compression_ratio": fp16_bytes / comp_bytes,
+        "bits_per_element": 8 * comp_bytes / (total_chunks * 4),
+        "kernel_sha256_16": kernel_hash(),
+    }
+    del ws
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a host sample")
+        out["cpu_baseline"] = cpu_baseline(w, xs, cbs_host, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

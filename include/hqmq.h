@@ -161,6 +161,15 @@ int hqmq_make_codebook(uint64_t seed, int32_t layers, int32_t kv_heads, int32_t 
 int hqmq_encode(const hqmq_desc *d, const void *x, const float *codebook, const hqmq_enc *enc,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* hqmq_encode for profilers and benchmarks: identical work and results, and
+ * additionally records search_begin immediately before and search_end
+ * immediately after the launch of the nearest-codeword search kernel, on
+ * stream, so that hipEventElapsedTime gives that kernel's duration.  Either
+ * event may be NULL (not recorded).  Errors as hqmq_encode. */
+int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook,
+                      const hqmq_enc *enc, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream, hipEvent_t search_begin, hipEvent_t search_end);
+
 /* Wait for stream, read enc->status (16 bytes device to host) and return the
  * outlier count in *n_outliers.  Returns HQMQ_ECAPACITY (with the count
  * needed in *n_outliers) when the side list overflowed: re-allocate and

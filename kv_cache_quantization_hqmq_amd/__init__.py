@@ -6,11 +6,11 @@ binding (same function names).  Build with
 ``python -m kv_cache_quantization_hqmq_amd.build``.
 """
 from .hqmq import (CapacityError, Desc, HQMQError, Records, Sizes, allocate_records, decode,
-                   encode, hqmq_decode, hqmq_encode, hqmq_encode_result, hqmq_make_codebook,
+                   encode, hqmq_decode, hqmq_encode, hqmq_encode_result, hqmq_encode_timed, hqmq_make_codebook,
                    hqmq_sizes, hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_ROLE_K,
                    HQMQ_ROLE_V)
 
 __all__ = ["CapacityError", "Desc", "HQMQError", "Records", "Sizes", "allocate_records",
-           "decode", "encode", "hqmq_decode", "hqmq_encode", "hqmq_encode_result",
+           "decode", "encode", "hqmq_decode", "hqmq_encode", "hqmq_encode_result", "hqmq_encode_timed",
            "hqmq_make_codebook", "hqmq_sizes", "hqmq_strerror", "workspace", "HQMQ_F16",
            "HQMQ_F32", "HQMQ_ROLE_K", "HQMQ_ROLE_V"]

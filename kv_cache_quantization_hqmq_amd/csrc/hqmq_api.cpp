@@ -197,6 +197,12 @@ int hqmq_make_codebook(uint64_t seed, int32_t layers, int32_t kv_heads, int32_t 
 
 int hqmq_encode(const hqmq_desc *d, const void *x, const float *codebook, const hqmq_enc *enc,
                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return hqmq_encode_timed(d, x, codebook, enc, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, const hqmq_enc *enc,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t search_begin, hipEvent_t search_end) {
     hqmq::Geometry g;
     int rc = make_geometry(d, &g);
     if (rc != HQMQ_OK) return rc;
@@ -222,10 +228,12 @@ int hqmq_encode(const hqmq_desc *d, const void *x, const float *codebook, const 
     }
 
     hipError_t e = hipSuccess;
+    if (search_begin && hipEventRecord(search_begin, stream) != hipSuccess) return HQMQ_EHIP;
     if (chunks > 0) {
         e = hqmq::launch_encode_search(g, x, codebook, enc->idx, enc->hnorm, ws.s2, stream);
         if (e != hipSuccess) return HQMQ_EHIP;
     }
+    if (search_end && hipEventRecord(search_end, stream) != hipSuccess) return HQMQ_EHIP;
     if (med) {
         if (nb > 0) {
             e = hqmq::launch_med3_select(g, ws.s2, ws.thr, ws.counts, stream);

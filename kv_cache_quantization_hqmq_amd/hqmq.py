@@ -26,7 +26,7 @@ HQMQ_ROLE_K, HQMQ_ROLE_V = 0, 1
 
 # every symbol include/hqmq.h declares
 EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
-           "hqmq_encode_result", "hqmq_decode")
+           "hqmq_encode_timed", "hqmq_encode_result", "hqmq_decode")
 
 
 class HQMQError(RuntimeError):
@@ -100,12 +100,15 @@ def lib():
         L.hqmq_encode.argtypes = [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.POINTER(Enc), ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]
+        L.hqmq_encode_timed.argtypes = [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.POINTER(Enc), ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.hqmq_encode_result.argtypes = [ctypes.POINTER(Enc), ctypes.c_void_p,
                                          ctypes.POINTER(ctypes.c_uint64)]
         L.hqmq_decode.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Enc), ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
-        for f in ("hqmq_sizes", "hqmq_make_codebook", "hqmq_encode", "hqmq_encode_result",
-                  "hqmq_decode"):
+        for f in ("hqmq_sizes", "hqmq_make_codebook", "hqmq_encode", "hqmq_encode_timed",
+                  "hqmq_encode_result", "hqmq_decode"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -152,6 +155,17 @@ def hqmq_encode(desc: Desc, x, codebook, rec: "Records", workspace=None, stream=
     rc = lib().hqmq_encode(ctypes.byref(desc), _ptr(x), _ptr(codebook), ctypes.byref(rec.c),
                            _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "hqmq_encode")
+
+
+def hqmq_encode_timed(desc: Desc, x, codebook, rec: "Records", workspace=None, stream=None,
+                      search_begin=None, search_end=None) -> None:
+    """hqmq_encode plus HIP events (raw hipEvent_t handles) recorded around
+    the search kernel on the same stream."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().hqmq_encode_timed(ctypes.byref(desc), _ptr(x), _ptr(codebook), ctypes.byref(rec.c),
+                                 _ptr(workspace), ws_bytes, _stream(stream), search_begin,
+                                 search_end)
+    _check(rc, "hqmq_encode_timed")
 
 
 def hqmq_encode_result(rec: "Records", stream=None) -> int:
