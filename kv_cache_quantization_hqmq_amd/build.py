@@ -25,6 +25,14 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall",
 ]
+# kernels only (the host API validates floats and keeps IEEE semantics)
+KERNEL_FLAGS = [
+    # inputs are finite by contract: lets v_max/v_max3 take MFMA results
+    # without canonicalising them first
+    "-fno-honor-nans",
+    # MFMA results in arch VGPRs (no v_accvgpr_read per result)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+]
 
 
 def _run(cmd, verbose):
@@ -47,8 +55,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(bdir, exist_ok=True)
     for src in ("hqmq_kernels.hip", "hqmq_api.cpp"):
         obj = os.path.join(bdir, src + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
-        _run([HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        extra = ["-x", "hip", *KERNEL_FLAGS] if src.endswith(".hip") else []
+        _run([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)

@@ -121,6 +121,16 @@ struct Philox4x64 {
     }
 };
 
+// Nearest value on the double-binary16 grid used for codebooks: hi + lo with
+// hi = fp16(q) and lo = fp16(q - hi), both rounded to nearest even (q - hi is
+// exact in fp32, and so is the sum).  The encode kernels split a codebook
+// value into exactly these two parts for the f16 matrix cores.
+float double_f16(float q) {
+    const _Float16 hi = static_cast<_Float16>(q);
+    const _Float16 lo = static_cast<_Float16>(q - static_cast<float>(hi));
+    return static_cast<float>(hi) + static_cast<float>(lo);
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,7 +197,7 @@ int hqmq_make_codebook(uint64_t seed, int32_t layers, int32_t kv_heads, int32_t 
                 }
                 if (!(n2 <= 1.0)) continue;  // rejection: uniform in the ball
                 const double r = std::sqrt(n2);
-                for (int m = 0; m < 4; ++m) q[4 * s + m] = static_cast<float>(v[m] / r);
+                for (int m = 0; m < 4; ++m) q[4 * s + m] = double_f16(static_cast<float>(v[m] / r));
                 ++s;
             }
         }

@@ -88,6 +88,30 @@ __device__ __forceinline__ float sqrt_rn(float a) {
     return tiny ? y * 0x1p-50f : y;
 }
 
+// binary16 half-norm code fp16_rn(sqrt_rn(s2) / 2).  v_sqrt_f32 is within one
+// ulp, so its half rounds to the same binary16 as the exact value unless it
+// lies within one fp32 ulp of a binary16 rounding boundary; only then (about
+// 3 in 8192 chunks) is the correctly rounded root computed.
+__device__ __forceinline__ uint16_t half_norm_code(float s2) {
+    const float h = __builtin_amdgcn_sqrtf(s2) * 0.5f;
+    const uint16_t c = f32_to_f16_bits(h);
+    const uint32_t hb = __float_as_uint(h);
+    if (s2 > 0x1p-100f && f32_to_f16_bits(__uint_as_float(hb + 1u)) == c &&
+        f32_to_f16_bits(__uint_as_float(hb - 1u)) == c)
+        return c;
+    return f32_to_f16_bits(sqrt_rn(s2) * 0.5f);
+}
+
+// Score of the best 2T element for one s from t = (<x, e_m q_s>)_m:
+// max(|t|_inf, |t|_1 / 2) (a unit +-e_m scores +-t_m; a half-unit
+// (s0..s3)/2 scores sum s_m t_m / 2, largest with s_m = sign t_m).
+__device__ __forceinline__ float best_primary(f32x4 d) {
+    const float e0 = fabsf(d[0]), e1 = fabsf(d[1]), e2 = fabsf(d[2]), e3 = fabsf(d[3]);
+    const float m3 = fmaxf(fmaxf(e0, e1), e2);
+    const float h = ((e0 + e1) + (e2 + e3)) * 0.5f;
+    return fmaxf(fmaxf(m3, e3), h);
+}
+
 // Strict order of (score, s) candidates: higher score, then lower s.
 __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
     return sa > sb || (sa == sb && ia < ib);
@@ -109,6 +133,7 @@ struct EncArgs {
     int32_t S;
     int32_t NT;     // ceil(S / 4) tiles of 4 secondary codewords
     int32_t cpt;
+    int32_t log2_cpt;
     int32_t bits;
     int32_t words;
 };
@@ -154,8 +179,14 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
     }
 
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int tpg = 64 / a.cpt;
-    const int wpg = tpg * a.words;
+    // packing: lane w < wpg assembles word ww of token row tt of the group
+    const int wpg = (64 >> a.log2_cpt) * a.words;
+    const int p_tt = lane / a.words;
+    const int p_ww = lane - p_tt * a.words;
+    const int p_lo = 32 * p_ww;
+    const int p_cf = p_lo / a.bits;
+    const int p_cl = min(a.cpt - 1, (p_lo + 31) / a.bits);
+    uint32_t *idx_slice = a.idx + slice * a.tokens * a.words;
 
     for (int64_t g0 = c_begin + 64 * wave; g0 < c_end; g0 += 64 * 4) {
         const int64_t c = g0 + lane;
@@ -181,14 +212,20 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
         s2 = __builtin_fmaf(v1, v1, s2);
         s2 = __builtin_fmaf(v2, v2, s2);
         s2 = __builtin_fmaf(v3, v3, s2);
-        const uint16_t hn = f32_to_f16_bits(sqrt_rn(s2) * 0.5f);
+        const uint16_t hn = half_norm_code(s2);
 
-        // exact power-of-two normalisation for the search (argmax is
-        // scale-invariant; keeps every product far from the denormal range)
-        const float mx = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
-        const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-        const float x0 = __builtin_ldexpf(v0, -ex), x1 = __builtin_ldexpf(v1, -ex);
-        const float x2 = __builtin_ldexpf(v2, -ex), x3 = __builtin_ldexpf(v3, -ex);
+        // fp32 inputs: exact power-of-two normalisation for the search (the
+        // argmax is scale-invariant; keeps every product far from the
+        // denormal range).  fp16 inputs are at least 2^-24 and need none.
+        float x0 = v0, x1 = v1, x2 = v2, x3 = v3;
+        if constexpr (F32IN) {
+            const float mx = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
+            const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+            x0 = __builtin_ldexpf(v0, -ex);
+            x1 = __builtin_ldexpf(v1, -ex);
+            x2 = __builtin_ldexpf(v2, -ex);
+            x3 = __builtin_ldexpf(v3, -ex);
+        }
         *reinterpret_cast<float4 *>(&sx[wave][4 * lane]) = make_float4(x0, x1, x2, x3);
         wave_sync();
 
@@ -203,10 +240,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
 #pragma unroll
                 for (int t = 0; t < NT_REG; ++t) {
                     const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(A[t], bv, zero, 0, 0, 0);
-                    const float e0 = fabsf(d[0]), e1 = fabsf(d[1]), e2 = fabsf(d[2]), e3 = fabsf(d[3]);
-                    const float linf = fmaxf(fmaxf(e0, e1), fmaxf(e2, e3));
-                    const float l1 = (e0 + e1) + (e2 + e3);
-                    const float sc = fmaxf(linf + linf, l1);
+                    const float sc = best_primary(d);
                     if (sc > best) { best = sc; bt = t; }
                 }
             } else {
@@ -214,10 +248,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
                     const float v = sq[16 * t + a_off];
                     const float at = neg ? -v : v;
                     const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(at, bv, zero, 0, 0, 0);
-                    const float e0 = fabsf(d[0]), e1 = fabsf(d[1]), e2 = fabsf(d[2]), e3 = fabsf(d[3]);
-                    const float linf = fmaxf(fmaxf(e0, e1), fmaxf(e2, e3));
-                    const float l1 = (e0 + e1) + (e2 + e3);
-                    const float sc = fmaxf(linf + linf, l1);
+                    const float sc = best_primary(d);
                     if (sc > best) { best = sc; bt = t; }
                 }
             }
@@ -287,20 +318,16 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
 
         // pack the codes of the group's token rows into 32-bit words
         if (lane < wpg) {
-            const int tt = lane / a.words;
-            const int ww = lane - tt * a.words;
-            const int64_t tok = g0 / a.cpt + tt;
-            if (tok * a.cpt < c_end) {
-                const int lo = 32 * ww;
-                const int cf = lo / a.bits;
-                const int cl = min(a.cpt - 1, (lo + 31) / a.bits);
+            const int64_t tok = (g0 >> a.log2_cpt) + p_tt;
+            if ((tok << a.log2_cpt) < c_end) {
                 uint32_t word = 0;
-                for (int cc = cf; cc <= cl; ++cc) {
-                    const uint32_t v = scode[wave][tt * a.cpt + cc];
-                    const int sh = cc * a.bits - lo;
+                const uint32_t *cr = &scode[wave][p_tt << a.log2_cpt];
+                for (int cc = p_cf; cc <= p_cl; ++cc) {
+                    const uint32_t v = cr[cc];
+                    const int sh = cc * a.bits - p_lo;
                     word |= sh >= 0 ? (v << sh) : (v >> (-sh));
                 }
-                a.idx[(slice * a.tokens + tok) * a.words + ww] = word;
+                idx_slice[tok * a.words + p_ww] = word;
             }
         }
         wave_sync();
@@ -723,6 +750,7 @@ hipError_t launch_encode_search(const Geometry &g, const void *x, const float *c
     a.S = g.S;
     a.NT = static_cast<int32_t>(ceil_div(g.S, 4));
     a.cpt = g.cpt;
+    a.log2_cpt = __builtin_ctz(static_cast<unsigned>(g.cpt));
     a.bits = g.bits;
     a.words = g.words;
     const dim3 grid(static_cast<unsigned>(g.slices * a.tiles_per_slice));

@@ -77,6 +77,8 @@ def _configure(L):
     L.or_philox4x64_10.argtypes = [_u64p, _u64p, _u64p]
     L.or_make_codebook.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, _f32p]
+    L.or_codebook_value.argtypes = [ctypes.c_float]
+    L.or_codebook_value.restype = ctypes.c_double
     L.or_norm2.argtypes = [_f32p]
     L.or_norm2.restype = ctypes.c_float
     L.or_half_norm_bits.argtypes = [ctypes.c_float]
@@ -156,6 +158,10 @@ def philox4x64_10(ctr, key) -> np.ndarray:
     out = np.empty(4, np.uint64)
     lib().or_philox4x64_10(_p(c, _u64p), _p(k, _u64p), _p(out, _u64p))
     return out
+
+
+def codebook_value(q: float) -> float:
+    return float(lib().or_codebook_value(float(np.float32(q))))
 
 
 def make_codebook(seed: int, layers: int, heads: int, role: int, S: int) -> np.ndarray:

@@ -32,6 +32,7 @@
  *                                   2x2 complex-matrix representation)
  *   or_f16_bits, or_f16_value ..... pinned (numpy float16 conversion)
  *   or_philox4x64_10 .............. pinned (numpy.random.Philox)
+ *   or_codebook_value ............. pinned (numpy float16 rounding)
  *   or_make_codebook .............. partially pinned (generator pinned;
  *                                   unit norm, determinism, moments) --
  *                                   the codebook values themselves are a
@@ -185,6 +186,19 @@ void or_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out
     out[3] = x3;
 }
 
+/* Codebook values are held on the "double binary16" grid: a value q is used
+ * as q_eff = h + l with h = binary16(q) and l = binary16(q - h) (q - h is
+ * exact in fp32 and fp64).  A reading: the pages fix no precision for the
+ * secondary codebook; this one keeps 22 significant bits and lets fp16
+ * inputs be multiplied by the two parts exactly in fp32.  Values produced
+ * by or_make_codebook are already on the grid (q_eff == q). */
+double or_codebook_value(float q)
+{
+    double h = or_f16_value(or_f16_bits((double)q));
+    double l = or_f16_value(or_f16_bits((double)q - h));
+    return h + l;
+}
+
 /* The S "random unit quaternions" of one (layer, head, role) ([ABS]: a
  * seeded per-(layer, head) codebook; [NL-M] 1 and [PT-M] 1: drawn per
  * (layer, head, role) without calibration).  The pages name no distribution
@@ -194,7 +208,8 @@ void or_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out
  *   candidate j uses the Philox block of counter (j, 0, 0, 0); its four words
  *   give v_m = (2 (w_m >> 40) - 2^24 + 1) / 2^24, an odd multiple of 2^-24 in
  *   (-1, 1); the candidate is kept when sum v_m^2 <= 1 (exact in fp64);
- *   q = v / sqrt(sum v_m^2) in fp64, rounded to fp32.
+ *   q = v / sqrt(sum v_m^2) in fp64, rounded to fp32 and then to the double
+ *   binary16 grid (or_codebook_value).
  * Candidates are consumed in order until S are kept.
  * out: [layers][heads][S][4] fp32. */
 void or_make_codebook(uint64_t seed, int layers, int heads, int role, int S, float *out)
@@ -218,7 +233,7 @@ void or_make_codebook(uint64_t seed, int layers, int heads, int role, int S, flo
                     continue;
                 double r = sqrt(n2);
                 for (int m = 0; m < 4; ++m)
-                    dst[kept * 4 + m] = (float)(v[m] / r);
+                    dst[kept * 4 + m] = (float)or_codebook_value((float)(v[m] / r));
                 ++kept;
             }
         }
@@ -260,7 +275,7 @@ void or_codeword(const float *q, int k, double out[4])
     double a[4], b[4];
     or_t2_element(p, a);
     for (int m = 0; m < 4; ++m)
-        b[m] = (double)q[4 * s + m];
+        b[m] = or_codebook_value(q[4 * s + m]);
     or_qmul(a, b, out);
 }
 

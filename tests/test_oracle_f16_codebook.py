@@ -94,3 +94,21 @@ def test_codebook_is_uniform_on_s3():
         assert stats.kstest(q[:, m], cdf).pvalue > 1e-4
     # pairs of coordinates are uncorrelated in sign (no axis preference)
     assert abs(np.mean(np.sign(q[:, 0] * q[:, 1]))) < 5 / np.sqrt(N)
+
+
+def test_codebook_values_are_on_the_double_binary16_grid():
+    """Codebook values are used as h + l, h = fp16(q), l = fp16(q - h)
+    (numpy's float16 rounding here); generated codebooks are on that grid."""
+    rng = np.random.default_rng(8)
+    qs = np.concatenate([rng.uniform(-1, 1, 5000), rng.normal(size=2000) * 1e-3,
+                         [1.0, -1.0, 0.0, 1e-6, -3e-5, 0.999999]]).astype(np.float32)
+    for q in qs:
+        h = np.float16(q)
+        l = np.float16(np.float32(q) - np.float32(h))
+        assert O.codebook_value(q) == float(h) + float(l), q
+    cb = O.make_codebook(3, 2, 3, 1, 64).ravel()
+    assert all(O.codebook_value(v) == float(v) for v in cb)
+    # 22 significant bits: within 2^-22 of the fp32 value for normal-range parts
+    q = rng.uniform(0.25, 1, 1000).astype(np.float32)
+    err = np.array([abs(O.codebook_value(v) - float(v)) / float(v) for v in q])
+    assert err.max() <= 2.0 ** -22
