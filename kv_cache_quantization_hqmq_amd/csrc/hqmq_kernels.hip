@@ -31,6 +31,8 @@ namespace hqmq {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kEncThreads = 256;   // 4 waves; each wave encodes 64 chunks per step
 constexpr int kMedThreads = 512;
@@ -62,6 +64,16 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
 }
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Codebook values are used on the double-binary16 grid: hi + lo with
+// hi = fp16(q), lo = fp16(q - hi) (q - hi and the sum are exact in fp32).
+// Generated codebooks are already on it; any other codebook is rounded the
+// same way wherever the kernels read it.
+__device__ __forceinline__ float double_f16(float q) {
+    const _Float16 hi = static_cast<_Float16>(q);
+    const _Float16 lo = static_cast<_Float16>(q - static_cast<float>(hi));
+    return static_cast<float>(hi) + static_cast<float>(lo);
 }
 
 // Correctly rounded fp32 square root of a >= 0.  v_sqrt_f32 is within one
@@ -112,6 +124,28 @@ __device__ __forceinline__ float best_primary(f32x4 d) {
     return fmaxf(fmaxf(m3, e3), h);
 }
 
+// Index p of the best 2T element for secondary codeword qs: t = (<x, e_m q_s>)_m
+// in fp32; a unit +-e_m (p = 2 m + sign) wins when |t|_inf >= |t|_1 / 2
+// (lowest m, + before -), otherwise the half-unit with s_m = sign t_m
+// (p = 8 + sum of (t_m < 0) 2^m; 0 counts as +).
+__device__ __forceinline__ int primary_index(const float *qs, float x0, float x1, float x2, float x3) {
+    const float q0 = qs[0], q1 = qs[1], q2 = qs[2], q3 = qs[3];
+    const float t0 = __builtin_fmaf(q3, x3, __builtin_fmaf(q2, x2, __builtin_fmaf(q1, x1, q0 * x0)));
+    const float t1 = __builtin_fmaf(q2, x3, __builtin_fmaf(-q3, x2, __builtin_fmaf(q0, x1, -q1 * x0)));
+    const float t2 = __builtin_fmaf(-q1, x3, __builtin_fmaf(q0, x2, __builtin_fmaf(q3, x1, -q2 * x0)));
+    const float t3 = __builtin_fmaf(q0, x3, __builtin_fmaf(q1, x2, __builtin_fmaf(-q2, x1, -q3 * x0)));
+    const float e0 = fabsf(t0), e1 = fabsf(t1), e2 = fabsf(t2), e3 = fabsf(t3);
+    float linf = e0;
+    int mi = 0;
+    float tm = t0;
+    if (e1 > linf) { linf = e1; mi = 1; tm = t1; }
+    if (e2 > linf) { linf = e2; mi = 2; tm = t2; }
+    if (e3 > linf) { linf = e3; mi = 3; tm = t3; }
+    const float l1 = (e0 + e1) + (e2 + e3);
+    if (linf + linf >= l1) return 2 * mi + (tm < 0.0f ? 1 : 0);
+    return 8 + (t0 < 0.0f ? 1 : 0) + (t1 < 0.0f ? 2 : 0) + (t2 < 0.0f ? 4 : 0) + (t3 < 0.0f ? 8 : 0);
+}
+
 // Strict order of (score, s) candidates: higher score, then lower s.
 __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
     return sa > sb || (sa == sb && ia < ib);
@@ -156,7 +190,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
     {
         const float *q = a.cb + slice * a.S * 4;
         const int nq = 16 * NT;
-        for (int i = threadIdx.x; i < nq; i += kEncThreads) sq[i] = i < 4 * a.S ? q[i] : 0.0f;
+        for (int i = threadIdx.x; i < nq; i += kEncThreads) sq[i] = i < 4 * a.S ? double_f16(q[i]) : 0.0f;
     }
     __syncthreads();
 
@@ -286,28 +320,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
             s_best = min(ki, 4 * NT - 1);
         }
 
-        // Primary index from the winning s: t = (<x, e_m q_s>)_m in fp32.
-        const float *qs = &sq[4 * s_best];
-        const float q0 = qs[0], q1 = qs[1], q2 = qs[2], q3 = qs[3];
-        const float t0 = __builtin_fmaf(q3, x3, __builtin_fmaf(q2, x2, __builtin_fmaf(q1, x1, q0 * x0)));
-        const float t1 = __builtin_fmaf(q2, x3, __builtin_fmaf(-q3, x2, __builtin_fmaf(q0, x1, -q1 * x0)));
-        const float t2 = __builtin_fmaf(-q1, x3, __builtin_fmaf(q0, x2, __builtin_fmaf(q3, x1, -q2 * x0)));
-        const float t3 = __builtin_fmaf(q0, x3, __builtin_fmaf(q1, x2, __builtin_fmaf(-q2, x1, -q3 * x0)));
-        const float e0 = fabsf(t0), e1 = fabsf(t1), e2 = fabsf(t2), e3 = fabsf(t3);
-        float linf = e0;
-        int mi = 0;
-        float tm = t0;
-        if (e1 > linf) { linf = e1; mi = 1; tm = t1; }
-        if (e2 > linf) { linf = e2; mi = 2; tm = t2; }
-        if (e3 > linf) { linf = e3; mi = 3; tm = t3; }
-        const float l1 = (e0 + e1) + (e2 + e3);
-        int p;
-        if (linf + linf >= l1) {
-            p = 2 * mi + (tm < 0.0f ? 1 : 0);
-        } else {
-            p = 8 + (t0 < 0.0f ? 1 : 0) + (t1 < 0.0f ? 2 : 0) + (t2 < 0.0f ? 4 : 0) + (t3 < 0.0f ? 8 : 0);
-        }
-        const uint32_t code = s2 > 0.0f ? static_cast<uint32_t>(24 * s_best + p) : 0u;
+        const uint32_t code = s2 > 0.0f ? static_cast<uint32_t>(24 * s_best + primary_index(&sq[4 * s_best], x0, x1, x2, x3)) : 0u;
 
         if (valid) {
             a.hnorm[gc] = hn;
@@ -317,6 +330,166 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
         wave_sync();
 
         // pack the codes of the group's token rows into 32-bit words
+        if (lane < wpg) {
+            const int64_t tok = (g0 >> a.log2_cpt) + p_tt;
+            if ((tok << a.log2_cpt) < c_end) {
+                uint32_t word = 0;
+                const uint32_t *cr = &scode[wave][p_tt << a.log2_cpt];
+                for (int cc = p_cf; cc <= p_cl; ++cc) {
+                    const uint32_t v = cr[cc];
+                    const int sh = cc * a.bits - p_lo;
+                    word |= sh >= 0 ? (v << sh) : (v >> (-sh));
+                }
+                idx_slice[tok * a.words + p_ww] = word;
+            }
+        }
+        wave_sync();
+    }
+}
+
+// --------------------------------------------------------------------------
+// Encode search for fp16 inputs on the f16 matrix cores.
+//
+// v_mfma_f32_32x32x8_f16 computes 32 rows (8 secondary codewords x 4 basis
+// units e_m) against 32 chunks with K = 8: k = 0..3 multiply the chunk's four
+// fp16 components by the hi parts of the rows e_m q_s, k = 4..7 by the lo
+// parts.  Every product is exact in fp32 and D accumulates in fp32, so t is
+// the fp32 transform of the exact codebook value.  Lane l supplies A row
+// l % 32, k block l / 32, and B column l % 32 (the raw 8-byte chunk, the same
+// for both k blocks); D VGPR 4 a + r of lane l is row 8 a + 4 (l / 32) + r,
+// column l % 32: t_r of s = 8 tile + 2 a + l / 32 for chunk l % 32.
+// --------------------------------------------------------------------------
+template <int NT8, bool WITH_S2>
+__global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a) {
+    constexpr int kQ = NT8 > 0 ? 32 * NT8 : 4 * kMaxS;
+    __shared__ __attribute__((aligned(16))) float sq[kQ];
+    __shared__ uint32_t scode[4][64];
+
+    const int64_t tile = blockIdx.x;
+    const int64_t slice = tile / a.tiles_per_slice;
+    const int64_t c_begin = (tile - slice * a.tiles_per_slice) * a.tile_chunks;
+    const int64_t c_end = min(c_begin + static_cast<int64_t>(a.tile_chunks), a.n_slice);
+    const int NT = NT8 > 0 ? NT8 : (a.S + 7) / 8;
+    {
+        const float *q = a.cb + slice * a.S * 4;
+        const int nq = 32 * NT;
+        for (int i = threadIdx.x; i < nq; i += kEncThreads) sq[i] = i < 4 * a.S ? double_f16(q[i]) : 0.0f;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 31;
+    const int hh = lane >> 5;            // K block: 0 = hi parts, 1 = lo parts
+    const int m_row = col & 3;
+    const int s_loc = col >> 2;
+
+    // A operand of tile t: row (s = 8 t + s_loc, m = m_row), k = 0..3 of the
+    // hi (hh = 0) or lo (hh = 1) part of (e_m q_s)[k] = sign(m, k) q_s[m ^ k]
+    auto a_operand = [&](int t) {
+        const float *qs = &sq[4 * (8 * t + s_loc)];
+        f16x4 r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float v = qs[m_row ^ k];
+            const _Float16 hi = static_cast<_Float16>(v);
+            const _Float16 part = hh ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
+            r[k] = ((kNegMask >> (4 * m_row + k)) & 1u) ? -part : part;
+        }
+        return r;
+    };
+    f16x4 A[NT8 > 0 ? NT8 : 1];
+    if constexpr (NT8 > 0) {
+#pragma unroll
+        for (int t = 0; t < NT8; ++t) A[t] = a_operand(t);
+    }
+
+    const f32x16 zero = {};
+    const int wpg = (64 >> a.log2_cpt) * a.words;
+    const int p_tt = lane / a.words;
+    const int p_ww = lane - p_tt * a.words;
+    const int p_lo = 32 * p_ww;
+    const int p_cf = p_lo / a.bits;
+    const int p_cl = min(a.cpt - 1, (p_lo + 31) / a.bits);
+    uint32_t *idx_slice = a.idx + slice * a.tokens * a.words;
+    const uint2 *xs = static_cast<const uint2 *>(a.x) + slice * a.n_slice;
+
+    for (int64_t g0 = c_begin + 64 * wave; g0 < c_end; g0 += 64 * 4) {
+        // B operands: chunk g0 + 32 b + col of both column blocks
+        uint2 xr[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int64_t c = g0 + 32 * b + col;
+            xr[b] = c < c_end ? xs[c] : make_uint2(0u, 0u);
+        }
+        float bsc[2];
+        int bsi[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const f16x4 bv = __builtin_bit_cast(f16x4, xr[b]);
+            float best = -1.0f;
+            int bk = 0;
+            if constexpr (NT8 > 0) {
+#pragma unroll
+                for (int t = 0; t < NT8; ++t) {
+                    const f32x16 d = __builtin_amdgcn_mfma_f32_32x32x8f16(A[t], bv, zero, 0, 0, 0);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 tv = {d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]};
+                        const float sc = best_primary(tv);
+                        if (sc > best) { best = sc; bk = 8 * t + 2 * g; }
+                    }
+                }
+            } else {
+                for (int t = 0; t < NT; ++t) {
+                    const f32x16 d = __builtin_amdgcn_mfma_f32_32x32x8f16(a_operand(t), bv, zero, 0, 0, 0);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 tv = {d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]};
+                        const float sc = best_primary(tv);
+                        if (sc > best) { best = sc; bk = 8 * t + 2 * g; }
+                    }
+                }
+            }
+            bsc[b] = best;
+            bsi[b] = bk + hh;
+        }
+
+        // the two lane halves hold the other parity of s for the same
+        // chunks; exchanging one block each leaves lane l with chunk g0 + l
+        int s_best;
+        {
+            const float ss = hh ? bsc[0] : bsc[1];
+            const int si = hh ? bsi[0] : bsi[1];
+            float ks = hh ? bsc[1] : bsc[0];
+            int ki = hh ? bsi[1] : bsi[0];
+            const float rs = __shfl_xor(ss, 32);
+            const int ri = __shfl_xor(si, 32);
+            if (better(rs, ri, ks, ki)) { ks = rs; ki = ri; }
+            s_best = min(ki, 8 * NT - 1);
+        }
+        const int64_t c = g0 + lane;
+        const bool valid = c < c_end;
+        const uint2 own = hh ? xr[1] : xr[0];
+        const float v0 = f16_bits_to_f32(static_cast<uint16_t>(own.x));
+        const float v1 = f16_bits_to_f32(static_cast<uint16_t>(own.x >> 16));
+        const float v2 = f16_bits_to_f32(static_cast<uint16_t>(own.y));
+        const float v3 = f16_bits_to_f32(static_cast<uint16_t>(own.y >> 16));
+
+        // declared fp32 squared norm and its binary16 half-norm code
+        float s2 = v0 * v0;
+        s2 = __builtin_fmaf(v1, v1, s2);
+        s2 = __builtin_fmaf(v2, v2, s2);
+        s2 = __builtin_fmaf(v3, v3, s2);
+        const uint16_t hn = half_norm_code(s2);
+
+        const uint32_t code = s2 > 0.0f ? static_cast<uint32_t>(24 * s_best + primary_index(&sq[4 * s_best], v0, v1, v2, v3)) : 0u;
+        if (valid) {
+            a.hnorm[slice * a.n_slice + c] = hn;
+            if constexpr (WITH_S2) a.s2[slice * a.n_slice + c] = s2;
+        }
+        scode[wave][lane] = code;
+        wave_sync();
         if (lane < wpg) {
             const int64_t tok = (g0 >> a.log2_cpt) + p_tt;
             if ((tok << a.log2_cpt) < c_end) {
@@ -613,11 +786,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     if constexpr (TABLE) {
         for (int k = threadIdx.x; k < ncw; k += kDecThreads) {
             const int s = k / 24;
-            tab[k] = codeword_f32(q + 4 * s, k - 24 * s);
+            const float qe[4] = {double_f16(q[4 * s]), double_f16(q[4 * s + 1]),
+                                 double_f16(q[4 * s + 2]), double_f16(q[4 * s + 3])};
+            tab[k] = codeword_f32(qe, k - 24 * s);
         }
     } else {
         for (int s = threadIdx.x; s < a.S; s += kDecThreads) {
-            f32x4 v = {q[4 * s], q[4 * s + 1], q[4 * s + 2], q[4 * s + 3]};
+            f32x4 v = {double_f16(q[4 * s]), double_f16(q[4 * s + 1]), double_f16(q[4 * s + 2]),
+                       double_f16(q[4 * s + 3])};
             tab[s] = v;
         }
     }
@@ -767,9 +943,22 @@ hipError_t launch_encode_search(const Geometry &g, const void *x, const float *c
             else HQMQ_ENC(NT, false, false);     \
         }                                        \
     } while (0)
-    if (a.NT == 2) HQMQ_ENC_NT(2);
-    else if (a.NT == 8) HQMQ_ENC_NT(8);
-    else HQMQ_ENC_NT(0);
+#define HQMQ_ENC_H(NT8)                                                                             \
+    do {                                                                                            \
+        if (ws2) hipLaunchKernelGGL((encode_search_h_kernel<NT8, true>), grid, block, 0, st, a);   \
+        else hipLaunchKernelGGL((encode_search_h_kernel<NT8, false>), grid, block, 0, st, a);      \
+    } while (0)
+    if (g.f32) {
+        if (a.NT == 2) HQMQ_ENC_NT(2);
+        else if (a.NT == 8) HQMQ_ENC_NT(8);
+        else HQMQ_ENC_NT(0);
+    } else {
+        const int nt8 = (g.S + 7) / 8;
+        if (nt8 == 1) HQMQ_ENC_H(1);
+        else if (nt8 == 4) HQMQ_ENC_H(4);
+        else HQMQ_ENC_H(0);
+    }
+#undef HQMQ_ENC_H
 #undef HQMQ_ENC_NT
 #undef HQMQ_ENC
     return hipGetLastError();
