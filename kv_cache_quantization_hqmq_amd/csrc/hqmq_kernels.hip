@@ -33,12 +33,14 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kEncThreads = 256;   // 4 waves; each wave encodes 64 chunks per step
 constexpr int kMedThreads = 512;
 constexpr int kFlagThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kDecThreads = 256;   // each thread decodes 4 chunks per step
+constexpr int kDecUnroll = 8;      // steps whose loads a thread issues together
 constexpr int kMaxS = 1024;
 constexpr int kTableMaxS = 64;     // decode keeps the 24 S codewords in LDS up to here
 
@@ -730,6 +732,7 @@ struct DecArgs {
     int64_t bps;
     int32_t S;
     int32_t cpt;
+    int32_t log2_cpt;
     int32_t bits;
     int32_t words;
 };
@@ -773,9 +776,16 @@ __device__ __forceinline__ void store_chunk(void *y, int64_t gc, f32x4 v) {
     }
 }
 
+// Codes and half-norms of the 2 chunks c, c+1 of one token row.
+struct DecPair {
+    uint32_t w0, w1;   // the row words holding the 2 codes
+    uint32_t sh;       // bit offset of the first code in w0
+    uint32_t h;        // 2 binary16 half-norm codes
+};
+
 template <bool F32OUT, bool TABLE>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
-    __shared__ f32x4 tab[TABLE ? 24 * kTableMaxS : kMaxS];
+    extern __shared__ f32x4 tab[];   // TABLE: the 24 S codewords; else the S q_s
     const int64_t slice = blockIdx.x / a.wg_per_slice;
     const int64_t r0 = (blockIdx.x - slice * a.wg_per_slice) * a.wg_chunks;
     const int64_t r1 = min(r0 + a.wg_chunks, a.n_slice);
@@ -799,67 +809,84 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     }
     __syncthreads();
 
-    const uint32_t cmask = (1u << a.bits) - 1u;
-    for (int64_t c = r0 + 4 * threadIdx.x; c < r1; c += 4 * kDecThreads) {
-        const int64_t tok = c / a.cpt;
-        const int j = static_cast<int>(c - tok * a.cpt);
-        const uint32_t *rowp = a.idx + (sbase / a.cpt + tok) * a.words;
-        const int o = j * a.bits;
+    const uint32_t *idx_s = a.idx + slice * a.tokens * a.words;
+    const uint32_t *hn_s = reinterpret_cast<const uint32_t *>(a.hnorm + sbase);
+    const int cmask = a.cpt - 1;
+    const uint32_t kmask = (1u << a.bits) - 1u;
+    const int last_word = a.words - 1;
+
+    // Each lane decodes 2 chunks per step, so one 16-byte store per lane
+    // writes 1 KB of contiguous fp16 output per wave instruction.  Every
+    // load is unconditional (clamped to the row) and kDecUnroll steps' loads
+    // are issued before any is used.
+    auto load = [&](int64_t c) {
+        DecPair d;
+        const int64_t row = c >> a.log2_cpt;
+        const int o = static_cast<int>(c & cmask) * a.bits;
         const int w0 = o >> 5;
-        const int sh = o & 31;
-        uint64_t win = rowp[w0];
-        if (w0 + 1 < a.words) win |= static_cast<uint64_t>(rowp[w0 + 1]) << 32;
-        win >>= sh;
-        if (sh + 4 * a.bits > 64) win |= static_cast<uint64_t>(rowp[w0 + 2]) << (64 - sh);
-        const uint2 hr = *reinterpret_cast<const uint2 *>(a.hnorm + sbase + c);
-        const uint16_t h[4] = {static_cast<uint16_t>(hr.x), static_cast<uint16_t>(hr.x >> 16),
-                               static_cast<uint16_t>(hr.y), static_cast<uint16_t>(hr.y >> 16)};
-        f32x4 out[4];
-        bool flagged = false;
+        const uint32_t *rp = idx_s + row * a.words;
+        d.w0 = rp[w0];
+        d.w1 = rp[min(w0 + 1, last_word)];
+        d.sh = static_cast<uint32_t>(o & 31);
+        d.h = hn_s[c >> 1];
+        return d;
+    };
+    constexpr int kStep = 2 * kDecThreads;   // chunks per block step
+    for (int64_t c0 = r0 + 2 * threadIdx.x; c0 < r1; c0 += static_cast<int64_t>(kStep) * kDecUnroll) {
+        DecPair pd[kDecUnroll];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t k = static_cast<uint32_t>(win >> (i * a.bits)) & cmask;
-            k = min(k, static_cast<uint32_t>(ncw - 1));
-            flagged |= (h[i] & 0x8000u) != 0;
-            const float r = 2.0f * f16_bits_to_f32(static_cast<uint16_t>(h[i] & 0x7FFFu));
-            f32x4 cw;
-            if constexpr (TABLE) {
-                cw = tab[k];
-            } else {
-                const int s = static_cast<int>(k / 24u);
-                const f32x4 qv = tab[s];
-                const float qa[4] = {qv[0], qv[1], qv[2], qv[3]};
-                cw = codeword_f32(qa, static_cast<int>(k) - 24 * s);
-            }
-            out[i] = r * cw;
+        for (int u = 0; u < kDecUnroll; ++u) {
+            const int64_t c = c0 + static_cast<int64_t>(u) * kStep;
+            pd[u] = c < r1 ? load(c) : DecPair{};
         }
-        const int64_t gc = sbase + c;
-        if (!flagged) {
-            if constexpr (F32OUT) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) store_chunk<true>(a.y, gc + i, out[i]);
-            } else {
-                uint4 o0, o1;
-                o0.x = static_cast<uint32_t>(f32_to_f16_bits(out[0][0])) | (static_cast<uint32_t>(f32_to_f16_bits(out[0][1])) << 16);
-                o0.y = static_cast<uint32_t>(f32_to_f16_bits(out[0][2])) | (static_cast<uint32_t>(f32_to_f16_bits(out[0][3])) << 16);
-                o0.z = static_cast<uint32_t>(f32_to_f16_bits(out[1][0])) | (static_cast<uint32_t>(f32_to_f16_bits(out[1][1])) << 16);
-                o0.w = static_cast<uint32_t>(f32_to_f16_bits(out[1][2])) | (static_cast<uint32_t>(f32_to_f16_bits(out[1][3])) << 16);
-                o1.x = static_cast<uint32_t>(f32_to_f16_bits(out[2][0])) | (static_cast<uint32_t>(f32_to_f16_bits(out[2][1])) << 16);
-                o1.y = static_cast<uint32_t>(f32_to_f16_bits(out[2][2])) | (static_cast<uint32_t>(f32_to_f16_bits(out[2][3])) << 16);
-                o1.z = static_cast<uint32_t>(f32_to_f16_bits(out[3][0])) | (static_cast<uint32_t>(f32_to_f16_bits(out[3][1])) << 16);
-                o1.w = static_cast<uint32_t>(f32_to_f16_bits(out[3][2])) | (static_cast<uint32_t>(f32_to_f16_bits(out[3][3])) << 16);
-                uint4 *yp = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + 4 * gc);
-                yp[0] = o0;
-                yp[1] = o1;
+        for (int u = 0; u < kDecUnroll; ++u) {
+            const int64_t c = c0 + static_cast<int64_t>(u) * kStep;
+            if (c >= r1) break;
+            const DecPair &cur = pd[u];
+            const uint64_t win = ((static_cast<uint64_t>(cur.w1) << 32) | cur.w0) >> cur.sh;
+            f32x4 out[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                uint32_t k = static_cast<uint32_t>(win >> (i * a.bits)) & kmask;
+                k = min(k, static_cast<uint32_t>(ncw - 1));
+                // flagged (outlier) chunks get a placeholder here and their
+                // side-list values after the barrier below
+                const uint16_t hi = static_cast<uint16_t>(cur.h >> (16 * i));
+                const float r = 2.0f * f16_bits_to_f32(static_cast<uint16_t>(hi & 0x7FFFu));
+                f32x4 cw;
+                if constexpr (TABLE) {
+                    cw = tab[k];
+                } else {
+                    const int s = static_cast<int>(k / 24u);
+                    const f32x4 qv = tab[s];
+                    const float qa[4] = {qv[0], qv[1], qv[2], qv[3]};
+                    cw = codeword_f32(qa, static_cast<int>(k) - 24 * s);
+                }
+                out[i] = r * cw;
             }
-        } else {
+            const int64_t gc = sbase + c;
+            if constexpr (F32OUT) {
+                f32x4 *yp = reinterpret_cast<f32x4 *>(a.y) + gc;
+                __builtin_nontemporal_store(out[0], yp);
+                __builtin_nontemporal_store(out[1], yp + 1);
+            } else {
+                u32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!(h[i] & 0x8000u)) store_chunk<F32OUT>(a.y, gc + i, out[i]);
+                for (int i = 0; i < 2; ++i) {
+                    o[2 * i] = static_cast<uint32_t>(f32_to_f16_bits(out[i][0])) |
+                               (static_cast<uint32_t>(f32_to_f16_bits(out[i][1])) << 16);
+                    o[2 * i + 1] = static_cast<uint32_t>(f32_to_f16_bits(out[i][2])) |
+                                   (static_cast<uint32_t>(f32_to_f16_bits(out[i][3])) << 16);
+                }
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.y) + 4 * gc));
+            }
         }
     }
 
     if (a.bps > 0) {
+        // the bulk stores above are complete and visible to the block
+        __syncthreads();
         // side-list entries of [r0, r1): the batches covering the range give
         // an index window; a 256-way search finds the first position >= r0.
         const int64_t bl = r0 / a.batch_chunks;
@@ -1020,8 +1047,9 @@ hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t 
                          uint64_t capacity, const float *codebook, void *y, hipStream_t st) {
     const int64_t total = g.slices * g.n_slice;
     if (total == 0) return hipSuccess;
-    int64_t wgc = round_up(ceil_div(total, 4096), 4 * kDecThreads);
-    wgc = wgc < 4 * kDecThreads ? 4 * kDecThreads : (wgc > 16384 ? 16384 : wgc);
+    int64_t wgc = round_up(ceil_div(total, 4096), 2 * kDecThreads);
+    wgc = wgc < 2 * kDecThreads ? 2 * kDecThreads : (wgc > 32768 ? 32768 : wgc);
+    if (wgc >= 2 * kDecThreads * kDecUnroll) wgc = round_up(wgc, 2 * kDecThreads * kDecUnroll);
     DecArgs a;
     a.idx = idx;
     a.hnorm = hnorm;
@@ -1039,17 +1067,19 @@ hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t 
     a.bps = g.batch_chunks > 0 ? g.batches_per_slice : 0;
     a.S = g.S;
     a.cpt = g.cpt;
+    a.log2_cpt = __builtin_ctz(static_cast<unsigned>(g.cpt));
     a.bits = g.bits;
     a.words = g.words;
     const dim3 grid(static_cast<unsigned>(g.slices * a.wg_per_slice));
     const dim3 block(kDecThreads);
     const bool table = g.S <= kTableMaxS;
+    const size_t lds = (table ? 24 * static_cast<size_t>(g.S) : static_cast<size_t>(g.S)) * sizeof(f32x4);
     if (g.f32) {
-        if (table) hipLaunchKernelGGL((decode_kernel<true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, 0, st, a);
+        if (table) hipLaunchKernelGGL((decode_kernel<true, true>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, lds, st, a);
     } else {
-        if (table) hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, 0, st, a);
+        if (table) hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, lds, st, a);
     }
     return hipGetLastError();
 }
