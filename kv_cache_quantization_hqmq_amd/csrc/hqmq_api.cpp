@@ -60,31 +60,27 @@ int make_geometry(const hqmq_desc *d, hqmq::Geometry *g) {
     return HQMQ_OK;
 }
 
-struct Workspace {
-    float *s2;
-    float *thr;
-    uint32_t *counts;
-};
+// Med3x workspace: hist [batches][2048] u32 | counts [batches] u32 |
+// mask [batches][mask_words] u32 (one bit per chunk).
+int64_t mask_words(const hqmq::Geometry &g) { return 2 * ((g.batch_chunks + 63) / 64); }
 
-uint64_t workspace_layout(const hqmq::Geometry &g, void *base, Workspace *w) {
-    if (g.batch_chunks == 0) {
-        if (w) *w = Workspace{nullptr, nullptr, nullptr};
-        return 0;
-    }
-    const uint64_t chunks = static_cast<uint64_t>(g.slices * g.n_slice);
+uint64_t workspace_layout(const hqmq::Geometry &g, void *base, hqmq::Med3Work *w) {
+    if (g.batch_chunks == 0) return 0;
     const uint64_t nb = static_cast<uint64_t>(g.slices * g.batches_per_slice);
+    const uint64_t mw = static_cast<uint64_t>(mask_words(g));
     uint64_t off = 0;
-    const uint64_t o_s2 = off;
-    off = align_up(off + chunks * 4, kWsAlign);
-    const uint64_t o_thr = off;
-    off = align_up(off + nb * 4, kWsAlign);
+    const uint64_t o_hist = off;
+    off = align_up(off + nb * 2048 * 4, kWsAlign);
     const uint64_t o_cnt = off;
     off = align_up(off + nb * 4, kWsAlign);
+    const uint64_t o_mask = off;
+    off = align_up(off + nb * mw * 4, kWsAlign);
     if (w) {
         char *b = static_cast<char *>(base);
-        w->s2 = reinterpret_cast<float *>(b + o_s2);
-        w->thr = reinterpret_cast<float *>(b + o_thr);
+        w->hist = reinterpret_cast<uint32_t *>(b + o_hist);
         w->counts = reinterpret_cast<uint32_t *>(b + o_cnt);
+        w->mask = reinterpret_cast<uint32_t *>(b + o_mask);
+        w->mask_words = static_cast<int64_t>(mw);
     }
     return off;
 }
@@ -225,7 +221,7 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
         if (!aligned(x, 16) || !aligned(codebook, 16) || !aligned(enc->idx, 4) || !aligned(enc->hnorm, 8))
             return HQMQ_EINVAL;
     }
-    Workspace ws{nullptr, nullptr, nullptr};
+    hqmq::Med3Work ws{};
     if (med) {
         if (!enc->batch_offsets || !enc->status || !aligned(enc->batch_offsets, 8) || !aligned(enc->status, 8))
             return HQMQ_EINVAL;
@@ -235,29 +231,35 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
         if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign)))
             return HQMQ_EINVAL;
         workspace_layout(g, workspace, &ws);
+    } else if (enc->status && !aligned(enc->status, 8)) {
+        return HQMQ_EINVAL;
     }
 
     hipError_t e = hipSuccess;
+    if (med && nb > 0) {
+        // clear the batch histograms the search accumulates
+        e = hqmq::launch_fill_u32(ws.hist, nb * 2048, 0u, stream);
+        if (e != hipSuccess) return HQMQ_EHIP;
+    }
     if (search_begin && hipEventRecord(search_begin, stream) != hipSuccess) return HQMQ_EHIP;
     if (chunks > 0) {
-        e = hqmq::launch_encode_search(g, x, codebook, enc->idx, enc->hnorm, ws.s2, stream);
+        e = hqmq::launch_encode_search(g, x, codebook, enc->idx, enc->hnorm, med && nb > 0 ? &ws : nullptr, stream);
         if (e != hipSuccess) return HQMQ_EHIP;
     }
     if (search_end && hipEventRecord(search_end, stream) != hipSuccess) return HQMQ_EHIP;
     if (med) {
         if (nb > 0) {
-            e = hqmq::launch_med3_select(g, ws.s2, ws.thr, ws.counts, stream);
+            e = hqmq::launch_med3_select(g, x, enc->hnorm, ws, stream);
             if (e == hipSuccess)
                 e = hqmq::launch_med3_scan(nb, ws.counts, enc->batch_offsets, enc->out_capacity, enc->status, stream);
             if (e == hipSuccess)
-                e = hqmq::launch_med3_flag(g, x, ws.s2, ws.thr, enc->batch_offsets, enc->hnorm, enc->out_pos,
-                                           enc->out_val, enc->out_capacity, stream);
+                e = hqmq::launch_med3_gather(g, x, ws, enc->batch_offsets, enc->hnorm, enc->out_pos, enc->out_val,
+                                             enc->out_capacity, stream);
         } else {
             e = hqmq::launch_fill_u64(enc->batch_offsets, 1, 0, stream);
             if (e == hipSuccess) e = hqmq::launch_fill_u64(enc->status, 2, 0, stream);
         }
     } else if (enc->status) {
-        if (!aligned(enc->status, 8)) return HQMQ_EINVAL;
         e = hqmq::launch_fill_u64(enc->status, 2, 0, stream);
     }
     return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;

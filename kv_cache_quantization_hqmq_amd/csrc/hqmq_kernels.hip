@@ -36,7 +36,6 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kEncThreads = 256;   // 4 waves; each wave encodes 64 chunks per step
-constexpr int kMedThreads = 512;
 constexpr int kFlagThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kDecThreads = 256;   // each thread decodes 4 chunks per step
@@ -161,7 +160,6 @@ struct EncArgs {
     const float *cb;
     uint32_t *idx;
     uint16_t *hnorm;
-    float *s2;
     int64_t n_slice;
     int64_t tiles_per_slice;
     int64_t tokens;
@@ -172,27 +170,82 @@ struct EncArgs {
     int32_t log2_cpt;
     int32_t bits;
     int32_t words;
+    // Med3x (batch_chunks == 0: off).  Tiles are grouped by batch and
+    // accumulate the batch's histogram of half-norm codes.
+    int32_t tiles_per_batch;
+    int64_t batch_chunks;
+    int64_t bps;            // batches per slice
+    int64_t nbatch;         // slices * bps
+    int32_t xcd_map;        // 1: a batch's tiles are dispatched to one XCD
+    uint32_t *hist;         // [nbatch][2048] histograms of hnorm >> 4, zeroed
 };
+
+// Chunk range of this block.  Without Med3x: tiles_per_slice tiles per
+// slice.  With Med3x: tiles_per_batch tiles per batch, the last one partial
+// or empty; blocks are dispatched to the 8 XCDs round-robin, so with
+// xcd_map block b serves batch (b / 8 / tiles_per_batch) * 8 + b % 8 and the
+// histogram atomics of a batch stay within one XCD.
+struct TileCoords {
+    int64_t slice, c_begin, c_end;
+    int64_t batch, b_lo, b_n;   // Med3x: batch index, first chunk, chunk count
+};
+
+__device__ __forceinline__ TileCoords tile_coords(const EncArgs &a) {
+    TileCoords t;
+    const int64_t bid = blockIdx.x;
+    if (a.batch_chunks == 0) {
+        t.slice = bid / a.tiles_per_slice;
+        t.c_begin = (bid - t.slice * a.tiles_per_slice) * a.tile_chunks;
+        t.c_end = min(t.c_begin + static_cast<int64_t>(a.tile_chunks), a.n_slice);
+        t.batch = -1;
+        t.b_lo = 0;
+        t.b_n = 0;
+        return t;
+    }
+    const int64_t tpb = a.tiles_per_batch;
+    int64_t batch, tile;
+    if (a.xcd_map) {
+        const int64_t j = bid >> 3;
+        batch = (j / tpb) * 8 + (bid & 7);
+        tile = j - (j / tpb) * tpb;
+    } else {
+        batch = bid / tpb;
+        tile = bid - batch * tpb;
+    }
+    t.batch = batch;
+    t.slice = batch / a.bps;
+    t.b_lo = (batch - t.slice * a.bps) * a.batch_chunks;
+    t.b_n = min(a.batch_chunks, a.n_slice - t.b_lo);
+    t.c_begin = t.b_lo + tile * a.tile_chunks;
+    t.c_end = min(t.c_begin + static_cast<int64_t>(a.tile_chunks), t.b_lo + t.b_n);
+    return t;
+}
+
+__device__ void med3_after_tile(const EncArgs &a, const TileCoords &tc, uint32_t *shist, uint32_t *sh);
 
 // NT_REG > 0: S <= 4 NT_REG and the A operands live in registers.
 // NT_REG == 0: any S <= kMaxS, A read from the LDS copy of the codebook.
-template <int NT_REG, bool F32IN, bool WITH_S2>
+template <int NT_REG, bool F32IN, bool MED>
 __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
     constexpr int kQ = NT_REG > 0 ? 16 * NT_REG : 4 * kMaxS;
     __shared__ __attribute__((aligned(16))) float sq[kQ];
     __shared__ __attribute__((aligned(16))) float sx[4][64 * 4];
     __shared__ uint32_t scode[4][64];
+    __shared__ uint32_t shist[MED ? 2048 : 1];
+    __shared__ uint32_t sh[kEncThreads / 64 + 3];
 
-    const int64_t tile = blockIdx.x;
-    const int64_t slice = tile / a.tiles_per_slice;
-    const int64_t c_begin = (tile - slice * a.tiles_per_slice) * a.tile_chunks;
-    const int64_t c_end = min(c_begin + static_cast<int64_t>(a.tile_chunks), a.n_slice);
+    const TileCoords tc = tile_coords(a);
+    const int64_t slice = tc.slice;
+    const int64_t c_begin = tc.c_begin;
+    const int64_t c_end = tc.c_end;
     const int NT = NT_REG > 0 ? NT_REG : a.NT;
 
     {
         const float *q = a.cb + slice * a.S * 4;
         const int nq = 16 * NT;
         for (int i = threadIdx.x; i < nq; i += kEncThreads) sq[i] = i < 4 * a.S ? double_f16(q[i]) : 0.0f;
+        if constexpr (MED)
+            for (int i = threadIdx.x; i < 2048; i += kEncThreads) shist[i] = 0;
     }
     __syncthreads();
 
@@ -326,7 +379,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
 
         if (valid) {
             a.hnorm[gc] = hn;
-            if constexpr (WITH_S2) a.s2[gc] = s2;
+            if constexpr (MED) atomicAdd(&shist[hn >> 4], 1u);
         }
         scode[wave][lane] = code;
         wave_sync();
@@ -347,6 +400,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
         }
         wave_sync();
     }
+    if constexpr (MED) med3_after_tile(a, tc, shist, sh);
 }
 
 // --------------------------------------------------------------------------
@@ -361,21 +415,25 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
 // for both k blocks); D VGPR 4 a + r of lane l is row 8 a + 4 (l / 32) + r,
 // column l % 32: t_r of s = 8 tile + 2 a + l / 32 for chunk l % 32.
 // --------------------------------------------------------------------------
-template <int NT8, bool WITH_S2>
+template <int NT8, bool MED>
 __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a) {
     constexpr int kQ = NT8 > 0 ? 32 * NT8 : 4 * kMaxS;
     __shared__ __attribute__((aligned(16))) float sq[kQ];
     __shared__ uint32_t scode[4][64];
+    __shared__ uint32_t shist[MED ? 2048 : 1];
+    __shared__ uint32_t sh[kEncThreads / 64 + 3];
 
-    const int64_t tile = blockIdx.x;
-    const int64_t slice = tile / a.tiles_per_slice;
-    const int64_t c_begin = (tile - slice * a.tiles_per_slice) * a.tile_chunks;
-    const int64_t c_end = min(c_begin + static_cast<int64_t>(a.tile_chunks), a.n_slice);
+    const TileCoords tc = tile_coords(a);
+    const int64_t slice = tc.slice;
+    const int64_t c_begin = tc.c_begin;
+    const int64_t c_end = tc.c_end;
     const int NT = NT8 > 0 ? NT8 : (a.S + 7) / 8;
     {
         const float *q = a.cb + slice * a.S * 4;
         const int nq = 32 * NT;
         for (int i = threadIdx.x; i < nq; i += kEncThreads) sq[i] = i < 4 * a.S ? double_f16(q[i]) : 0.0f;
+        if constexpr (MED)
+            for (int i = threadIdx.x; i < 2048; i += kEncThreads) shist[i] = 0;
     }
     __syncthreads();
 
@@ -488,7 +546,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
         const uint32_t code = s2 > 0.0f ? static_cast<uint32_t>(24 * s_best + primary_index(&sq[4 * s_best], v0, v1, v2, v3)) : 0u;
         if (valid) {
             a.hnorm[slice * a.n_slice + c] = hn;
-            if constexpr (WITH_S2) a.s2[slice * a.n_slice + c] = s2;
+            if constexpr (MED) atomicAdd(&shist[hn >> 4], 1u);
         }
         scode[wave][lane] = code;
         wave_sync();
@@ -507,6 +565,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
         }
         wave_sync();
     }
+    if constexpr (MED) med3_after_tile(a, tc, shist, sh);
 }
 
 // --------------------------------------------------------------------------
@@ -542,81 +601,255 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *total, T *sh) {
 }
 
 // --------------------------------------------------------------------------
-// Med3x: exact lower median of s2 per batch (three radix digits of the fp32
-// bit pattern: non-negative floats order like their bits), threshold
-// fl(fl(C*C) * median) and the count of s2 > threshold.
+// Med3x.  The batch's median is the exact lower median of its fp32 squared
+// norms s2 (rank floor((n-1)/2)); outliers are the chunks with
+// s2 > fl(fl(C*C) * median) (r > C r_med, strict).
+//
+// The stored half-norm code h(s2) = fp16_rn(sqrt_rn(s2) / 2) is monotone in
+// s2, so ranks by s2 refine ranks by h: h_a < h_b implies s2_a < s2_b.  The
+// search kernel histograms h >> 4 per batch; the select kernel finds the
+// median's code h_med and its rank among the chunks with that code, then the
+// exact s2 median among those few chunks (s2 recomputed from x with the same
+// declared fp32 operations); a chunk is an outlier if h > h(thr), or if
+// h == h(thr) and its exact s2 > thr.
 // --------------------------------------------------------------------------
-struct MedArgs {
-    const float *s2;
-    float *thr;
-    uint32_t *counts;
+
+// Called by every thread of a Med3x tile after its search loop: merge the
+// tile's code histogram into its batch's (read by the next kernel).
+__device__ void med3_after_tile(const EncArgs &a, const TileCoords &tc, uint32_t *shist, uint32_t *) {
+    __syncthreads();
+    uint32_t *gh = a.hist + tc.batch * 2048;
+    for (int i = threadIdx.x; i < 2048; i += kEncThreads) {
+        const uint32_t v = shist[i];
+        if (v) atomicAdd(&gh[i], v);
+    }
+}
+
+constexpr int kSelThreads = 256;
+constexpr int kCandCap = 4096;
+
+struct SelArgs {
+    const void *x;
+    const uint16_t *hnorm;
+    const uint32_t *hist;   // [nbatch][2048] counts of h >> 4
+    uint32_t *counts;       // [nbatch]
+    uint32_t *mask;         // [nbatch][mask_words]
+    int64_t mask_words;
     int64_t n_slice;
     int64_t batch_chunks;
     int64_t bps;
     float C;
+    int32_t f32;
 };
 
-__global__ __launch_bounds__(kMedThreads) void med3_select_kernel(MedArgs a) {
+// Declared fp32 squared norm of chunk gc (the search kernel's operations).
+__device__ __forceinline__ float chunk_s2(const SelArgs &a, int64_t gc) {
+    float v0, v1, v2, v3;
+    if (a.f32) {
+        const float4 f = static_cast<const float4 *>(a.x)[gc];
+        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
+    } else {
+        const uint2 r = static_cast<const uint2 *>(a.x)[gc];
+        v0 = f16_bits_to_f32(static_cast<uint16_t>(r.x));
+        v1 = f16_bits_to_f32(static_cast<uint16_t>(r.x >> 16));
+        v2 = f16_bits_to_f32(static_cast<uint16_t>(r.y));
+        v3 = f16_bits_to_f32(static_cast<uint16_t>(r.y >> 16));
+    }
+    float s2 = v0 * v0;
+    s2 = __builtin_fmaf(v1, v1, s2);
+    s2 = __builtin_fmaf(v2, v2, s2);
+    s2 = __builtin_fmaf(v3, v3, s2);
+    return s2;
+}
+
+// Digit of rank k in hist[0 .. nbins) (nbins a multiple of the block size or
+// smaller than it): found[0] = digit, found[1] = rank within it.  All
+// threads of the block must call it.
+__device__ void select_digit(const uint32_t *hist, int nbins, uint32_t k, uint32_t *found, uint32_t *sh) {
+    const int per = nbins >= kSelThreads ? nbins / kSelThreads : 1;
+    const int first = threadIdx.x * per;
+    uint32_t local = 0;
+    for (int j = 0; j < per; ++j)
+        if (first + j < nbins) local += hist[first + j];
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<uint32_t, kSelThreads>(local, &tot, sh);
+    if (k >= ex && k < ex + local) {
+        uint32_t cum = ex;
+        for (int j = 0; j < per; ++j) {
+            const uint32_t h = hist[first + j];
+            if (k < cum + h) {
+                found[0] = static_cast<uint32_t>(first + j);
+                found[1] = k - cum;
+                break;
+            }
+            cum += h;
+        }
+    }
+    __syncthreads();
+}
+
+// The k-th smallest (0-based) of the fp32 values s2 of the chunks of the
+// batch whose code equals hsel, by three radix digits of the bit pattern.
+// Values come from vals[0 .. m) in LDS when vals != nullptr, otherwise they
+// are recomputed from x in passes over the batch.
+__device__ float kth_s2(const SelArgs &a, const uint16_t *codes, int64_t gbase, int64_t n, uint32_t hsel,
+                        const float *vals, uint32_t m, uint32_t k, uint32_t *hist, uint32_t *found,
+                        uint32_t *sh) {
+    const int shifts[3] = {20, 9, 0};
+    const int widths[3] = {11, 11, 9};
+    uint32_t prefix = 0;
+    for (int d = 0; d < 3; ++d) {
+        const int shift = shifts[d], width = widths[d], above = shift + width;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int i = threadIdx.x; i < (1 << width); i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        if (vals) {
+            for (uint32_t i = threadIdx.x; i < m; i += kSelThreads) {
+                const uint32_t key = __float_as_uint(vals[i]);
+                if ((key >> above) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+            }
+        } else {
+            for (int64_t i = threadIdx.x; i < n; i += kSelThreads) {
+                if (codes[i] != hsel) continue;
+                const uint32_t key = __float_as_uint(chunk_s2(a, gbase + i));
+                if ((key >> above) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+            }
+        }
+        __syncthreads();
+        select_digit(hist, 1 << width, k, found, sh);
+        prefix = (prefix << width) | found[0];
+        k = found[1];
+        __syncthreads();
+    }
+    return __uint_as_float(prefix);
+}
+
+__global__ __launch_bounds__(kSelThreads) void med3_select_kernel(SelArgs a) {
     __shared__ uint32_t hist[2048];
-    __shared__ uint32_t sh[kMedThreads / 64 + 1];
-    __shared__ uint32_t found[2];
+    __shared__ uint32_t cand[kCandCap];
+    __shared__ float candv[kCandCap];
+    __shared__ uint32_t sh[kSelThreads / 64 + 4];
+    uint32_t *found = sh + kSelThreads / 64 + 1;
 
     const int64_t bid = blockIdx.x;
     const int64_t slice = bid / a.bps;
     const int64_t lo = (bid - slice * a.bps) * a.batch_chunks;
     const int64_t n = min(a.batch_chunks, a.n_slice - lo);
-    const uint32_t *keys = reinterpret_cast<const uint32_t *>(a.s2 + slice * a.n_slice + lo);
+    const int64_t gbase = slice * a.n_slice + lo;
+    const uint16_t *codes = a.hnorm + gbase;
+    const uint32_t k = static_cast<uint32_t>((n - 1) / 2);
 
-    uint32_t k = static_cast<uint32_t>((n - 1) / 2);
-    uint32_t prefix = 0;
-    const int shifts[3] = {20, 9, 0};
-    const int widths[3] = {11, 11, 9};
-    for (int d = 0; d < 3; ++d) {
-        const int shift = shifts[d];
-        const int width = widths[d];
-        const int nbins = 1 << width;
-        const uint32_t dmask = static_cast<uint32_t>(nbins - 1);
-        const int above = shift + width;
-        for (int i = threadIdx.x; i < nbins; i += kMedThreads) hist[i] = 0;
-        __syncthreads();
-        for (int64_t i = threadIdx.x; i < n; i += kMedThreads) {
-            const uint32_t key = keys[i];
-            if ((key >> above) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        const int per = nbins / kMedThreads;
-        uint32_t local = 0;
-        for (int j = 0; j < per; ++j) local += hist[threadIdx.x * per + j];
-        uint32_t tot;
-        const uint32_t ex = block_exclusive_scan<uint32_t, kMedThreads>(local, &tot, sh);
-        if (k >= ex && k < ex + local) {
-            uint32_t cum = ex;
-            for (int j = 0; j < per; ++j) {
-                const uint32_t h = hist[threadIdx.x * per + j];
-                if (k < cum + h) {
-                    found[0] = static_cast<uint32_t>(threadIdx.x * per + j);
-                    found[1] = k - cum;
-                    break;
+    // code bits 14..4 (bit 15 is 0 before outliers are flagged)
+    const uint32_t *gh = a.hist + bid * 2048;
+    for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = gh[i];
+    __syncthreads();
+    select_digit(hist, 2048, k, found, sh);
+    const uint32_t d1 = found[0];
+    const uint32_t k1 = found[1];
+    const uint32_t m1 = hist[d1];
+    __syncthreads();
+
+    // code bits 3..0 among the chunks of digit d1; their positions are kept
+    // in LDS when they fit
+    const bool keep = m1 <= static_cast<uint32_t>(kCandCap);
+    if (threadIdx.x < 16) hist[threadIdx.x] = 0;
+    if (threadIdx.x == 0) sh[kSelThreads / 64 + 3] = 0;
+    __syncthreads();
+    {
+        // 4 codes per 8-byte load (a batch starts at a multiple of 4 chunks)
+        const uint2 *c4 = reinterpret_cast<const uint2 *>(codes);
+        const int64_t n4 = n >> 2;
+        constexpr int U = 8;
+        for (int64_t i0 = threadIdx.x; i0 < n4; i0 += static_cast<int64_t>(kSelThreads) * U) {
+            uint2 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + static_cast<int64_t>(u) * kSelThreads;
+                v[u] = i < n4 ? c4[i] : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = i0 + static_cast<int64_t>(u) * kSelThreads;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = e < 2 ? v[u].x : v[u].y;
+                    const uint32_t c = (w >> (16 * (e & 1))) & 0xFFFFu;
+                    if ((c >> 4) != d1 || i >= n4) continue;
+                    atomicAdd(&hist[c & 15u], 1u);
+                    if (keep) {
+                        const uint32_t slot = atomicAdd(&sh[kSelThreads / 64 + 3], 1u);
+                        if (slot < static_cast<uint32_t>(kCandCap)) cand[slot] = static_cast<uint32_t>(4 * i + e);
+                    }
                 }
-                cum += h;
+            }
+        }
+        for (int64_t i = 4 * n4 + threadIdx.x; i < n; i += kSelThreads) {
+            const uint32_t c = codes[i];
+            if ((c >> 4) != d1) continue;
+            atomicAdd(&hist[c & 15u], 1u);
+            if (keep) {
+                const uint32_t slot = atomicAdd(&sh[kSelThreads / 64 + 3], 1u);
+                if (slot < static_cast<uint32_t>(kCandCap)) cand[slot] = static_cast<uint32_t>(i);
+            }
+        }
+    }
+    __syncthreads();
+    select_digit(hist, 16, k1, found, sh);
+    const uint32_t hmed = (d1 << 4) | found[0];
+    const uint32_t k2 = found[1];
+    __syncthreads();
+
+    // exact s2 of the chunks with code hmed, then the k2-th smallest
+    float med;
+    if (keep) {
+        if (threadIdx.x == 0) sh[kSelThreads / 64 + 3] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < m1; i += kSelThreads) {
+            const uint32_t off = min(cand[i], static_cast<uint32_t>(n - 1));
+            if (codes[off] == hmed) {
+                const uint32_t slot = atomicAdd(&sh[kSelThreads / 64 + 3], 1u);
+                if (slot < static_cast<uint32_t>(kCandCap)) candv[slot] = chunk_s2(a, gbase + off);
             }
         }
         __syncthreads();
-        prefix = (prefix << width) | found[0];
-        k = found[1];
+        const uint32_t m2 = min(sh[kSelThreads / 64 + 3], static_cast<uint32_t>(kCandCap));
         __syncthreads();
+        med = kth_s2(a, codes, gbase, n, hmed, candv, m2, k2, hist, found, sh);
+    } else {
+        med = kth_s2(a, codes, gbase, n, hmed, nullptr, 0, k2, hist, found, sh);
     }
-    const float med = __uint_as_float(prefix);
     const float cc = a.C * a.C;
     const float thr = cc * med;
+    const uint32_t hthr = half_norm_code(thr);
+
+    // outlier bitmask: wave w ballots 64 consecutive chunks at a time, eight
+    // groups per iteration in flight
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint32_t *mrow = a.mask + bid * a.mask_words;
     uint32_t cnt = 0;
-    for (int64_t i = threadIdx.x; i < n; i += kMedThreads) cnt += __uint_as_float(keys[i]) > thr ? 1u : 0u;
-    uint32_t tot;
-    block_exclusive_scan<uint32_t, kMedThreads>(cnt, &tot, sh);
-    if (threadIdx.x == 0) {
-        a.thr[bid] = thr;
-        a.counts[bid] = tot;
+    constexpr int U = 8;
+    for (int64_t g0 = 64 * wave; g0 < n; g0 += 64 * 4 * U) {
+        uint32_t cv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = g0 + 64 * 4 * u + lane;
+            cv[u] = i < n ? codes[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t gb = g0 + 64 * 4 * u;
+            const int64_t i = gb + lane;
+            bool f = i < n && cv[u] > hthr;
+            if (i < n && cv[u] == hthr) f = chunk_s2(a, gbase + i) > thr;
+            const uint64_t m = __ballot(f);
+            if (gb < n && lane < 2) mrow[(gb >> 5) + lane] = static_cast<uint32_t>(m >> (32 * lane));
+            cnt += lane == 0 ? static_cast<uint32_t>(__popcll(m)) : 0u;
+        }
     }
+    uint32_t tot;
+    block_exclusive_scan<uint32_t, kSelThreads>(cnt, &tot, sh);
+    if (threadIdx.x == 0) a.counts[bid] = tot;
 }
 
 __global__ __launch_bounds__(kScanThreads) void med3_scan_kernel(int64_t nb, const uint32_t *counts,
@@ -641,10 +874,9 @@ __global__ __launch_bounds__(kScanThreads) void med3_scan_kernel(int64_t nb, con
     }
 }
 
-struct FlagArgs {
+struct GatherArgs {
     const void *x;
-    const float *s2;
-    const float *thr;
+    const uint32_t *mask;
     const uint64_t *offsets;
     uint16_t *hnorm;
     uint32_t *out_pos;
@@ -653,40 +885,34 @@ struct FlagArgs {
     int64_t n_slice;
     int64_t batch_chunks;
     int64_t bps;
+    int64_t mask_words;
     int32_t f32;
 };
 
-// Ordered outlier write: one block per batch walks the batch in order, a
-// block scan gives every outlier its rank, and the entry lands at
-// batch_offsets[batch] + rank (dropped past the capacity).
-__global__ __launch_bounds__(kFlagThreads) void med3_flag_kernel(FlagArgs a) {
+// Ordered outlier write: one block per batch walks the batch's bitmask in
+// order, a block scan of the word popcounts ranks every outlier, and its
+// entry lands at batch_offsets[batch] + rank (dropped past the capacity).
+// The chunk's half-norm record gets the outlier flag (bit 15).
+__global__ __launch_bounds__(kFlagThreads) void med3_gather_kernel(GatherArgs a) {
     __shared__ uint32_t sh[kFlagThreads / 64 + 1];
     const int64_t bid = blockIdx.x;
     const int64_t slice = bid / a.bps;
     const int64_t lo = (bid - slice * a.bps) * a.batch_chunks;
     const int64_t n = min(a.batch_chunks, a.n_slice - lo);
+    const int64_t nw = (n + 31) >> 5;
     const int64_t sbase = slice * a.n_slice;
-    const float thr = a.thr[bid];
-    const uint64_t base = a.offsets[bid];
-    const float *keys = a.s2 + sbase + lo;
-
-    uint64_t running = 0;
-    for (int64_t off = 0; off < n; off += 4 * kFlagThreads) {
-        const int64_t i0 = off + 4 * threadIdx.x;
-        bool f[4];
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            f[e] = (i0 + e < n) && keys[i0 + e] > thr;
-            cnt += f[e] ? 1u : 0u;
-        }
+    const uint32_t *mrow = a.mask + bid * a.mask_words;
+    uint64_t running = a.offsets[bid];
+    for (int64_t w0 = 0; w0 < nw; w0 += kFlagThreads) {
+        const int64_t w = w0 + threadIdx.x;
+        uint32_t word = w < nw ? mrow[w] : 0u;
         uint32_t tot;
-        const uint32_t ex = block_exclusive_scan<uint32_t, kFlagThreads>(cnt, &tot, sh);
-        uint64_t pos = base + running + ex;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (!f[e]) continue;
-            const int64_t cs = lo + i0 + e;       // chunk position in the slice
+        const uint32_t ex = block_exclusive_scan<uint32_t, kFlagThreads>(static_cast<uint32_t>(__popc(word)), &tot, sh);
+        uint64_t pos = running + ex;
+        while (word) {
+            const int b = __ffs(word) - 1;
+            word &= word - 1u;
+            const int64_t cs = lo + 32 * w + b;   // chunk position in the slice
             const int64_t gc = sbase + cs;
             if (pos < a.capacity) {
                 a.out_pos[pos] = static_cast<uint32_t>(cs);
@@ -705,6 +931,11 @@ __global__ __launch_bounds__(kFlagThreads) void med3_flag_kernel(FlagArgs a) {
         }
         running += tot;
     }
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t v) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
 }
 
 __global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v) {
@@ -932,48 +1163,60 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // Launchers.
 // --------------------------------------------------------------------------
 hipError_t launch_encode_search(const Geometry &g, const void *x, const float *codebook,
-                                uint32_t *idx, uint16_t *hnorm, float *s2, hipStream_t st) {
+                                uint32_t *idx, uint16_t *hnorm, const Med3Work *med, hipStream_t st) {
     const int64_t total = g.slices * g.n_slice;
     if (total == 0) return hipSuccess;
-    // tiles: multiples of 256 chunks (4 waves x 64), enough blocks to fill
-    // 256 CUs several times, at most 8192 chunks so a block's codebook setup
-    // stays amortised
-    int64_t tile = round_up(ceil_div(total, 4096), 256);
-    tile = tile < 256 ? 256 : (tile > 8192 ? 8192 : tile);
-    EncArgs a;
+    EncArgs a = {};
     a.x = x;
     a.cb = codebook;
     a.idx = idx;
     a.hnorm = hnorm;
-    a.s2 = s2;
     a.n_slice = g.n_slice;
-    a.tiles_per_slice = ceil_div(g.n_slice, tile);
     a.tokens = g.tokens;
-    a.tile_chunks = static_cast<int32_t>(tile);
     a.S = g.S;
     a.NT = static_cast<int32_t>(ceil_div(g.S, 4));
     a.cpt = g.cpt;
     a.log2_cpt = __builtin_ctz(static_cast<unsigned>(g.cpt));
     a.bits = g.bits;
     a.words = g.words;
-    const dim3 grid(static_cast<unsigned>(g.slices * a.tiles_per_slice));
+    int64_t blocks;
+    if (med) {
+        // tiles of at most 8192 chunks inside each batch
+        int64_t tile = round_up(g.batch_chunks, 256);
+        if (tile > 8192) tile = 8192;
+        a.tile_chunks = static_cast<int32_t>(tile);
+        a.tiles_per_batch = static_cast<int32_t>(ceil_div(g.batch_chunks, tile));
+        a.batch_chunks = g.batch_chunks;
+        a.bps = g.batches_per_slice;
+        a.nbatch = g.slices * g.batches_per_slice;
+        a.xcd_map = (a.nbatch % 8 == 0 && a.tiles_per_batch > 1) ? 1 : 0;
+        a.hist = med->hist;
+        a.tiles_per_slice = 0;
+        blocks = a.nbatch * a.tiles_per_batch;
+    } else {
+        // tiles: multiples of 256 chunks (4 waves x 64), enough blocks to fill
+        // 256 CUs several times, at most 8192 chunks so a block's codebook
+        // setup stays amortised
+        int64_t tile = round_up(ceil_div(total, 4096), 256);
+        tile = tile < 256 ? 256 : (tile > 8192 ? 8192 : tile);
+        a.tile_chunks = static_cast<int32_t>(tile);
+        a.tiles_per_slice = ceil_div(g.n_slice, tile);
+        a.batch_chunks = 0;
+        blocks = g.slices * a.tiles_per_slice;
+    }
+    const dim3 grid(static_cast<unsigned>(blocks));
     const dim3 block(kEncThreads);
-    const bool ws2 = s2 != nullptr;
-#define HQMQ_ENC(NT, F32, WS2) hipLaunchKernelGGL((encode_search_kernel<NT, F32, WS2>), grid, block, 0, st, a)
+    const bool m = med != nullptr;
+#define HQMQ_ENC(NT, F32, MED) hipLaunchKernelGGL((encode_search_kernel<NT, F32, MED>), grid, block, 0, st, a)
 #define HQMQ_ENC_NT(NT)                          \
     do {                                         \
-        if (g.f32) {                             \
-            if (ws2) HQMQ_ENC(NT, true, true);   \
-            else HQMQ_ENC(NT, true, false);      \
-        } else {                                 \
-            if (ws2) HQMQ_ENC(NT, false, true);  \
-            else HQMQ_ENC(NT, false, false);     \
-        }                                        \
+        if (m) HQMQ_ENC(NT, true, true);         \
+        else HQMQ_ENC(NT, true, false);          \
     } while (0)
-#define HQMQ_ENC_H(NT8)                                                                             \
-    do {                                                                                            \
-        if (ws2) hipLaunchKernelGGL((encode_search_h_kernel<NT8, true>), grid, block, 0, st, a);   \
-        else hipLaunchKernelGGL((encode_search_h_kernel<NT8, false>), grid, block, 0, st, a);      \
+#define HQMQ_ENC_H(NT8)                                                                            \
+    do {                                                                                           \
+        if (m) hipLaunchKernelGGL((encode_search_h_kernel<NT8, true>), grid, block, 0, st, a);    \
+        else hipLaunchKernelGGL((encode_search_h_kernel<NT8, false>), grid, block, 0, st, a);     \
     } while (0)
     if (g.f32) {
         if (a.NT == 2) HQMQ_ENC_NT(2);
@@ -991,22 +1234,6 @@ hipError_t launch_encode_search(const Geometry &g, const void *x, const float *c
     return hipGetLastError();
 }
 
-hipError_t launch_med3_select(const Geometry &g, const float *s2, float *thr, uint32_t *counts,
-                              hipStream_t st) {
-    const int64_t nb = g.slices * g.batches_per_slice;
-    if (nb == 0) return hipSuccess;
-    MedArgs a;
-    a.s2 = s2;
-    a.thr = thr;
-    a.counts = counts;
-    a.n_slice = g.n_slice;
-    a.batch_chunks = g.batch_chunks;
-    a.bps = g.batches_per_slice;
-    a.C = g.med_C;
-    hipLaunchKernelGGL(med3_select_kernel, dim3(static_cast<unsigned>(nb)), dim3(kMedThreads), 0, st, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_med3_scan(int64_t batches, const uint32_t *counts, uint64_t *offsets,
                             uint64_t capacity, uint64_t *status, hipStream_t st) {
     hipLaunchKernelGGL(med3_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, batches, counts, offsets,
@@ -1014,15 +1241,34 @@ hipError_t launch_med3_scan(int64_t batches, const uint32_t *counts, uint64_t *o
     return hipGetLastError();
 }
 
-hipError_t launch_med3_flag(const Geometry &g, const void *x, const float *s2, const float *thr,
-                            const uint64_t *offsets, uint16_t *hnorm, uint32_t *out_pos,
-                            uint16_t *out_val, uint64_t capacity, hipStream_t st) {
+hipError_t launch_med3_select(const Geometry &g, const void *x, const uint16_t *hnorm, const Med3Work &med,
+                              hipStream_t st) {
     const int64_t nb = g.slices * g.batches_per_slice;
     if (nb == 0) return hipSuccess;
-    FlagArgs a;
+    SelArgs a;
     a.x = x;
-    a.s2 = s2;
-    a.thr = thr;
+    a.hnorm = hnorm;
+    a.hist = med.hist;
+    a.counts = med.counts;
+    a.mask = med.mask;
+    a.mask_words = med.mask_words;
+    a.n_slice = g.n_slice;
+    a.batch_chunks = g.batch_chunks;
+    a.bps = g.batches_per_slice;
+    a.C = g.med_C;
+    a.f32 = g.f32;
+    hipLaunchKernelGGL(med3_select_kernel, dim3(static_cast<unsigned>(nb)), dim3(kSelThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_med3_gather(const Geometry &g, const void *x, const Med3Work &med,
+                              const uint64_t *offsets, uint16_t *hnorm, uint32_t *out_pos,
+                              uint16_t *out_val, uint64_t capacity, hipStream_t st) {
+    const int64_t nb = g.slices * g.batches_per_slice;
+    if (nb == 0) return hipSuccess;
+    GatherArgs a;
+    a.x = x;
+    a.mask = med.mask;
     a.offsets = offsets;
     a.hnorm = hnorm;
     a.out_pos = out_pos;
@@ -1031,8 +1277,15 @@ hipError_t launch_med3_flag(const Geometry &g, const void *x, const float *s2, c
     a.n_slice = g.n_slice;
     a.batch_chunks = g.batch_chunks;
     a.bps = g.batches_per_slice;
+    a.mask_words = med.mask_words;
     a.f32 = g.f32;
-    hipLaunchKernelGGL(med3_flag_kernel, dim3(static_cast<unsigned>(nb)), dim3(kFlagThreads), 0, st, a);
+    hipLaunchKernelGGL(med3_gather_kernel, dim3(static_cast<unsigned>(nb)), dim3(kFlagThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, st, p, n, v);
     return hipGetLastError();
 }
 

@@ -24,13 +24,22 @@ struct Geometry {
     float med_C;
 };
 
-// Encode: nearest codeword, norm code and (when s2 != nullptr) the fp32
-// squared norms for Med3x.
-hipError_t launch_encode_search(const Geometry &g, const void *x, const float *codebook,
-                                uint32_t *idx, uint16_t *hnorm, float *s2, hipStream_t st);
+// Med3x scratch (inside the caller's workspace).
+struct Med3Work {
+    uint32_t *hist;      // [batches][2048] histograms of the half-norm code >> 4
+    uint32_t *counts;    // [batches] outliers per batch
+    uint32_t *mask;      // [batches][mask_words] outlier bitmasks
+    int64_t mask_words;
+};
 
-// Med3x: per-batch exact lower median, threshold and outlier count.
-hipError_t launch_med3_select(const Geometry &g, const float *s2, float *thr, uint32_t *counts,
+// Encode: nearest codeword and norm code per chunk; with med != nullptr the
+// launch also accumulates each batch's code histogram (med->hist must be
+// zero).
+hipError_t launch_encode_search(const Geometry &g, const void *x, const float *codebook,
+                                uint32_t *idx, uint16_t *hnorm, const Med3Work *med, hipStream_t st);
+
+// Med3x: per batch, exact median, threshold, outlier count and bitmask.
+hipError_t launch_med3_select(const Geometry &g, const void *x, const uint16_t *hnorm, const Med3Work &med,
                               hipStream_t st);
 
 // Exclusive scan of the per-batch counts into batch_offsets, total and
@@ -38,14 +47,15 @@ hipError_t launch_med3_select(const Geometry &g, const float *s2, float *thr, ui
 hipError_t launch_med3_scan(int64_t batches, const uint32_t *counts, uint64_t *offsets,
                             uint64_t capacity, uint64_t *status, hipStream_t st);
 
-// Ordered side-list write and hnorm flagging.
-hipError_t launch_med3_flag(const Geometry &g, const void *x, const float *s2, const float *thr,
-                            const uint64_t *offsets, uint16_t *hnorm, uint32_t *out_pos,
-                            uint16_t *out_val, uint64_t capacity, hipStream_t st);
+// Ordered side-list write from the bitmasks, outlier flag into hnorm.
+hipError_t launch_med3_gather(const Geometry &g, const void *x, const Med3Work &med,
+                              const uint64_t *offsets, uint16_t *hnorm, uint32_t *out_pos,
+                              uint16_t *out_val, uint64_t capacity, hipStream_t st);
 
-// Zero a few u64 words (status / offsets of empty or Med3x-off calls) with a
-// kernel rather than a memset node.
+// Fill words with a kernel rather than a memset node (status / offsets of
+// empty or Med3x-off calls, Med3x histograms).
 hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
 
 // Decode: bulk gather-multiply plus outlier re-insertion.
 hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t *hnorm,

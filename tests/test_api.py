@@ -131,7 +131,7 @@ def test_sizes_follow_the_layout(L, H, T, D, S, dt, Bt):
         assert s.offsets_bytes == (s.batches + 1) * 8
         per = [min(Bc, T - i * Bc) * cpt // 2 for i in range(nb)]
         assert s.max_outliers == L * H * sum(per)
-        assert s.workspace_bytes >= s.chunks * 4 + s.batches * 8
+        assert s.workspace_bytes >= s.batches * (2048 * 4 + 4) + s.chunks // 8
     else:
         assert s.workspace_bytes == 0
 
