@@ -1046,34 +1046,85 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     const uint32_t kmask = (1u << a.bits) - 1u;
     const int last_word = a.words - 1;
 
-    // Each lane decodes 2 chunks per step, so one 16-byte store per lane
-    // writes 1 KB of contiguous fp16 output per wave instruction.  Every
-    // load is unconditional (clamped to the row) and kDecUnroll steps' loads
-    // are issued before any is used.
+    // Each wave decodes a contiguous quarter of the block's range, 2 chunks
+    // per lane per step, so one 16-byte store per lane writes 1 KB of
+    // contiguous fp16 output.  Outlier chunks (bit 15 of the half-norm code)
+    // take their side-list values in the same pass: the side list is sorted
+    // by position, so a wave finds the first entry at or after its range
+    // once and then ranks its flagged chunks step by step with a ballot.
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t wlen = (r1 - r0 + 4 * 128 - 1) / (4 * 128) * 128;   // multiple of a wave step
+    const int64_t w0 = min(r0 + wave * wlen, r1);
+    const int64_t w1 = min(w0 + wlen, r1);
+    const uint2 *sval = reinterpret_cast<const uint2 *>(a.out_val);
+
+    // first side-list entry with position >= w0 (64-way search per round)
+    uint64_t e_next = 0, e_end = 0;
+    if (a.bps > 0 && w0 < w1) {
+        const int64_t bl = w0 / a.batch_chunks;
+        const int64_t bh = (w1 - 1) / a.batch_chunks;
+        uint64_t lo = a.offsets[slice * a.bps + bl];
+        uint64_t hi = a.offsets[slice * a.bps + bh + 1];
+        hi = hi < a.capacity ? hi : a.capacity;
+        lo = lo < hi ? lo : hi;
+        e_end = hi;
+        while (hi > lo) {
+            const uint64_t len = hi - lo;
+            const uint64_t step = (len + 63) / 64;
+            const uint64_t i = lo + static_cast<uint64_t>(lane) * step;
+            const bool below = i < hi && static_cast<int64_t>(a.out_pos[i]) < w0;
+            const int cnt = __popcll(__ballot(below));
+            if (cnt == 0) break;
+            const uint64_t nlo = lo + static_cast<uint64_t>(cnt - 1) * step + 1;
+            const uint64_t nhi = lo + static_cast<uint64_t>(cnt) * step;
+            hi = nhi < hi ? nhi : hi;
+            lo = nlo;
+        }
+        e_next = lo;
+    }
+
     auto load = [&](int64_t c) {
         DecPair d;
         const int64_t row = c >> a.log2_cpt;
         const int o = static_cast<int>(c & cmask) * a.bits;
-        const int w0 = o >> 5;
+        const int w = o >> 5;
         const uint32_t *rp = idx_s + row * a.words;
-        d.w0 = rp[w0];
-        d.w1 = rp[min(w0 + 1, last_word)];
+        d.w0 = rp[w];
+        d.w1 = rp[min(w + 1, last_word)];
         d.sh = static_cast<uint32_t>(o & 31);
         d.h = hn_s[c >> 1];
         return d;
     };
-    constexpr int kStep = 2 * kDecThreads;   // chunks per block step
-    for (int64_t c0 = r0 + 2 * threadIdx.x; c0 < r1; c0 += static_cast<int64_t>(kStep) * kDecUnroll) {
+    constexpr int kWaveStep = 128;   // chunks per wave step
+    for (int64_t c0 = w0 + 2 * lane; c0 < w1; c0 += static_cast<int64_t>(kWaveStep) * kDecUnroll) {
         DecPair pd[kDecUnroll];
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
-            const int64_t c = c0 + static_cast<int64_t>(u) * kStep;
-            pd[u] = c < r1 ? load(c) : DecPair{};
+            const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
+            pd[u] = c < w1 ? load(c) : DecPair{};
+        }
+        // side-list values of this iteration's flagged chunks, in order
+        uint2 ov[kDecUnroll][2];
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+            const bool f0 = (pd[u].h & 0x8000u) != 0;
+            const bool f1 = (pd[u].h & 0x80000000u) != 0;
+            const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m0 >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m0), 0u)) +
+                                   __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m1 >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m1), 0u));
+            const uint64_t e0 = e_next + below;
+            const uint64_t e1 = e0 + (f0 ? 1 : 0);
+            ov[u][0] = f0 && e0 < e_end ? sval[e0] : make_uint2(0u, 0u);
+            ov[u][1] = f1 && e1 < e_end ? sval[e1] : make_uint2(0u, 0u);
+            e_next += static_cast<uint64_t>(__popcll(m0) + __popcll(m1));
         }
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
-            const int64_t c = c0 + static_cast<int64_t>(u) * kStep;
-            if (c >= r1) break;
+            const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
+            if (c >= w1) break;
             const DecPair &cur = pd[u];
             const uint64_t win = ((static_cast<uint64_t>(cur.w1) << 32) | cur.w0) >> cur.sh;
             f32x4 out[2];
@@ -1081,8 +1132,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
             for (int i = 0; i < 2; ++i) {
                 uint32_t k = static_cast<uint32_t>(win >> (i * a.bits)) & kmask;
                 k = min(k, static_cast<uint32_t>(ncw - 1));
-                // flagged (outlier) chunks get a placeholder here and their
-                // side-list values after the barrier below
                 const uint16_t hi = static_cast<uint16_t>(cur.h >> (16 * i));
                 const float r = 2.0f * f16_bits_to_f32(static_cast<uint16_t>(hi & 0x7FFFu));
                 f32x4 cw;
@@ -1095,6 +1144,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
                     cw = codeword_f32(qa, static_cast<int>(k) - 24 * s);
                 }
                 out[i] = r * cw;
+                if (hi & 0x8000u) {
+                    const uint2 v = ov[u][i];
+                    const f32x4 f = {f16_bits_to_f32(static_cast<uint16_t>(v.x)), f16_bits_to_f32(static_cast<uint16_t>(v.x >> 16)),
+                                     f16_bits_to_f32(static_cast<uint16_t>(v.y)), f16_bits_to_f32(static_cast<uint16_t>(v.y >> 16))};
+                    out[i] = f;
+                }
             }
             const int64_t gc = sbase + c;
             if constexpr (F32OUT) {
@@ -1111,44 +1166,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
                                    (static_cast<uint32_t>(f32_to_f16_bits(out[i][3])) << 16);
                 }
                 __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.y) + 4 * gc));
-            }
-        }
-    }
-
-    if (a.bps > 0) {
-        // the bulk stores above are complete and visible to the block
-        __syncthreads();
-        // side-list entries of [r0, r1): the batches covering the range give
-        // an index window; a 256-way search finds the first position >= r0.
-        const int64_t bl = r0 / a.batch_chunks;
-        const int64_t bh = (r1 - 1) / a.batch_chunks;
-        uint64_t e1 = a.offsets[slice * a.bps + bh + 1];
-        uint64_t lo = a.offsets[slice * a.bps + bl];
-        e1 = e1 < a.capacity ? e1 : a.capacity;
-        lo = lo < e1 ? lo : e1;
-        uint64_t hi = e1;
-        while (hi > lo) {
-            const uint64_t len = hi - lo;
-            const uint64_t step = (len + kDecThreads - 1) / kDecThreads;
-            const uint64_t i = lo + static_cast<uint64_t>(threadIdx.x) * step;
-            const bool below = i < hi && static_cast<int64_t>(a.out_pos[i]) < r0;
-            const int cnt = __syncthreads_count(below);
-            if (cnt == 0) break;
-            const uint64_t nlo = lo + static_cast<uint64_t>(cnt - 1) * step + 1;
-            const uint64_t nhi_c = lo + static_cast<uint64_t>(cnt) * step;
-            hi = nhi_c < hi ? nhi_c : hi;
-            lo = nlo;
-        }
-        for (uint64_t e = lo + threadIdx.x; e < e1; e += kDecThreads) {
-            const int64_t p = a.out_pos[e];
-            if (p >= r1) break;
-            const uint2 v = reinterpret_cast<const uint2 *>(a.out_val)[e];
-            if constexpr (F32OUT) {
-                f32x4 f = {f16_bits_to_f32(static_cast<uint16_t>(v.x)), f16_bits_to_f32(static_cast<uint16_t>(v.x >> 16)),
-                           f16_bits_to_f32(static_cast<uint16_t>(v.y)), f16_bits_to_f32(static_cast<uint16_t>(v.y >> 16))};
-                store_chunk<true>(a.y, sbase + p, f);
-            } else {
-                reinterpret_cast<uint2 *>(a.y)[sbase + p] = v;
             }
         }
     }
@@ -1300,9 +1317,10 @@ hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t 
                          uint64_t capacity, const float *codebook, void *y, hipStream_t st) {
     const int64_t total = g.slices * g.n_slice;
     if (total == 0) return hipSuccess;
+    // block ranges: multiples of 512 chunks (4 waves x 128), enough blocks
+    // to fill the chip, at most 32768 chunks
     int64_t wgc = round_up(ceil_div(total, 4096), 2 * kDecThreads);
     wgc = wgc < 2 * kDecThreads ? 2 * kDecThreads : (wgc > 32768 ? 32768 : wgc);
-    if (wgc >= 2 * kDecThreads * kDecUnroll) wgc = round_up(wgc, 2 * kDecThreads * kDecUnroll);
     DecArgs a;
     a.idx = idx;
     a.hnorm = hnorm;
