@@ -73,15 +73,15 @@ def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def traffic_per_launch():
-    """HBM bytes per search-kernel launch from the committed counter summary,
-    or None when it is missing or was taken from another kernel source."""
+def traffic_per_launch(key: str = "search_bytes_per_launch"):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken from another kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     t = json.load(open(TRAFFIC_FILE))
     if t.get("kernel_sha256_16") != kernel_hash():
         return None
-    return t.get("search_bytes_per_launch")
+    return t.get(key)
 
 
 def cpu_baseline(w, xs, cbs, seconds: float):
@@ -150,6 +150,18 @@ def summarize_rocpd(db: str, match: str = "hqmq"):
               f"{100 * r[5] / total:.1f} | {r[6]} | {r[7]} | {r[8]} | {r[9]} | {r[10]} |")
 
 
+def summarize_pmc(db: str):
+    """Per-kernel average of each collected counter (per dispatch) of a
+    rocprofv3 --pmc database, as JSON lines."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select kernel_name, counter_name, count(*), avg(value), min(value), max(value) "
+                     "from counters_collection group by kernel_name, counter_name").fetchall()
+    for r in rows:
+        print(json.dumps({"kernel": r[0].replace("(anonymous namespace)::", "").split("(")[0],
+                          "counter": r[1], "dispatches": r[2], "avg": r[3], "min": r[4], "max": r[5]}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,9 +172,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize", metavar="ROCPD_DB", help="print a kernel table of a rocprofv3 database")
+    ap.add_argument("--summarize-pmc", metavar="ROCPD_DB", help="print per-kernel counter averages")
     args = ap.parse_args()
     if args.summarize:
         summarize_rocpd(args.summarize)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -274,7 +290,7 @@ def main():
     flops_launch = 32 * w.S * chunks_role           # 16 S FMA per chunk (the method's minimum)
     s_ms = mean(search_ms)
     achieved_tf = flops_launch / (s_ms * 1e-3) / 1e12
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch() if w.wid == 4 else None
     d_ms = mean(dec_ms)
     dec_bytes_launch = rec_bytes + chunks_role * 8 + 12 * (sum(n_out.values()) / len(w.roles)) + \
         sz.offsets_bytes
@@ -303,6 +319,7 @@ def main():
                      "algorithmic_per_launch": flops_launch, "avg_launch_ms": s_ms},
         "roofline_decode": {"bound": "hbm", "kernel": "decode", "achieved": dec_gbps,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
+                            "traffic": traffic_per_launch("decode_bytes_per_launch") if w.wid == 4 else None,
                             "algorithmic_per_launch": dec_bytes_launch, "avg_launch_ms": d_ms},
         "encode_chunks_per_s": total_chunks / (sum(enc_ms) / args.steps * 1e-3),
         "decode_chunks_per_s": total_chunks / (sum(dec_ms) / args.steps * 1e-3),
