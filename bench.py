@@ -162,12 +162,109 @@ def summarize_pmc(db: str):
                           "counter": r[1], "dispatches": r[2], "avg": r[3], "min": r[4], "max": r[5]}))
 
 
+def decode_step_bench(args, w):
+    """Decode-step workload: the cache of ``w.sequences`` sequences (stacked on
+    the token axis of every (layer, head)) is encoded once, untimed; one step
+    then encodes the step's appended tokens (one per sequence, a Med3x batch of
+    their own) and decodes the whole cache to fp16 into the buffer that held
+    the input, for K and V."""
+    import torch
+    import kv_cache_quantization_hqmq_amd as K
+    import synth
+    torch.cuda.set_device(0)
+    sh = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, w.S, K.HQMQ_F16,
+                       w.med_batch_tokens, w.med_C)
+    desc_a = K.Desc.make(w.layers, w.heads, w.append_tokens, w.head_dim, w.S, K.HQMQ_F16,
+                         w.append_tokens, w.med_C)
+    sz, sza = K.hqmq_sizes(desc), K.hqmq_sizes(desc_a)
+    log(f"workload {synth.describe(w)}; {sz.chunks} cached + {sza.chunks} appended chunks per role")
+    ys, cbs, recs, xa, reca, n_out = {}, {}, {}, {}, {}, {}
+    ws = K.workspace(desc)
+    ws_a = K.workspace(desc_a)
+    for role in w.roles:
+        t = time.perf_counter()
+        ys[role] = synth.generate(w, role, "cuda")
+        cbs[role] = torch.from_numpy(K.hqmq_make_codebook(w.codebook_seed, w.layers, w.heads,
+                                                           role, w.S)).cuda()
+        recs[role] = K.encode(desc, ys[role], cbs[role], ws=ws)
+        n_out[role] = recs[role].n_outliers
+        torch.cuda.synchronize()
+        log(f"role {role}: cache generated and encoded in {time.perf_counter() - t:.1f} s, "
+            f"{n_out[role]} outliers ({n_out[role] / sz.chunks:.4%})")
+        xa[role] = [synth.generate_append(w, role, i, "cuda") for i in range(args.steps + args.warmup)]
+        reca[role] = K.allocate_records(desc_a)
+    del ws
+    torch.cuda.synchronize()
+
+    def step(i, events=None):
+        if events:
+            ev.record(events[0], sh)
+        for role in w.roles:
+            K.hqmq_encode(desc_a, xa[role][i], cbs[role], reca[role], ws_a, sh)
+        if events:
+            ev.record(events[1], sh)
+        for role in w.roles:
+            K.hqmq_decode(desc, recs[role], cbs[role], ys[role], sh)
+            if events:
+                ev.record(events[2 + role], sh)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [tuple(ev.create() for _ in range(2 + len(w.roles))) for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    ms_step = 1000.0 * (time.perf_counter() - t0) / args.steps
+    enc_ms = sum(ev.ms(e[0], e[1]) for e in evs) / args.steps
+    dec_ms = [ev.ms(e[1 + r], e[2 + r]) for e in evs for r in range(len(w.roles))]
+    for e in evs:
+        for x in e:
+            ev.destroy(x)
+    app_out = {r: K.hqmq_encode_result(reca[r], sh) for r in w.roles}
+    d_ms = sum(dec_ms) / len(dec_ms)
+    rec_bytes = sz.idx_bytes + sz.hnorm_bytes
+    dec_bytes = [rec_bytes + sz.chunks * 8 + 12 * n_out[r] + sz.offsets_bytes for r in w.roles]
+    dec_gbps = sum(dec_bytes) / len(dec_bytes) / (d_ms * 1e-3) / 1e9
+    roles = len(w.roles)
+    work = roles * (sz.chunks + sza.chunks)
+    out = {
+        "metric": METRIC,
+        "value": work / (ms_step * 1e-3),
+        "unit": "chunks/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.heads,
+                   "sequences": w.sequences, "cached_tokens_per_sequence": w.tokens // w.sequences,
+                   "appended_tokens_per_step": w.append_tokens, "head_dim": w.head_dim,
+                   "roles": "K+V", "input": w.dtype, "S": w.S,
+                   "med3_batch_tokens": w.med_batch_tokens, "med3_C": w.med_C,
+                   "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "decode", "achieved": dec_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "algorithmic_per_launch": sum(dec_bytes) / len(dec_bytes), "avg_launch_ms": d_ms},
+        "encode_appended_ms": enc_ms,
+        "decode_ms_per_role": d_ms,
+        "decode_GBps_fp16_out": roles * sz.chunks * 8 / (roles * d_ms * 1e-3) / 1e9,
+        "appended_outliers_last_step": app_out,
+        "cache_outlier_fraction": sum(n_out.values()) / (roles * sz.chunks),
+        "kernel_sha256_16": kernel_hash(),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=4, help="1..4 (see synth.WORKLOADS)")
+    ap.add_argument("--workload", type=int, default=4, help="1..5 (see synth.WORKLOADS; 5 is the decode step)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -198,7 +295,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     if w.sequences > 1:
-        raise SystemExit("the decode-step workload is timed by its own driver")
+        decode_step_bench(args, w)
+        return
     dev = "cuda"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
