@@ -106,6 +106,8 @@ def _configure(L):
     L.or_round_f32.argtypes = [_f64p, ctypes.c_int64, _f32p]
     L.or_round_f16.argtypes = [_f64p, ctypes.c_int64, _u16p]
     L.or_num_threads.restype = ctypes.c_int
+    L.or_attend.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int, _f64p, ctypes.c_int,
+                            ctypes.c_double, _f64p]
     return L
 
 
@@ -279,6 +281,21 @@ def decode_range(codes, hnorm, T: int, D: int, q, side_pos=None, side_val=None,
     if r < 0:
         raise ValueError("or_decode_range: inconsistent records")
     return y
+
+
+def attend(k, v, q, scale: float) -> np.ndarray:
+    """Attention of query rows q [G, D] over k, v [T, D] (fp64): out [G, D]."""
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    q = np.ascontiguousarray(np.atleast_2d(q), dtype=np.float64)
+    T, D = k.shape
+    G = q.shape[0]
+    out = np.empty((G, D), np.float64)
+    if T == 0:
+        out[:] = 0.0
+        return out
+    lib().or_attend(_p(k, _f64p), _p(v, _f64p), T, D, _p(q, _f64p), G, float(scale), _p(out, _f64p))
+    return out
 
 
 # --------------------------------------------------------------- tensors

@@ -23,6 +23,9 @@
  *   [FR-MEC] signal-ia-rouge.vercel.app article, section "La mecanique :
  *            pourquoi les quaternions de Hurwitz".
  *   [FR-OUT] same article, section "Le probleme des outliers : Med3x".
+ *   [NL-LAT] gist.science/nl/paper/2605.27646, "Technische Samenvatting",
+ *            "Memory en Latentie" (a fused kernel decodes K/V inside the
+ *            attention loop of a decode step).
  *
  * Where the pages leave a step open, the reading used here is stated at the
  * function.  Every reading is also listed in the repository's design notes.
@@ -44,6 +47,9 @@
  *   or_lower_median, Med3x ........ pinned (numpy partition, designed inputs)
  *   or_pack_row ................... pinned (bit-by-bit unpack in numpy)
  *   or_encode_range/or_decode_range pinned through the above + closed forms
+ *   or_attend ..................... pinned (closed forms: uniform scores,
+ *                                   one token, dominant key; scipy softmax
+ *                                   on random inputs; token permutation)
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -shared -fPIC
  * (-ffp-contract=off: every fp32 operation that the declared norm code uses
@@ -538,6 +544,47 @@ void or_round_f16(const double *y, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = or_f16_bits(y[i]);
+}
+
+/* Decode-step attention of G query rows over T cached tokens ([NL-LAT]):
+ * the plain definition, in fp64.  For each query row g:
+ *   s_t = scale * <q_g, k_t>,  w_t = exp(s_t) / sum_u exp(s_u),
+ *   out_g = sum_t w_t v_t.
+ * The largest s_t is subtracted before exp (same w_t, no overflow).  k and v
+ * are [T][D] (the decoded cache values), q [G][D], out [G][D]; T = 0 gives
+ * zeros. */
+void or_attend(const double *k, const double *v, int64_t T, int D, const double *q, int G,
+               double scale, double *out)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int g = 0; g < G; ++g) {
+        const double *qg = q + (int64_t)g * D;
+        double *og = out + (int64_t)g * D;
+        for (int d = 0; d < D; ++d)
+            og[d] = 0.0;
+        if (T == 0)
+            continue;
+        double smax = -INFINITY;
+        for (int64_t t = 0; t < T; ++t) {
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += qg[d] * k[t * D + d];
+            s[t] = scale * acc;
+            if (s[t] > smax)
+                smax = s[t];
+        }
+        double z = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            s[t] = exp(s[t] - smax);
+            z += s[t];
+        }
+        for (int64_t t = 0; t < T; ++t)
+            for (int d = 0; d < D; ++d)
+                og[d] += s[t] * v[t * D + d];
+        for (int d = 0; d < D; ++d)
+            og[d] /= z;
+    }
+    free(s);
 }
 
 int or_num_threads(void)

@@ -15,6 +15,7 @@ import pytest
 
 import oracle as O
 from tests import test_oracle_algebra as A
+from tests import test_oracle_attend as T
 from tests import test_oracle_f16_codebook as F
 from tests import test_oracle_med3_codec as M
 from tests import test_oracle_quantizer as Q
@@ -69,6 +70,19 @@ MUTANTS = [
     ("decode-norm-factor",
      "double r = 2.0 * or_f16_value(hnorm[i]);", "double r = or_f16_value(hnorm[i]);",
      M.test_decode_closed_form_and_round_trip),
+    ("attend-no-scale",
+     "s[t] = scale * acc;", "s[t] = acc;",
+     lambda: T.test_attend_matches_scipy_softmax(7, 64, 4, 0.125)),
+    ("attend-skips-first-token",
+     "for (int64_t t = 0; t < T; ++t)\n            for (int d = 0; d < D; ++d)\n                og[d] += s[t] * v[t * D + d];",
+     "for (int64_t t = 1; t < T; ++t)\n            for (int d = 0; d < D; ++d)\n                og[d] += s[t] * v[t * D + d];",
+     T.test_one_token_gives_its_value),
+    ("attend-normalises-by-count",
+     "og[d] /= z;", "og[d] /= (double)T;",
+     T.test_dominant_key_gives_its_value),
+    ("attend-values-from-keys",
+     "og[d] += s[t] * v[t * D + d];", "og[d] += s[t] * k[t * D + d];",
+     T.test_uniform_scores_give_the_mean_of_v),
     ("side-pos-drops-offset",
      "side_pos[n_out] = (uint32_t)((t0 + t) * cpt + c);", "side_pos[n_out] = (uint32_t)(t * cpt + c);",
      M.test_batches_and_partial_tail),
