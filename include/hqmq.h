@@ -187,6 +187,58 @@ int hqmq_encode_result(const hqmq_enc *enc, hipStream_t stream, uint64_t *n_outl
 int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, void *y,
                 hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Decode-step attention read straight from the records (gist.science/nl
+ * "Technische Samenvatting", "Memory en Latentie": a fused kernel decodes K
+ * and V inside the attention loop instead of dequantising the whole cache
+ * each step).  For one layer of an encoded cache, every sequence b and query
+ * head j (GQA: query head j reads KV head j / group):
+ *
+ *     out[b][j] = sum_t softmax_t(scale <q[b][j], k_t>) v_t,
+ *
+ * t over tokens [seq_start[b], seq_start[b] + seq_len[b]) of the (layer, KV
+ * head) slice, k_t and v_t the binary16 values hqmq_decode would write.
+ * Scores are fp32 sums of exact binary16 products; the softmax runs in fp32
+ * and the weights enter the value sum rounded to binary16 (each within a
+ * relative 2^-11), normalised by the sum of the same rounded weights.  An
+ * empty sequence gives zeros.
+ * ------------------------------------------------------------------------ */
+typedef struct hqmq_attn_desc {
+    int32_t batch;      /* sequences, >= 0 */
+    int32_t group;      /* query heads per KV head, 1..16 */
+    int32_t layer;      /* cache layer attended, 0 .. layers - 1 */
+    int32_t max_len;    /* upper bound of every seq_len[b] (sizes the launch), >= 0 */
+    float scale;        /* logit scale, finite (for example 1 / sqrt(head_dim)) */
+    int32_t reserved;   /* must be 0 */
+} hqmq_attn_desc;
+
+typedef struct hqmq_attn_sizes_t {
+    uint64_t workspace_bytes;   /* batch * kv_heads * group * splits * (head_dim + 2) * 4 */
+    int32_t splits;             /* token splits per sequence */
+    int32_t split_tokens;       /* tokens per split, a multiple of 64 */
+} hqmq_attn_sizes_t;
+
+/* Workspace size and split plan of hqmq_attend for cache d and request a.
+ * Host only.  Errors: HQMQ_EINVAL (NULL pointer, invalid descriptor or
+ * request), HQMQ_ENOTSUP (d->dtype not HQMQ_F16, head_dim not 64, 128 or
+ * 256, or a launch beyond the kernel's limits). */
+int hqmq_attn_sizes(const hqmq_desc *d, const hqmq_attn_desc *a, hqmq_attn_sizes_t *out);
+
+/* Attention of one decode step over layer a->layer of the cache encoded as
+ * k (role K, codebook_k) and v (role V, codebook_v), both from hqmq_encode
+ * with descriptor d.  Device arrays: q [batch][kv_heads * group][head_dim]
+ * binary16 (8-byte aligned); seq_start [batch] int64 and seq_len [batch]
+ * int32 (token ranges within each slice; a range is clipped to the slice
+ * and to max_len, a negative length counts as 0); out [batch][kv_heads *
+ * group][head_dim] fp32; workspace of at least hqmq_attn_sizes()
+ * .workspace_bytes, 16-byte aligned.  Asynchronous on stream; nothing is
+ * enqueued when validation fails.  Errors: HQMQ_EINVAL, HQMQ_ENOTSUP (as
+ * hqmq_attn_sizes), HQMQ_EHIP. */
+int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, const float *codebook_k,
+                const hqmq_enc *v, const float *codebook_v, const void *q, const int64_t *seq_start,
+                const int32_t *seq_len, float *out, void *workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,12 +5,13 @@ in ``include/hqmq.h``; ``kv_cache_quantization_hqmq_amd.hqmq`` is its ctypes
 binding (same function names).  Build with
 ``python -m kv_cache_quantization_hqmq_amd.build``.
 """
-from .hqmq import (CapacityError, Desc, HQMQError, Records, Sizes, allocate_records, decode,
-                   encode, hqmq_decode, hqmq_encode, hqmq_encode_result, hqmq_encode_timed, hqmq_make_codebook,
-                   hqmq_sizes, hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_ROLE_K,
-                   HQMQ_ROLE_V)
+from .hqmq import (AttnDesc, AttnSizes, CapacityError, Desc, HQMQError, Records, Sizes,
+                   allocate_records, attend, decode, encode, hqmq_attend, hqmq_attn_sizes, hqmq_decode,
+                   hqmq_encode, hqmq_encode_result, hqmq_encode_timed, hqmq_make_codebook, hqmq_sizes,
+                   hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_ROLE_K, HQMQ_ROLE_V)
 
-__all__ = ["CapacityError", "Desc", "HQMQError", "Records", "Sizes", "allocate_records",
-           "decode", "encode", "hqmq_decode", "hqmq_encode", "hqmq_encode_result", "hqmq_encode_timed",
+__all__ = ["AttnDesc", "AttnSizes", "CapacityError", "Desc", "HQMQError", "Records", "Sizes",
+           "allocate_records", "attend", "decode", "encode", "hqmq_attend", "hqmq_attn_sizes",
+           "hqmq_decode", "hqmq_encode", "hqmq_encode_result", "hqmq_encode_timed",
            "hqmq_make_codebook", "hqmq_sizes", "hqmq_strerror", "workspace", "HQMQ_F16",
            "HQMQ_F32", "HQMQ_ROLE_K", "HQMQ_ROLE_V"]

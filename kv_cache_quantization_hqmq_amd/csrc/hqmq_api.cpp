@@ -3,6 +3,7 @@
 // kernel launch sequence.  No device memory is allocated here.
 #include "hqmq.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -128,6 +129,33 @@ float double_f16(float q) {
 }
 
 }  // namespace
+
+// Validation and split plan of a decode-step attention request: enough
+// (sequence, head, split) blocks to fill the chip several times, splits of a
+// multiple of 64 tokens (4 waves x 16-token tiles).
+static int attn_plan(const hqmq_desc *d, const hqmq::Geometry &g, const hqmq_attn_desc *a, int32_t *nsplit,
+              int32_t *stok) {
+    if (!a) return HQMQ_EINVAL;
+    if (a->batch < 0 || a->group < 1 || a->group > 16 || a->max_len < 0 || a->reserved != 0 ||
+        !std::isfinite(a->scale))
+        return HQMQ_EINVAL;
+    if (a->layer < 0 || (a->layer >= d->layers && !(d->layers == 0 && a->batch == 0))) return HQMQ_EINVAL;
+    if (d->dtype != HQMQ_F16) return HQMQ_ENOTSUP;
+    if (hqmq::attend_lds_bytes(static_cast<int>(d->head_dim), g.S) == 0) return HQMQ_ENOTSUP;
+    if (hqmq::attend_lds_bytes(static_cast<int>(d->head_dim), g.S) > 160 * 1024) return HQMQ_ENOTSUP;
+    if (d->kv_heads > 4096) return HQMQ_ENOTSUP;
+    const int64_t pairs = std::max<int64_t>(1, static_cast<int64_t>(a->batch) * d->kv_heads);
+    int64_t want = (2048 + pairs - 1) / pairs;
+    const int64_t most = std::max<int64_t>(1, (static_cast<int64_t>(a->max_len) + 63) / 64);
+    want = std::min(std::max<int64_t>(want, 1), most);
+    int64_t st = ((a->max_len + want - 1) / want + 63) / 64 * 64;
+    if (st < 64) st = 64;
+    const int64_t ns = std::max<int64_t>(1, (a->max_len + st - 1) / st);
+    if (pairs * ns > (int64_t{1} << 31) - 1) return HQMQ_ENOTSUP;
+    *nsplit = static_cast<int32_t>(ns);
+    *stok = static_cast<int32_t>(st);
+    return HQMQ_OK;
+}
 
 extern "C" {
 
@@ -296,6 +324,81 @@ int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, 
                                              g.batch_chunks > 0 ? enc->batch_offsets : nullptr, enc->out_pos,
                                              enc->out_val, enc->out_capacity, codebook, y, stream);
     return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
+}
+
+int hqmq_attn_sizes(const hqmq_desc *d, const hqmq_attn_desc *a, hqmq_attn_sizes_t *out) {
+    if (!out) return HQMQ_EINVAL;
+    hqmq::Geometry g;
+    int rc = make_geometry(d, &g);
+    if (rc != HQMQ_OK) return rc;
+    int32_t nsplit = 0, stok = 0;
+    rc = attn_plan(d, g, a, &nsplit, &stok);
+    if (rc != HQMQ_OK) return rc;
+    out->splits = nsplit;
+    out->split_tokens = stok;
+    out->workspace_bytes = static_cast<uint64_t>(a->batch) * d->kv_heads * a->group * nsplit *
+                           (d->head_dim + 2) * 4;
+    return HQMQ_OK;
+}
+
+int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, const float *codebook_k,
+                const hqmq_enc *v, const float *codebook_v, const void *q, const int64_t *seq_start,
+                const int32_t *seq_len, float *out, void *workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    hqmq_attn_sizes_t sz;
+    int rc = hqmq_attn_sizes(d, a, &sz);
+    if (rc != HQMQ_OK) return rc;
+    if (!k || !v) return HQMQ_EINVAL;
+    if (a->batch == 0 || d->kv_heads == 0) return HQMQ_OK;
+    if (!q || !seq_start || !seq_len || !out || !workspace || workspace_bytes < sz.workspace_bytes)
+        return HQMQ_EINVAL;
+    if (!aligned(q, 8) || !aligned(seq_start, 8) || !aligned(seq_len, 4) || !aligned(out, 4) ||
+        !aligned(workspace, 16))
+        return HQMQ_EINVAL;
+    hqmq::Geometry g;
+    make_geometry(d, &g);
+    const hqmq_enc *enc[2] = {k, v};
+    const float *cb[2] = {codebook_k, codebook_v};
+    hqmq::AttRole role[2];
+    for (int r = 0; r < 2; ++r) {
+        const hqmq_enc *e = enc[r];
+        const bool data = g.tokens > 0;
+        if (data && (!e->idx || !e->hnorm || !cb[r] || !aligned(e->idx, 4) || !aligned(e->hnorm, 16) ||
+                     !aligned(cb[r], 16)))
+            return HQMQ_EINVAL;
+        if (data && g.batch_chunks > 0) {
+            if (!e->batch_offsets || !aligned(e->batch_offsets, 8)) return HQMQ_EINVAL;
+            if (e->out_capacity > 0 && (!e->out_pos || !e->out_val || !aligned(e->out_pos, 4) ||
+                                        !aligned(e->out_val, 8)))
+                return HQMQ_EINVAL;
+        }
+        role[r] = hqmq::AttRole{e->idx, e->hnorm, g.batch_chunks > 0 ? e->batch_offsets : nullptr, e->out_pos,
+                                e->out_val, g.batch_chunks > 0 ? e->out_capacity : 0, cb[r]};
+    }
+    hqmq::AttLaunch L;
+    L.k = role[0];
+    L.v = role[1];
+    L.q = static_cast<const uint16_t *>(q);
+    L.seq_start = seq_start;
+    L.seq_len = seq_len;
+    L.part = static_cast<float *>(workspace);
+    L.out = out;
+    L.tokens = g.tokens;
+    L.batch_chunks = g.batch_chunks;
+    L.bps = g.batch_chunks > 0 ? g.batches_per_slice : 0;
+    L.layer = a->layer;
+    L.heads = static_cast<int32_t>(d->kv_heads);
+    L.group = a->group;
+    L.batch = a->batch;
+    L.nsplit = sz.splits;
+    L.split_tokens = sz.split_tokens;
+    L.max_len = a->max_len;
+    L.head_dim = static_cast<int32_t>(d->head_dim);
+    L.S = g.S;
+    L.bits = g.bits;
+    L.words = g.words;
+    L.scale = a->scale;
+    return hqmq::launch_attend(L, stream) == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
 }
 
 }  // extern "C"

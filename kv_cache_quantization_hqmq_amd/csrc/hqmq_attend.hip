@@ -1,0 +1,483 @@
+// Decode-step attention read straight from HQMQ records, for AMD Instinct
+// MI355X (gfx950).
+//
+// The pages' latency result (gist.science/nl "Technische Samenvatting",
+// "Memory en Latentie"; gist.science/pt "Memória e Latência") is a fused
+// kernel that decodes K and V inside the attention loop instead of
+// dequantising the whole cache every step.  This file is that operation:
+// for one layer, every sequence b and query head j (reading KV head
+// j / group),
+//
+//     out[b][j] = sum_t softmax_t(scale <q[b][j], k_t>) v_t,
+//
+// over the sequence's tokens of the encoded cache, where k_t and v_t are the
+// fp16 values the decode kernel writes (bulk chunks 2 hnorm (q_p * q_s)
+// rounded to binary16; Med3x outlier chunks their side-list values).
+//
+// Layout of the work.  A block takes one (sequence, KV head, token split);
+// each of its 4 waves walks a contiguous quarter of the split in tiles of 16
+// tokens: it decodes the tile's K and V chunks from the records into LDS
+// (the same arithmetic as the decode kernel, so the values are bit-identical),
+// computes the 16 x 16 score tile S[token][query head] with
+// v_mfma_f32_16x16x16f16 (exact fp16 products, fp32 sums), updates an online
+// softmax in fp32, and accumulates O^T[dim][head] += V^T P^T with the same
+// MFMA, P in binary16 scaled by 2^15 (normal down to p = 2^-29).  The
+// normaliser sums the same rounded weights, so the result is an exact convex
+// combination of the v_t up to that weight rounding.  Waves and splits are
+// merged by log-sum-exp; a second kernel combines the splits of each head.
+#include <hip/hip_runtime.h>
+
+#include "hqmq_device.h"
+#include "hqmq_launch.h"
+
+namespace hqmq {
+namespace {
+
+constexpr int kAttThreads = 256;
+constexpr int kAttWaves = kAttThreads / 64;
+constexpr int kTile = 16;            // tokens per wave step (one MFMA tile)
+constexpr float kPScale = 15.0f;     // weights are 2^(s - m + 15), at most 2^15
+constexpr int kAttTableMaxS = 64;    // the 24 S codewords of K and V in LDS up to here
+
+struct AttArgs {
+    AttRole r[2];               // K, V
+    const uint16_t *q;          // [batch][heads * group][D] binary16
+    const int64_t *seq_start;   // [batch] first token of each sequence in the slice
+    const int32_t *seq_len;     // [batch]
+    float *part;                // [batch][heads * group][nsplit][D + 2]: m, l, o[D]
+    int64_t tokens;             // tokens per slice
+    int64_t batch_chunks;       // Med3x batch length in chunks (0: off)
+    int64_t bps;                // Med3x batches per slice
+    int32_t layer, heads, group, nsplit, split_tokens, max_len, S, bits, words;
+    float qscale;               // scale * log2(e)
+};
+
+// Exclusive prefix sum over the wave, in lane order, of counts below 32.
+__device__ __forceinline__ uint32_t wave_excl_small(uint32_t v, uint32_t *total) {
+    uint32_t ex = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        const uint64_t m = __ballot((v >> k) & 1u);
+        ex += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))
+              << k;
+        tot += static_cast<uint32_t>(__popcll(m)) << k;
+    }
+    *total = tot;
+    return ex;
+}
+
+// First side-list entry of slice sl at or after position p0, among the
+// entries of the Med3x batches that overlap [p0, p1) (64-way search per
+// round); *e_end receives the end of those entries.
+__device__ uint64_t first_entry(const AttRole &r, int64_t sl, int64_t bps, int64_t batch_chunks, int64_t p0,
+                                int64_t p1, uint64_t *e_end, int lane) {
+    *e_end = 0;
+    if (bps <= 0 || p0 >= p1) return 0;
+    const int64_t bl = p0 / batch_chunks;
+    const int64_t bh = (p1 - 1) / batch_chunks;
+    uint64_t lo = r.offsets[sl * bps + bl];
+    uint64_t hi = r.offsets[sl * bps + bh + 1];
+    hi = hi < r.capacity ? hi : r.capacity;
+    lo = lo < hi ? lo : hi;
+    *e_end = hi;
+    while (hi > lo) {
+        const uint64_t len = hi - lo;
+        const uint64_t step = (len + 63) / 64;
+        const uint64_t i = lo + static_cast<uint64_t>(lane) * step;
+        const bool below = i < hi && static_cast<int64_t>(r.out_pos[i]) < p0;
+        const int cnt = __popcll(__ballot(below));
+        if (cnt == 0) break;
+        const uint64_t nlo = lo + static_cast<uint64_t>(cnt - 1) * step + 1;
+        const uint64_t nhi = lo + static_cast<uint64_t>(cnt) * step;
+        hi = nhi < hi ? nhi : hi;
+        lo = nlo;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ uint2 pack_f16x4(f32x4 y) {
+    return make_uint2(static_cast<uint32_t>(f32_to_f16_bits(y[0])) | (static_cast<uint32_t>(f32_to_f16_bits(y[1])) << 16),
+                      static_cast<uint32_t>(f32_to_f16_bits(y[2])) | (static_cast<uint32_t>(f32_to_f16_bits(y[3])) << 16));
+}
+
+template <int D>
+struct AttShape {
+    static constexpr int CPT = D / 4;              // chunks per token
+    static constexpr int CPL = CPT / 4;            // chunks per lane of a 16-token tile
+    static constexpr int KB = D / 16;              // 16-dim blocks
+    static constexpr int NU = D / 64;              // chunk groups per lane in the V operand
+    static constexpr int ROWB = CPT * 8 + 16;      // bytes per decoded token row (padded)
+    static constexpr int TILEB = kTile * ROWB;     // bytes per decoded tile
+    static_assert(16 * (D + 2) * 4 <= 2 * TILEB, "merge area must fit in a wave's tiles");
+};
+
+template <int D, bool TABLE>
+__global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
+    using Sh = AttShape<D>;
+    constexpr int CPT = Sh::CPT, CPL = Sh::CPL, KB = Sh::KB, NU = Sh::NU, ROWB = Sh::ROWB, TILEB = Sh::TILEB;
+
+    extern __shared__ f32x4 smem[];
+    const int ntab = TABLE ? 24 * a.S : a.S;
+    f32x4 *tab = smem;                                                     // [2][ntab]
+    unsigned char *tiles = reinterpret_cast<unsigned char *>(smem + 2 * ntab);   // [waves][2][TILEB]
+
+    const int nsplit = a.nsplit;
+    const int64_t bh = blockIdx.x / nsplit;
+    const int split = static_cast<int>(blockIdx.x - bh * nsplit);
+    const int b = static_cast<int>(bh / a.heads);
+    const int h = static_cast<int>(bh - static_cast<int64_t>(b) * a.heads);
+    const int G = a.group;
+    const int64_t Hq = static_cast<int64_t>(a.heads) * G;
+    const int64_t sl = static_cast<int64_t>(a.layer) * a.heads + h;
+
+    // the sequence's tokens, clamped to the slice
+    const int64_t start = a.seq_start[b];
+    int64_t len = a.seq_len[b];
+    len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+    if (start < 0 || start > a.tokens) len = 0;
+    else len = len < a.tokens - start ? len : a.tokens - start;
+    const int64_t t_lo = static_cast<int64_t>(split) * a.split_tokens;
+    const int64_t t_hi = t_lo + a.split_tokens < len ? t_lo + a.split_tokens : len;
+    float *part = a.part + ((static_cast<int64_t>(b) * Hq + static_cast<int64_t>(h) * G) * nsplit + split) * (D + 2);
+    const int64_t pstride = static_cast<int64_t>(nsplit) * (D + 2);   // between query heads
+    if (t_lo >= t_hi) {
+        for (int i = threadIdx.x; i < G * (D + 2); i += kAttThreads) {
+            const int n = i / (D + 2), e = i - n * (D + 2);
+            part[n * pstride + e] = e == 0 ? -INFINITY : 0.0f;
+        }
+        return;
+    }
+
+    // codeword tables of K and V: TABLE: 2 (a_p * q_s) for the 24 S codes,
+    // else the S secondary codewords
+    for (int r = 0; r < 2; ++r) {
+        const float *q = a.r[r].cb + sl * a.S * 4;
+        for (int k = threadIdx.x; k < ntab; k += kAttThreads) {
+            if constexpr (TABLE) {
+                const int s = k / 24;
+                const float qe[4] = {double_f16(q[4 * s]), double_f16(q[4 * s + 1]), double_f16(q[4 * s + 2]),
+                                     double_f16(q[4 * s + 3])};
+                tab[r * ntab + k] = 2.0f * codeword_f32(qe, k - 24 * s);
+            } else {
+                const f32x4 v = {double_f16(q[4 * k]), double_f16(q[4 * k + 1]), double_f16(q[4 * k + 2]),
+                                 double_f16(q[4 * k + 3])};
+                tab[r * ntab + k] = v;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t wq = a.split_tokens / kAttWaves;   // a multiple of the tile
+    const int64_t w_lo = t_lo + wave * wq < t_hi ? t_lo + wave * wq : t_hi;
+    const int64_t w_hi = w_lo + wq < t_hi ? w_lo + wq : t_hi;
+    unsigned char *tk = tiles + wave * 2 * TILEB;
+    unsigned char *tv = tk + TILEB;
+    const int n = lane & 15;     // query head within the group (MFMA column)
+    const int g = lane >> 4;     // lane group
+
+    // query operand of S = K q: B[k = 4 g + j][n] = q[head n][16 kb + 4 g + j]
+    f16x4 qv[KB];
+    {
+        const uint16_t *qp = a.q + (static_cast<int64_t>(b) * Hq + static_cast<int64_t>(h) * G + (n < G ? n : 0)) * D;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const uint2 u = n < G ? *reinterpret_cast<const uint2 *>(qp + 16 * kb + 4 * g) : make_uint2(0u, 0u);
+            qv[kb] = __builtin_bit_cast(f16x4, u);
+        }
+    }
+
+    // side-list cursors of K and V for this wave's tokens
+    uint64_t cur[2], end[2];
+    {
+        const int64_t p0 = (start + w_lo) * CPT, p1 = (start + w_hi) * CPT;
+        cur[0] = first_entry(a.r[0], sl, a.bps, a.batch_chunks, p0, p1, &end[0], lane);
+        cur[1] = first_entry(a.r[1], sl, a.bps, a.batch_chunks, p0, p1, &end[1], lane);
+    }
+
+    const uint32_t kmask = (1u << a.bits) - 1u;
+    const uint32_t kmax = static_cast<uint32_t>(24 * a.S - 1);
+    const int last_word = a.words - 1;
+
+    // Decode the 16-token tile at t0 of role r into dst[token][chunk] (fp16):
+    // lane l takes token l / 4 and the CPL chunks from (l % 4) CPL, so lane
+    // order is position order and flagged chunks rank with a wave prefix sum.
+    auto decode_tile = [&](int r, int64_t t0, int nvalid, unsigned char *dst) {
+        const AttRole &R = a.r[r];
+        const int i = lane >> 2;
+        const int c0 = (lane & 3) * CPL;
+        const bool valid = i < nvalid;
+        const int64_t row = sl * a.tokens + start + t0 + i;   // token row in the tensor
+        uint32_t hw[CPL / 2];
+        if (valid) {
+            const uint4 *hp = reinterpret_cast<const uint4 *>(R.hnorm + row * CPT + c0);
+            if constexpr (CPL == 4) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(hp);
+                hw[0] = u.x;
+                hw[1] = u.y;
+            } else {
+#pragma unroll
+                for (int v = 0; v < CPL / 8; ++v) {
+                    const uint4 u = hp[v];
+                    hw[4 * v] = u.x;
+                    hw[4 * v + 1] = u.y;
+                    hw[4 * v + 2] = u.z;
+                    hw[4 * v + 3] = u.w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < CPL / 2; ++v) hw[v] = 0u;
+        }
+        const uint32_t *rp = R.idx + row * a.words;
+        uint32_t code[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; j += 2) {
+            const int o = (c0 + j) * a.bits;
+            const int w = o >> 5;
+            uint32_t w0 = 0u, w1 = 0u;
+            if (valid) {
+                w0 = rp[w];
+                w1 = rp[w + 1 < last_word ? w + 1 : last_word];
+            }
+            const uint64_t win = ((static_cast<uint64_t>(w1) << 32) | w0) >> (o & 31);
+            const uint32_t k0 = static_cast<uint32_t>(win) & kmask;
+            const uint32_t k1 = static_cast<uint32_t>(win >> a.bits) & kmask;
+            code[j] = k0 < kmax ? k0 : kmax;
+            code[j + 1] = k1 < kmax ? k1 : kmax;
+        }
+        uint2 val[CPL];
+        uint32_t fl = 0u;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const uint32_t hb = (hw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            fl |= (hb >> 15) << j;
+            const float hv = f16_bits_to_f32(static_cast<uint16_t>(hb & 0x7FFFu));
+            f32x4 y;
+            if constexpr (TABLE) {
+                y = hv * tab[r * ntab + code[j]];
+            } else {
+                const int s = static_cast<int>(code[j] / 24u);
+                const f32x4 qs = tab[r * ntab + s];
+                const float qa[4] = {qs[0], qs[1], qs[2], qs[3]};
+                y = (2.0f * hv) * codeword_f32(qa, static_cast<int>(code[j]) - 24 * s);
+            }
+            val[j] = pack_f16x4(y);
+        }
+        // Med3x outlier chunks take their side-list values, in position order
+        if (__ballot(fl != 0u)) {
+            uint32_t tot;
+            const uint32_t ex = wave_excl_small(static_cast<uint32_t>(__popc(fl)), &tot);
+            uint64_t e = cur[r] + ex;
+            const uint2 *sval = reinterpret_cast<const uint2 *>(R.out_val);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                if ((fl >> j) & 1u) {
+                    if (e < end[r]) val[j] = sval[e];
+                    ++e;
+                }
+            }
+            cur[r] += tot;
+        }
+        uint2 *dp = reinterpret_cast<uint2 *>(dst + i * ROWB + c0 * 8);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) dp[j] = val[j];
+    };
+
+    float m_run = -INFINITY;   // running max of the scaled scores (log2 units), head n
+    float l_run = 0.0f;        // this lane's part of the normaliser of head n
+    f32x4 o[KB];               // O^T tiles: o[4 u + c][i] = dim 4 (4 g + i + 16 u) + c of head n
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) o[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int64_t t0 = w_lo; t0 < w_hi; t0 += kTile) {
+        const int nvalid = static_cast<int>(w_hi - t0 < kTile ? w_hi - t0 : kTile);
+        decode_tile(0, t0, nvalid, tk);
+        decode_tile(1, t0, nvalid, tv);
+        wave_sync();
+
+        // S[token 4 g + i][head n]: A[m = token n][k = 4 g + j] = K[token n][16 kb + 4 g + j]
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const f16x4 ka = __builtin_bit_cast(f16x4, *reinterpret_cast<const uint2 *>(tk + n * ROWB + (4 * kb + g) * 8));
+            s = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, qv[kb], s, 0, 0, 0);
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[i] = 4 * g + i < nvalid ? s[i] * a.qscale : -INFINITY;
+            tmax = fmaxf(tmax, s[i]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);
+        if (__ballot(m_new > m_run)) {
+            const float alpha = exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) o[kb] *= alpha;
+        }
+        m_run = m_new;
+        f16x4 ph;
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const _Float16 p = static_cast<_Float16>(exp2f(s[i] - m_run + kPScale));
+            ph[i] = p;
+            psum += static_cast<float>(p);
+        }
+        l_run += psum;
+
+        // O^T += V^T P^T: A[m = n][k = 4 g + j] = V[token 4 g + j][dim 4 (n + 16 u) + c],
+        // B[k = 4 g + j][n] = P[head n][token 4 g + j] (this lane's own weights)
+        uint2 vv[4][NU];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                vv[j][u] = *reinterpret_cast<const uint2 *>(tv + (4 * g + j) * ROWB + (n + 16 * u) * 8);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int sh = 16 * (c & 1);
+                uint32_t e[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) e[j] = ((c < 2 ? vv[j][u].x : vv[j][u].y) >> sh) & 0xFFFFu;
+                const uint2 pk = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+                o[4 * u + c] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, pk), ph, o[4 * u + c], 0, 0, 0);
+            }
+        }
+        wave_sync();
+    }
+
+    // merge the waves: each writes (m, l, o) of its 16 heads into its own
+    // tile area, then the block combines them by log-sum-exp
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    float *mw = reinterpret_cast<float *>(tk);   // [16] m, [16] l, [16][D] o
+    if (g == 0) {
+        mw[n] = m_run;
+        mw[16 + n] = l_tot;
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mw[32 + n * D + 4 * (4 * g + i + 16 * u) + c] = o[4 * u + c][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * D; e += kAttThreads) {
+        const int hn = e / D, d = e - hn * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, reinterpret_cast<const float *>(tiles + w * 2 * TILEB)[hn]);
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kAttWaves; ++w) {
+            const float *mv = reinterpret_cast<const float *>(tiles + w * 2 * TILEB);
+            const float wt = mv[hn] == -INFINITY ? 0.0f : exp2f(mv[hn] - M);
+            L += wt * mv[16 + hn];
+            O += wt * mv[32 + hn * D + d];
+        }
+        float *ph = part + hn * pstride;
+        ph[2 + d] = O;
+        if (d == 0) {
+            ph[0] = M;
+            ph[1] = L;
+        }
+    }
+}
+
+// out[row][d] = sum_j w_j o_j[d] / sum_j w_j l_j, w_j = 2^(m_j - max m).
+template <int D>
+__global__ __launch_bounds__(D) void attend_combine_kernel(const float *part, int nsplit, float *out) {
+    const int64_t row = blockIdx.x;
+    const float *p = part + row * nsplit * (D + 2);
+    float M = -INFINITY;
+    for (int j = 0; j < nsplit; ++j) M = fmaxf(M, p[j * (D + 2)]);
+    const int d = threadIdx.x;
+    float L = 0.0f, O = 0.0f;
+    for (int j = 0; j < nsplit; ++j) {
+        const float mj = p[j * (D + 2)];
+        const float w = mj == -INFINITY ? 0.0f : exp2f(mj - M);
+        L += w * p[j * (D + 2) + 1];
+        O += w * p[j * (D + 2) + 2 + d];
+    }
+    out[row * D + d] = L > 0.0f ? O / L : 0.0f;
+}
+
+template <int D>
+size_t attend_lds(int S, bool table) {
+    const int ntab = table ? 24 * S : S;
+    return 2 * static_cast<size_t>(ntab) * sizeof(f32x4) + kAttWaves * 2 * static_cast<size_t>(AttShape<D>::TILEB);
+}
+
+template <int D>
+hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
+    AttArgs a;
+    a.r[0] = L.k;
+    a.r[1] = L.v;
+    a.q = L.q;
+    a.seq_start = L.seq_start;
+    a.seq_len = L.seq_len;
+    a.part = L.part;
+    a.tokens = L.tokens;
+    a.batch_chunks = L.batch_chunks;
+    a.bps = L.bps;
+    a.layer = L.layer;
+    a.heads = L.heads;
+    a.group = L.group;
+    a.nsplit = L.nsplit;
+    a.split_tokens = L.split_tokens;
+    a.max_len = L.max_len;
+    a.S = L.S;
+    a.bits = L.bits;
+    a.words = L.words;
+    a.qscale = L.scale * 1.4426950408889634f;
+    const bool table = L.S <= kAttTableMaxS;
+    const size_t lds = attend_lds<D>(L.S, table);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(L.batch) * L.heads * L.nsplit));
+    const void *kern = table ? reinterpret_cast<const void *>(&attend_split_kernel<D, true>)
+                             : reinterpret_cast<const void *>(&attend_split_kernel<D, false>);
+    // more than the default 64 KB of dynamic LDS must be asked for
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    if (table) {
+        hipLaunchKernelGGL((attend_split_kernel<D, true>), grid, dim3(kAttThreads), lds, st, a);
+    } else {
+        hipLaunchKernelGGL((attend_split_kernel<D, false>), grid, dim3(kAttThreads), lds, st, a);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attend_combine_kernel<D>), dim3(static_cast<unsigned>(static_cast<int64_t>(L.batch) * L.heads * L.group)),
+                       dim3(D), 0, st, L.part, L.nsplit, L.out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attend_lds_bytes(int head_dim, int S) {
+    const bool table = S <= kAttTableMaxS;
+    switch (head_dim) {
+        case 64: return attend_lds<64>(S, table);
+        case 128: return attend_lds<128>(S, table);
+        case 256: return attend_lds<256>(S, table);
+        default: return 0;
+    }
+}
+
+hipError_t launch_attend(const AttLaunch &L, hipStream_t st) {
+    if (L.batch == 0 || L.group == 0) return hipSuccess;
+    switch (L.head_dim) {
+        case 64: return launch_attend_d<64>(L, st);
+        case 128: return launch_attend_d<128>(L, st);
+        case 256: return launch_attend_d<256>(L, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace hqmq

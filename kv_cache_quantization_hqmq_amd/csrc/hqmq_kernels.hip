@@ -25,15 +25,11 @@
 // scores differ by less than fp32 rounding (near ties).
 #include <hip/hip_runtime.h>
 
+#include "hqmq_device.h"
 #include "hqmq_launch.h"
 
 namespace hqmq {
 namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kEncThreads = 256;   // 4 waves; each wave encodes 64 chunks per step
 constexpr int kFlagThreads = 256;
@@ -42,40 +38,6 @@ constexpr int kDecThreads = 256;   // each thread decodes 4 chunks per step
 constexpr int kDecUnroll = 8;      // steps whose loads a thread issues together
 constexpr int kMaxS = 1024;
 constexpr int kTableMaxS = 64;     // decode keeps the 24 S codewords in LDS up to here
-
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// (e_m * q)[k] = sign(m, k) q[m ^ k] for e = (1, i, j, k) under the Hamilton
-// product: i q = (-q1, q0, -q3, q2), j q = (-q2, q3, q0, -q1),
-// k q = (-q3, -q2, q1, q0).  Bit (4 m + k) of kNegMask marks a minus sign.
-constexpr uint32_t kNegMask = 0x3950u;
-
-__device__ __forceinline__ float unit_row(const float *q, int m, int k) {
-    const float v = q[m ^ k];
-    return ((kNegMask >> (4 * m + k)) & 1u) ? -v : v;
-}
-
-// binary16 helpers (round to nearest even: the hardware default mode).
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-}
-__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, h));
-}
-
-// Codebook values are used on the double-binary16 grid: hi + lo with
-// hi = fp16(q), lo = fp16(q - hi) (q - hi and the sum are exact in fp32).
-// Generated codebooks are already on it; any other codebook is rounded the
-// same way wherever the kernels read it.
-__device__ __forceinline__ float double_f16(float q) {
-    const _Float16 hi = static_cast<_Float16>(q);
-    const _Float16 lo = static_cast<_Float16>(q - static_cast<float>(hi));
-    return static_cast<float>(hi) + static_cast<float>(lo);
-}
 
 // Correctly rounded fp32 square root of a >= 0.  v_sqrt_f32 is within one
 // ulp; the result is then moved to the neighbour whose rounding interval
@@ -967,33 +929,6 @@ struct DecArgs {
     int32_t bits;
     int32_t words;
 };
-
-// Codeword a_p * q_s in fp32 from the four rows e_m * q_s.
-__device__ __forceinline__ f32x4 codeword_f32(const float *q, int p) {
-    f32x4 c;
-    if (p < 8) {
-        const int m = p >> 1;
-        const bool ng = p & 1;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float v = unit_row(q, m, k);
-            c[k] = ng ? -v : v;
-        }
-    } else {
-        const int bits = p - 8;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float r[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float v = unit_row(q, m, k);
-                r[m] = ((bits >> m) & 1) ? -v : v;
-            }
-            c[k] = ((r[0] + r[1]) + (r[2] + r[3])) * 0.5f;
-        }
-    }
-    return c;
-}
 
 template <bool F32OUT>
 __device__ __forceinline__ void store_chunk(void *y, int64_t gc, f32x4 v) {

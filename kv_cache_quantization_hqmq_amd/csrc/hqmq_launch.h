@@ -62,4 +62,34 @@ hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t 
                          const uint64_t *offsets, const uint32_t *out_pos, const uint16_t *out_val,
                          uint64_t capacity, const float *codebook, void *y, hipStream_t st);
 
+// One encoded tensor (K or V) as the attention kernel reads it.
+struct AttRole {
+    const uint32_t *idx;
+    const uint16_t *hnorm;
+    const uint64_t *offsets;   // Med3x batch offsets (nullptr when off)
+    const uint32_t *out_pos;
+    const uint16_t *out_val;
+    uint64_t capacity;
+    const float *cb;           // [layers][kv_heads][S][4]
+};
+
+// Decode-step attention over one layer of an encoded cache.
+struct AttLaunch {
+    AttRole k, v;
+    const uint16_t *q;          // [batch][heads * group][head_dim] binary16
+    const int64_t *seq_start;   // [batch]
+    const int32_t *seq_len;     // [batch]
+    float *part;                // [batch][heads * group][nsplit][head_dim + 2]
+    float *out;                 // [batch][heads * group][head_dim]
+    int64_t tokens;             // tokens per slice
+    int64_t batch_chunks;       // Med3x batch length in chunks (0 = off)
+    int64_t bps;                // Med3x batches per slice (0 = off)
+    int32_t layer, heads, group, batch, nsplit, split_tokens, max_len, head_dim, S, bits, words;
+    float scale;
+};
+
+// Dynamic LDS of the attention kernel for this shape (0: unsupported head_dim).
+size_t attend_lds_bytes(int head_dim, int S);
+hipError_t launch_attend(const AttLaunch &L, hipStream_t st);
+
 }  // namespace hqmq

@@ -26,7 +26,8 @@ HQMQ_ROLE_K, HQMQ_ROLE_V = 0, 1
 
 # every symbol include/hqmq.h declares
 EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
-           "hqmq_encode_timed", "hqmq_encode_result", "hqmq_decode")
+           "hqmq_encode_timed", "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes",
+           "hqmq_attend")
 
 
 class HQMQError(RuntimeError):
@@ -80,6 +81,22 @@ class Enc(ctypes.Structure):
                 ("status", ctypes.c_void_p)]
 
 
+class AttnDesc(ctypes.Structure):
+    """hqmq_attn_desc."""
+    _fields_ = [("batch", ctypes.c_int32), ("group", ctypes.c_int32), ("layer", ctypes.c_int32),
+                ("max_len", ctypes.c_int32), ("scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+    @classmethod
+    def make(cls, batch, group, layer, max_len, scale) -> "AttnDesc":
+        return cls(batch, group, layer, max_len, scale, 0)
+
+
+class AttnSizes(ctypes.Structure):
+    """hqmq_attn_sizes_t."""
+    _fields_ = [("workspace_bytes", ctypes.c_uint64), ("splits", ctypes.c_int32),
+                ("split_tokens", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -107,8 +124,14 @@ def lib():
                                          ctypes.POINTER(ctypes.c_uint64)]
         L.hqmq_decode.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Enc), ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
+        L.hqmq_attn_sizes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(AttnDesc),
+                                      ctypes.POINTER(AttnSizes)]
+        L.hqmq_attend.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(AttnDesc), ctypes.POINTER(Enc),
+                                  ctypes.c_void_p, ctypes.POINTER(Enc), ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         for f in ("hqmq_sizes", "hqmq_make_codebook", "hqmq_encode", "hqmq_encode_timed",
-                  "hqmq_encode_result", "hqmq_decode"):
+                  "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes", "hqmq_attend"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -183,6 +206,23 @@ def hqmq_decode(desc: Desc, rec: "Records", codebook, y, stream=None) -> None:
     _check(rc, "hqmq_decode")
 
 
+def hqmq_attn_sizes(desc: Desc, adesc: AttnDesc) -> AttnSizes:
+    out = AttnSizes()
+    _check(lib().hqmq_attn_sizes(ctypes.byref(desc), ctypes.byref(adesc), ctypes.byref(out)),
+           "hqmq_attn_sizes")
+    return out
+
+
+def hqmq_attend(desc: Desc, adesc: AttnDesc, rec_k: "Records", codebook_k, rec_v: "Records",
+                codebook_v, q, seq_start, seq_len, out, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().hqmq_attend(ctypes.byref(desc), ctypes.byref(adesc), ctypes.byref(rec_k.c),
+                           _ptr(codebook_k), ctypes.byref(rec_v.c), _ptr(codebook_v), _ptr(q),
+                           _ptr(seq_start), _ptr(seq_len), _ptr(out), _ptr(workspace), ws_bytes,
+                           _stream(stream))
+    _check(rc, "hqmq_attend")
+
+
 # ------------------------------------------------------------------ buffers
 @dataclass
 class Records:
@@ -247,3 +287,26 @@ def decode(desc: Desc, rec: Records, codebook, y=None, stream=None):
         y = torch.empty(desc.shape, dtype=dt, device=rec.idx.device)
     hqmq_decode(desc, rec, codebook, y, stream)
     return y
+
+
+def attend(desc: Desc, layer: int, rec_k: Records, codebook_k, rec_v: Records, codebook_v, q,
+           seq_start, seq_len, max_len: int, scale: float | None = None, out=None, ws=None,
+           stream=None):
+    """Decode-step attention over one layer of an encoded cache.  q is
+    [batch, kv_heads * group, head_dim] fp16 on the device; seq_start (int64)
+    and seq_len (int32) are device tensors of length batch.  Returns out
+    [batch, kv_heads * group, head_dim] fp32."""
+    import math
+    import torch
+    batch, hq, D = q.shape
+    group = hq // desc.kv_heads
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    a = AttnDesc.make(batch, group, layer, max_len, scale)
+    if ws is None:
+        n = hqmq_attn_sizes(desc, a).workspace_bytes
+        ws = torch.empty((max(int(n), 16),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((batch, hq, D), dtype=torch.float32, device=q.device)
+    hqmq_attend(desc, a, rec_k, codebook_k, rec_v, codebook_v, q, seq_start, seq_len, out, ws, stream)
+    return out

@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header(tmp_path):
     """Field offsets and sizes of the ctypes structs equal what a C compiler
     makes of include/hqmq.h."""
-    structs = {"hqmq_desc": B.Desc, "hqmq_sizes_t": B.Sizes, "hqmq_enc": B.Enc}
+    structs = {"hqmq_desc": B.Desc, "hqmq_sizes_t": B.Sizes, "hqmq_enc": B.Enc,
+               "hqmq_attn_desc": B.AttnDesc, "hqmq_attn_sizes_t": B.AttnSizes}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hqmq.h"', "int main(void){"]
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -149,3 +150,68 @@ def test_codebook_validation():
         K.hqmq_make_codebook(0, 1, 1, 2, 8)
     with pytest.raises(K.HQMQError):
         K.hqmq_make_codebook(0, 1, 1, 0, 0)
+
+
+# ---------------------------------------------------------------- attention
+_CACHE = dict(layers=32, kv_heads=8, tokens=32 * 32768, head_dim=128, S=32, dtype=B.HQMQ_F16,
+              med_batch_tokens=4096, med_C=3.0)
+
+
+def _attn(**kw):
+    a = dict(batch=32, group=4, layer=0, max_len=32768, scale=0.088)
+    a.update(kw)
+    return B.AttnDesc.make(**a)
+
+
+def test_attn_plan_covers_every_token():
+    d = K.Desc.make(**_CACHE)
+    for batch, max_len in [(32, 32768), (1, 1), (3, 1000), (1, 200000), (64, 4096), (5, 0)]:
+        s = B.hqmq_attn_sizes(d, _attn(batch=batch, max_len=max_len))
+        assert s.split_tokens % 64 == 0 and s.split_tokens >= 64
+        assert s.splits >= 1 and s.splits * s.split_tokens >= max_len
+        assert (s.splits - 1) * s.split_tokens < max(max_len, 1)
+        assert s.workspace_bytes == batch * 8 * 4 * s.splits * (128 + 2) * 4
+
+
+@pytest.mark.parametrize("kw", [dict(group=0), dict(group=17), dict(layer=32), dict(layer=-1),
+                                dict(batch=-1), dict(max_len=-1), dict(scale=float("inf")),
+                                dict(scale=float("nan"))])
+def test_attn_request_validation(kw):
+    d = K.Desc.make(**_CACHE)
+    with pytest.raises(K.HQMQError) as e:
+        B.hqmq_attn_sizes(d, _attn(**kw))
+    assert e.value.code == B.HQMQ_EINVAL
+
+
+def test_attn_reserved_must_be_zero():
+    d = K.Desc.make(**_CACHE)
+    a = _attn()
+    a.reserved = 1
+    with pytest.raises(K.HQMQError):
+        B.hqmq_attn_sizes(d, a)
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=B.HQMQ_F32), dict(head_dim=32), dict(head_dim=16)])
+def test_attn_unsupported_caches(kw):
+    c = dict(_CACHE)
+    c.update(kw)
+    with pytest.raises(K.HQMQError) as e:
+        B.hqmq_attn_sizes(K.Desc.make(**c), _attn())
+    assert e.value.code == B.HQMQ_ENOTSUP
+
+
+def test_attend_rejects_before_enqueueing():
+    """Validation fails before any HIP call: NULL buffers, short workspace."""
+    d = K.Desc.make(**_CACHE)
+    enc = B.Enc(16, 16, 16, 16, 16, 100, 16)
+    L = B.lib()
+
+    def call(q=16, start=16, length=16, out=16, ws=16, ws_bytes=1 << 30, a=None):
+        return L.hqmq_attend(ctypes.byref(d), ctypes.byref(a or _attn()), ctypes.byref(enc), 16,
+                             ctypes.byref(enc), 16, q, start, length, out, ws, ws_bytes, None)
+    assert call(q=None) == B.HQMQ_EINVAL
+    assert call(start=None) == B.HQMQ_EINVAL
+    assert call(out=None) == B.HQMQ_EINVAL
+    assert call(ws_bytes=100) == B.HQMQ_EINVAL
+    assert call(q=18) == B.HQMQ_EINVAL          # misaligned query
+    assert call(a=_attn(batch=0), q=None) == B.HQMQ_OK
