@@ -164,21 +164,29 @@ def summarize_pmc(db: str):
 
 def decode_step_bench(args, w):
     """Decode-step workload: the cache of ``w.sequences`` sequences (stacked on
-    the token axis of every (layer, head)) is encoded once, untimed; one step
-    then encodes the step's appended tokens (one per sequence, a Med3x batch of
-    their own) and decodes the whole cache to fp16 into the buffer that held
-    the input, for K and V."""
+    the token axis of every (layer, head)) is encoded once, untimed.  One step
+    encodes the step's appended tokens (one per sequence, a Med3x batch of
+    their own) for K and V and then runs the attention of every layer over the
+    cache, read straight from the records (hqmq_attend, GQA group 4).  For
+    comparison the same step is also timed the "fake-quant" way: decode the
+    whole cache to fp16 (hqmq_decode, K and V) and run attention on it with
+    torch's batched matmuls."""
+    import math
     import torch
     import kv_cache_quantization_hqmq_amd as K
     import synth
     torch.cuda.set_device(0)
     sh = torch.cuda.current_stream().cuda_stream
     ev = HipEvents()
+    group = 4
     desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, w.S, K.HQMQ_F16,
                        w.med_batch_tokens, w.med_C)
     desc_a = K.Desc.make(w.layers, w.heads, w.append_tokens, w.head_dim, w.S, K.HQMQ_F16,
                          w.append_tokens, w.med_C)
     sz, sza = K.hqmq_sizes(desc), K.hqmq_sizes(desc_a)
+    L, H, D, nseq = w.layers, w.heads, w.head_dim, w.sequences
+    Tc = w.tokens // nseq
+    scale = 1.0 / math.sqrt(D)
     log(f"workload {synth.describe(w)}; {sz.chunks} cached + {sza.chunks} appended chunks per role")
     ys, cbs, recs, xa, reca, n_out = {}, {}, {}, {}, {}, {}
     ws = K.workspace(desc)
@@ -196,61 +204,115 @@ def decode_step_bench(args, w):
         xa[role] = [synth.generate_append(w, role, i, "cuda") for i in range(args.steps + args.warmup)]
         reca[role] = K.allocate_records(desc_a)
     del ws
+    starts = torch.arange(nseq, dtype=torch.int64, device="cuda") * Tc
+    lens = torch.full((nseq,), Tc, dtype=torch.int32, device="cuda")
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(4242)
+    qs = torch.randn((L, nseq, H * group, D), generator=gq, device="cuda").to(torch.float16)
+    adesc = [K.AttnDesc.make(nseq, group, l, Tc, scale) for l in range(L)]
+    asz = K.hqmq_attn_sizes(desc, adesc[0])
+    aws = torch.empty((int(asz.workspace_bytes),), dtype=torch.uint8, device="cuda")
+    aout = torch.empty((L, nseq, H * group, D), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
-    def step(i, events=None):
-        if events:
-            ev.record(events[0], sh)
+    def encode_appended(i):
         for role in w.roles:
             K.hqmq_encode(desc_a, xa[role][i], cbs[role], reca[role], ws_a, sh)
-        if events:
-            ev.record(events[1], sh)
+
+    def fused_step(i, e=None):
+        if e:
+            ev.record(e[0], sh)
+        encode_appended(i)
+        if e:
+            ev.record(e[1], sh)
+        for l in range(L):
+            K.hqmq_attend(desc, adesc[l], recs[0], cbs[0], recs[1], cbs[1], qs[l], starts, lens,
+                          aout[l], aws, sh)
+        if e:
+            ev.record(e[2], sh)
+
+    def torch_attention(l):
+        # decoded cache [H][nseq * Tc][D] -> [H * nseq, Tc, D]; contiguous operands only
+        k = ys[0][l].view(H * nseq, Tc, D)
+        v = ys[1][l].view(H * nseq, Tc, D)
+        q = qs[l].view(nseq, H, group, D).transpose(0, 1).reshape(H * nseq, group, D)
+        s = torch.bmm(k, q.transpose(1, 2).contiguous()).float() * scale
+        p = torch.softmax(s, dim=1)
+        return torch.bmm(p.transpose(1, 2).contiguous().to(torch.float16), v)
+
+    def fakequant_step(i, e=None):
+        if e:
+            ev.record(e[0], sh)
+        encode_appended(i)
         for role in w.roles:
             K.hqmq_decode(desc, recs[role], cbs[role], ys[role], sh)
-            if events:
-                ev.record(events[2 + role], sh)
+        if e:
+            ev.record(e[1], sh)
+        for l in range(L):
+            torch_attention(l)
+        if e:
+            ev.record(e[2], sh)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [tuple(ev.create() for _ in range(2 + len(w.roles))) for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    ms_step = 1000.0 * (time.perf_counter() - t0) / args.steps
-    enc_ms = sum(ev.ms(e[0], e[1]) for e in evs) / args.steps
-    dec_ms = [ev.ms(e[1 + r], e[2 + r]) for e in evs for r in range(len(w.roles))]
-    for e in evs:
-        for x in e:
-            ev.destroy(x)
+    def timed(fn, n_events):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        evs = [tuple(ev.create() for _ in range(n_events)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(args.warmup + i, evs[i])
+        torch.cuda.synchronize()
+        wall = 1000.0 * (time.perf_counter() - t0) / args.steps
+        parts = [sum(ev.ms(e[j], e[j + 1]) for e in evs) / args.steps for j in range(n_events - 1)]
+        for e in evs:
+            for x in e:
+                ev.destroy(x)
+        return wall, parts
+
+    log(f"timing {args.steps} fused steps")
+    fused_ms, (enc_ms, att_ms) = timed(fused_step, 3)
+    assert torch.isfinite(aout).all(), "attention produced non-finite values"
+    log(f"timing {args.steps} fake-quant steps")
+    fq_ms, (fq_dec_ms, fq_att_ms) = timed(fakequant_step, 3)
     app_out = {r: K.hqmq_encode_result(reca[r], sh) for r in w.roles}
-    d_ms = sum(dec_ms) / len(dec_ms)
+
     rec_bytes = sz.idx_bytes + sz.hnorm_bytes
-    dec_bytes = [rec_bytes + sz.chunks * 8 + 12 * n_out[r] + sz.offsets_bytes for r in w.roles]
-    dec_gbps = sum(dec_bytes) / len(dec_bytes) / (d_ms * 1e-3) / 1e9
+    side = sum(12 * n_out[r] for r in w.roles)
+    # one attention launch reads one layer's K and V records and side entries
+    att_bytes = (2 * rec_bytes + side) / L + nseq * H * group * D * (2 + 4)
+    att_launch_ms = att_ms / L
+    att_gbps = att_bytes / (att_launch_ms * 1e-3) / 1e9
+    dec_ms = fq_dec_ms - enc_ms
+    dec_bytes = sum(rec_bytes + sz.chunks * 8 + 12 * n_out[r] + sz.offsets_bytes for r in w.roles)
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
     roles = len(w.roles)
     work = roles * (sz.chunks + sza.chunks)
     out = {
         "metric": METRIC,
-        "value": work / (ms_step * 1e-3),
+        "value": work / (fused_ms * 1e-3),
         "unit": "chunks/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": fused_ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.heads,
-                   "sequences": w.sequences, "cached_tokens_per_sequence": w.tokens // w.sequences,
-                   "appended_tokens_per_step": w.append_tokens, "head_dim": w.head_dim,
+        "config": {"workload": w.name, "layers": L, "kv_heads": H, "query_heads": H * group,
+                   "sequences": nseq, "cached_tokens_per_sequence": Tc,
+                   "appended_tokens_per_step": w.append_tokens, "head_dim": D,
                    "roles": "K+V", "input": w.dtype, "S": w.S,
                    "med3_batch_tokens": w.med_batch_tokens, "med3_C": w.med_C,
+                   "step": "encode appended tokens + attention of every layer read from the records",
                    "parallelism": "none"},
-        "roofline": {"bound": "hbm", "kernel": "decode", "achieved": dec_gbps, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS, "traffic": None,
-                     "algorithmic_per_launch": sum(dec_bytes) / len(dec_bytes), "avg_launch_ms": d_ms},
+        "roofline": {"bound": "hbm", "kernel": "attend (one layer)", "achieved": att_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": att_gbps / PEAK_HBM_GBPS,
+                     "traffic": None, "algorithmic_per_launch": att_bytes, "avg_launch_ms": att_launch_ms},
         "encode_appended_ms": enc_ms,
-        "decode_ms_per_role": d_ms,
-        "decode_GBps_fp16_out": roles * sz.chunks * 8 / (roles * d_ms * 1e-3) / 1e9,
+        "attention_ms_per_step": att_ms,
+        "fakequant": {"ms_per_step": fq_ms, "decode_ms": dec_ms, "torch_attention_ms": fq_att_ms,
+                      "decode_roofline": {"bound": "hbm", "achieved": dec_gbps,
+                                          "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                          "frac": dec_gbps / PEAK_HBM_GBPS,
+                                          "algorithmic_per_launch": dec_bytes / roles,
+                                          "avg_launch_ms": dec_ms / roles}},
+        "fused_speedup_vs_fakequant": fq_ms / fused_ms,
         "appended_outliers_last_step": app_out,
         "cache_outlier_fraction": sum(n_out.values()) / (roles * sz.chunks),
         "kernel_sha256_16": kernel_hash(),

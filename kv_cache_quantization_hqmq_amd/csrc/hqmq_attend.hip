@@ -96,11 +96,6 @@ __device__ uint64_t first_entry(const AttRole &r, int64_t sl, int64_t bps, int64
     return lo;
 }
 
-__device__ __forceinline__ uint2 pack_f16x4(f32x4 y) {
-    return make_uint2(static_cast<uint32_t>(f32_to_f16_bits(y[0])) | (static_cast<uint32_t>(f32_to_f16_bits(y[1])) << 16),
-                      static_cast<uint32_t>(f32_to_f16_bits(y[2])) | (static_cast<uint32_t>(f32_to_f16_bits(y[3])) << 16));
-}
-
 template <int D>
 struct AttShape {
     static constexpr int CPT = D / 4;              // chunks per token
@@ -112,7 +107,33 @@ struct AttShape {
     static_assert(16 * (D + 2) * 4 <= 2 * TILEB, "merge area must fit in a wave's tiles");
 };
 
-template <int D, bool TABLE>
+// Record words of one role's 16-token tile held by one lane: the half-norm
+// codes of its CPL chunks and the index words holding their codes (BITS > 0:
+// the NW consecutive row words from the first code's word; BITS = 0, any code
+// width: two words per chunk pair).
+constexpr int max_code_shift(int cpl, int bits) {
+    int m = 0;
+    for (int q = 0; q < 4; ++q) m = ((q * cpl * bits) & 31) > m ? ((q * cpl * bits) & 31) : m;
+    return m;
+}
+
+// Whether every lane's NW words lie inside its token row.
+constexpr bool words_in_row(int cpl, int bits, int nw) {
+    for (int q = 0; q < 4; ++q)
+        if ((q * cpl * bits) / 32 + nw > (4 * cpl * bits + 31) / 32) return false;
+    return true;
+}
+
+template <int D, int BITS>
+struct TileRegs {
+    static constexpr int CPL = D / 16;
+    static constexpr int NW = BITS > 0 ? (max_code_shift(CPL, BITS) + CPL * BITS + 31) / 32 : CPL;
+    static_assert(BITS == 0 || words_in_row(CPL, BITS, NW), "a lane's words must stay in its row");
+    uint32_t hw[CPL / 2];
+    uint32_t w[NW];
+};
+
+template <int D, bool TABLE, int BITS>
 __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     using Sh = AttShape<D>;
     constexpr int CPT = Sh::CPT, CPL = Sh::CPL, KB = Sh::KB, NU = Sh::NU, ROWB = Sh::ROWB, TILEB = Sh::TILEB;
@@ -169,7 +190,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // the wave index is uniform in a wave: say so, so that the wave's token
+    // range, tile bases and side-list cursors live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t wq = a.split_tokens / kAttWaves;   // a multiple of the tile
     const int64_t w_lo = t_lo + wave * wq < t_hi ? t_lo + wave * wq : t_hi;
     const int64_t w_hi = w_lo + wq < t_hi ? w_lo + wq : t_hi;
@@ -201,89 +224,180 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     const uint32_t kmax = static_cast<uint32_t>(24 * a.S - 1);
     const int last_word = a.words - 1;
 
-    // Decode the 16-token tile at t0 of role r into dst[token][chunk] (fp16):
-    // lane l takes token l / 4 and the CPL chunks from (l % 4) CPL, so lane
-    // order is position order and flagged chunks rank with a wave prefix sum.
-    auto decode_tile = [&](int r, int64_t t0, int nvalid, unsigned char *dst) {
+    // Lane l decodes token l / 4 of a 16-token tile, chunks (l % 4) CPL ..
+    // + CPL - 1, so lane order is position order and a tile's flagged chunks
+    // rank with one wave prefix sum.  The records of tile t + 1 are loaded
+    // while tile t is decoded and used (two register sets, used in turn), and
+    // each role keeps the next 64 side-list entries in registers (one per
+    // lane), loaded one tile ahead.
+    const int ti = lane >> 2;
+    const int c0 = (lane & 3) * CPL;
+    const int cbits = BITS > 0 ? BITS : a.bits;
+    const uint32_t sh0 = static_cast<uint32_t>(c0 * cbits) & 31u;
+    const int w0 = (c0 * cbits) >> 5;
+    const int64_t row0 = sl * a.tokens + start;   // the sequence's first token row
+
+    // Loads are unconditional (lanes past a tile's end read the tile's last
+    // valid row and are masked when decoded) and address a tile base common
+    // to the wave plus a per-lane offset, so that the compiler keeps them in
+    // flight across the decode of the current tile.
+    auto load_tile = [&](int r, int64_t t0, int nvalid, TileRegs<D, BITS> &tr) {
         const AttRole &R = a.r[r];
-        const int i = lane >> 2;
-        const int c0 = (lane & 3) * CPL;
-        const bool valid = i < nvalid;
-        const int64_t row = sl * a.tokens + start + t0 + i;   // token row in the tensor
-        uint32_t hw[CPL / 2];
-        if (valid) {
-            const uint4 *hp = reinterpret_cast<const uint4 *>(R.hnorm + row * CPT + c0);
-            if constexpr (CPL == 4) {
-                const uint2 u = *reinterpret_cast<const uint2 *>(hp);
-                hw[0] = u.x;
-                hw[1] = u.y;
-            } else {
+        const int64_t tb = row0 + (nvalid > 0 ? t0 : w_lo);
+        const uint32_t ri = static_cast<uint32_t>(nvalid > 0 ? (ti < nvalid ? ti : nvalid - 1) : 0);
+        const uint16_t *hp = (R.hnorm + tb * CPT) + (ri * static_cast<uint32_t>(CPT) + static_cast<uint32_t>(c0));
+        if constexpr (CPL == 4) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(hp);
+            tr.hw[0] = u.x;
+            tr.hw[1] = u.y;
+        } else {
 #pragma unroll
-                for (int v = 0; v < CPL / 8; ++v) {
-                    const uint4 u = hp[v];
-                    hw[4 * v] = u.x;
-                    hw[4 * v + 1] = u.y;
-                    hw[4 * v + 2] = u.z;
-                    hw[4 * v + 3] = u.w;
-                }
+            for (int v = 0; v < CPL / 8; ++v) {
+                const uint4 u = reinterpret_cast<const uint4 *>(hp)[v];
+                tr.hw[4 * v] = u.x;
+                tr.hw[4 * v + 1] = u.y;
+                tr.hw[4 * v + 2] = u.z;
+                tr.hw[4 * v + 3] = u.w;
+            }
+        }
+        const uint32_t *ib = R.idx + tb * a.words;   // the tile's first row
+        const uint32_t ro = ri * static_cast<uint32_t>(a.words);
+        if constexpr (BITS > 0) {
+#pragma unroll
+            for (int k = 0; k < TileRegs<D, BITS>::NW; ++k) tr.w[k] = ib[ro + static_cast<uint32_t>(w0 + k)];
+        } else {
+#pragma unroll
+            for (int j = 0; j < CPL; j += 2) {
+                const int w = ((c0 + j) * a.bits) >> 5;
+                tr.w[j] = ib[ro + static_cast<uint32_t>(w)];
+                tr.w[j + 1] = ib[ro + static_cast<uint32_t>(w + 1 < last_word ? w + 1 : last_word)];
+            }
+        }
+    };
+
+    // entries at and past end[r] are never used; lanes past it read a valid
+    // address (the last entry, or the half-norm array when there is none)
+    uint64_t sv[2];   // side-list entries cur[r] + lane (4 x fp16 each)
+    auto load_window = [&](int r) {
+        const uint64_t left = end[r] - cur[r];   // entries from cur[r] on (end >= cur)
+        const uint32_t last = left > 64u ? 63u : (left > 0u ? static_cast<uint32_t>(left) - 1u : 0u);
+        const uint64_t *base = left > 0u ? reinterpret_cast<const uint64_t *>(a.r[r].out_val) + cur[r]
+                                         : reinterpret_cast<const uint64_t *>(a.r[r].hnorm);
+        const uint32_t li = static_cast<uint32_t>(lane);
+        sv[r] = base[li < last ? li : last];
+    };
+    load_window(0);
+    load_window(1);
+
+    // Decode a loaded tile of role r into dst[token][chunk] (fp16), with the
+    // decoder's arithmetic: 2 hnorm (a_p * q_s) in fp32, rounded to binary16.
+    auto decode_tile = [&](int r, const TileRegs<D, BITS> &tr, int nvalid, unsigned char *dst) {
+        const bool valid = ti < nvalid;
+        uint32_t hw[CPL / 2];
+#pragma unroll
+        for (int v = 0; v < CPL / 2; ++v) hw[v] = valid ? tr.hw[v] : 0u;
+        uint32_t code[CPL];
+        if constexpr (BITS > 0) {
+            constexpr int NW = TileRegs<D, BITS>::NW;
+            uint32_t nw[NW];   // the lane's codes from bit 0
+#pragma unroll
+            for (int k = 0; k + 1 < NW; ++k) nw[k] = __builtin_amdgcn_alignbit(tr.w[k + 1], tr.w[k], sh0);
+            nw[NW - 1] = tr.w[NW - 1] >> sh0;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                constexpr uint32_t m = (1u << BITS) - 1u;
+                const int p = j * BITS, k = p >> 5, sft = p & 31;
+                uint32_t v;
+                if (sft + BITS <= 32) v = (nw[k] >> sft) & m;
+                else v = __builtin_amdgcn_alignbit(nw[k + 1], nw[k], sft) & m;
+                code[j] = v < kmax ? v : kmax;
             }
         } else {
 #pragma unroll
-            for (int v = 0; v < CPL / 2; ++v) hw[v] = 0u;
-        }
-        const uint32_t *rp = R.idx + row * a.words;
-        uint32_t code[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; j += 2) {
-            const int o = (c0 + j) * a.bits;
-            const int w = o >> 5;
-            uint32_t w0 = 0u, w1 = 0u;
-            if (valid) {
-                w0 = rp[w];
-                w1 = rp[w + 1 < last_word ? w + 1 : last_word];
+            for (int j = 0; j < CPL; j += 2) {
+                const int o = (c0 + j) * a.bits;
+                const uint64_t win = ((static_cast<uint64_t>(tr.w[j + 1]) << 32) | tr.w[j]) >> (o & 31);
+                const uint32_t k0 = static_cast<uint32_t>(win) & kmask;
+                const uint32_t k1 = static_cast<uint32_t>(win >> a.bits) & kmask;
+                code[j] = k0 < kmax ? k0 : kmax;
+                code[j + 1] = k1 < kmax ? k1 : kmax;
             }
-            const uint64_t win = ((static_cast<uint64_t>(w1) << 32) | w0) >> (o & 31);
-            const uint32_t k0 = static_cast<uint32_t>(win) & kmask;
-            const uint32_t k1 = static_cast<uint32_t>(win >> a.bits) & kmask;
-            code[j] = k0 < kmax ? k0 : kmax;
-            code[j + 1] = k1 < kmax ? k1 : kmax;
         }
-        uint2 val[CPL];
-        uint32_t fl = 0u;
+        f32x4 cw[CPL];   // TABLE: 2 (a_p * q_s); else a_p * q_s
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            const uint32_t hb = (hw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-            fl |= (hb >> 15) << j;
-            const float hv = f16_bits_to_f32(static_cast<uint16_t>(hb & 0x7FFFu));
-            f32x4 y;
             if constexpr (TABLE) {
-                y = hv * tab[r * ntab + code[j]];
+                cw[j] = tab[r * ntab + code[j]];
             } else {
                 const int s = static_cast<int>(code[j] / 24u);
                 const f32x4 qs = tab[r * ntab + s];
                 const float qa[4] = {qs[0], qs[1], qs[2], qs[3]};
-                y = (2.0f * hv) * codeword_f32(qa, static_cast<int>(code[j]) - 24 * s);
+                cw[j] = codeword_f32(qa, static_cast<int>(code[j]) - 24 * s);
             }
-            val[j] = pack_f16x4(y);
         }
-        // Med3x outlier chunks take their side-list values, in position order
+        uint2 val[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const float hv = f16_bits_to_f32(static_cast<uint16_t>((hw[j >> 1] >> (16 * (j & 1))) & 0x7FFFu));
+            const f32x4 y = TABLE ? hv * cw[j] : (2.0f * hv) * cw[j];
+            const f16x4 hy = {static_cast<_Float16>(y[0]), static_cast<_Float16>(y[1]), static_cast<_Float16>(y[2]),
+                              static_cast<_Float16>(y[3])};
+            val[j] = __builtin_bit_cast(uint2, hy);
+        }
+        uint2 *dp = reinterpret_cast<uint2 *>(dst + ti * ROWB + c0 * 8);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) dp[j] = val[j];
+        uint32_t fl = 0u;   // Med3x flags (bit 15 of each code), chunk order
+#pragma unroll
+        for (int v = 0; v < CPL / 2; ++v) fl |= (((hw[v] >> 15) & 1u) | ((hw[v] >> 30) & 2u)) << (2 * v);
+        // Outlier chunks take their side-list values, in position order: the
+        // tile's k-th flagged chunk is entry cur + k.  Each round writes one
+        // flagged chunk per lane over its bulk value in LDS, taking entries
+        // below 64 from the register window; a tile with more than 64 flagged
+        // chunks reads the rest in rounds of 64 (rare; those loads are used
+        // at once, inside that uniform branch).
         if (__ballot(fl != 0u)) {
             uint32_t tot;
             const uint32_t ex = wave_excl_small(static_cast<uint32_t>(__popc(fl)), &tot);
-            uint64_t e = cur[r] + ex;
-            const uint2 *sval = reinterpret_cast<const uint2 *>(R.out_val);
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                if ((fl >> j) & 1u) {
-                    if (e < end[r]) val[j] = sval[e];
+            const uint64_t left = end[r] - cur[r];
+            const uint32_t lim = left < 0xFFFFFFFFu ? static_cast<uint32_t>(left) : 0xFFFFFFFFu;
+            uint32_t f = fl, e = ex;
+            while (__ballot(f != 0u && e < 64u)) {
+                const bool act = f != 0u && e < 64u;
+                const int src = static_cast<int>(e & 63u);
+                const uint32_t vx = __shfl(static_cast<uint32_t>(sv[r]), src);
+                const uint32_t vy = __shfl(static_cast<uint32_t>(sv[r] >> 32), src);
+                if (act) {
+                    const int j = __builtin_ctz(f);
+                    *reinterpret_cast<uint2 *>(dst + ti * ROWB + (c0 + j) * 8) =
+                        e < lim ? make_uint2(vx, vy) : make_uint2(0u, 0u);
+                    f &= f - 1u;
                     ++e;
+                }
+            }
+            if (tot > 64u) {
+                for (uint32_t base = 64u; base < tot; base += 64u) {
+                    const uint32_t li = base + static_cast<uint32_t>(lane);
+                    const uint64_t w = reinterpret_cast<const uint64_t *>(a.r[r].out_val)[cur[r] + (li < lim ? li : lim - 1u)];
+                    __builtin_amdgcn_s_waitcnt(0);
+                    while (__ballot(f != 0u && e < base + 64u)) {
+                        const bool act = f != 0u && e < base + 64u;
+                        const int src = static_cast<int>((e - base) & 63u);
+                        const uint32_t vx = __shfl(static_cast<uint32_t>(w), src);
+                        const uint32_t vy = __shfl(static_cast<uint32_t>(w >> 32), src);
+                        if (act) {
+                            const int j = __builtin_ctz(f);
+                            *reinterpret_cast<uint2 *>(dst + ti * ROWB + (c0 + j) * 8) =
+                                e < lim ? make_uint2(vx, vy) : make_uint2(0u, 0u);
+                            f &= f - 1u;
+                            ++e;
+                        }
+                    }
                 }
             }
             cur[r] += tot;
         }
-        uint2 *dp = reinterpret_cast<uint2 *>(dst + i * ROWB + c0 * 8);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) dp[j] = val[j];
+        load_window(r);
     };
 
     float m_run = -INFINITY;   // running max of the scaled scores (log2 units), head n
@@ -292,10 +406,15 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) o[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int64_t t0 = w_lo; t0 < w_hi; t0 += kTile) {
+    // one 16-token tile: prefetch the next into nxt, decode cur, attend
+    auto step = [&](int64_t t0, TileRegs<D, BITS>(&cur_t)[2], TileRegs<D, BITS>(&nxt_t)[2]) {
         const int nvalid = static_cast<int>(w_hi - t0 < kTile ? w_hi - t0 : kTile);
-        decode_tile(0, t0, nvalid, tk);
-        decode_tile(1, t0, nvalid, tv);
+        const int64_t t1 = t0 + kTile;
+        const int nv1 = t1 < w_hi ? static_cast<int>(w_hi - t1 < kTile ? w_hi - t1 : kTile) : 0;
+        load_tile(0, t1, nv1, nxt_t[0]);
+        load_tile(1, t1, nv1, nxt_t[1]);
+        decode_tile(0, cur_t[0], nvalid, tk);
+        decode_tile(1, cur_t[1], nvalid, tv);
         wave_sync();
 
         // S[token 4 g + i][head n]: A[m = token n][k = 4 g + j] = K[token n][16 kb + 4 g + j]
@@ -343,15 +462,27 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         for (int u = 0; u < NU; ++u) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int sh = 16 * (c & 1);
-                uint32_t e[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) e[j] = ((c < 2 ? vv[j][u].x : vv[j][u].y) >> sh) & 0xFFFFu;
-                const uint2 pk = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+                // halves c of tokens 4 g + 0..3: byte selectors of v_perm_b32
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t x0 = c < 2 ? vv[0][u].x : vv[0][u].y, x1 = c < 2 ? vv[1][u].x : vv[1][u].y;
+                const uint32_t x2 = c < 2 ? vv[2][u].x : vv[2][u].y, x3 = c < 2 ? vv[3][u].x : vv[3][u].y;
+                const uint2 pk = make_uint2(__builtin_amdgcn_perm(x1, x0, sel), __builtin_amdgcn_perm(x3, x2, sel));
                 o[4 * u + c] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, pk), ph, o[4 * u + c], 0, 0, 0);
             }
         }
         wave_sync();
+    };
+
+    TileRegs<D, BITS> ta[2], tb[2];
+    if (w_lo < w_hi) {
+        const int nv = static_cast<int>(w_hi - w_lo < kTile ? w_hi - w_lo : kTile);
+        load_tile(0, w_lo, nv, ta[0]);
+        load_tile(1, w_lo, nv, ta[1]);
+    }
+    for (int64_t t0 = w_lo; t0 < w_hi; t0 += 2 * kTile) {
+        step(t0, ta, tb);
+        if (t0 + kTile >= w_hi) break;
+        step(t0 + kTile, tb, ta);
     }
 
     // merge the waves: each writes (m, l, o) of its 16 heads into its own
@@ -441,15 +572,24 @@ hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
     const bool table = L.S <= kAttTableMaxS;
     const size_t lds = attend_lds<D>(L.S, table);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(L.batch) * L.heads * L.nsplit));
-    const void *kern = table ? reinterpret_cast<const void *>(&attend_split_kernel<D, true>)
-                             : reinterpret_cast<const void *>(&attend_split_kernel<D, false>);
+    // code widths of the common codebooks (S = 8: 8 bits, S = 32: 10) get
+    // extraction at fixed bit positions; any other width the general path
+    const void *kern;
+    if (table && L.bits == 10) kern = reinterpret_cast<const void *>(&attend_split_kernel<D, true, 10>);
+    else if (table && L.bits == 8) kern = reinterpret_cast<const void *>(&attend_split_kernel<D, true, 8>);
+    else if (table) kern = reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0>);
+    else kern = reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0>);
     // more than the default 64 KB of dynamic LDS must be asked for
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    if (table) {
-        hipLaunchKernelGGL((attend_split_kernel<D, true>), grid, dim3(kAttThreads), lds, st, a);
+    if (table && L.bits == 10) {
+        hipLaunchKernelGGL((attend_split_kernel<D, true, 10>), grid, dim3(kAttThreads), lds, st, a);
+    } else if (table && L.bits == 8) {
+        hipLaunchKernelGGL((attend_split_kernel<D, true, 8>), grid, dim3(kAttThreads), lds, st, a);
+    } else if (table) {
+        hipLaunchKernelGGL((attend_split_kernel<D, true, 0>), grid, dim3(kAttThreads), lds, st, a);
     } else {
-        hipLaunchKernelGGL((attend_split_kernel<D, false>), grid, dim3(kAttThreads), lds, st, a);
+        hipLaunchKernelGGL((attend_split_kernel<D, false, 0>), grid, dim3(kAttThreads), lds, st, a);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
