@@ -36,7 +36,13 @@ namespace {
 constexpr int kAttThreads = 256;
 constexpr int kAttWaves = kAttThreads / 64;
 constexpr int kTile = 16;            // tokens per wave step (one MFMA tile)
-constexpr float kPScale = 15.0f;     // weights are 2^(s - m + 15), at most 2^15
+// Softmax weights enter the value sum as binary16 2^(s - m + kPScale), m a
+// reference max that is raised only when a score exceeds it by more than
+// kLazy (log2 units): weights stay below 2^(kPScale + kLazy) = 2^15 and stay
+// normal down to 2^(-14 - kPScale) of the reference, and the accumulators are
+// rescaled only when the reference moves.
+constexpr float kPScale = 8.0f;
+constexpr float kLazy = 7.0f;
 constexpr int kAttTableMaxS = 64;    // the 24 S codewords of K and V in LDS up to here
 
 struct AttArgs {
@@ -104,7 +110,7 @@ struct AttShape {
     static constexpr int NU = D / 64;              // chunk groups per lane in the V operand
     static constexpr int ROWB = CPT * 8 + 16;      // bytes per decoded token row (padded)
     static constexpr int TILEB = kTile * ROWB;     // bytes per decoded tile
-    static_assert(16 * (D + 2) * 4 <= 2 * TILEB, "merge area must fit in a wave's tiles");
+    static constexpr int MERGEB = (32 + 16 * D) * 4;   // a wave's m, l and o for the merge
 };
 
 // Record words of one role's 16-token tile held by one lane: the half-norm
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     extern __shared__ f32x4 smem[];
     const int ntab = TABLE ? 24 * a.S : a.S;
     f32x4 *tab = smem;                                                     // [2][ntab]
-    unsigned char *tiles = reinterpret_cast<unsigned char *>(smem + 2 * ntab);   // [waves][2][TILEB]
+    unsigned char *tiles = reinterpret_cast<unsigned char *>(smem + 2 * ntab);   // [waves][TILEB]
 
     const int nsplit = a.nsplit;
     const int64_t bh = blockIdx.x / nsplit;
@@ -196,8 +202,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     const int64_t wq = a.split_tokens / kAttWaves;   // a multiple of the tile
     const int64_t w_lo = t_lo + wave * wq < t_hi ? t_lo + wave * wq : t_hi;
     const int64_t w_hi = w_lo + wq < t_hi ? w_lo + wq : t_hi;
-    unsigned char *tk = tiles + wave * 2 * TILEB;
-    unsigned char *tv = tk + TILEB;
+    unsigned char *tt = tiles + wave * TILEB;   // this wave's decoded tile (K, then V)
     const int n = lane & 15;     // query head within the group (MFMA column)
     const int g = lane >> 4;     // lane group
 
@@ -413,15 +418,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         const int nv1 = t1 < w_hi ? static_cast<int>(w_hi - t1 < kTile ? w_hi - t1 : kTile) : 0;
         load_tile(0, t1, nv1, nxt_t[0]);
         load_tile(1, t1, nv1, nxt_t[1]);
-        decode_tile(0, cur_t[0], nvalid, tk);
-        decode_tile(1, cur_t[1], nvalid, tv);
+        decode_tile(0, cur_t[0], nvalid, tt);
         wave_sync();
 
         // S[token 4 g + i][head n]: A[m = token n][k = 4 g + j] = K[token n][16 kb + 4 g + j]
         f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const f16x4 ka = __builtin_bit_cast(f16x4, *reinterpret_cast<const uint2 *>(tk + n * ROWB + (4 * kb + g) * 8));
+            const f16x4 ka = __builtin_bit_cast(f16x4, *reinterpret_cast<const uint2 *>(tt + n * ROWB + (4 * kb + g) * 8));
             s = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, qv[kb], s, 0, 0, 0);
         }
         float tmax = -INFINITY;
@@ -432,14 +436,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        if (__ballot(m_new > m_run)) {
-            const float alpha = exp2f(m_run - m_new);
+        if (__ballot(tmax > m_run + kLazy)) {
+            const float m_new = tmax > m_run + kLazy ? tmax : m_run;
+            const float alpha = exp2f(m_run - m_new);   // 1 where unchanged, 0 from -inf
             l_run *= alpha;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) o[kb] *= alpha;
+            m_run = m_new;
         }
-        m_run = m_new;
+        wave_sync();   // the K tile has been read: V goes into the same place
+        decode_tile(1, cur_t[1], nvalid, tt);
+        wave_sync();
         f16x4 ph;
         float psum = 0.0f;
 #pragma unroll
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int u = 0; u < NU; ++u)
-                vv[j][u] = *reinterpret_cast<const uint2 *>(tv + (4 * g + j) * ROWB + (n + 16 * u) * 8);
+                vv[j][u] = *reinterpret_cast<const uint2 *>(tt + (4 * g + j) * ROWB + (n + 16 * u) * 8);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
 #pragma unroll
@@ -489,7 +496,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     // tile area, then the block combines them by log-sum-exp
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    float *mw = reinterpret_cast<float *>(tk);   // [16] m, [16] l, [16][D] o
+    __syncthreads();   // every wave is done with the tables and tiles
+    unsigned char *merge = reinterpret_cast<unsigned char *>(smem);   // [waves][MERGEB]
+    float *mw = reinterpret_cast<float *>(merge + wave * Sh::MERGEB);   // [16] m, [16] l, [16][D] o
     if (g == 0) {
         mw[n] = m_run;
         mw[16 + n] = l_tot;
@@ -505,11 +514,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         const int hn = e / D, d = e - hn * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, reinterpret_cast<const float *>(tiles + w * 2 * TILEB)[hn]);
+        for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, reinterpret_cast<const float *>(merge + w * Sh::MERGEB)[hn]);
         float L = 0.0f, O = 0.0f;
 #pragma unroll
         for (int w = 0; w < kAttWaves; ++w) {
-            const float *mv = reinterpret_cast<const float *>(tiles + w * 2 * TILEB);
+            const float *mv = reinterpret_cast<const float *>(merge + w * Sh::MERGEB);
             const float wt = mv[hn] == -INFINITY ? 0.0f : exp2f(mv[hn] - M);
             L += wt * mv[16 + hn];
             O += wt * mv[32 + hn * D + d];
@@ -544,7 +553,9 @@ __global__ __launch_bounds__(D) void attend_combine_kernel(const float *part, in
 template <int D>
 size_t attend_lds(int S, bool table) {
     const int ntab = table ? 24 * S : S;
-    return 2 * static_cast<size_t>(ntab) * sizeof(f32x4) + kAttWaves * 2 * static_cast<size_t>(AttShape<D>::TILEB);
+    const size_t loop = 2 * static_cast<size_t>(ntab) * sizeof(f32x4) + kAttWaves * static_cast<size_t>(AttShape<D>::TILEB);
+    const size_t merge = kAttWaves * static_cast<size_t>(AttShape<D>::MERGEB);
+    return loop > merge ? loop : merge;
 }
 
 template <int D>
@@ -580,8 +591,11 @@ hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
     else if (table) kern = reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0>);
     else kern = reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0>);
     // more than the default 64 KB of dynamic LDS must be asked for
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (lds > 64 * 1024) {
+        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
     if (table && L.bits == 10) {
         hipLaunchKernelGGL((attend_split_kernel<D, true, 10>), grid, dim3(kAttThreads), lds, st, a);
     } else if (table && L.bits == 8) {
