@@ -449,32 +449,38 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const f16x4 bv = __builtin_bit_cast(f16x4, xr[b]);
+            // running best over the MFMA tiles t: the best of a tile's four
+            // scores (s = 8 t + 2 g + hh, g = 0..3) replaces the running one
+            // when strictly larger, with the tile and its four scores; which g
+            // it was is resolved once at the end (first g reaching it), so the
+            // result is the sequential strict argmax in s order
             float best = -1.0f;
-            int bk = 0;
+            int bt = 0;
+            f32x4 bs = {-1.0f, -1.0f, -1.0f, -1.0f};
+            auto tile = [&](int t, const f32x16 &d) {
+                f32x4 sc;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 tv = {d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]};
+                    sc[g] = best_primary(tv);
+                }
+                const float m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                if (m > best) {
+                    best = m;
+                    bt = t;
+                    bs = sc;
+                }
+            };
             if constexpr (NT8 > 0) {
 #pragma unroll
-                for (int t = 0; t < NT8; ++t) {
-                    const f32x16 d = __builtin_amdgcn_mfma_f32_32x32x8f16(A[t], bv, zero, 0, 0, 0);
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 tv = {d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]};
-                        const float sc = best_primary(tv);
-                        if (sc > best) { best = sc; bk = 8 * t + 2 * g; }
-                    }
-                }
+                for (int t = 0; t < NT8; ++t) tile(t, __builtin_amdgcn_mfma_f32_32x32x8f16(A[t], bv, zero, 0, 0, 0));
             } else {
-                for (int t = 0; t < NT; ++t) {
-                    const f32x16 d = __builtin_amdgcn_mfma_f32_32x32x8f16(a_operand(t), bv, zero, 0, 0, 0);
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 tv = {d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]};
-                        const float sc = best_primary(tv);
-                        if (sc > best) { best = sc; bk = 8 * t + 2 * g; }
-                    }
-                }
+                for (int t = 0; t < NT; ++t)
+                    tile(t, __builtin_amdgcn_mfma_f32_32x32x8f16(a_operand(t), bv, zero, 0, 0, 0));
             }
+            const int g = bs[0] == best ? 0 : (bs[1] == best ? 1 : (bs[2] == best ? 2 : 3));
             bsc[b] = best;
-            bsi[b] = bk + hh;
+            bsi[b] = 8 * bt + 2 * g + hh;
         }
 
         // the two lane halves hold the other parity of s for the same
