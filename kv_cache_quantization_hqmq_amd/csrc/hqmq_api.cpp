@@ -265,8 +265,11 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
 
     hipError_t e = hipSuccess;
     if (med && nb > 0) {
-        // clear the batch histograms the search accumulates
-        e = hqmq::launch_fill_u32(ws.hist, nb * 2048, 0u, stream);
+        // clear the batch histograms the search accumulates and the outlier
+        // bitmasks the select kernel ORs bits into (one contiguous range)
+        const int64_t words = (reinterpret_cast<char *>(ws.mask + nb * ws.mask_words) -
+                               reinterpret_cast<char *>(ws.hist)) / 4;
+        e = hqmq::launch_fill_u32(ws.hist, words, 0u, stream);
         if (e != hipSuccess) return HQMQ_EHIP;
     }
     if (search_begin && hipEventRecord(search_begin, stream) != hipSuccess) return HQMQ_EHIP;

@@ -598,7 +598,7 @@ constexpr int kCandCap = 4096;
 
 struct SelArgs {
     const void *x;
-    const uint16_t *hnorm;
+    uint16_t *hnorm;        // read; the single-pass select also sets outlier flags
     const uint32_t *hist;   // [nbatch][2048] counts of h >> 4
     uint32_t *counts;       // [nbatch]
     uint32_t *mask;         // [nbatch][mask_words]
@@ -820,6 +820,191 @@ __global__ __launch_bounds__(kSelThreads) void med3_select_kernel(SelArgs a) {
     if (threadIdx.x == 0) a.counts[bid] = tot;
 }
 
+// Single-pass select for batches of at most kSel1MaxChunks chunks.  The
+// median's top bin d1 (from the search kernel's histogram) bounds the median
+// s2 to [4 v(16 d1 - 1)^2, 4 v(16 d1 + 16)^2] (v the binary16 value of a
+// code: the half-norm of any s2 with a code in the bin lies strictly between
+// the neighbouring codes' values), hence the threshold code to [hlo, hhi]
+// (the code is monotone in s2).  One read of the batch's codes then (1)
+// refines the median as before (low 4 bits, candidate positions), (2) flags
+// every code above hhi as an outlier (bitmask bit, bit 15 in hnorm) and
+// (3) keeps the positions of codes in [hlo, hhi]; once the exact threshold
+// is known those are decided exactly (s2 recomputed where the code equals
+// the threshold's).  Bits are ORed into the batch's bitmask, which the
+// encode call zeroes together with the histograms.  The decisions are the two-pass kernel's.  If the
+// undecided list overflows, one more pass decides the codes in [hlo, hhi].
+// A batch is a whole number of token rows (n a multiple of 4).
+constexpr int kSel1MaxChunks = 131072;
+constexpr int kCand1Cap = 3000;   // with the other LDS arrays: 4 blocks per CU
+constexpr int kUnc1Cap = 2048;
+
+__global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t cand[kCand1Cap];
+    __shared__ float candv[kCand1Cap];
+    __shared__ uint32_t unc[kUnc1Cap];
+    __shared__ uint32_t sh[kSelThreads / 64 + 6];
+    uint32_t *found = sh + kSelThreads / 64 + 1;
+    uint32_t *ncand = sh + kSelThreads / 64 + 3;
+    uint32_t *nunc = sh + kSelThreads / 64 + 4;
+    uint32_t *nout = sh + kSelThreads / 64 + 5;
+
+    const int64_t bid = blockIdx.x;
+    const int64_t slice = bid / a.bps;
+    const int64_t lo = (bid - slice * a.bps) * a.batch_chunks;
+    const int n = static_cast<int>(min(a.batch_chunks, a.n_slice - lo));
+    const int64_t gbase = slice * a.n_slice + lo;
+    uint16_t *codes = a.hnorm + gbase;
+    const uint32_t k = static_cast<uint32_t>((n - 1) / 2);
+
+    const uint32_t *gh = a.hist + bid * 2048;
+    for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = gh[i];
+    __syncthreads();
+    select_digit(hist, 2048, k, found, sh);
+    const uint32_t d1 = found[0];
+    const uint32_t k1 = found[1];
+    const uint32_t m1 = hist[d1];
+    __syncthreads();
+
+    // threshold code bounds from the median's bin
+    const float cc = a.C * a.C;
+    const uint32_t cl = d1 << 4, ch = cl | 15u;
+    const float vlo = cl > 0 ? f16_bits_to_f32(static_cast<uint16_t>(cl - 1)) : 0.0f;
+    const float vhi = f16_bits_to_f32(static_cast<uint16_t>(ch + 1 < 0x7C00u ? ch + 1 : 0x7BFFu));
+    const uint32_t hlo = half_norm_code(cc * (4.0f * vlo * vlo));
+    const uint32_t hhi = ch + 1 < 0x7C00u ? half_norm_code(cc * (4.0f * vhi * vhi)) : 0x7FFFu;
+
+    const bool keep = m1 <= static_cast<uint32_t>(kCand1Cap);
+    if (threadIdx.x < 16) hist[threadIdx.x] = 0;
+    if (threadIdx.x == 0) { *ncand = 0; *nunc = 0; *nout = 0; }
+    __syncthreads();
+
+    // the one pass: 4 codes per 8-byte load (a batch is a whole number of
+    // token rows, so n is a multiple of 4), eight loads per thread in flight;
+    // definite outliers are ORed into the batch's bitmask (zeroed before the
+    // search) and get their flag in the same 8 bytes written back
+    uint32_t *mrow = a.mask + bid * a.mask_words;
+    uint32_t cnt = 0;
+    {
+        uint2 *c4 = reinterpret_cast<uint2 *>(codes);
+        const int n4 = n >> 2;
+        constexpr int U = 8;
+        for (int i0 = threadIdx.x; i0 < n4; i0 += kSelThreads * U) {
+            uint2 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = i0 + kSelThreads * u;
+                v[u] = q < n4 ? c4[q] : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = i0 + kSelThreads * u;
+                if (q >= n4) continue;
+                uint32_t nib = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = e < 2 ? v[u].x : v[u].y;
+                    const uint32_t c = (w >> (16 * (e & 1))) & 0xFFFFu;
+                    const int i = 4 * q + e;
+                    if ((c >> 4) == d1) {
+                        atomicAdd(&hist[c & 15u], 1u);
+                        if (keep) {
+                            const uint32_t slot = atomicAdd(ncand, 1u);
+                            if (slot < static_cast<uint32_t>(kCand1Cap)) cand[slot] = static_cast<uint32_t>(i);
+                        }
+                    }
+                    if (c > hhi) nib |= 1u << e;
+                    else if (c >= hlo) {
+                        const uint32_t slot = atomicAdd(nunc, 1u);
+                        if (slot < static_cast<uint32_t>(kUnc1Cap)) unc[slot] = static_cast<uint32_t>(i);
+                    }
+                }
+                if (nib) {
+                    atomicOr(&mrow[q >> 3], nib << (4 * (q & 7)));
+                    cnt += static_cast<uint32_t>(__popc(nib));
+                    uint2 f = v[u];
+                    f.x |= ((nib & 1u) ? 0x8000u : 0u) | ((nib & 2u) ? 0x80000000u : 0u);
+                    f.y |= ((nib & 4u) ? 0x8000u : 0u) | ((nib & 8u) ? 0x80000000u : 0u);
+                    c4[q] = f;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    select_digit(hist, 16, k1, found, sh);
+    const uint32_t hmed = (d1 << 4) | found[0];
+    const uint32_t k2 = found[1];
+    __syncthreads();
+
+    // exact median among the chunks with code hmed (never flagged: a code
+    // in the median's bin is at most hhi)
+    float med;
+    if (keep) {
+        if (threadIdx.x == 0) *ncand = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < m1; i += kSelThreads) {
+            const uint32_t off = min(cand[i], static_cast<uint32_t>(n - 1));
+            if (codes[off] == hmed) {
+                const uint32_t slot = atomicAdd(ncand, 1u);
+                if (slot < static_cast<uint32_t>(kCand1Cap)) candv[slot] = chunk_s2(a, gbase + off);
+            }
+        }
+        __syncthreads();
+        const uint32_t m2 = min(*ncand, static_cast<uint32_t>(kCand1Cap));
+        __syncthreads();
+        if (m2 <= 256) {
+            // few values: the k2-th smallest directly, by counting for each
+            // value those below it and those not above it
+            float *res = reinterpret_cast<float *>(found);
+            if (threadIdx.x == 0) *res = candv[0];
+            __syncthreads();
+            if (threadIdx.x < m2) {
+                const float v = candv[threadIdx.x];
+                uint32_t below = 0, upto = 0;
+                for (uint32_t j = 0; j < m2; ++j) {
+                    const float w = candv[j];
+                    below += w < v ? 1u : 0u;
+                    upto += w <= v ? 1u : 0u;
+                }
+                if (below <= k2 && k2 < upto) *res = v;
+            }
+            __syncthreads();
+            med = *res;
+            __syncthreads();
+        } else {
+            med = kth_s2(a, codes, gbase, n, hmed, candv, m2, k2, hist, found, sh);
+        }
+    } else {
+        med = kth_s2(a, codes, gbase, n, hmed, nullptr, 0, k2, hist, found, sh);
+    }
+    const float thr = cc * med;
+    const uint32_t hthr = half_norm_code(thr);
+
+    // the undecided codes in [hlo, hhi]
+    auto decide = [&](int i, uint32_t c) {
+        if (c > hthr || (c == hthr && chunk_s2(a, gbase + i) > thr)) {
+            atomicOr(&mrow[i >> 5], 1u << (i & 31));
+            codes[i] = static_cast<uint16_t>(c | 0x8000u);
+            atomicAdd(nout, 1u);
+        }
+    };
+    const uint32_t nu = *nunc;
+    if (nu <= static_cast<uint32_t>(kUnc1Cap)) {
+        for (uint32_t j = threadIdx.x; j < nu; j += kSelThreads) {
+            const int i = static_cast<int>(unc[j]);
+            decide(i, codes[i]);
+        }
+    } else {
+        for (int i = threadIdx.x; i < n; i += kSelThreads) {
+            const uint32_t c = codes[i];
+            if (c >= hlo && c <= hhi) decide(i, c);
+        }
+    }
+    uint32_t tot;
+    block_exclusive_scan<uint32_t, kSelThreads>(cnt, &tot, sh);
+    if (threadIdx.x == 0) a.counts[bid] = tot + *nout;
+}
+
 __global__ __launch_bounds__(kScanThreads) void med3_scan_kernel(int64_t nb, const uint32_t *counts,
                                                                  uint64_t *offsets, uint64_t capacity,
                                                                  uint64_t *status) {
@@ -855,12 +1040,14 @@ struct GatherArgs {
     int64_t bps;
     int64_t mask_words;
     int32_t f32;
+    int32_t set_flags;   // 0 when the select kernel has already flagged hnorm
 };
 
 // Ordered outlier write: one block per batch walks the batch's bitmask in
 // order, a block scan of the word popcounts ranks every outlier, and its
 // entry lands at batch_offsets[batch] + rank (dropped past the capacity).
-// The chunk's half-norm record gets the outlier flag (bit 15).
+// The chunk's half-norm record gets the outlier flag (bit 15) unless the
+// select kernel has set it.
 __global__ __launch_bounds__(kFlagThreads) void med3_gather_kernel(GatherArgs a) {
     __shared__ uint32_t sh[kFlagThreads / 64 + 1];
     const int64_t bid = blockIdx.x;
@@ -894,7 +1081,7 @@ __global__ __launch_bounds__(kFlagThreads) void med3_gather_kernel(GatherArgs a)
                 }
                 reinterpret_cast<uint2 *>(a.out_val)[pos] = v;
             }
-            a.hnorm[gc] = static_cast<uint16_t>(a.hnorm[gc] | 0x8000u);
+            if (a.set_flags) a.hnorm[gc] = static_cast<uint16_t>(a.hnorm[gc] | 0x8000u);
             ++pos;
         }
         running += tot;
@@ -1113,6 +1300,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Batches small enough for the single-pass select (its bitmask is in LDS).
+bool med3_single_pass(const Geometry &g) { return g.batch_chunks <= kSel1MaxChunks; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 }  // namespace
@@ -1199,7 +1389,7 @@ hipError_t launch_med3_scan(int64_t batches, const uint32_t *counts, uint64_t *o
     return hipGetLastError();
 }
 
-hipError_t launch_med3_select(const Geometry &g, const void *x, const uint16_t *hnorm, const Med3Work &med,
+hipError_t launch_med3_select(const Geometry &g, const void *x, uint16_t *hnorm, const Med3Work &med,
                               hipStream_t st) {
     const int64_t nb = g.slices * g.batches_per_slice;
     if (nb == 0) return hipSuccess;
@@ -1215,7 +1405,10 @@ hipError_t launch_med3_select(const Geometry &g, const void *x, const uint16_t *
     a.bps = g.batches_per_slice;
     a.C = g.med_C;
     a.f32 = g.f32;
-    hipLaunchKernelGGL(med3_select_kernel, dim3(static_cast<unsigned>(nb)), dim3(kSelThreads), 0, st, a);
+    if (med3_single_pass(g))
+        hipLaunchKernelGGL(med3_select1_kernel, dim3(static_cast<unsigned>(nb)), dim3(kSelThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(med3_select_kernel, dim3(static_cast<unsigned>(nb)), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -1237,6 +1430,7 @@ hipError_t launch_med3_gather(const Geometry &g, const void *x, const Med3Work &
     a.bps = g.batches_per_slice;
     a.mask_words = med.mask_words;
     a.f32 = g.f32;
+    a.set_flags = med3_single_pass(g) ? 0 : 1;
     hipLaunchKernelGGL(med3_gather_kernel, dim3(static_cast<unsigned>(nb)), dim3(kFlagThreads), 0, st, a);
     return hipGetLastError();
 }

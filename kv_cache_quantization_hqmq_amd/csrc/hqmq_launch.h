@@ -38,8 +38,9 @@ struct Med3Work {
 hipError_t launch_encode_search(const Geometry &g, const void *x, const float *codebook,
                                 uint32_t *idx, uint16_t *hnorm, const Med3Work *med, hipStream_t st);
 
-// Med3x: per batch, exact median, threshold, outlier count and bitmask.
-hipError_t launch_med3_select(const Geometry &g, const void *x, const uint16_t *hnorm, const Med3Work &med,
+// Med3x: per batch, exact median, threshold, outlier count and bitmask (and,
+// for batches of at most 131072 chunks, the outlier flags in hnorm).
+hipError_t launch_med3_select(const Geometry &g, const void *x, uint16_t *hnorm, const Med3Work &med,
                               hipStream_t st);
 
 // Exclusive scan of the per-batch counts into batch_offsets, total and
@@ -47,7 +48,8 @@ hipError_t launch_med3_select(const Geometry &g, const void *x, const uint16_t *
 hipError_t launch_med3_scan(int64_t batches, const uint32_t *counts, uint64_t *offsets,
                             uint64_t capacity, uint64_t *status, hipStream_t st);
 
-// Ordered side-list write from the bitmasks, outlier flag into hnorm.
+// Ordered side-list write from the bitmasks (and the outlier flags in hnorm
+// where the select kernel has not set them).
 hipError_t launch_med3_gather(const Geometry &g, const void *x, const Med3Work &med,
                               const uint64_t *offsets, uint16_t *hnorm, uint32_t *out_pos,
                               uint16_t *out_val, uint64_t capacity, hipStream_t st);

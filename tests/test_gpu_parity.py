@@ -58,6 +58,8 @@ CASES = [
     (1, 1, 97, 128, 1024, "f16", 32),
     (1, 1, 4100, 128, 32, "f32", 4096),
     (3, 2, 2051, 128, 8, "f16", 1024),
+    # batches above 131072 chunks take the two-pass Med3x select
+    (1, 1, 4200, 256, 32, "f16", 2100),
 ]
 
 
@@ -74,6 +76,32 @@ def test_small_shapes_every_chunk(L, H, T, D, S, dt, B):
     rep, rec, _ = _check(desc, x, cb_host, cb)
     if B > 0:
         assert rep["outliers"] > 0
+
+
+def test_med3_many_chunks_at_the_threshold():
+    """Two batches whose chunks have norm 1 except thousands at exactly C = 3
+    times that norm or one binary16 step above or below it (and a few large
+    outliers): the threshold code is crowded, so the single-pass select's
+    list of undecided codes overflows in the first batch (6000 of them) and
+    not in the second (1000); strict > leaves the chunks exactly at the
+    threshold in the bulk."""
+    T, D, B = 8192, 128, 4096
+    cpt = D // 4
+    x = np.full((T * cpt, 4), 0.5, np.float16)
+    rng = np.random.default_rng(9)
+    three_half = np.float16(1.5)
+    vals = np.array([three_half, np.nextafter(three_half, np.float16(2)),
+                     np.nextafter(three_half, np.float16(1))], np.float16)
+    for b, m in ((0, 6000), (1, 1000)):
+        idx = b * B * cpt + rng.choice(B * cpt, size=m, replace=False)
+        x[idx] = vals[rng.integers(3, size=m)][:, None]
+        big = b * B * cpt + rng.choice(B * cpt, size=50, replace=False)
+        x[big] = np.float16(15.0)
+    xt = torch.from_numpy(x.reshape(1, 1, T, D)).cuda()
+    cb_host, cb = _cb(1, 1, 32)
+    desc = K.Desc.make(1, 1, T, D, 32, K.HQMQ_F16, B, 3.0)
+    rep, rec, _ = _check(desc, xt, cb_host, cb)
+    assert rep["outliers"] > 0
 
 
 def test_empty_inputs():
