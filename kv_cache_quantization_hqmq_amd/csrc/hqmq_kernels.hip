@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
     constexpr int kQ = NT_REG > 0 ? 16 * NT_REG : 4 * kMaxS;
     __shared__ __attribute__((aligned(16))) float sq[kQ];
     __shared__ __attribute__((aligned(16))) float sx[4][64 * 4];
-    __shared__ uint32_t scode[4][64];
+    __shared__ uint32_t sword[4][64];   // the group's packed index words, per wave
     __shared__ uint32_t shist[MED ? 2048 : 1];
     __shared__ uint32_t sh[kEncThreads / 64 + 3];
 
@@ -230,13 +230,10 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
     }
 
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    // packing: lane w < wpg assembles word ww of token row tt of the group
+    // packing: lane w < wpg stores word ww of token row tt of the group
     const int wpg = (64 >> a.log2_cpt) * a.words;
     const int p_tt = lane / a.words;
     const int p_ww = lane - p_tt * a.words;
-    const int p_lo = 32 * p_ww;
-    const int p_cf = p_lo / a.bits;
-    const int p_cl = min(a.cpt - 1, (p_lo + 31) / a.bits);
     uint32_t *idx_slice = a.idx + slice * a.tokens * a.words;
 
     for (int64_t g0 = c_begin + 64 * wave; g0 < c_end; g0 += 64 * 4) {
@@ -343,22 +340,22 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
             a.hnorm[gc] = hn;
             if constexpr (MED) atomicAdd(&shist[hn >> 4], 1u);
         }
-        scode[wave][lane] = code;
+        // pack the group's codes into its token rows' words: every code is
+        // ORed into the one or two words it spans, then lane w < wpg stores
+        // word w (codes past the range are 0 and leave their words as they are)
+        if (lane < wpg) sword[wave][lane] = 0u;
         wave_sync();
-
-        // pack the codes of the group's token rows into 32-bit words
+        {
+            const int bit = (lane & (a.cpt - 1)) * a.bits;
+            uint32_t *wr = &sword[wave][(lane >> a.log2_cpt) * a.words + (bit >> 5)];
+            const int sft = bit & 31;
+            atomicOr(wr, code << sft);
+            if (sft + a.bits > 32) atomicOr(wr + 1, code >> (32 - sft));
+        }
+        wave_sync();
         if (lane < wpg) {
             const int64_t tok = (g0 >> a.log2_cpt) + p_tt;
-            if ((tok << a.log2_cpt) < c_end) {
-                uint32_t word = 0;
-                const uint32_t *cr = &scode[wave][p_tt << a.log2_cpt];
-                for (int cc = p_cf; cc <= p_cl; ++cc) {
-                    const uint32_t v = cr[cc];
-                    const int sh = cc * a.bits - p_lo;
-                    word |= sh >= 0 ? (v << sh) : (v >> (-sh));
-                }
-                idx_slice[tok * a.words + p_ww] = word;
-            }
+            if ((tok << a.log2_cpt) < c_end) idx_slice[tok * a.words + p_ww] = sword[wave][lane];
         }
         wave_sync();
     }
@@ -381,7 +378,7 @@ template <int NT8, bool MED>
 __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a) {
     constexpr int kQ = NT8 > 0 ? 32 * NT8 : 4 * kMaxS;
     __shared__ __attribute__((aligned(16))) float sq[kQ];
-    __shared__ uint32_t scode[4][64];
+    __shared__ uint32_t sword[4][64];   // the group's packed index words, per wave
     __shared__ uint32_t shist[MED ? 2048 : 1];
     __shared__ uint32_t sh[kEncThreads / 64 + 3];
 
@@ -430,9 +427,6 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
     const int wpg = (64 >> a.log2_cpt) * a.words;
     const int p_tt = lane / a.words;
     const int p_ww = lane - p_tt * a.words;
-    const int p_lo = 32 * p_ww;
-    const int p_cf = p_lo / a.bits;
-    const int p_cl = min(a.cpt - 1, (p_lo + 31) / a.bits);
     uint32_t *idx_slice = a.idx + slice * a.tokens * a.words;
     const uint2 *xs = static_cast<const uint2 *>(a.x) + slice * a.n_slice;
 
@@ -516,20 +510,22 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
             a.hnorm[slice * a.n_slice + c] = hn;
             if constexpr (MED) atomicAdd(&shist[hn >> 4], 1u);
         }
-        scode[wave][lane] = code;
+        // pack the group's codes into its token rows' words: every code is
+        // ORed into the one or two words it spans, then lane w < wpg stores
+        // word w (codes past the range are 0 and leave their words as they are)
+        if (lane < wpg) sword[wave][lane] = 0u;
+        wave_sync();
+        {
+            const int bit = (lane & (a.cpt - 1)) * a.bits;
+            uint32_t *wr = &sword[wave][(lane >> a.log2_cpt) * a.words + (bit >> 5)];
+            const int sft = bit & 31;
+            atomicOr(wr, code << sft);
+            if (sft + a.bits > 32) atomicOr(wr + 1, code >> (32 - sft));
+        }
         wave_sync();
         if (lane < wpg) {
             const int64_t tok = (g0 >> a.log2_cpt) + p_tt;
-            if ((tok << a.log2_cpt) < c_end) {
-                uint32_t word = 0;
-                const uint32_t *cr = &scode[wave][p_tt << a.log2_cpt];
-                for (int cc = p_cf; cc <= p_cl; ++cc) {
-                    const uint32_t v = cr[cc];
-                    const int sh = cc * a.bits - p_lo;
-                    word |= sh >= 0 ? (v << sh) : (v >> (-sh));
-                }
-                idx_slice[tok * a.words + p_ww] = word;
-            }
+            if ((tok << a.log2_cpt) < c_end) idx_slice[tok * a.words + p_ww] = sword[wave][lane];
         }
         wave_sync();
     }
