@@ -321,6 +321,127 @@ def decode_step_bench(args, w):
     print(json.dumps(out), flush=True)
 
 
+def _int_per_token(x, bits: int):
+    """Naive symmetric per-(token, head) integer quantisation of x [..., D]
+    (absmax scale in fp16, round to nearest): the baseline the pages compare
+    against, as a torch reference for the quality report."""
+    import torch
+    qmax = 2 ** (bits - 1) - 1
+    xf = x.float()
+    scale = (xf.abs().amax(dim=-1, keepdim=True) / qmax).to(torch.float16).float()
+    q = torch.where(scale > 0, torch.round(xf / scale.clamp_min(1e-30)), torch.zeros_like(xf)).clamp(-qmax, qmax)
+    return (q * scale).to(x.dtype)
+
+
+def _errors(x, y, q=None, scale=None):
+    """Relative MSE, mean cosine of 4-element chunks' directions (degrees of
+    the mean angle), mean cosine of head vectors, and, for queries q, the
+    relative error of single-query attention outputs over the tokens of
+    every (layer, head) (fp32 softmax of q k / sqrt(D), values y vs x)."""
+    import torch
+    xf, yf = x.float(), y.float()
+    rel = float(((yf - xf) ** 2).sum() / (xf ** 2).sum())
+    xc, yc = xf.reshape(-1, 4), yf.reshape(-1, 4)
+    nx, ny = xc.norm(dim=1), yc.norm(dim=1)
+    ok = (nx > 0) & (ny > 0)
+    cosc = ((xc * yc).sum(dim=1)[ok] / (nx[ok] * ny[ok])).clamp(-1, 1)
+    ang = float(torch.rad2deg(torch.acos(cosc)).mean())
+    cosv = float(torch.nn.functional.cosine_similarity(xf.reshape(-1, xf.shape[-1]),
+                                                       yf.reshape(-1, yf.shape[-1]), dim=1).mean())
+    out = {"rel_mse": rel, "chunk_angle_deg": ang, "vector_cosine": cosv}
+    return out
+
+
+def _attention_error(kx, vx, ky, vy, q, scale):
+    """Relative error of single-query attention outputs with (ky, vy) in
+    place of (kx, vx): kx.. [L, H, T, D], q [L, H, D]; fp32 throughout."""
+    import torch
+    L, H, T, D = kx.shape
+    num, den = 0.0, 0.0
+    for l in range(L):
+        qf = q[l].float().unsqueeze(1)                      # [H, 1, D]
+        ref = torch.softmax(torch.bmm(qf, kx[l].float().transpose(1, 2).contiguous()) * scale, -1)
+        ref = torch.bmm(ref, vx[l].float())
+        got = torch.softmax(torch.bmm(qf, ky[l].float().transpose(1, 2).contiguous()) * scale, -1)
+        got = torch.bmm(got, vy[l].float())
+        num += float(((got - ref) ** 2).sum())
+        den += float((ref ** 2).sum())
+    return (num / den) ** 0.5
+
+
+def quality_report(args):
+    """Reconstruction quality on the synthetic inputs (no model weights or
+    datasets exist here): the covering trend of the random multiplicative
+    codebook against S (Prop. 3.1 gives only O((24 S)^(-1/3))), Med3x on
+    outlier-heavy inputs, and naive per-token integer quantisation at several
+    widths, each with its storage cost in bits per element."""
+    import math
+    import numpy as np
+    import torch
+    import kv_cache_quantization_hqmq_amd as K
+    import synth
+    torch.cuda.set_device(0)
+    rep = {"report": "HQMQ reconstruction quality on synthetic KV tensors (one MI355X)", "data": "synthetic"}
+
+    def run(w, x, role, S, B):
+        desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, S, K.HQMQ_F16, B, 3.0)
+        cb = torch.from_numpy(K.hqmq_make_codebook(w.codebook_seed, w.layers, w.heads, role, S)).cuda()
+        rec = K.encode(desc, x, cb)
+        y = K.decode(desc, rec, cb)
+        sz = K.hqmq_sizes(desc)
+        nbytes = sz.idx_bytes + sz.hnorm_bytes + 12 * rec.n_outliers + sz.offsets_bytes + sz.codebook_bytes
+        return y, 8.0 * nbytes / (sz.chunks * 4), rec.n_outliers / sz.chunks
+
+    # 1) covering trend on i.i.d. N(0,1) (every direction equally likely)
+    w = synth.WORKLOADS[2].scaled(layers=4, heads=8, tokens=8192, dist="normal", data_seed=4401)
+    x = synth.generate(w, 0, "cuda")
+    trend = []
+    for S in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
+        y, bits, _ = run(w, x, 0, S, 0)
+        e = _errors(x, y)
+        trend.append({"S": S, "codewords": 24 * S, "bits_per_element": bits, **e})
+        log(f"S={S}: {e}")
+        del y
+    xs = np.log([t["codewords"] for t in trend])
+    slope = float(np.polyfit(xs, np.log([t["chunk_angle_deg"] for t in trend]), 1)[0])
+    rep["covering_trend"] = {"workload": f"N(0,1) [{w.layers}, {w.heads}, {w.tokens}, {w.head_dim}] fp16",
+                             "points": trend, "angle_vs_codewords_loglog_slope": slope,
+                             "expected_slope": -1.0 / 3.0}
+    del x
+
+    # 2) outlier-heavy and lognormal-channel K/V: HQMQ (Med3x on/off) vs int-k per token
+    cases = [(synth.WORKLOADS[3].scaled(layers=4, heads=4, tokens=8192, data_seed=4402), 32),
+             (synth.WORKLOADS[2].scaled(layers=4, heads=8, tokens=8192, data_seed=4403), 8)]
+    rep["comparisons"] = []
+    for w, S in cases:
+        xs_ = {r: synth.generate(w, r, "cuda") for r in (0, 1)}
+        g = torch.Generator(device="cuda")
+        g.manual_seed(77)
+        q = torch.randn((w.layers, w.heads, w.head_dim), generator=g, device="cuda").to(torch.float16)
+        sc = 1.0 / math.sqrt(w.head_dim)
+        rows = []
+        variants = [("hqmq_med3", S, 4096), ("hqmq_no_med3", S, 0)]
+        for name, SS, B in variants:
+            ys, bits, fo = {}, 0.0, 0.0
+            for r in (0, 1):
+                ys[r], b_, f_ = run(w, xs_[r], r, SS, B)
+                bits += b_ / 2
+                fo += f_ / 2
+            e = _errors(torch.cat([xs_[0], xs_[1]]), torch.cat([ys[0], ys[1]]))
+            e["attention_rel_error"] = _attention_error(xs_[0], xs_[1], ys[0], ys[1], q, sc)
+            rows.append({"method": name, "S": SS, "med3_batch_tokens": B, "bits_per_element": bits,
+                         "outlier_fraction": fo, **e})
+            log(f"{w.name} {name}: {rows[-1]}")
+        for bw in (4, 6, 8):
+            ys = {r: _int_per_token(xs_[r], bw) for r in (0, 1)}
+            e = _errors(torch.cat([xs_[0], xs_[1]]), torch.cat([ys[0], ys[1]]))
+            e["attention_rel_error"] = _attention_error(xs_[0], xs_[1], ys[0], ys[1], q, sc)
+            rows.append({"method": f"int{bw}_per_token", "bits_per_element": bw + 16.0 / w.head_dim, **e})
+            log(f"{w.name} int{bw}: {rows[-1]}")
+        rep["comparisons"].append({"workload": synth.describe(w), "rows": rows})
+    print(json.dumps(rep), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +451,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--quality", action="store_true", help="print the synthetic quality report instead")
     ap.add_argument("--summarize", metavar="ROCPD_DB", help="print a kernel table of a rocprofv3 database")
     ap.add_argument("--summarize-pmc", metavar="ROCPD_DB", help="print per-kernel counter averages")
     args = ap.parse_args()
@@ -353,6 +475,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.quality:
+        quality_report(args)
         return
 
     w = synth.WORKLOADS[args.workload]
