@@ -106,6 +106,11 @@ def _configure(L):
     L.or_round_f32.argtypes = [_f64p, ctypes.c_int64, _f32p]
     L.or_round_f16.argtypes = [_f64p, ctypes.c_int64, _u16p]
     L.or_num_threads.restype = ctypes.c_int
+    L.or_compact_norm.argtypes = [ctypes.c_uint16, ctypes.c_int]
+    L.or_compact_norm.restype = ctypes.c_uint32
+    L.or_compact_to_h16.argtypes = [ctypes.c_uint32, ctypes.c_int]
+    L.or_compact_to_h16.restype = ctypes.c_uint16
+    L.or_compact_norms.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int, _u32p]
     L.or_attend.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int, _f64p, ctypes.c_int,
                             ctypes.c_double, _f64p]
     return L
@@ -281,6 +286,20 @@ def decode_range(codes, hnorm, T: int, D: int, q, side_pos=None, side_val=None,
     if r < 0:
         raise ValueError("or_decode_range: inconsistent records")
     return y
+
+
+def compact_norms(h16, b: int) -> np.ndarray:
+    """Compact norm codes (b bits) of binary16 half-norm records."""
+    h = np.ascontiguousarray(h16, dtype=np.uint16)
+    out = np.empty(h.shape, np.uint32)
+    lib().or_compact_norms(_p(h, _u16p), h.size, int(b), _p(out, _u32p))
+    return out
+
+
+def compact_to_h16(codes, b: int) -> np.ndarray:
+    """Half-norm records (binary16 pattern, or the flag) of compact codes."""
+    c = np.asarray(codes, dtype=np.uint32).ravel()
+    return np.array([lib().or_compact_to_h16(int(v), int(b)) for v in c], np.uint16).reshape(np.shape(codes))
 
 
 def attend(k, v, q, scale: float) -> np.ndarray:

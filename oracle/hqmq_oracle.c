@@ -47,6 +47,9 @@
  *   or_lower_median, Med3x ........ pinned (numpy partition, designed inputs)
  *   or_pack_row ................... pinned (bit-by-bit unpack in numpy)
  *   or_encode_range/or_decode_range pinned through the above + closed forms
+ *   or_compact_norm ............... pinned (brute-force nearest value of the
+ *                                   format over every binary16 input; flag,
+ *                                   identity at b = 15, error bound)
  *   or_attend ..................... pinned (closed forms: uniform scores,
  *                                   one token, dominant key; scipy softmax
  *                                   on random inputs; token permutation)
@@ -544,6 +547,60 @@ void or_round_f16(const double *y, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = or_f16_bits(y[i]);
+}
+
+/* Compact norm code (reading: the pages' bit figures -- about 3.79 bits
+ * per element at S = 8, about 5 at S = 32 [ABS], [FR-MEC] -- are two codes
+ * of log2(24 S) bits per 4-element chunk, so the norm gets as many bits as
+ * the direction index; the pages do not give its format).  With b the code
+ * width and m = b - 5: the binary16 half-norm h16 (outlier flag clear) is
+ * rounded to the nearest value of a float with 5 exponent bits (bias 15,
+ * subnormals like binary16) and m mantissa bits, a tie going to the even
+ * code, capped at that float's largest finite value; the code is the top b bits of the
+ * binary16 pattern of the rounded value (its low 10 - m bits are zero).
+ * The all-ones code (an infinity of that format) marks a Med3x outlier. */
+uint32_t or_compact_norm(uint16_t h16, int b)
+{
+    const int m = b - 5;
+    if (h16 & 0x8000u)
+        return (1u << b) - 1u;
+    const double v = or_f16_value(h16);
+    double q;   /* spacing of the format's values around v */
+    if (v < ldexp(1.0, -14)) {
+        q = ldexp(1.0, -14 - m);
+    } else {
+        int e;
+        frexp(v, &e);   /* v in [2^(e-1), 2^e) */
+        q = ldexp(1.0, e - 1 - m);
+    }
+    /* the two neighbouring values of the format (v / q is exact), capped at
+     * its largest finite value; the nearer one, on a tie the even code */
+    const double t = v / q, f = floor(t);
+    const double vmax = (2.0 - ldexp(1.0, -m)) * 32768.0;
+    const double lo = f * q < vmax ? f * q : vmax;
+    const double hi = (f + 1.0) * q < vmax ? (f + 1.0) * q : vmax;
+    const uint32_t clo = (uint32_t)or_f16_bits(lo) >> (10 - m);
+    const uint32_t chi = (uint32_t)or_f16_bits(hi) >> (10 - m);
+    if (t - f < 0.5)
+        return clo;
+    if (t - f > 0.5)
+        return chi;
+    return (clo & 1u) ? chi : clo;
+}
+
+/* The binary16 half-norm record a compact norm code stands for: the flag
+ * (0x8000) for the all-ones code, else the code's binary16 pattern. */
+uint16_t or_compact_to_h16(uint32_t c, int b)
+{
+    if (c == (1u << b) - 1u)
+        return 0x8000u;
+    return (uint16_t)(c << (15 - b));
+}
+
+void or_compact_norms(const uint16_t *h16, int64_t n, int b, uint32_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = or_compact_norm(h16[i], b);
 }
 
 /* Decode-step attention of G query rows over T cached tokens ([NL-LAT]):

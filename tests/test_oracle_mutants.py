@@ -16,6 +16,7 @@ import pytest
 import oracle as O
 from tests import test_oracle_algebra as A
 from tests import test_oracle_attend as T
+from tests import test_oracle_compact_norm as CN
 from tests import test_oracle_f16_codebook as F
 from tests import test_oracle_med3_codec as M
 from tests import test_oracle_quantizer as Q
@@ -83,6 +84,15 @@ MUTANTS = [
     ("attend-values-from-keys",
      "og[d] += s[t] * v[t * D + d];", "og[d] += s[t] * k[t * D + d];",
      T.test_uniform_scores_give_the_mean_of_v),
+    ("compact-norm-truncates",
+     "    if (t - f < 0.5)\n        return clo;", "    if (t - f < 1.0)\n        return clo;",
+     lambda: CN.test_rounds_to_the_nearest_value_ties_to_even(10)),
+    ("compact-norm-ties-odd",
+     "return (clo & 1u) ? chi : clo;", "return (clo & 1u) ? clo : chi;",
+     lambda: CN.test_rounds_to_the_nearest_value_ties_to_even(8)),
+    ("compact-norm-no-cap",
+     "    const double hi = (f + 1.0) * q < vmax ? (f + 1.0) * q : vmax;", "    const double hi = (f + 1.0) * q;",
+     lambda: CN.test_monotone_bounded_and_flagged(8)),
     ("side-pos-drops-offset",
      "side_pos[n_out] = (uint32_t)((t0 + t) * cpt + c);", "side_pos[n_out] = (uint32_t)(t * cpt + c);",
      M.test_batches_and_partial_tail),
