@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "HQMQ encode & decode chunks/s and GB/s (fp16 in) on 1 MI355X; % of roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+NORM_FORMATS = {"f16": 0, "packed": 1}   # hqmq_desc.norm_format
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-70b-kv-128k.json")
 
@@ -179,10 +180,11 @@ def decode_step_bench(args, w):
     sh = torch.cuda.current_stream().cuda_stream
     ev = HipEvents()
     group = 4
+    nf = NORM_FORMATS[args.norm_format]
     desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, w.S, K.HQMQ_F16,
-                       w.med_batch_tokens, w.med_C)
+                       w.med_batch_tokens, w.med_C, nf)
     desc_a = K.Desc.make(w.layers, w.heads, w.append_tokens, w.head_dim, w.S, K.HQMQ_F16,
-                         w.append_tokens, w.med_C)
+                         w.append_tokens, w.med_C, nf)
     sz, sza = K.hqmq_sizes(desc), K.hqmq_sizes(desc_a)
     L, H, D, nseq = w.layers, w.heads, w.head_dim, w.sequences
     Tc = w.tokens // nseq
@@ -299,6 +301,7 @@ def decode_step_bench(args, w):
                    "appended_tokens_per_step": w.append_tokens, "head_dim": D,
                    "roles": "K+V", "input": w.dtype, "S": w.S,
                    "med3_batch_tokens": w.med_batch_tokens, "med3_C": w.med_C,
+                   "norm_format": args.norm_format,
                    "step": "encode appended tokens + attention of every layer read from the records",
                    "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": "attend (one layer)", "achieved": att_gbps,
@@ -315,6 +318,8 @@ def decode_step_bench(args, w):
         "fused_speedup_vs_fakequant": fq_ms / fused_ms,
         "appended_outliers_last_step": app_out,
         "cache_outlier_fraction": sum(n_out.values()) / (roles * sz.chunks),
+        "cache_bits_per_element": 8 * sum(rec_bytes + 12 * n_out[r] + sz.offsets_bytes for r in w.roles)
+        / (roles * sz.chunks * 4),
         "kernel_sha256_16": kernel_hash(),
         "cpu_baseline": None,
     }
@@ -383,8 +388,8 @@ def quality_report(args):
     torch.cuda.set_device(0)
     rep = {"report": "HQMQ reconstruction quality on synthetic KV tensors (one MI355X)", "data": "synthetic"}
 
-    def run(w, x, role, S, B):
-        desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, S, K.HQMQ_F16, B, 3.0)
+    def run(w, x, role, S, B, nf=0):
+        desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, S, K.HQMQ_F16, B, 3.0, nf)
         cb = torch.from_numpy(K.hqmq_make_codebook(w.codebook_seed, w.layers, w.heads, role, S)).cuda()
         rec = K.encode(desc, x, cb)
         y = K.decode(desc, rec, cb)
@@ -420,11 +425,12 @@ def quality_report(args):
         q = torch.randn((w.layers, w.heads, w.head_dim), generator=g, device="cuda").to(torch.float16)
         sc = 1.0 / math.sqrt(w.head_dim)
         rows = []
-        variants = [("hqmq_med3", S, 4096), ("hqmq_no_med3", S, 0)]
-        for name, SS, B in variants:
+        variants = [("hqmq_med3", S, 4096, 0), ("hqmq_no_med3", S, 0, 0),
+                    ("hqmq_med3_packed_norms", S, 4096, 1), ("hqmq_no_med3_packed_norms", S, 0, 1)]
+        for name, SS, B, nf in variants:
             ys, bits, fo = {}, 0.0, 0.0
             for r in (0, 1):
-                ys[r], b_, f_ = run(w, xs_[r], r, SS, B)
+                ys[r], b_, f_ = run(w, xs_[r], r, SS, B, nf)
                 bits += b_ / 2
                 fo += f_ / 2
             e = _errors(torch.cat([xs_[0], xs_[1]]), torch.cat([ys[0], ys[1]]))
@@ -449,6 +455,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="1..5 (see synth.WORKLOADS; 5 is the decode step)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--norm-format", choices=sorted(NORM_FORMATS), default="f16",
+                    help="norm records: binary16 half-norms, or packed b-bit compact codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--quality", action="store_true", help="print the synthetic quality report instead")
@@ -491,7 +499,8 @@ def main():
     ev = HipEvents()
 
     desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, w.S,
-                       K.HQMQ_F32 if w.dtype == "f32" else K.HQMQ_F16, w.med_batch_tokens, w.med_C)
+                       K.HQMQ_F32 if w.dtype == "f32" else K.HQMQ_F16, w.med_batch_tokens, w.med_C,
+                       NORM_FORMATS[args.norm_format])
     sz = K.hqmq_sizes(desc)
     log(f"workload {synth.describe(w)}; {sz.chunks} chunks per role")
 
@@ -575,7 +584,8 @@ def main():
     flops_launch = 32 * w.S * chunks_role           # 16 S FMA per chunk (the method's minimum)
     s_ms = mean(search_ms)
     achieved_tf = flops_launch / (s_ms * 1e-3) / 1e12
-    traffic = traffic_per_launch() if w.wid == 4 else None
+    # counters were taken on the binary16-norm configuration
+    traffic = traffic_per_launch() if (w.wid == 4 and args.norm_format == "f16") else None
     d_ms = mean(dec_ms)
     dec_bytes_launch = rec_bytes + chunks_role * 8 + 12 * (sum(n_out.values()) / len(w.roles)) + \
         sz.offsets_bytes
@@ -597,14 +607,15 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.heads,
                    "tokens": w.tokens, "head_dim": w.head_dim, "roles": "K+V" if len(w.roles) == 2 else "K",
                    "input": w.dtype, "S": w.S, "med3_batch_tokens": w.med_batch_tokens,
-                   "med3_C": w.med_C, "parallelism": "none"},
+                   "med3_C": w.med_C, "norm_format": args.norm_format, "parallelism": "none"},
         "roofline": {"bound": "mfma", "kernel": "encode_search", "achieved": achieved_tf,
                      "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tf / PEAK_FP32_MFMA_TFLOPS, "traffic": traffic,
                      "algorithmic_per_launch": flops_launch, "avg_launch_ms": s_ms},
         "roofline_decode": {"bound": "hbm", "kernel": "decode", "achieved": dec_gbps,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
-                            "traffic": traffic_per_launch("decode_bytes_per_launch") if w.wid == 4 else None,
+                            "traffic": traffic_per_launch("decode_bytes_per_launch")
+                            if (w.wid == 4 and args.norm_format == "f16") else None,
                             "algorithmic_per_launch": dec_bytes_launch, "avg_launch_ms": d_ms},
         "encode_chunks_per_s": total_chunks / (sum(enc_ms) / args.steps * 1e-3),
         "decode_chunks_per_s": total_chunks / (sum(dec_ms) / args.steps * 1e-3),

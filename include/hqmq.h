@@ -26,10 +26,19 @@
  *          2T order p: +1, -1, +i, -i, +j, -j, +k, -k, then (s0,s1,s2,s3)/2
  *          with s_m = -1 iff bit m of p - 8 is set.  The record always holds
  *          the nearest codeword, also for an outlier chunk.
- *   hnorm  [layers][kv_heads][tokens][head_dim / 4] u16.  binary16 of
- *          sqrt_rn(s2) / 2 with s2 = fma(x3,x3, fma(x2,x2, fma(x1,x1, x0*x0)))
- *          in fp32; bit 15 (the sign bit, free since norms are >= 0) is the
- *          Med3x outlier flag.
+ *   hnorm  norm_format HQMQ_NORM_F16: [layers][kv_heads][tokens][head_dim / 4]
+ *          u16, the binary16 half-norm h16 = binary16 of sqrt_rn(s2) / 2 with
+ *          s2 = fma(x3,x3, fma(x2,x2, fma(x1,x1, x0*x0))) in fp32; bit 15 (the
+ *          sign bit, free since norms are >= 0) is the Med3x outlier flag.
+ *          norm_format HQMQ_NORM_PACKED: u32 words laid out exactly like idx
+ *          (b bits per chunk, the same b), holding the compact norm code: h16
+ *          rounded to nearest (a tie to the even code) to a float with 5
+ *          exponent bits and b - 5 mantissa bits, capped at its largest
+ *          finite value, as the top b bits of the binary16 pattern; the
+ *          all-ones code is the outlier flag.  Then a chunk costs 2 b bits
+ *          (S = 8: 4 bits per element, S = 32: 5), the pages' accounting of
+ *          two log2(24 S)-bit codes per chunk (abstract: ~3.79 bits at S = 8,
+ *          ~5 at S = 32) with whole bits.
  *   side list (Med3x only): out_pos[e] u32 = t * head_dim / 4 + c (position
  *          in its slice), out_val[4e..4e+3] = the chunk's values as binary16
  *          (fp32 inputs rounded to nearest even).  Ordered by (slice, batch,
@@ -39,8 +48,9 @@
  *   status [2] u64: status[0] = outliers found, status[1] = 1 when they did
  *          not fit out_capacity (entries past the capacity are dropped).
  *
- * Decoding: bulk chunk y = (2 * hnorm) * (q_p * q_s) in fp32, rounded to the
- * output type; outlier chunk y = its side-list values.
+ * Decoding: bulk chunk y = (2 * h) * (q_p * q_s) in fp32, rounded to the
+ * output type, h the binary16 half-norm (packed format: the value the code
+ * stands for); outlier chunk y = its side-list values.
  *
  * Threading: every entry point is stateless and re-entrant; device work is
  * enqueued on the caller's stream and nothing is allocated.  Calls on
@@ -73,6 +83,9 @@ enum { HQMQ_F16 = 0, HQMQ_F32 = 1 };
 /* Roles: which cache tensor a codebook belongs to. */
 enum { HQMQ_ROLE_K = 0, HQMQ_ROLE_V = 1 };
 
+/* Norm record formats (see hnorm above). */
+enum { HQMQ_NORM_F16 = 0, HQMQ_NORM_PACKED = 1 };
+
 /* Problem descriptor (a plain value, read only during the call).
  *   layers, kv_heads, tokens >= 0 (any of them 0 = empty input)
  *   head_dim in {16, 32, 64, 128, 256}
@@ -82,7 +95,8 @@ enum { HQMQ_ROLE_K = 0, HQMQ_ROLE_V = 1 };
  *       block is its own batch.  Median over the batch's chunks ("the
  *       current batch", gist.science/nl Methodologie 3).
  *   med_C: Med3x multiplier, the pages fix 3 (finite, > 0 when Med3x is on)
- *   dtype: HQMQ_F16 or HQMQ_F32 for x (and y). */
+ *   dtype: HQMQ_F16 or HQMQ_F32 for x (and y)
+ *   norm_format: HQMQ_NORM_F16 or HQMQ_NORM_PACKED. */
 typedef struct hqmq_desc {
     int64_t layers;
     int64_t kv_heads;
@@ -92,7 +106,7 @@ typedef struct hqmq_desc {
     int32_t dtype;
     int64_t med_batch_tokens;
     float med_C;
-    int32_t reserved;
+    int32_t norm_format;
 } hqmq_desc;
 
 /* Sizes of every buffer a call needs, in bytes (hqmq_sizes). */
@@ -104,19 +118,22 @@ typedef struct hqmq_sizes_t {
     int64_t max_outliers;       /* sum over batches of floor(n_batch / 2) */
     uint64_t input_bytes;       /* x (and y) */
     uint64_t idx_bytes;
-    uint64_t hnorm_bytes;
+    uint64_t hnorm_bytes;       /* chunks * 2 (binary16), or idx_bytes (packed) */
     uint64_t offsets_bytes;     /* (batches + 1) * 8, 0 when Med3x is off */
     uint64_t side_entry_bytes;  /* 12 bytes per outlier (4 pos + 8 values) */
-    uint64_t workspace_bytes;   /* encode scratch, 0 when Med3x is off */
+    uint64_t workspace_bytes;   /* encode scratch: Med3x histograms and bitmasks, and
+                                   the binary16 half-norms when packed (0 if neither) */
     uint64_t codebook_bytes;    /* layers * kv_heads * S * 16 */
 } hqmq_sizes_t;
 
 /* Encoded records: device pointers owned by the caller (see layout above).
- * batch_offsets, out_pos, out_val and status may be NULL when Med3x is off;
- * out_pos/out_val may be NULL when out_capacity is 0. */
+ * hnorm is the norm plane in the descriptor's norm_format (u16 half-norms,
+ * or the packed u32 words).  batch_offsets, out_pos, out_val and status may
+ * be NULL when Med3x is off; out_pos/out_val may be NULL when out_capacity
+ * is 0. */
 typedef struct hqmq_enc {
     uint32_t *idx;
-    uint16_t *hnorm;
+    void *hnorm;                /* 8-byte aligned (16 for hqmq_attend) */
     uint64_t *batch_offsets;
     uint32_t *out_pos;
     uint16_t *out_val;
@@ -151,7 +168,8 @@ int hqmq_make_codebook(uint64_t seed, int32_t layers, int32_t kv_heads, int32_t 
  * 1; the identity <x, q_p q_s> = <conj(q_p) x, q_s> of the isometry argument,
  * abstract), then, when Med3x is on, the exact lower median of s2 per batch,
  * outliers s2 > fl(fl(C*C) * median) flagged in hnorm and copied to the side
- * list in order.  workspace: device scratch of at least
+ * list in order; with HQMQ_NORM_PACKED the flagged half-norms are last turned
+ * into packed compact codes.  workspace: device scratch of at least
  * hqmq_sizes().workspace_bytes, 256-byte aligned (may be NULL when that is 0).
  * Asynchronous on stream; nothing is enqueued when validation fails.  Ties
  * between exactly equal fp32 scores keep the smallest code.
@@ -178,8 +196,9 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook,
 int hqmq_encode_result(const hqmq_enc *enc, hipStream_t stream, uint64_t *n_outliers);
 
 /* Decode enc into y (device, same shape as x, d->dtype, 16-byte aligned):
- * bulk chunks r^ (q_p q_s) with r^ = 2 hnorm, computed in fp32 and rounded
- * to nearest even; outlier chunks take their side-list values (the decoder
+ * bulk chunks r^ (q_p q_s) with r^ = 2 h, h the half-norm of the record
+ * (packed: the binary16 value its code stands for), computed in fp32 and
+ * rounded to nearest even; outlier chunks take their side-list values (the decoder
  * the pages run before or inside attention: gist.science "Memory en
  * Latentie").  enc must come from a successful hqmq_encode with the same
  * descriptor and codebook.  Asynchronous on stream.

@@ -8,10 +8,11 @@ binding (same function names).  Build with
 from .hqmq import (AttnDesc, AttnSizes, CapacityError, Desc, HQMQError, Records, Sizes,
                    allocate_records, attend, decode, encode, hqmq_attend, hqmq_attn_sizes, hqmq_decode,
                    hqmq_encode, hqmq_encode_result, hqmq_encode_timed, hqmq_make_codebook, hqmq_sizes,
-                   hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_ROLE_K, HQMQ_ROLE_V)
+                   hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_NORM_F16, HQMQ_NORM_PACKED,
+                   HQMQ_ROLE_K, HQMQ_ROLE_V)
 
 __all__ = ["AttnDesc", "AttnSizes", "CapacityError", "Desc", "HQMQError", "Records", "Sizes",
            "allocate_records", "attend", "decode", "encode", "hqmq_attend", "hqmq_attn_sizes",
            "hqmq_decode", "hqmq_encode", "hqmq_encode_result", "hqmq_encode_timed",
            "hqmq_make_codebook", "hqmq_sizes", "hqmq_strerror", "workspace", "HQMQ_F16",
-           "HQMQ_F32", "HQMQ_ROLE_K", "HQMQ_ROLE_V"]
+           "HQMQ_F32", "HQMQ_NORM_F16", "HQMQ_NORM_PACKED", "HQMQ_ROLE_K", "HQMQ_ROLE_V"]

@@ -33,6 +33,7 @@ int make_geometry(const hqmq_desc *d, hqmq::Geometry *g) {
     if (!head_dim_ok(d->head_dim)) return HQMQ_EINVAL;
     if (d->S < 1 || d->S > kMaxS) return HQMQ_EINVAL;
     if (d->dtype != HQMQ_F16 && d->dtype != HQMQ_F32) return HQMQ_EINVAL;
+    if (d->norm_format != HQMQ_NORM_F16 && d->norm_format != HQMQ_NORM_PACKED) return HQMQ_EINVAL;
     if (d->med_batch_tokens < 0) return HQMQ_EINVAL;
     if (d->med_batch_tokens > 0 && !(std::isfinite(d->med_C) && d->med_C > 0.0f)) return HQMQ_EINVAL;
     const int64_t cpt = d->head_dim / 4;
@@ -56,32 +57,45 @@ int make_geometry(const hqmq_desc *d, hqmq::Geometry *g) {
         g->batches_per_slice = 0;
     }
     g->med_C = d->med_C;
+    g->npack = d->norm_format == HQMQ_NORM_PACKED ? 1 : 0;
     // grids are one-dimensional: keep the block count well inside 2^31
     if (g->slices > 0 && g->n_slice / 256 + 1 > (int64_t{1} << 31) / g->slices) return HQMQ_ENOTSUP;
     return HQMQ_OK;
 }
 
-// Med3x workspace: hist [batches][2048] u32 | counts [batches] u32 |
-// mask [batches][mask_words] u32 (one bit per chunk).
+// Encode workspace.  Med3x: hist [batches][2048] u32 | counts [batches] u32 |
+// mask [batches][mask_words] u32 (one bit per chunk).  Packed norms: the
+// binary16 half-norm plane [chunks] u16 that the search writes, Med3x flags,
+// and the pack kernel reads.
 int64_t mask_words(const hqmq::Geometry &g) { return 2 * ((g.batch_chunks + 63) / 64); }
 
 uint64_t workspace_layout(const hqmq::Geometry &g, void *base, hqmq::Med3Work *w) {
-    if (g.batch_chunks == 0) return 0;
-    const uint64_t nb = static_cast<uint64_t>(g.slices * g.batches_per_slice);
-    const uint64_t mw = static_cast<uint64_t>(mask_words(g));
     uint64_t off = 0;
-    const uint64_t o_hist = off;
-    off = align_up(off + nb * 2048 * 4, kWsAlign);
-    const uint64_t o_cnt = off;
-    off = align_up(off + nb * 4, kWsAlign);
-    const uint64_t o_mask = off;
-    off = align_up(off + nb * mw * 4, kWsAlign);
+    uint64_t o_hist = 0, o_cnt = 0, o_mask = 0, o_h16 = 0;
+    const uint64_t mw = static_cast<uint64_t>(mask_words(g));
+    if (g.batch_chunks > 0) {
+        const uint64_t nb = static_cast<uint64_t>(g.slices * g.batches_per_slice);
+        o_hist = off;
+        off = align_up(off + nb * 2048 * 4, kWsAlign);
+        o_cnt = off;
+        off = align_up(off + nb * 4, kWsAlign);
+        o_mask = off;
+        off = align_up(off + nb * mw * 4, kWsAlign);
+    }
+    if (g.npack) {
+        o_h16 = off;
+        off = align_up(off + static_cast<uint64_t>(g.slices * g.n_slice) * 2, kWsAlign);
+    }
     if (w) {
         char *b = static_cast<char *>(base);
-        w->hist = reinterpret_cast<uint32_t *>(b + o_hist);
-        w->counts = reinterpret_cast<uint32_t *>(b + o_cnt);
-        w->mask = reinterpret_cast<uint32_t *>(b + o_mask);
-        w->mask_words = static_cast<int64_t>(mw);
+        *w = hqmq::Med3Work{};
+        if (g.batch_chunks > 0) {
+            w->hist = reinterpret_cast<uint32_t *>(b + o_hist);
+            w->counts = reinterpret_cast<uint32_t *>(b + o_cnt);
+            w->mask = reinterpret_cast<uint32_t *>(b + o_mask);
+            w->mask_words = static_cast<int64_t>(mw);
+        }
+        if (g.npack) w->h16 = reinterpret_cast<uint16_t *>(b + o_h16);
     }
     return off;
 }
@@ -189,7 +203,7 @@ int hqmq_sizes(const hqmq_desc *d, hqmq_sizes_t *out) {
     out->max_outliers = mo;
     out->input_bytes = static_cast<uint64_t>(out->chunks) * 4 * (g.f32 ? 4 : 2);
     out->idx_bytes = static_cast<uint64_t>(g.slices * g.tokens) * g.words * 4;
-    out->hnorm_bytes = static_cast<uint64_t>(out->chunks) * 2;
+    out->hnorm_bytes = g.npack ? out->idx_bytes : static_cast<uint64_t>(out->chunks) * 2;
     out->offsets_bytes = g.batch_chunks > 0 ? static_cast<uint64_t>(out->batches + 1) * 8 : 0;
     out->side_entry_bytes = 12;
     out->workspace_bytes = workspace_layout(g, nullptr, nullptr);
@@ -255,13 +269,18 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
             return HQMQ_EINVAL;
         if (enc->out_capacity > 0 && (!enc->out_pos || !enc->out_val || !aligned(enc->out_val, 8)))
             return HQMQ_EINVAL;
-        const uint64_t need = workspace_layout(g, nullptr, nullptr);
-        if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign)))
-            return HQMQ_EINVAL;
-        workspace_layout(g, workspace, &ws);
     } else if (enc->status && !aligned(enc->status, 8)) {
         return HQMQ_EINVAL;
     }
+    {
+        const uint64_t need = workspace_layout(g, nullptr, nullptr);
+        if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign)))
+            return HQMQ_EINVAL;
+        if (need > 0) workspace_layout(g, workspace, &ws);
+    }
+    // the binary16 half-norms: the record itself, or (packed) the scratch
+    // plane the pack kernel turns into compact codes at the end
+    uint16_t *h16 = g.npack ? ws.h16 : static_cast<uint16_t *>(enc->hnorm);
 
     hipError_t e = hipSuccess;
     if (med && nb > 0) {
@@ -274,17 +293,17 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
     }
     if (search_begin && hipEventRecord(search_begin, stream) != hipSuccess) return HQMQ_EHIP;
     if (chunks > 0) {
-        e = hqmq::launch_encode_search(g, x, codebook, enc->idx, enc->hnorm, med && nb > 0 ? &ws : nullptr, stream);
+        e = hqmq::launch_encode_search(g, x, codebook, enc->idx, h16, med && nb > 0 ? &ws : nullptr, stream);
         if (e != hipSuccess) return HQMQ_EHIP;
     }
     if (search_end && hipEventRecord(search_end, stream) != hipSuccess) return HQMQ_EHIP;
     if (med) {
         if (nb > 0) {
-            e = hqmq::launch_med3_select(g, x, enc->hnorm, ws, stream);
+            e = hqmq::launch_med3_select(g, x, h16, ws, stream);
             if (e == hipSuccess)
                 e = hqmq::launch_med3_scan(nb, ws.counts, enc->batch_offsets, enc->out_capacity, enc->status, stream);
             if (e == hipSuccess)
-                e = hqmq::launch_med3_gather(g, x, ws, enc->batch_offsets, enc->hnorm, enc->out_pos, enc->out_val,
+                e = hqmq::launch_med3_gather(g, x, ws, enc->batch_offsets, h16, enc->out_pos, enc->out_val,
                                              enc->out_capacity, stream);
         } else {
             e = hqmq::launch_fill_u64(enc->batch_offsets, 1, 0, stream);
@@ -293,6 +312,8 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
     } else if (enc->status) {
         e = hqmq::launch_fill_u64(enc->status, 2, 0, stream);
     }
+    if (e == hipSuccess && g.npack && chunks > 0)
+        e = hqmq::launch_pack_norms(g, h16, static_cast<uint32_t *>(enc->hnorm), stream);
     return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
 }
 
@@ -375,7 +396,7 @@ int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, 
                                         !aligned(e->out_val, 8)))
                 return HQMQ_EINVAL;
         }
-        role[r] = hqmq::AttRole{e->idx, e->hnorm, g.batch_chunks > 0 ? e->batch_offsets : nullptr, e->out_pos,
+        role[r] = hqmq::AttRole{e->idx, static_cast<const uint16_t *>(e->hnorm), g.batch_chunks > 0 ? e->batch_offsets : nullptr, e->out_pos,
                                 e->out_val, g.batch_chunks > 0 ? e->out_capacity : 0, cb[r]};
     }
     hqmq::AttLaunch L;
@@ -400,6 +421,7 @@ int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, 
     L.S = g.S;
     L.bits = g.bits;
     L.words = g.words;
+    L.npack = g.npack;
     L.scale = a->scale;
     return hqmq::launch_attend(L, stream) == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
 }

@@ -11,8 +11,9 @@
 //     out[b][j] = sum_t softmax_t(scale <q[b][j], k_t>) v_t,
 //
 // over the sequence's tokens of the encoded cache, where k_t and v_t are the
-// fp16 values the decode kernel writes (bulk chunks 2 hnorm (q_p * q_s)
-// rounded to binary16; Med3x outlier chunks their side-list values).
+// fp16 values the decode kernel writes (bulk chunks 2 h (q_p * q_s) rounded
+// to binary16, h the record's half-norm, stored as binary16 or as a packed
+// compact code; Med3x outlier chunks their side-list values).
 //
 // Layout of the work.  A block takes one (sequence, KV head, token split);
 // each of its 4 waves walks a contiguous quarter of the split in tiles of 16
@@ -56,7 +57,7 @@ struct AttArgs {
     int64_t bps;                // Med3x batches per slice
     int32_t layer, heads, group, nsplit, split_tokens, max_len, S, bits, words;
     float qscale;               // scale * log2(e)
-};
+};  // r[].hnorm: binary16 half-norms, or packed compact codes (kernel's NPACK)
 
 // Exclusive prefix sum over the wave, in lane order, of counts below 32.
 __device__ __forceinline__ uint32_t wave_excl_small(uint32_t v, uint32_t *total) {
@@ -116,7 +117,8 @@ struct AttShape {
 // Record words of one role's 16-token tile held by one lane: the half-norm
 // codes of its CPL chunks and the index words holding their codes (BITS > 0:
 // the NW consecutive row words from the first code's word; BITS = 0, any code
-// width: two words per chunk pair).
+// width: two words per chunk pair).  Packed norms (NPACK) sit at the same word
+// places as the index codes and are held the same way.
 constexpr int max_code_shift(int cpl, int bits) {
     int m = 0;
     for (int q = 0; q < 4; ++q) m = ((q * cpl * bits) & 31) > m ? ((q * cpl * bits) & 31) : m;
@@ -130,16 +132,16 @@ constexpr bool words_in_row(int cpl, int bits, int nw) {
     return true;
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool NPACK>
 struct TileRegs {
     static constexpr int CPL = D / 16;
     static constexpr int NW = BITS > 0 ? (max_code_shift(CPL, BITS) + CPL * BITS + 31) / 32 : CPL;
     static_assert(BITS == 0 || words_in_row(CPL, BITS, NW), "a lane's words must stay in its row");
-    uint32_t hw[CPL / 2];
+    uint32_t hw[NPACK ? NW : CPL / 2];   // binary16 code pairs, or packed norm words
     uint32_t w[NW];
 };
 
-template <int D, bool TABLE, int BITS>
+template <int D, bool TABLE, int BITS, bool NPACK>
 __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     using Sh = AttShape<D>;
     constexpr int CPT = Sh::CPT, CPL = Sh::CPL, KB = Sh::KB, NU = Sh::NU, ROWB = Sh::ROWB, TILEB = Sh::TILEB;
@@ -246,12 +248,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     // valid row and are masked when decoded) and address a tile base common
     // to the wave plus a per-lane offset, so that the compiler keeps them in
     // flight across the decode of the current tile.
-    auto load_tile = [&](int r, int64_t t0, int nvalid, TileRegs<D, BITS> &tr) {
+    auto load_tile = [&](int r, int64_t t0, int nvalid, TileRegs<D, BITS, NPACK> &tr) {
         const AttRole &R = a.r[r];
         const int64_t tb = row0 + (nvalid > 0 ? t0 : w_lo);
         const uint32_t ri = static_cast<uint32_t>(nvalid > 0 ? (ti < nvalid ? ti : nvalid - 1) : 0);
         const uint16_t *hp = (R.hnorm + tb * CPT) + (ri * static_cast<uint32_t>(CPT) + static_cast<uint32_t>(c0));
-        if constexpr (CPL == 4) {
+        if constexpr (NPACK) {
+            // the norm words at the index words' places (loaded below)
+        } else if constexpr (CPL == 4) {
             const uint2 u = *reinterpret_cast<const uint2 *>(hp);
             tr.hw[0] = u.x;
             tr.hw[1] = u.y;
@@ -266,16 +270,26 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
             }
         }
         const uint32_t *ib = R.idx + tb * a.words;   // the tile's first row
+        const uint32_t *nb = reinterpret_cast<const uint32_t *>(R.hnorm) + tb * a.words;
         const uint32_t ro = ri * static_cast<uint32_t>(a.words);
         if constexpr (BITS > 0) {
 #pragma unroll
-            for (int k = 0; k < TileRegs<D, BITS>::NW; ++k) tr.w[k] = ib[ro + static_cast<uint32_t>(w0 + k)];
+            for (int k = 0; k < TileRegs<D, BITS, NPACK>::NW; ++k) {
+                tr.w[k] = ib[ro + static_cast<uint32_t>(w0 + k)];
+                if constexpr (NPACK) tr.hw[k] = nb[ro + static_cast<uint32_t>(w0 + k)];
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < CPL; j += 2) {
                 const int w = ((c0 + j) * a.bits) >> 5;
-                tr.w[j] = ib[ro + static_cast<uint32_t>(w)];
-                tr.w[j + 1] = ib[ro + static_cast<uint32_t>(w + 1 < last_word ? w + 1 : last_word)];
+                const uint32_t o0 = ro + static_cast<uint32_t>(w);
+                const uint32_t o1 = ro + static_cast<uint32_t>(w + 1 < last_word ? w + 1 : last_word);
+                tr.w[j] = ib[o0];
+                tr.w[j + 1] = ib[o1];
+                if constexpr (NPACK) {
+                    tr.hw[j] = nb[o0];
+                    tr.hw[j + 1] = nb[o1];
+                }
             }
         }
     };
@@ -296,38 +310,52 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
 
     // Decode a loaded tile of role r into dst[token][chunk] (fp16), with the
     // decoder's arithmetic: 2 hnorm (a_p * q_s) in fp32, rounded to binary16.
-    auto decode_tile = [&](int r, const TileRegs<D, BITS> &tr, int nvalid, unsigned char *dst) {
-        const bool valid = ti < nvalid;
-        uint32_t hw[CPL / 2];
-#pragma unroll
-        for (int v = 0; v < CPL / 2; ++v) hw[v] = valid ? tr.hw[v] : 0u;
-        uint32_t code[CPL];
+    // the lane's CPL codes from its record words (index or packed norm)
+    using Words = uint32_t[TileRegs<D, BITS, NPACK>::NW];
+    auto extract = [&](const Words &tw, uint32_t (&out)[CPL]) {
         if constexpr (BITS > 0) {
-            constexpr int NW = TileRegs<D, BITS>::NW;
+            constexpr int NW = TileRegs<D, BITS, NPACK>::NW;
             uint32_t nw[NW];   // the lane's codes from bit 0
 #pragma unroll
-            for (int k = 0; k + 1 < NW; ++k) nw[k] = __builtin_amdgcn_alignbit(tr.w[k + 1], tr.w[k], sh0);
-            nw[NW - 1] = tr.w[NW - 1] >> sh0;
+            for (int k = 0; k + 1 < NW; ++k) nw[k] = __builtin_amdgcn_alignbit(tw[k + 1], tw[k], sh0);
+            nw[NW - 1] = tw[NW - 1] >> sh0;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 constexpr uint32_t m = (1u << BITS) - 1u;
                 const int p = j * BITS, k = p >> 5, sft = p & 31;
-                uint32_t v;
-                if (sft + BITS <= 32) v = (nw[k] >> sft) & m;
-                else v = __builtin_amdgcn_alignbit(nw[k + 1], nw[k], sft) & m;
-                code[j] = v < kmax ? v : kmax;
+                if (sft + BITS <= 32) out[j] = (nw[k] >> sft) & m;
+                else out[j] = __builtin_amdgcn_alignbit(nw[k + 1], nw[k], sft) & m;
             }
         } else {
 #pragma unroll
             for (int j = 0; j < CPL; j += 2) {
                 const int o = (c0 + j) * a.bits;
-                const uint64_t win = ((static_cast<uint64_t>(tr.w[j + 1]) << 32) | tr.w[j]) >> (o & 31);
-                const uint32_t k0 = static_cast<uint32_t>(win) & kmask;
-                const uint32_t k1 = static_cast<uint32_t>(win >> a.bits) & kmask;
-                code[j] = k0 < kmax ? k0 : kmax;
-                code[j + 1] = k1 < kmax ? k1 : kmax;
+                const uint64_t win = ((static_cast<uint64_t>(tw[j + 1]) << 32) | tw[j]) >> (o & 31);
+                out[j] = static_cast<uint32_t>(win) & kmask;
+                out[j + 1] = static_cast<uint32_t>(win >> a.bits) & kmask;
             }
         }
+    };
+
+    auto decode_tile = [&](int r, const TileRegs<D, BITS, NPACK> &tr, int nvalid, unsigned char *dst) {
+        const bool valid = ti < nvalid;
+        uint32_t hw[CPL / 2];
+        if constexpr (NPACK) {
+            uint32_t nc[CPL];
+            extract(tr.hw, nc);
+            const int nbits = BITS > 0 ? BITS : a.bits;
+#pragma unroll
+            for (int v = 0; v < CPL / 2; ++v)
+                hw[v] = valid ? compact_norm_h16(nc[2 * v], nbits) | (compact_norm_h16(nc[2 * v + 1], nbits) << 16)
+                              : 0u;
+        } else {
+#pragma unroll
+            for (int v = 0; v < CPL / 2; ++v) hw[v] = valid ? tr.hw[v] : 0u;
+        }
+        uint32_t code[CPL];
+        extract(tr.w, code);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) code[j] = code[j] < kmax ? code[j] : kmax;
         f32x4 cw[CPL];   // TABLE: 2 (a_p * q_s); else a_p * q_s
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -412,7 +440,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     for (int kb = 0; kb < KB; ++kb) o[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // one 16-token tile: prefetch the next into nxt, decode cur, attend
-    auto step = [&](int64_t t0, TileRegs<D, BITS>(&cur_t)[2], TileRegs<D, BITS>(&nxt_t)[2]) {
+    auto step = [&](int64_t t0, TileRegs<D, BITS, NPACK>(&cur_t)[2], TileRegs<D, BITS, NPACK>(&nxt_t)[2]) {
         const int nvalid = static_cast<int>(w_hi - t0 < kTile ? w_hi - t0 : kTile);
         const int64_t t1 = t0 + kTile;
         const int nv1 = t1 < w_hi ? static_cast<int>(w_hi - t1 < kTile ? w_hi - t1 : kTile) : 0;
@@ -480,7 +508,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         wave_sync();
     };
 
-    TileRegs<D, BITS> ta[2], tb[2];
+    TileRegs<D, BITS, NPACK> ta[2], tb[2];
     if (w_lo < w_hi) {
         const int nv = static_cast<int>(w_hi - w_lo < kTile ? w_hi - w_lo : kTile);
         load_tile(0, w_lo, nv, ta[0]);
@@ -558,6 +586,14 @@ size_t attend_lds(int S, bool table) {
     return loop > merge ? loop : merge;
 }
 
+template <int D, bool NPACK>
+const void *split_kernel_for(bool table, int bits) {
+    if (table && bits == 10) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 10, NPACK>);
+    if (table && bits == 8) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 8, NPACK>);
+    if (table) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0, NPACK>);
+    return reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0, NPACK>);
+}
+
 template <int D>
 hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
     AttArgs a;
@@ -585,26 +621,16 @@ hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(L.batch) * L.heads * L.nsplit));
     // code widths of the common codebooks (S = 8: 8 bits, S = 32: 10) get
     // extraction at fixed bit positions; any other width the general path
-    const void *kern;
-    if (table && L.bits == 10) kern = reinterpret_cast<const void *>(&attend_split_kernel<D, true, 10>);
-    else if (table && L.bits == 8) kern = reinterpret_cast<const void *>(&attend_split_kernel<D, true, 8>);
-    else if (table) kern = reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0>);
-    else kern = reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0>);
+    const void *kern = L.npack ? split_kernel_for<D, true>(table, L.bits) : split_kernel_for<D, false>(table, L.bits);
     // more than the default 64 KB of dynamic LDS must be asked for
     hipError_t e = hipSuccess;
     if (lds > 64 * 1024) {
         e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    if (table && L.bits == 10) {
-        hipLaunchKernelGGL((attend_split_kernel<D, true, 10>), grid, dim3(kAttThreads), lds, st, a);
-    } else if (table && L.bits == 8) {
-        hipLaunchKernelGGL((attend_split_kernel<D, true, 8>), grid, dim3(kAttThreads), lds, st, a);
-    } else if (table) {
-        hipLaunchKernelGGL((attend_split_kernel<D, true, 0>), grid, dim3(kAttThreads), lds, st, a);
-    } else {
-        hipLaunchKernelGGL((attend_split_kernel<D, false, 0>), grid, dim3(kAttThreads), lds, st, a);
-    }
+    void *args[] = {&a};
+    e = hipLaunchKernel(kern, grid, dim3(kAttThreads), args, lds, st);
+    if (e != hipSuccess) return e;
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attend_combine_kernel<D>), dim3(static_cast<unsigned>(static_cast<int64_t>(L.batch) * L.heads * L.group)),

@@ -76,5 +76,27 @@ __device__ __forceinline__ f32x4 codeword_f32(const float *q, int p) {
     return c;
 }
 
+// Compact norm code of a binary16 half-norm record h (b bits, 5 <= b <= 15):
+// the flag bit maps to the all-ones code; otherwise h is rounded to a float
+// with 5 exponent bits and b - 5 mantissa bits, i.e. to the nearest binary16
+// pattern whose low 15 - b bits are zero (positive binary16 patterns are
+// ordered like their values and evenly spaced within a binade, so rounding
+// the pattern rounds the value; on a tie the even code wins), capped at the
+// largest finite value of the narrower format.  The code is the top b bits
+// of that pattern.
+__device__ __forceinline__ uint32_t compact_norm_code(uint32_t h, int bits) {
+    if (h & 0x8000u) return (1u << bits) - 1u;
+    const int sh = 15 - bits;
+    const uint32_t c = sh > 0 ? (h + (1u << (sh - 1)) - 1u + ((h >> sh) & 1u)) >> sh : h;
+    const uint32_t cap = (31u << (bits - 5)) - 1u;
+    return c < cap ? c : cap;
+}
+
+// The binary16 half-norm record a compact code stands for (the flag for the
+// all-ones code).
+__device__ __forceinline__ uint32_t compact_norm_h16(uint32_t c, int bits) {
+    return c == (1u << bits) - 1u ? 0x8000u : c << (15 - bits);
+}
+
 }  // namespace
 }  // namespace hqmq

@@ -1095,11 +1095,51 @@ __global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v) {
 }
 
 // --------------------------------------------------------------------------
+// Packed norm format: the compact codes of a binary16 half-norm plane, packed
+// per token row like the index codes.  Each thread converts 4 chunks (one
+// 8-byte load); a block covers 1024 chunks, i.e. whole token rows, ORs the
+// codes into its rows' words in LDS and stores them.
+// --------------------------------------------------------------------------
+constexpr int kPackThreads = 256;
+constexpr int kPackChunks = 4 * kPackThreads;
+
+__global__ __launch_bounds__(kPackThreads) void pack_norms_kernel(const uint16_t *h16, uint32_t *words, int64_t total,
+                                                                  int32_t log2_cpt, int32_t bits, int32_t W) {
+    __shared__ uint32_t sw[kPackChunks];   // rows * W <= 1024 * 15 / 32 + 256
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kPackChunks;
+    const int rows = kPackChunks >> log2_cpt;
+    const int nw = rows * W;
+    for (int i = threadIdx.x; i < nw; i += kPackThreads) sw[i] = 0u;
+    __syncthreads();
+    const int64_t c = c0 + 4 * threadIdx.x;
+    if (c < total) {   // total and c are multiples of 4
+        const uint2 u = *reinterpret_cast<const uint2 *>(h16 + c);
+        const uint32_t h[4] = {u.x & 0xFFFFu, u.x >> 16, u.y & 0xFFFFu, u.y >> 16};
+        const int cmask = (1 << log2_cpt) - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int lc = 4 * threadIdx.x + j;
+            const uint32_t code = compact_norm_code(h[j], bits);
+            const int bit = (lc & cmask) * bits;
+            uint32_t *wr = &sw[(lc >> log2_cpt) * W + (bit >> 5)];
+            const int sft = bit & 31;
+            atomicOr(wr, code << sft);
+            if (sft + bits > 32) atomicOr(wr + 1, code >> (32 - sft));
+        }
+    }
+    __syncthreads();
+    const int64_t row0 = c0 >> log2_cpt;
+    const int64_t valid = min(static_cast<int64_t>(rows), (total >> log2_cpt) - row0) * W;
+    uint32_t *dst = words + row0 * W;
+    for (int i = threadIdx.x; i < valid; i += kPackThreads) dst[i] = sw[i];
+}
+
+// --------------------------------------------------------------------------
 // Decode kernel: one block per contiguous chunk range of one slice.
 // --------------------------------------------------------------------------
 struct DecArgs {
     const uint32_t *idx;
-    const uint16_t *hnorm;
+    const void *hnorm;   // binary16 half-norms, or (NPACK) packed compact codes
     const uint64_t *offsets;
     const uint32_t *out_pos;
     const uint16_t *out_val;
@@ -1136,9 +1176,10 @@ struct DecPair {
     uint32_t w0, w1;   // the row words holding the 2 codes
     uint32_t sh;       // bit offset of the first code in w0
     uint32_t h;        // 2 binary16 half-norm codes
+    uint32_t n0, n1;   // NPACK: the norm row words at the index words' places
 };
 
-template <bool F32OUT, bool TABLE>
+template <bool F32OUT, bool TABLE, bool NPACK>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     extern __shared__ f32x4 tab[];   // TABLE: the 24 S codewords; else the S q_s
     const int64_t slice = blockIdx.x / a.wg_per_slice;
@@ -1165,7 +1206,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     __syncthreads();
 
     const uint32_t *idx_s = a.idx + slice * a.tokens * a.words;
-    const uint32_t *hn_s = reinterpret_cast<const uint32_t *>(a.hnorm + sbase);
+    // half-norm code pairs (u32 per 2 chunks), or the packed norm rows
+    const uint32_t *hn_s = NPACK ? static_cast<const uint32_t *>(a.hnorm) + slice * a.tokens * a.words
+                                 : static_cast<const uint32_t *>(a.hnorm) + (sbase >> 1);
     const int cmask = a.cpt - 1;
     const uint32_t kmask = (1u << a.bits) - 1u;
     const int last_word = a.words - 1;
@@ -1217,7 +1260,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
         d.w0 = rp[w];
         d.w1 = rp[min(w + 1, last_word)];
         d.sh = static_cast<uint32_t>(o & 31);
-        d.h = hn_s[c >> 1];
+        if constexpr (NPACK) {
+            const uint32_t *np = hn_s + row * a.words;
+            d.n0 = np[w];
+            d.n1 = np[min(w + 1, last_word)];
+            d.h = 0u;
+        } else {
+            d.h = hn_s[c >> 1];
+            d.n0 = d.n1 = 0u;
+        }
         return d;
     };
     constexpr int kWaveStep = 128;   // chunks per wave step
@@ -1227,6 +1278,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
         for (int u = 0; u < kDecUnroll; ++u) {
             const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
             pd[u] = c < w1 ? load(c) : DecPair{};
+        }
+        if constexpr (NPACK) {
+#pragma unroll
+            for (int u = 0; u < kDecUnroll; ++u) {
+                const uint64_t nwin = ((static_cast<uint64_t>(pd[u].n1) << 32) | pd[u].n0) >> pd[u].sh;
+                const uint32_t k0 = static_cast<uint32_t>(nwin) & kmask;
+                const uint32_t k1 = static_cast<uint32_t>(nwin >> a.bits) & kmask;
+                pd[u].h = compact_norm_h16(k0, a.bits) | (compact_norm_h16(k1, a.bits) << 16);
+            }
         }
         // side-list values of this iteration's flagged chunks, in order
         uint2 ov[kDecUnroll][2];
@@ -1443,7 +1503,16 @@ hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t *hnorm,
+hipError_t launch_pack_norms(const Geometry &g, const uint16_t *h16, uint32_t *words, hipStream_t st) {
+    const int64_t total = g.slices * g.n_slice;
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = ceil_div(total, kPackChunks);
+    hipLaunchKernelGGL(pack_norms_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kPackThreads), 0, st, h16, words,
+                       total, static_cast<int32_t>(__builtin_ctz(static_cast<unsigned>(g.cpt))), g.bits, g.words);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const void *hnorm,
                          const uint64_t *offsets, const uint32_t *out_pos, const uint16_t *out_val,
                          uint64_t capacity, const float *codebook, void *y, hipStream_t st) {
     const int64_t total = g.slices * g.n_slice;
@@ -1476,12 +1545,20 @@ hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t 
     const dim3 block(kDecThreads);
     const bool table = g.S <= kTableMaxS;
     const size_t lds = (table ? 24 * static_cast<size_t>(g.S) : static_cast<size_t>(g.S)) * sizeof(f32x4);
-    if (g.f32) {
-        if (table) hipLaunchKernelGGL((decode_kernel<true, true>), grid, block, lds, st, a);
-        else hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, lds, st, a);
+    if (g.npack) {
+        if (g.f32) {
+            if (table) hipLaunchKernelGGL((decode_kernel<true, true, true>), grid, block, lds, st, a);
+            else hipLaunchKernelGGL((decode_kernel<true, false, true>), grid, block, lds, st, a);
+        } else {
+            if (table) hipLaunchKernelGGL((decode_kernel<false, true, true>), grid, block, lds, st, a);
+            else hipLaunchKernelGGL((decode_kernel<false, false, true>), grid, block, lds, st, a);
+        }
+    } else if (g.f32) {
+        if (table) hipLaunchKernelGGL((decode_kernel<true, true, false>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((decode_kernel<true, false, false>), grid, block, lds, st, a);
     } else {
-        if (table) hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, lds, st, a);
-        else hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, lds, st, a);
+        if (table) hipLaunchKernelGGL((decode_kernel<false, true, false>), grid, block, lds, st, a);
+        else hipLaunchKernelGGL((decode_kernel<false, false, false>), grid, block, lds, st, a);
     }
     return hipGetLastError();
 }

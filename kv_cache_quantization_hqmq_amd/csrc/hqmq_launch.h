@@ -22,14 +22,16 @@ struct Geometry {
     int64_t batch_chunks;    // Med3x batch length in chunks (0 = off)
     int64_t batches_per_slice;
     float med_C;
+    int32_t npack;           // 1: norms as packed compact codes (b bits per chunk)
 };
 
-// Med3x scratch (inside the caller's workspace).
+// Encode scratch (inside the caller's workspace).
 struct Med3Work {
     uint32_t *hist;      // [batches][2048] histograms of the half-norm code >> 4
     uint32_t *counts;    // [batches] outliers per batch
     uint32_t *mask;      // [batches][mask_words] outlier bitmasks
     int64_t mask_words;
+    uint16_t *h16;       // packed norm format: the binary16 half-norm plane
 };
 
 // Encode: nearest codeword and norm code per chunk; with med != nullptr the
@@ -59,8 +61,13 @@ hipError_t launch_med3_gather(const Geometry &g, const void *x, const Med3Work &
 hipError_t launch_fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
 
-// Decode: bulk gather-multiply plus outlier re-insertion.
-hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const uint16_t *hnorm,
+// Packed norm format: compact codes of the binary16 half-norms h16 (flag
+// bit -> all-ones code), packed per token row like the index codes.
+hipError_t launch_pack_norms(const Geometry &g, const uint16_t *h16, uint32_t *words, hipStream_t st);
+
+// Decode: bulk gather-multiply plus outlier re-insertion (hnorm: the norm
+// plane in the geometry's format).
+hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const void *hnorm,
                          const uint64_t *offsets, const uint32_t *out_pos, const uint16_t *out_val,
                          uint64_t capacity, const float *codebook, void *y, hipStream_t st);
 
@@ -73,7 +80,7 @@ struct AttRole {
     const uint16_t *out_val;
     uint64_t capacity;
     const float *cb;           // [layers][kv_heads][S][4]
-};
+};  // hnorm: binary16 half-norms, or packed compact codes (AttLaunch::npack)
 
 // Decode-step attention over one layer of an encoded cache.
 struct AttLaunch {
@@ -86,7 +93,7 @@ struct AttLaunch {
     int64_t tokens;             // tokens per slice
     int64_t batch_chunks;       // Med3x batch length in chunks (0 = off)
     int64_t bps;                // Med3x batches per slice (0 = off)
-    int32_t layer, heads, group, batch, nsplit, split_tokens, max_len, head_dim, S, bits, words;
+    int32_t layer, heads, group, batch, nsplit, split_tokens, max_len, head_dim, S, bits, words, npack;
     float scale;
 };
 

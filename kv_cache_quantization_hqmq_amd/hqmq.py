@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libhqmq.so")
 HQMQ_OK, HQMQ_EINVAL, HQMQ_ENOTSUP, HQMQ_ECAPACITY, HQMQ_EHIP = 0, -1, -2, -3, -4
 HQMQ_F16, HQMQ_F32 = 0, 1
 HQMQ_ROLE_K, HQMQ_ROLE_V = 0, 1
+HQMQ_NORM_F16, HQMQ_NORM_PACKED = 0, 1
 
 # every symbol include/hqmq.h declares
 EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
@@ -48,12 +49,12 @@ class Desc(ctypes.Structure):
                 ("tokens", ctypes.c_int64), ("head_dim", ctypes.c_int64),
                 ("S", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("med_batch_tokens", ctypes.c_int64), ("med_C", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("norm_format", ctypes.c_int32)]
 
     @classmethod
     def make(cls, layers, kv_heads, tokens, head_dim, S, dtype=HQMQ_F16,
-             med_batch_tokens=0, med_C=3.0) -> "Desc":
-        return cls(layers, kv_heads, tokens, head_dim, S, dtype, med_batch_tokens, med_C, 0)
+             med_batch_tokens=0, med_C=3.0, norm_format=HQMQ_NORM_F16) -> "Desc":
+        return cls(layers, kv_heads, tokens, head_dim, S, dtype, med_batch_tokens, med_C, norm_format)
 
     @property
     def shape(self):
@@ -245,7 +246,10 @@ def allocate_records(desc: Desc, capacity: int | None = None, device="cuda") -> 
     T, W, cpt = desc.tokens, sz.words_per_token, desc.head_dim // 4
     L, H = desc.layers, desc.kv_heads
     idx = torch.empty((L, H, T, W), dtype=torch.int32, device=device)
-    hnorm = torch.empty((L, H, T, cpt), dtype=torch.int16, device=device)
+    if desc.norm_format == HQMQ_NORM_PACKED:   # u32 words laid out like idx
+        hnorm = torch.empty((L, H, T, W), dtype=torch.int32, device=device)
+    else:
+        hnorm = torch.empty((L, H, T, cpt), dtype=torch.int16, device=device)
     med = desc.med_batch_tokens > 0
     if capacity is None:
         capacity = min(sz.max_outliers, max(1, sz.chunks // 8)) if med else 0

@@ -37,12 +37,20 @@ def f16_values(y64: np.ndarray) -> np.ndarray:
     return O.round_f16(y64).view(np.float16).astype(np.float64)
 
 
-def oracle_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float):
+def oracle_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float, npack: bool = False):
     """Oracle records and binary16 decoded values of tokens [t0, t0+T) of one
-    slice (t0 a multiple of the Med3x batch)."""
+    slice (t0 a multiple of the Med3x batch).  r["hrec"] is the norm record
+    as the GPU stores it: binary16 codes, or (npack) compact codes, whose
+    half-norms the decode then uses."""
     T, D = x.shape
     r = O.encode_range(x, q, t0, B, C)
-    y = O.decode_range(r["codes"], r["hnorm"], T, D, q, r["side_pos"] if B else None,
+    hn = r["hnorm"]
+    r["hrec"] = hn
+    if npack:
+        b = O.code_bits(q.shape[0])
+        r["hrec"] = O.compact_norms(hn, b)
+        hn = O.compact_to_h16(r["hrec"], b)
+    y = O.decode_range(r["codes"], hn, T, D, q, r["side_pos"] if B else None,
                        r["side_val"] if B else None, t0)
     return r, f16_values(y)
 
@@ -53,7 +61,10 @@ def gpu_slice_records(desc: K.Desc, rec, l: int, h: int, t0: int, T: int):
     cpt = D // 4
     b = O.code_bits(int(desc.S))
     codes = P.unpack_words(rec.idx[l, h, t0:t0 + T].cpu().numpy().view(np.uint32), cpt, b).reshape(-1)
-    hn = rec.hnorm[l, h, t0:t0 + T].cpu().numpy().view(np.uint16).reshape(-1)
+    if desc.norm_format == K.HQMQ_NORM_PACKED:
+        hn = P.unpack_words(rec.hnorm[l, h, t0:t0 + T].cpu().numpy().view(np.uint32), cpt, b).reshape(-1)
+    else:
+        hn = rec.hnorm[l, h, t0:t0 + T].cpu().numpy().view(np.uint16).reshape(-1)
     pos = val = None
     B = int(desc.med_batch_tokens)
     if B > 0:
@@ -73,7 +84,7 @@ def record_mismatches(r: dict, g) -> tuple[int, int]:
     codes, hn, pos, val = g
     diff = codes != r["codes"]
     near = diff & (r["gap"] < P.GAP_EXEMPT)
-    bad = int((diff & ~near).sum()) + int((hn != r["hnorm"]).sum())
+    bad = int((diff & ~near).sum()) + int((hn != r["hrec"].reshape(-1)).sum())
     if pos is not None:
         if len(pos) != len(r["side_pos"]):
             bad += abs(len(pos) - len(r["side_pos"])) + 1
@@ -97,13 +108,15 @@ def make_queries(batch: int, hq: int, D: int, seed: int, device="cuda"):
     return torch.randn((batch, hq, D), generator=g, device=device).to(torch.float16)
 
 
-def run_case(w: synth.Workload, seqs, group: int, scale: float, layers=None, max_len=None, seed=0):
+def run_case(w: synth.Workload, seqs, group: int, scale: float, layers=None, max_len=None, seed=0,
+             norm_format: int = K.HQMQ_NORM_F16):
     """Encode w's K and V on the GPU, attend over seqs = [(start, len)], and
     compare every (layer, sequence, query head) with the oracle.  Returns a
     report with the worst error / tolerance ratio, the near-tie codes the two
     encoders chose differently (allowed) and every other record difference
     (must be 0)."""
-    desc = GC.desc_for(w)
+    desc = GC.desc_for(w, norm_format=norm_format)
+    npack = norm_format == K.HQMQ_NORM_PACKED
     L, H, Tt, D = desc.shape
     xs, cbh, cbd, recs = {}, {}, {}, {}
     for role in (0, 1):
@@ -126,7 +139,7 @@ def run_case(w: synth.Workload, seqs, group: int, scale: float, layers=None, max
             dec = {}
             for role in (0, 1):
                 x = xs[role][l, h].float().cpu().numpy()
-                r, dec[role] = oracle_slice(x, cbh[role][l, h], 0, w.med_batch_tokens, w.med_C)
+                r, dec[role] = oracle_slice(x, cbh[role][l, h], 0, w.med_batch_tokens, w.med_C, npack)
                 near, bad = record_mismatches(r, gpu_slice_records(desc, recs[role], l, h, 0, Tt))
                 rep["near_tie_codes"] += near
                 rep["record_mismatch"] += bad

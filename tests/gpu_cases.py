@@ -11,9 +11,10 @@ import synth
 from tests import parity as P
 
 
-def desc_for(w: synth.Workload, tokens: int | None = None) -> K.Desc:
+def desc_for(w: synth.Workload, tokens: int | None = None, norm_format: int = K.HQMQ_NORM_F16) -> K.Desc:
     return K.Desc.make(w.layers, w.heads, w.tokens if tokens is None else tokens, w.head_dim, w.S,
-                       K.HQMQ_F32 if w.dtype == "f32" else K.HQMQ_F16, w.med_batch_tokens, w.med_C)
+                       K.HQMQ_F32 if w.dtype == "f32" else K.HQMQ_F16, w.med_batch_tokens, w.med_C,
+                       norm_format)
 
 
 def codebook(w: synth.Workload, role: int, device="cuda"):
@@ -55,6 +56,6 @@ def compare(desc: K.Desc, x: torch.Tensor, cb_host: np.ndarray, rec, y: torch.Te
             pos = rec.out_pos[e0:e1].cpu().numpy()
             val = rec.out_val[e0:e1].cpu().numpy()
         r = P.compare_slice(xs, cb_host[l, h], t0, Bc, float(desc.med_C), words, hn, pos, val, ys,
-                            int(desc.S), desc.dtype == K.HQMQ_F32)
+                            int(desc.S), desc.dtype == K.HQMQ_F32, desc.norm_format == K.HQMQ_NORM_PACKED)
         rep.merge(r)
     return rep

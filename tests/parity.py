@@ -8,6 +8,8 @@ The bar (from the method's definition and the build's contract):
     1e-6; below that several codes are correct, and the GPU's choice must
     score within 1e-6 of the oracle's best;
   * packed index words: bit-exact on every token row whose codes all match;
+  * packed norm format: the compact norm codes, and so their words, bit-exact
+    (they follow from the half-norm codes, which are exact);
   * decoded values: |y_gpu - y_oracle| <= 1e-3 * r^ per element (r^ the
     decoded chunk norm), outlier chunks exact.
 """
@@ -51,10 +53,11 @@ class Report(dict):
 def compare_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float,
                   g_words: np.ndarray, g_hnorm: np.ndarray, g_pos: np.ndarray | None,
                   g_val: np.ndarray | None, g_y: np.ndarray | None, S: int,
-                  out_f32: bool) -> Report:
+                  out_f32: bool, npack: bool = False) -> Report:
     """Compare the GPU records of tokens [t0, t0+T) of one slice with the
     oracle.  x: [T, D] input values; g_*: the GPU's records for the same
-    tokens (g_pos/g_val: the side-list entries of those batches)."""
+    tokens (g_pos/g_val: the side-list entries of those batches; g_hnorm:
+    [T, cpt] binary16 codes, or with npack the [T, W] packed norm words)."""
     T, D = x.shape
     cpt = D // 4
     b = O.code_bits(S)
@@ -65,10 +68,23 @@ def compare_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float,
     hn_o = ref["hnorm"].reshape(T, cpt)
     gap = ref["gap"].reshape(T, cpt)
 
-    # half-norm codes and flags: bit-exact
-    hn_g = np.asarray(g_hnorm).reshape(T, cpt).view(np.uint16)
-    bad = np.argwhere(hn_g != hn_o)
-    assert bad.size == 0, f"hnorm differs at {bad[:5].tolist()}: gpu {hn_g[tuple(bad[0])]:#x} oracle {hn_o[tuple(bad[0])]:#x}"
+    if npack:
+        # compact norm codes (and their packed words): bit-exact; the decode
+        # below then uses the half-norm records those codes stand for
+        nc_o = O.compact_norms(hn_o, b)
+        wg = np.asarray(g_hnorm).view(np.uint32).reshape(T, W)
+        nc_g = unpack_words(wg, cpt, b)
+        bad = np.argwhere(nc_g != nc_o)
+        assert bad.size == 0, \
+            f"norm code differs at {bad[:5].tolist()}: gpu {nc_g[tuple(bad[0])]:#x} oracle {nc_o[tuple(bad[0])]:#x}"
+        np.testing.assert_array_equal(wg, np.stack([O.pack_row(nc_o[t], b, W) for t in range(T)]))
+        hn_o = O.compact_to_h16(nc_o, b)
+    else:
+        # half-norm codes and flags: bit-exact
+        hn_g = np.asarray(g_hnorm).reshape(T, cpt).view(np.uint16)
+        bad = np.argwhere(hn_g != hn_o)
+        assert bad.size == 0, \
+            f"hnorm differs at {bad[:5].tolist()}: gpu {hn_g[tuple(bad[0])]:#x} oracle {hn_o[tuple(bad[0])]:#x}"
 
     # side list: bit-exact
     if B > 0:

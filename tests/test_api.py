@@ -63,7 +63,8 @@ def test_strerror():
 
 @pytest.mark.parametrize("field,value", [
     ("head_dim", 96), ("head_dim", 0), ("head_dim", 512), ("S", 0), ("S", 1025),
-    ("dtype", 2), ("layers", -1), ("tokens", -5), ("med_batch_tokens", -1)])
+    ("dtype", 2), ("layers", -1), ("tokens", -5), ("med_batch_tokens", -1), ("norm_format", 2),
+    ("norm_format", -1)])
 def test_descriptor_validation(field, value):
     d = K.Desc.make(2, 2, 64, 128, 8, K.HQMQ_F16, 16, 3.0)
     setattr(d, field, value)
@@ -135,6 +136,26 @@ def test_sizes_follow_the_layout(L, H, T, D, S, dt, Bt):
         assert s.workspace_bytes >= s.batches * (2048 * 4 + 4) + s.chunks // 8
     else:
         assert s.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("L,H,T,D,S,Bt", [
+    (80, 8, 131072, 128, 32, 4096), (32, 8, 32768, 128, 8, 0), (2, 3, 1001, 64, 13, 256), (1, 1, 5, 16, 1, 0),
+    (1, 2, 7, 256, 1024, 3)])
+def test_sizes_packed_norms(L, H, T, D, S, Bt):
+    """Packed norms: the norm plane has the index plane's size (b bits per
+    chunk in the same row words), and the encode workspace adds a binary16
+    half-norm plane (2 bytes per chunk) to what Med3x needs."""
+    f16 = K.hqmq_sizes(K.Desc.make(L, H, T, D, S, K.HQMQ_F16, Bt, 3.0))
+    pk = K.hqmq_sizes(K.Desc.make(L, H, T, D, S, K.HQMQ_F16, Bt, 3.0, K.HQMQ_NORM_PACKED))
+    assert pk.hnorm_bytes == pk.idx_bytes == f16.idx_bytes
+    assert pk.code_bits == f16.code_bits and pk.chunks == f16.chunks
+    assert pk.workspace_bytes >= f16.workspace_bytes + 2 * pk.chunks
+    assert pk.workspace_bytes <= f16.workspace_bytes + 2 * pk.chunks + 256
+    assert pk.workspace_bytes % 256 == 0
+    # with S = 8 and 32 the two planes cost 4 and 5 bits per element
+    if S in (8, 32):
+        bits = (pk.idx_bytes + pk.hnorm_bytes) * 8 / (pk.chunks * 4)
+        assert bits == {8: 4.0, 32: 5.0}[S]
 
 
 @pytest.mark.parametrize("seed,L,H,role,S", [(0, 1, 1, 0, 8), (0, 3, 5, 1, 32), (12345, 2, 2, 0, 1024),

@@ -53,6 +53,24 @@ def test_attend_d256_s100_codewords_built_per_chunk():
     _check(A.run_case(w, [(0, 1500), (512, 513)], 2, 1.0 / 16.0), "D=256 S=100")
 
 
+@pytest.mark.parametrize("group", [4, 8])
+def test_attend_packed_norms_d128_s32(group):
+    """Packed norm records (b = 10: 5 bits per element with the index codes)
+    read by the attention kernel, Med3x flags in both roles."""
+    _check(A.run_case(BASE, SEQS, group, 1.0 / math.sqrt(128), norm_format=K.HQMQ_NORM_PACKED),
+           f"packed G={group}")
+
+
+def test_attend_packed_norms_d64_s8_and_general_width():
+    w = synth.WORKLOADS[2].scaled(layers=1, heads=2, tokens=3000, data_seed=2304)
+    _check(A.run_case(w, [(0, 3000), (17, 1500), (2990, 10)], 4, 0.125, norm_format=K.HQMQ_NORM_PACKED),
+           "packed D=64 S=8")
+    w = synth.WORKLOADS[3].scaled(layers=1, heads=1, tokens=1500, head_dim=256, S=100,
+                                  med_batch_tokens=512, data_seed=2305)
+    _check(A.run_case(w, [(0, 1500), (512, 513)], 2, 1.0 / 16.0, norm_format=K.HQMQ_NORM_PACKED),
+           "packed D=256 S=100")
+
+
 def test_attend_clips_ranges():
     """Lengths beyond max_len, ranges past the slice end, a negative start and
     a negative length: the kernel attends over the clipped range (zeros when

@@ -78,6 +78,70 @@ def test_small_shapes_every_chunk(L, H, T, D, S, dt, B):
         assert rep["outliers"] > 0
 
 
+# packed norm format: code widths b = 5 (exponent-only compact codes) to
+# b = 15 (the binary16 pattern itself), with and without Med3x flags
+PACKED_CASES = [
+    (2, 3, 1000, 128, 8, "f16", 0),
+    (2, 3, 1501, 128, 32, "f16", 512),
+    (1, 2, 333, 256, 1, "f32", 100),
+    (2, 1, 129, 16, 40, "f16", 64),
+    (1, 1, 97, 128, 1024, "f16", 32),
+    (1, 2, 777, 64, 13, "f16", 0),
+]
+
+
+@pytest.mark.parametrize("L,H,T,D,S,dt,B", PACKED_CASES)
+def test_packed_norms_every_chunk(L, H, T, D, S, dt, B):
+    """Every compact norm code and packed word against the oracle, decoded
+    values from the half-norms the codes stand for; index codes and the side
+    list are those of the binary16-format encode of the same input."""
+    dtype = torch.float16 if dt == "f16" else torch.float32
+    x = _x((L, H, T, D), dtype, seed=L * 1000 + T + S + 7)
+    if B > 0:
+        x[:, :, :, 5] *= 40
+        x[:, :, ::97, :] *= 9
+    cb_host, cb = _cb(L, H, S)
+    f = K.HQMQ_F32 if dt == "f32" else K.HQMQ_F16
+    desc = K.Desc.make(L, H, T, D, S, f, B, 3.0, K.HQMQ_NORM_PACKED)
+    rep, rec, _ = _check(desc, x, cb_host, cb)
+    ref, _ = G.run(K.Desc.make(L, H, T, D, S, f, B, 3.0), x, cb)
+    assert torch.equal(rec.idx, ref.idx)
+    assert rec.n_outliers == ref.n_outliers
+    if B > 0:
+        n = int(rec.n_outliers)
+        assert n > 0
+        assert torch.equal(rec.batch_offsets, ref.batch_offsets)
+        assert torch.equal(rec.out_pos[:n], ref.out_pos[:n]) and torch.equal(rec.out_val[:n], ref.out_val[:n])
+
+
+@pytest.mark.parametrize("S", [1, 8, 32])
+def test_packed_norm_extremes(S):
+    """Chunk norms from zero through binary16 subnormals to the top of the
+    range (rounded up past the narrower format's largest value: capped), and
+    values on the exact rounding ties of the compact code."""
+    T, D = 256, 128
+    cpt = D // 4
+    rng = np.random.default_rng(S)
+    # one nonzero component per chunk: the half-norm is |x0| / 2 exactly
+    mag = np.ldexp(rng.uniform(1, 2, T * cpt), rng.integers(-24, 17, T * cpt))
+    mag[:64] = 0.0
+    mag[64:72] = [65504, 65504, 65472, 65440, 65376, 2.0 ** -24, 2.0 ** -23, 3 * 2.0 ** -24]
+    b = O.code_bits(S)
+    sh = 15 - b
+    if sh > 0:
+        # binary16 patterns halfway between two compact codes (x0 = 2 h16)
+        pat = (rng.integers(1, 30 << 10, 200) >> sh << sh) + (1 << (sh - 1))
+        mag[100:300] = 2.0 * pat.astype(np.uint16).view(np.float16).astype(np.float64)
+    x = np.zeros((T * cpt, 4), np.float32)
+    x[:, 0] = np.minimum(mag, 65504.0) * rng.choice([-1.0, 1.0], T * cpt)
+    x[72:76] = 65504.0    # half-norm 65504: above the largest compact value for b < 15
+    xt = torch.from_numpy(x.reshape(1, 1, T, D)).cuda()
+    cb_host, cb = _cb(1, 1, S)
+    for B in (0, 64):
+        desc = K.Desc.make(1, 1, T, D, S, K.HQMQ_F32, B, 3.0, K.HQMQ_NORM_PACKED)
+        _check(desc, xt, cb_host, cb)
+
+
 def test_med3_many_chunks_at_the_threshold():
     """Two batches whose chunks have norm 1 except thousands at exactly C = 3
     times that norm or one binary16 step above or below it (and a few large
