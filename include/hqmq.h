@@ -258,6 +258,102 @@ int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, 
                 const int32_t *seq_len, float *out, void *workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Paged cache with streaming append.  A serving loop keeps each role's
+ * records in a pool of fixed-size pages, appends every step's new tokens
+ * into free slots and attends over each sequence's pages (the decode-step
+ * use of gist.science/nl "Memory en Latentie").  An append call encodes its
+ * tokens exactly as hqmq_encode encodes a tensor of that many tokens: the
+ * Med3x batch is med_batch_tokens of the call's tokens of one (layer, head),
+ * so a decode step's tokens form one batch per (layer, head) ("the current
+ * batch", gist.science/nl Methodologie 3).
+ *
+ * Pool layout (P = page_tokens, W = words per token, cpt = head_dim / 4):
+ *   idx        [layers][kv_heads][num_pages][P][W] u32, token rows as in idx
+ *   hnorm      [layers][kv_heads][num_pages][P][cpt] u16 (HQMQ_NORM_F16), or
+ *              [layers][kv_heads][num_pages][P][W] u32 (HQMQ_NORM_PACKED)
+ *   side_count [layers][kv_heads][num_pages] u32: entries in each page's list
+ *   side_pos   [layers][kv_heads][num_pages][page_capacity] u32: o * cpt + c
+ *              for chunk c of the token at offset o of the page
+ *   side_val   [layers][kv_heads][num_pages][page_capacity][4] binary16
+ * Slot page * P + o is offset o of page `page`.  A page's side list holds
+ * its outlier chunks in position order.  Each (layer, head) slice of the
+ * pool is a record tensor of num_pages * P tokens in the layout above.
+ * ------------------------------------------------------------------------ */
+typedef struct hqmq_paged_desc {
+    int64_t num_pages;        /* pages in the pool, >= 0 */
+    int32_t page_tokens;      /* P: a multiple of 16, P * head_dim / 4 < 2^31 */
+    int32_t page_capacity;    /* side-list entries per (layer, head, page), >= 0 */
+} hqmq_paged_desc;
+
+/* One role's pool: device pointers owned by the caller (layout above;
+ * idx, side_count, side_pos 4-byte aligned, hnorm and side_val 16-byte
+ * aligned). */
+typedef struct hqmq_pages {
+    uint32_t *idx;
+    void *hnorm;
+    uint32_t *side_count;
+    uint32_t *side_pos;
+    uint16_t *side_val;
+} hqmq_pages;
+
+typedef struct hqmq_paged_sizes_t {
+    uint64_t idx_bytes;
+    uint64_t hnorm_bytes;
+    uint64_t side_count_bytes;
+    uint64_t side_pos_bytes;
+    uint64_t side_val_bytes;
+    uint64_t append_workspace_bytes;   /* hqmq_append of d->tokens tokens */
+} hqmq_paged_sizes_t;
+
+/* Pool sizes for codec descriptor d and pool p, and the workspace of an
+ * append of d->tokens tokens (the call's records with a worst-case side
+ * list, plus the encode scratch).  Host only.
+ * Errors: HQMQ_EINVAL (NULL pointer, invalid descriptor or pool),
+ * HQMQ_ENOTSUP (pool beyond 32-bit positions or grid limits). */
+int hqmq_paged_sizes(const hqmq_desc *d, const hqmq_paged_desc *p, hqmq_paged_sizes_t *out);
+
+/* Empty the n pages listed in pages (device int32 page ids): zero their
+ * side-list counts in every (layer, head), so they can take new tokens.
+ * Ids outside [0, num_pages) are skipped.  A fresh pool needs its whole
+ * side_count array zeroed (this call with every page, or a device fill).
+ * Asynchronous on stream.  Errors: HQMQ_EINVAL, HQMQ_EHIP. */
+int hqmq_paged_clear(const hqmq_desc *d, const hqmq_paged_desc *p, const hqmq_pages *pool,
+                     const int32_t *pages, int64_t n, hipStream_t stream);
+
+/* Append d->tokens tokens x [layers][kv_heads][tokens][head_dim] (d->dtype,
+ * 16-byte aligned) to the pool: token t of every (layer, head) goes to slot
+ * slots[t] (device int64).  The records are those hqmq_encode writes for x
+ * with descriptor d (codes, norms in d->norm_format, Med3x flags); the
+ * outlier chunks of each page go to the end of that page's side list.
+ * Preconditions, not checked: slots are distinct; the tokens one call
+ * writes to a page are consecutive in the call, in increasing offset order,
+ * and come after every token already in the page (the way a sequence
+ * grows).  A slot outside [0, num_pages * P) is skipped with its token.
+ * Entries past page_capacity are dropped: their chunks keep the bulk record
+ * (flag cleared).  status (device [2] u64, may be NULL) receives the
+ * outlier chunks of the tokens written and how many of them were dropped.  workspace: at least
+ * hqmq_paged_sizes().append_workspace_bytes for d, 256-byte aligned.
+ * Asynchronous on stream; nothing is enqueued when validation fails.
+ * Errors: HQMQ_EINVAL, HQMQ_ENOTSUP (as hqmq_paged_sizes), HQMQ_EHIP. */
+int hqmq_append(const hqmq_desc *d, const hqmq_paged_desc *p, const void *x, const int64_t *slots,
+                const float *codebook, const hqmq_pages *pool, uint64_t *status, void *workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* hqmq_attend over paged pools: sequence b's token t is at slot
+ * page_table[b * page_table_stride + t / P] * P + t % P of k and v (device
+ * int32 page table, ids in [0, num_pages)), and it has seq_len[b] tokens
+ * (a negative length counts as 0; clipped to max_len and to
+ * page_table_stride * P).  Scores, softmax, GQA and output as hqmq_attend;
+ * d gives the codec parameters (d->tokens is not used).  The workspace and
+ * split plan are hqmq_attn_sizes(d, a).  Errors: as hqmq_attend, and
+ * HQMQ_EINVAL for an invalid pool or page_table_stride < 1. */
+int hqmq_attend_paged(const hqmq_desc *d, const hqmq_paged_desc *p, const hqmq_attn_desc *a,
+                      const hqmq_pages *k, const float *codebook_k, const hqmq_pages *v,
+                      const float *codebook_v, const void *q, const int32_t *page_table,
+                      int32_t page_table_stride, const int32_t *seq_len, float *out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,14 +5,18 @@ in ``include/hqmq.h``; ``kv_cache_quantization_hqmq_amd.hqmq`` is its ctypes
 binding (same function names).  Build with
 ``python -m kv_cache_quantization_hqmq_amd.build``.
 """
-from .hqmq import (AttnDesc, AttnSizes, CapacityError, Desc, HQMQError, Records, Sizes,
-                   allocate_records, attend, decode, encode, hqmq_attend, hqmq_attn_sizes, hqmq_decode,
+from .hqmq import (AttnDesc, AttnSizes, CapacityError, Desc, HQMQError, PagedDesc, PagedSizes, Pages, Pool,
+                   Records, Sizes, allocate_pool, allocate_records, append, append_workspace, attend,
+                   attend_paged, decode, encode, hqmq_append, hqmq_attend, hqmq_attend_paged,
+                   hqmq_attn_sizes, hqmq_decode, hqmq_paged_clear, hqmq_paged_sizes,
                    hqmq_encode, hqmq_encode_result, hqmq_encode_timed, hqmq_make_codebook, hqmq_sizes,
                    hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_NORM_F16, HQMQ_NORM_PACKED,
                    HQMQ_ROLE_K, HQMQ_ROLE_V)
 
-__all__ = ["AttnDesc", "AttnSizes", "CapacityError", "Desc", "HQMQError", "Records", "Sizes",
-           "allocate_records", "attend", "decode", "encode", "hqmq_attend", "hqmq_attn_sizes",
+__all__ = ["AttnDesc", "AttnSizes", "CapacityError", "Desc", "HQMQError", "PagedDesc", "PagedSizes",
+           "Pages", "Pool", "Records", "Sizes", "allocate_pool", "allocate_records", "append",
+           "append_workspace", "attend", "attend_paged", "decode", "encode", "hqmq_append", "hqmq_attend",
+           "hqmq_attend_paged", "hqmq_attn_sizes", "hqmq_paged_clear", "hqmq_paged_sizes",
            "hqmq_decode", "hqmq_encode", "hqmq_encode_result", "hqmq_encode_timed",
            "hqmq_make_codebook", "hqmq_sizes", "hqmq_strerror", "workspace", "HQMQ_F16",
            "HQMQ_F32", "HQMQ_NORM_F16", "HQMQ_NORM_PACKED", "HQMQ_ROLE_K", "HQMQ_ROLE_V"]

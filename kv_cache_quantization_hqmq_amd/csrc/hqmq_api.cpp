@@ -171,6 +171,77 @@ static int attn_plan(const hqmq_desc *d, const hqmq::Geometry &g, const hqmq_att
     return HQMQ_OK;
 }
 
+// Paged pool geometry: validate p against the codec geometry g.
+static int paged_geometry(const hqmq::Geometry &g, const hqmq_paged_desc *p, int32_t *log2_page) {
+    if (!p) return HQMQ_EINVAL;
+    const int64_t P = p->page_tokens;
+    if (p->num_pages < 0 || p->page_capacity < 0 || P < 16 || (P & (P - 1)) != 0) return HQMQ_EINVAL;
+    if (p->num_pages >= (int64_t{1} << 31) || P * g.cpt >= (int64_t{1} << 31)) return HQMQ_ENOTSUP;
+    // pool rows and side entries stay well inside 2^62, grids inside 2^31 blocks
+    if (g.slices > 0 && p->num_pages > 0 &&
+        (p->num_pages * P > (int64_t{1} << 40) / g.slices ||
+         p->num_pages * static_cast<int64_t>(p->page_capacity) > (int64_t{1} << 40) / g.slices))
+        return HQMQ_ENOTSUP;
+    *log2_page = __builtin_ctzll(static_cast<unsigned long long>(P));
+    return HQMQ_OK;
+}
+
+// Append workspace: the encode scratch of the call's tensor, then its
+// records (binary16 norms) with a worst-case side list.
+struct AppendWork {
+    void *enc_ws;
+    uint64_t enc_ws_bytes;
+    uint32_t *idx;
+    uint16_t *h16;
+    uint64_t *offsets;
+    uint32_t *out_pos;
+    uint16_t *out_val;
+    uint64_t *status;
+    uint64_t capacity;
+};
+
+static uint64_t append_layout(const hqmq_desc *dc, void *base, AppendWork *w) {
+    hqmq_sizes_t sz;
+    if (hqmq_sizes(dc, &sz) != HQMQ_OK) return 0;
+    const uint64_t cap = static_cast<uint64_t>(sz.max_outliers);
+    uint64_t off = 0;
+    const uint64_t o_ws = off;
+    off = align_up(off + sz.workspace_bytes, kWsAlign);
+    const uint64_t o_idx = off;
+    off = align_up(off + sz.idx_bytes, kWsAlign);
+    const uint64_t o_h = off;
+    off = align_up(off + sz.hnorm_bytes, kWsAlign);
+    const uint64_t o_offs = off;
+    off = align_up(off + sz.offsets_bytes, kWsAlign);
+    const uint64_t o_pos = off;
+    off = align_up(off + cap * 4, kWsAlign);
+    const uint64_t o_val = off;
+    off = align_up(off + cap * 8, kWsAlign);
+    const uint64_t o_st = off;
+    off = align_up(off + 16, kWsAlign);
+    if (w) {
+        char *b = static_cast<char *>(base);
+        w->enc_ws = sz.workspace_bytes ? b + o_ws : nullptr;
+        w->enc_ws_bytes = sz.workspace_bytes;
+        w->idx = reinterpret_cast<uint32_t *>(b + o_idx);
+        w->h16 = reinterpret_cast<uint16_t *>(b + o_h);
+        w->offsets = reinterpret_cast<uint64_t *>(b + o_offs);
+        w->out_pos = reinterpret_cast<uint32_t *>(b + o_pos);
+        w->out_val = reinterpret_cast<uint16_t *>(b + o_val);
+        w->status = reinterpret_cast<uint64_t *>(b + o_st);
+        w->capacity = cap;
+    }
+    return off;
+}
+
+static bool pool_ok(const hqmq_pages *k, bool data) {
+    if (!k) return false;
+    if (!data) return true;
+    return k->idx && k->hnorm && k->side_count && aligned(k->idx, 4) && aligned(k->hnorm, 16) &&
+           aligned(k->side_count, 4) && (!k->side_pos || aligned(k->side_pos, 4)) &&
+           (!k->side_val || aligned(k->side_val, 16));
+}
+
 extern "C" {
 
 const char *hqmq_strerror(int code) {
@@ -399,7 +470,7 @@ int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, 
         role[r] = hqmq::AttRole{e->idx, static_cast<const uint16_t *>(e->hnorm), g.batch_chunks > 0 ? e->batch_offsets : nullptr, e->out_pos,
                                 e->out_val, g.batch_chunks > 0 ? e->out_capacity : 0, cb[r]};
     }
-    hqmq::AttLaunch L;
+    hqmq::AttLaunch L{};
     L.k = role[0];
     L.v = role[1];
     L.q = static_cast<const uint16_t *>(q);
@@ -423,6 +494,167 @@ int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, 
     L.words = g.words;
     L.npack = g.npack;
     L.scale = a->scale;
+    return hqmq::launch_attend(L, stream) == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
+}
+
+int hqmq_paged_sizes(const hqmq_desc *d, const hqmq_paged_desc *p, hqmq_paged_sizes_t *out) {
+    if (!out) return HQMQ_EINVAL;
+    hqmq::Geometry g;
+    int rc = make_geometry(d, &g);
+    if (rc != HQMQ_OK) return rc;
+    int32_t lp = 0;
+    rc = paged_geometry(g, p, &lp);
+    if (rc != HQMQ_OK) return rc;
+    std::memset(out, 0, sizeof(*out));
+    const uint64_t pages = static_cast<uint64_t>(g.slices) * static_cast<uint64_t>(p->num_pages);
+    const uint64_t rows = pages * static_cast<uint64_t>(p->page_tokens);
+    out->idx_bytes = rows * g.words * 4;
+    out->hnorm_bytes = g.npack ? out->idx_bytes : rows * g.cpt * 2;
+    out->side_count_bytes = pages * 4;
+    out->side_pos_bytes = pages * p->page_capacity * 4;
+    out->side_val_bytes = pages * p->page_capacity * 8;
+    hqmq_desc dc = *d;
+    dc.norm_format = HQMQ_NORM_F16;
+    out->append_workspace_bytes = append_layout(&dc, nullptr, nullptr);
+    return HQMQ_OK;
+}
+
+int hqmq_paged_clear(const hqmq_desc *d, const hqmq_paged_desc *p, const hqmq_pages *pool, const int32_t *pages,
+                     int64_t n, hipStream_t stream) {
+    hqmq::Geometry g;
+    int rc = make_geometry(d, &g);
+    if (rc != HQMQ_OK) return rc;
+    int32_t lp = 0;
+    rc = paged_geometry(g, p, &lp);
+    if (rc != HQMQ_OK) return rc;
+    if (!pool || n < 0) return HQMQ_EINVAL;
+    if (n == 0 || g.slices == 0) return HQMQ_OK;
+    if (!pages || !pool->side_count || !aligned(pages, 4) || !aligned(pool->side_count, 4)) return HQMQ_EINVAL;
+    if (n > (int64_t{1} << 40) / g.slices) return HQMQ_ENOTSUP;
+    hqmq::PagedPool pp{};
+    pp.side_count = pool->side_count;
+    pp.num_pages = p->num_pages;
+    pp.log2_page = lp;
+    return hqmq::launch_paged_clear(g.slices, pages, n, pp, stream) == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
+}
+
+int hqmq_append(const hqmq_desc *d, const hqmq_paged_desc *p, const void *x, const int64_t *slots,
+                const float *codebook, const hqmq_pages *pool, uint64_t *status, void *workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+    hqmq::Geometry g;
+    int rc = make_geometry(d, &g);
+    if (rc != HQMQ_OK) return rc;
+    int32_t lp = 0;
+    rc = paged_geometry(g, p, &lp);
+    if (rc != HQMQ_OK) return rc;
+    const bool med = g.batch_chunks > 0;
+    const int64_t chunks = g.slices * g.n_slice;
+    if (status && !aligned(status, 8)) return HQMQ_EINVAL;
+    if (!pool_ok(pool, chunks > 0)) return HQMQ_EINVAL;
+    if (chunks > 0 && med && p->page_capacity > 0 && (!pool->side_pos || !pool->side_val)) return HQMQ_EINVAL;
+    if (chunks > 0 && (!slots || !aligned(slots, 8))) return HQMQ_EINVAL;
+    hqmq_desc dc = *d;
+    dc.norm_format = HQMQ_NORM_F16;
+    const uint64_t need = append_layout(&dc, nullptr, nullptr);
+    if (chunks > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))) return HQMQ_EINVAL;
+    hipError_t e = hipSuccess;
+    if (status) {
+        e = hqmq::launch_fill_u64(status, 2, 0, stream);
+        if (e != hipSuccess) return HQMQ_EHIP;
+    }
+    if (chunks == 0) return HQMQ_OK;
+    AppendWork w;
+    append_layout(&dc, workspace, &w);
+    hqmq_enc enc{};
+    enc.idx = w.idx;
+    enc.hnorm = w.h16;
+    enc.batch_offsets = med ? w.offsets : nullptr;
+    enc.out_pos = med ? w.out_pos : nullptr;
+    enc.out_val = med ? w.out_val : nullptr;
+    enc.out_capacity = med ? w.capacity : 0;
+    enc.status = w.status;
+    // the call's records (the worst-case side list fits: no overflow)
+    rc = hqmq_encode(&dc, x, codebook, &enc, w.enc_ws, w.enc_ws_bytes, stream);
+    if (rc != HQMQ_OK) return rc;
+    hqmq::PagedPool pp;
+    pp.idx = pool->idx;
+    pp.hnorm = pool->hnorm;
+    pp.side_count = pool->side_count;
+    pp.side_pos = pool->side_pos;
+    pp.side_val = pool->side_val;
+    pp.num_pages = p->num_pages;
+    pp.log2_page = lp;
+    pp.cap = static_cast<uint32_t>(p->page_capacity);
+    if (med) {
+        e = hqmq::launch_paged_scatter(g, w.offsets, w.out_pos, w.out_val, slots, w.h16, pp, status, stream);
+        if (e != hipSuccess) return HQMQ_EHIP;
+    }
+    e = hqmq::launch_paged_rows(g, w.idx, w.h16, slots, pp, stream);
+    return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
+}
+
+int hqmq_attend_paged(const hqmq_desc *d, const hqmq_paged_desc *p, const hqmq_attn_desc *a, const hqmq_pages *k,
+                      const float *codebook_k, const hqmq_pages *v, const float *codebook_v, const void *q,
+                      const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_len, float *out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    hqmq_attn_sizes_t sz;
+    int rc = hqmq_attn_sizes(d, a, &sz);
+    if (rc != HQMQ_OK) return rc;
+    hqmq::Geometry g;
+    make_geometry(d, &g);
+    int32_t lp = 0;
+    rc = paged_geometry(g, p, &lp);
+    if (rc != HQMQ_OK) return rc;
+    if (page_table_stride < 1) return HQMQ_EINVAL;
+    if (a->batch > 0 && d->kv_heads > 0 && static_cast<int64_t>(a->batch) * page_table_stride > (int64_t{1} << 40))
+        return HQMQ_ENOTSUP;
+    const bool data = p->num_pages > 0;
+    if (!pool_ok(k, data) || !pool_ok(v, data)) return HQMQ_EINVAL;
+    if (a->batch == 0 || d->kv_heads == 0) return HQMQ_OK;
+    if (!q || !page_table || !seq_len || !out || !workspace || workspace_bytes < sz.workspace_bytes)
+        return HQMQ_EINVAL;
+    if (!aligned(q, 8) || !aligned(page_table, 4) || !aligned(seq_len, 4) || !aligned(out, 4) ||
+        !aligned(workspace, 16))
+        return HQMQ_EINVAL;
+    if (!data) return HQMQ_EINVAL;   // sequences need pages
+    const hqmq_pages *pools[2] = {k, v};
+    const float *cb[2] = {codebook_k, codebook_v};
+    hqmq::AttRole role[2];
+    for (int r = 0; r < 2; ++r) {
+        if (!cb[r] || !aligned(cb[r], 16)) return HQMQ_EINVAL;
+        if (p->page_capacity > 0 && (!pools[r]->side_pos || !pools[r]->side_val)) return HQMQ_EINVAL;
+        role[r] = hqmq::AttRole{pools[r]->idx, static_cast<const uint16_t *>(pools[r]->hnorm), nullptr,
+                                pools[r]->side_pos, pools[r]->side_val, 0, cb[r], pools[r]->side_count};
+    }
+    hqmq::AttLaunch L{};
+    L.k = role[0];
+    L.v = role[1];
+    L.q = static_cast<const uint16_t *>(q);
+    L.seq_start = nullptr;
+    L.seq_len = seq_len;
+    L.part = static_cast<float *>(workspace);
+    L.out = out;
+    L.tokens = 0;
+    L.batch_chunks = 0;
+    L.bps = 0;
+    L.layer = a->layer;
+    L.heads = static_cast<int32_t>(d->kv_heads);
+    L.group = a->group;
+    L.batch = a->batch;
+    L.nsplit = sz.splits;
+    L.split_tokens = sz.split_tokens;
+    L.max_len = a->max_len;
+    L.head_dim = static_cast<int32_t>(d->head_dim);
+    L.S = g.S;
+    L.bits = g.bits;
+    L.words = g.words;
+    L.npack = g.npack;
+    L.scale = a->scale;
+    L.page_table = page_table;
+    L.num_pages = p->num_pages;
+    L.pt_stride = page_table_stride;
+    L.log2_page = lp;
+    L.page_cap = static_cast<uint32_t>(p->page_capacity);
     return hqmq::launch_attend(L, stream) == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
 }
 

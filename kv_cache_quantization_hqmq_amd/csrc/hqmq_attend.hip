@@ -57,6 +57,11 @@ struct AttArgs {
     int64_t bps;                // Med3x batches per slice
     int32_t layer, heads, group, nsplit, split_tokens, max_len, S, bits, words;
     float qscale;               // scale * log2(e)
+    // paged pools (PAGED kernels): [batch][pt_stride] page ids, P = 2^log2_page
+    const int32_t *page_table;
+    int64_t num_pages;
+    int32_t pt_stride, log2_page;
+    uint32_t page_cap;          // side-list entries per (layer, head, page)
 };  // r[].hnorm: binary16 half-norms, or packed compact codes (kernel's NPACK)
 
 // Exclusive prefix sum over the wave, in lane order, of counts below 32.
@@ -74,9 +79,27 @@ __device__ __forceinline__ uint32_t wave_excl_small(uint32_t v, uint32_t *total)
     return ex;
 }
 
+// First entry in [lo, hi) of a position-sorted side list whose position is
+// at least p0 (hi when none): a 64-way search per round.
+__device__ uint64_t search_first(const uint32_t *out_pos, uint64_t lo, uint64_t hi, int64_t p0, int lane) {
+    while (hi > lo) {
+        const uint64_t len = hi - lo;
+        const uint64_t step = (len + 63) / 64;
+        const uint64_t i = lo + static_cast<uint64_t>(lane) * step;
+        const bool below = i < hi && static_cast<int64_t>(out_pos[i]) < p0;
+        const int cnt = __popcll(__ballot(below));
+        if (cnt == 0) break;
+        const uint64_t nlo = lo + static_cast<uint64_t>(cnt - 1) * step + 1;
+        const uint64_t nhi = lo + static_cast<uint64_t>(cnt) * step;
+        hi = nhi < hi ? nhi : hi;
+        lo = nlo;
+    }
+    return lo;
+}
+
 // First side-list entry of slice sl at or after position p0, among the
-// entries of the Med3x batches that overlap [p0, p1) (64-way search per
-// round); *e_end receives the end of those entries.
+// entries of the Med3x batches that overlap [p0, p1); *e_end receives the
+// end of those entries.
 __device__ uint64_t first_entry(const AttRole &r, int64_t sl, int64_t bps, int64_t batch_chunks, int64_t p0,
                                 int64_t p1, uint64_t *e_end, int lane) {
     *e_end = 0;
@@ -88,19 +111,15 @@ __device__ uint64_t first_entry(const AttRole &r, int64_t sl, int64_t bps, int64
     hi = hi < r.capacity ? hi : r.capacity;
     lo = lo < hi ? lo : hi;
     *e_end = hi;
-    while (hi > lo) {
-        const uint64_t len = hi - lo;
-        const uint64_t step = (len + 63) / 64;
-        const uint64_t i = lo + static_cast<uint64_t>(lane) * step;
-        const bool below = i < hi && static_cast<int64_t>(r.out_pos[i]) < p0;
-        const int cnt = __popcll(__ballot(below));
-        if (cnt == 0) break;
-        const uint64_t nlo = lo + static_cast<uint64_t>(cnt - 1) * step + 1;
-        const uint64_t nhi = lo + static_cast<uint64_t>(cnt) * step;
-        hi = nhi < hi ? nhi : hi;
-        lo = nlo;
-    }
-    return lo;
+    return search_first(r.out_pos, lo, hi, p0, lane);
+}
+
+// Paged pool: the side list of page slot ps = slice * num_pages + page is
+// entries [ps * cap, ps * cap + min(count, cap)).
+__device__ __forceinline__ void page_list(const AttRole &r, int64_t ps, uint32_t cap, uint64_t *lo, uint64_t *hi) {
+    const uint32_t n = r.side_count[ps];
+    *lo = static_cast<uint64_t>(ps) * cap;
+    *hi = *lo + (n < cap ? n : cap);
 }
 
 template <int D>
@@ -141,7 +160,7 @@ struct TileRegs {
     uint32_t w[NW];
 };
 
-template <int D, bool TABLE, int BITS, bool NPACK>
+template <int D, bool TABLE, int BITS, bool NPACK, bool PAGED>
 __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     using Sh = AttShape<D>;
     constexpr int CPT = Sh::CPT, CPL = Sh::CPL, KB = Sh::KB, NU = Sh::NU, ROWB = Sh::ROWB, TILEB = Sh::TILEB;
@@ -160,12 +179,18 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     const int64_t Hq = static_cast<int64_t>(a.heads) * G;
     const int64_t sl = static_cast<int64_t>(a.layer) * a.heads + h;
 
-    // the sequence's tokens, clamped to the slice
-    const int64_t start = a.seq_start[b];
+    // the sequence's tokens, clamped to the slice (paged: to its page table)
+    int64_t start = 0;
     int64_t len = a.seq_len[b];
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-    if (start < 0 || start > a.tokens) len = 0;
-    else len = len < a.tokens - start ? len : a.tokens - start;
+    if constexpr (PAGED) {
+        const int64_t most = static_cast<int64_t>(a.pt_stride) << a.log2_page;
+        len = len < most ? len : most;
+    } else {
+        start = a.seq_start[b];
+        if (start < 0 || start > a.tokens) len = 0;
+        else len = len < a.tokens - start ? len : a.tokens - start;
+    }
     const int64_t t_lo = static_cast<int64_t>(split) * a.split_tokens;
     const int64_t t_hi = t_lo + a.split_tokens < len ? t_lo + a.split_tokens : len;
     float *part = a.part + ((static_cast<int64_t>(b) * Hq + static_cast<int64_t>(h) * G) * nsplit + split) * (D + 2);
@@ -219,9 +244,30 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         }
     }
 
+    // Paged pool: token t of the sequence lies on page page_of(t) (ids are
+    // clamped into the pool), at row page_slot * P + t % P of the pool.
+    const int32_t *ptab = PAGED ? a.page_table + static_cast<int64_t>(b) * a.pt_stride : nullptr;
+    const int64_t page_mask = (int64_t{1} << a.log2_page) - 1;
+    auto page_slot = [&](int64_t t) -> int64_t {
+        int64_t pg = ptab[t >> a.log2_page];
+        pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+        return sl * a.num_pages + pg;
+    };
+
     // side-list cursors of K and V for this wave's tokens
-    uint64_t cur[2], end[2];
-    {
+    uint64_t cur[2] = {0, 0}, end[2] = {0, 0};
+    if constexpr (PAGED) {
+        if (w_lo < w_hi) {
+            const int64_t ps = page_slot(w_lo);
+            const int64_t p0 = (w_lo & page_mask) * CPT;
+            for (int r = 0; r < 2; ++r) {
+                uint64_t lo, hi;
+                page_list(a.r[r], ps, a.page_cap, &lo, &hi);
+                cur[r] = search_first(a.r[r].out_pos, lo, hi, p0, lane);
+                end[r] = hi;
+            }
+        }
+    } else {
         const int64_t p0 = (start + w_lo) * CPT, p1 = (start + w_hi) * CPT;
         cur[0] = first_entry(a.r[0], sl, a.bps, a.batch_chunks, p0, p1, &end[0], lane);
         cur[1] = first_entry(a.r[1], sl, a.bps, a.batch_chunks, p0, p1, &end[1], lane);
@@ -242,15 +288,20 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     const int cbits = BITS > 0 ? BITS : a.bits;
     const uint32_t sh0 = static_cast<uint32_t>(c0 * cbits) & 31u;
     const int w0 = (c0 * cbits) >> 5;
-    const int64_t row0 = sl * a.tokens + start;   // the sequence's first token row
+    const int64_t row0 = sl * a.tokens + start;   // the sequence's first token row (contiguous)
+    // row of the sequence's token t (the first of a tile: a tile never
+    // straddles pages)
+    auto tile_row = [&](int64_t t) -> int64_t {
+        if constexpr (PAGED) return (page_slot(t) << a.log2_page) + (t & page_mask);
+        else return row0 + t;
+    };
 
     // Loads are unconditional (lanes past a tile's end read the tile's last
     // valid row and are masked when decoded) and address a tile base common
     // to the wave plus a per-lane offset, so that the compiler keeps them in
     // flight across the decode of the current tile.
-    auto load_tile = [&](int r, int64_t t0, int nvalid, TileRegs<D, BITS, NPACK> &tr) {
+    auto load_tile = [&](int r, int64_t tb, int nvalid, TileRegs<D, BITS, NPACK> &tr) {
         const AttRole &R = a.r[r];
-        const int64_t tb = row0 + (nvalid > 0 ? t0 : w_lo);
         const uint32_t ri = static_cast<uint32_t>(nvalid > 0 ? (ti < nvalid ? ti : nvalid - 1) : 0);
         const uint16_t *hp = (R.hnorm + tb * CPT) + (ri * static_cast<uint32_t>(CPT) + static_cast<uint32_t>(c0));
         if constexpr (NPACK) {
@@ -337,7 +388,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         }
     };
 
-    auto decode_tile = [&](int r, const TileRegs<D, BITS, NPACK> &tr, int nvalid, unsigned char *dst) {
+    // (after the tile: the cursor moves to the next page's list first when
+    // the next tile starts a page, paged pools only)
+    auto decode_tile = [&](int r, const TileRegs<D, BITS, NPACK> &tr, int nvalid, unsigned char *dst, bool newpage,
+                           uint64_t nlo, uint64_t nhi) {
         const bool valid = ti < nvalid;
         uint32_t hw[CPL / 2];
         if constexpr (NPACK) {
@@ -430,6 +484,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
             }
             cur[r] += tot;
         }
+        if (PAGED && newpage) {
+            cur[r] = nlo;
+            end[r] = nhi;
+        }
         load_window(r);
     };
 
@@ -444,9 +502,20 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         const int nvalid = static_cast<int>(w_hi - t0 < kTile ? w_hi - t0 : kTile);
         const int64_t t1 = t0 + kTile;
         const int nv1 = t1 < w_hi ? static_cast<int>(w_hi - t1 < kTile ? w_hi - t1 : kTile) : 0;
-        load_tile(0, t1, nv1, nxt_t[0]);
-        load_tile(1, t1, nv1, nxt_t[1]);
-        decode_tile(0, cur_t[0], nvalid, tt);
+        const int64_t tb1 = tile_row(nv1 > 0 ? t1 : w_lo);
+        load_tile(0, tb1, nv1, nxt_t[0]);
+        load_tile(1, tb1, nv1, nxt_t[1]);
+        // paged: the side lists of the page the next tile starts
+        const bool newpage = PAGED && nv1 > 0 && (t1 & page_mask) == 0;
+        uint64_t nlo[2] = {0, 0}, nhi[2] = {0, 0};
+        if constexpr (PAGED) {
+            if (newpage) {
+                const int64_t ps = tb1 >> a.log2_page;
+                page_list(a.r[0], ps, a.page_cap, &nlo[0], &nhi[0]);
+                page_list(a.r[1], ps, a.page_cap, &nlo[1], &nhi[1]);
+            }
+        }
+        decode_tile(0, cur_t[0], nvalid, tt, newpage, nlo[0], nhi[0]);
         wave_sync();
 
         // S[token 4 g + i][head n]: A[m = token n][k = 4 g + j] = K[token n][16 kb + 4 g + j]
@@ -473,7 +542,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
             m_run = m_new;
         }
         wave_sync();   // the K tile has been read: V goes into the same place
-        decode_tile(1, cur_t[1], nvalid, tt);
+        decode_tile(1, cur_t[1], nvalid, tt, newpage, nlo[1], nhi[1]);
         wave_sync();
         f16x4 ph;
         float psum = 0.0f;
@@ -511,8 +580,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     TileRegs<D, BITS, NPACK> ta[2], tb[2];
     if (w_lo < w_hi) {
         const int nv = static_cast<int>(w_hi - w_lo < kTile ? w_hi - w_lo : kTile);
-        load_tile(0, w_lo, nv, ta[0]);
-        load_tile(1, w_lo, nv, ta[1]);
+        const int64_t tb0 = tile_row(w_lo);
+        load_tile(0, tb0, nv, ta[0]);
+        load_tile(1, tb0, nv, ta[1]);
     }
     for (int64_t t0 = w_lo; t0 < w_hi; t0 += 2 * kTile) {
         step(t0, ta, tb);
@@ -586,12 +656,12 @@ size_t attend_lds(int S, bool table) {
     return loop > merge ? loop : merge;
 }
 
-template <int D, bool NPACK>
+template <int D, bool NPACK, bool PAGED>
 const void *split_kernel_for(bool table, int bits) {
-    if (table && bits == 10) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 10, NPACK>);
-    if (table && bits == 8) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 8, NPACK>);
-    if (table) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0, NPACK>);
-    return reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0, NPACK>);
+    if (table && bits == 10) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 10, NPACK, PAGED>);
+    if (table && bits == 8) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 8, NPACK, PAGED>);
+    if (table) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0, NPACK, PAGED>);
+    return reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0, NPACK, PAGED>);
 }
 
 template <int D>
@@ -621,7 +691,16 @@ hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(L.batch) * L.heads * L.nsplit));
     // code widths of the common codebooks (S = 8: 8 bits, S = 32: 10) get
     // extraction at fixed bit positions; any other width the general path
-    const void *kern = L.npack ? split_kernel_for<D, true>(table, L.bits) : split_kernel_for<D, false>(table, L.bits);
+    a.page_table = L.page_table;
+    a.num_pages = L.num_pages;
+    a.pt_stride = L.pt_stride;
+    a.log2_page = L.log2_page;
+    a.page_cap = L.page_cap;
+    const bool paged = L.page_table != nullptr;
+    const void *kern = paged ? (L.npack ? split_kernel_for<D, true, true>(table, L.bits)
+                                        : split_kernel_for<D, false, true>(table, L.bits))
+                             : (L.npack ? split_kernel_for<D, true, false>(table, L.bits)
+                                        : split_kernel_for<D, false, false>(table, L.bits));
     // more than the default 64 KB of dynamic LDS must be asked for
     hipError_t e = hipSuccess;
     if (lds > 64 * 1024) {

@@ -1355,6 +1355,151 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     }
 }
 
+// --------------------------------------------------------------------------
+// Paged pool append.  The call's tokens are first encoded like any tensor
+// (records in workspace, binary16 norms with Med3x flags); these kernels
+// then move them into the pool.
+// --------------------------------------------------------------------------
+struct ScatterArgs {
+    const uint64_t *offsets;   // the call's batch offsets, slice-major
+    const uint32_t *out_pos;   // the call's side list (positions in the call's slice)
+    const uint16_t *out_val;
+    const int64_t *slots;      // [tokens] pool slot of each call token
+    uint16_t *h16;             // the call's norms: flags of dropped entries are cleared
+    uint32_t *side_count;
+    uint32_t *side_pos;
+    uint16_t *side_val;
+    uint64_t *status;          // [2] outliers, dropped (may be null)
+    int64_t slices, n_slice, num_pages, bps;
+    int32_t log2_cpt, log2_page;
+    uint32_t cap;
+};
+
+// One wave per slice walks the call's entries of that slice in list order
+// (position order), 64 at a time.  The entries of one page form one run
+// (the call writes a page's tokens consecutively and in order); a run's k-th
+// entry goes to index count(page) + k of the page's list, and the run's end
+// stores the new count.
+__global__ __launch_bounds__(256) void paged_scatter_kernel(ScatterArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (s >= a.slices) return;   // whole waves
+    const uint64_t e0 = a.offsets[s * a.bps], e1 = a.offsets[(s + 1) * a.bps];
+    const int64_t nslot = a.num_pages << a.log2_page;
+    const uint32_t cmask = (1u << a.log2_cpt) - 1u;
+    const int64_t pmask = (int64_t{1} << a.log2_page) - 1;
+    uint32_t *count_s = a.side_count + s * a.num_pages;
+    int cur_page = -1;    // page of the previous entry (-1: none or skipped)
+    uint32_t cur_idx = 0;  // list index the previous run would use next
+    uint32_t found = 0, dropped = 0;
+    for (uint64_t k = e0; k < e1; k += 64) {
+        const uint64_t e = k + static_cast<uint64_t>(lane);
+        const bool valid = e < e1;
+        const uint32_t pos = valid ? a.out_pos[e] : 0u;
+        const int64_t slot = valid ? a.slots[pos >> a.log2_cpt] : -1;
+        const bool ok = slot >= 0 && slot < nslot;
+        const int page = ok ? static_cast<int>(slot >> a.log2_page) : -1;
+        int prev = __shfl_up(page, 1);
+        if (lane == 0) prev = cur_page;
+        const bool start = ok && page != prev;
+        const uint64_t sm = __ballot(start);
+        // a run that ended with the previous chunk stores its count now
+        if (lane == 0 && cur_page >= 0 && page != cur_page)
+            count_s[cur_page] = cur_idx < a.cap ? cur_idx : a.cap;
+        const uint64_t upto = lane == 63 ? sm : (sm & ((uint64_t{2} << lane) - 1));
+        const int j = upto ? 63 - __clzll(static_cast<long long>(upto)) : -1;
+        uint32_t base = 0;
+        if (start) {
+            const uint32_t n = count_s[page];
+            base = n < a.cap ? n : a.cap;
+        }
+        const uint32_t bj = __shfl(base, j < 0 ? 0 : j);
+        const uint32_t idx = j >= 0 ? bj + static_cast<uint32_t>(lane - j) : cur_idx + static_cast<uint32_t>(lane);
+        if (ok) {
+            ++found;
+            if (idx < a.cap) {
+                const uint64_t d = static_cast<uint64_t>(s * a.num_pages + page) * a.cap + idx;
+                a.side_pos[d] = (static_cast<uint32_t>(slot & pmask) << a.log2_cpt) + (pos & cmask);
+                reinterpret_cast<uint2 *>(a.side_val)[d] = reinterpret_cast<const uint2 *>(a.out_val)[e];
+            } else {
+                ++dropped;   // the chunk keeps its bulk record
+                a.h16[s * a.n_slice + pos] = static_cast<uint16_t>(a.h16[s * a.n_slice + pos] & 0x7FFFu);
+            }
+        }
+        // a run that ends inside this chunk (or with the last entry) stores its count
+        const int next_page = __shfl_down(page, 1);
+        const bool ends = e + 1 == e1 || (lane < 63 && next_page != page);
+        if (ok && ends) count_s[page] = idx + 1 < a.cap ? idx + 1 : a.cap;
+        const int last = static_cast<int>(e1 - k > 64 ? 63 : e1 - k - 1);
+        cur_page = __shfl(page, last);
+        cur_idx = __shfl(idx, last) + 1u;
+    }
+    if (a.status) {
+        for (int o = 32; o > 0; o >>= 1) {
+            found += __shfl_xor(found, o);
+            dropped += __shfl_xor(dropped, o);
+        }
+        if (lane == 0) {
+            atomicAdd(reinterpret_cast<unsigned long long *>(a.status), static_cast<unsigned long long>(found));
+            atomicAdd(reinterpret_cast<unsigned long long *>(a.status) + 1, static_cast<unsigned long long>(dropped));
+        }
+    }
+}
+
+struct RowsArgs {
+    const uint32_t *idx;       // the call's index rows [slices][tokens][W]
+    const uint16_t *h16;       // the call's norms [slices][tokens][cpt]
+    const int64_t *slots;
+    uint32_t *pool_idx;
+    void *pool_norm;
+    int64_t slices, tokens, num_pages;
+    int32_t log2_page, cpt, bits, words, npack;
+};
+
+// One wave per (slice, call token): its index words and norms to the pool
+// row of its slot (norms packed into b-bit compact codes when npack).
+__global__ __launch_bounds__(256) void paged_rows_kernel(RowsArgs a) {
+    __shared__ uint32_t sw[4][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t rows = a.slices * a.tokens;
+    const int64_t nslot = a.num_pages << a.log2_page;
+    const int W = a.words;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave; r < rows; r += static_cast<int64_t>(gridDim.x) * 4) {
+        const int64_t s = r / a.tokens;
+        const int64_t slot = a.slots[r - s * a.tokens];
+        if (slot < 0 || slot >= nslot) continue;   // uniform in the wave
+        const int64_t dst = s * nslot + slot;
+        if (lane < W) a.pool_idx[dst * W + lane] = a.idx[r * W + lane];
+        const uint32_t h = lane < a.cpt ? a.h16[r * a.cpt + lane] : 0u;
+        if (!a.npack) {
+            if (lane < a.cpt) static_cast<uint16_t *>(a.pool_norm)[dst * a.cpt + lane] = static_cast<uint16_t>(h);
+        } else {
+            if (lane < W) sw[wave][lane] = 0u;
+            wave_sync();
+            if (lane < a.cpt) {
+                const uint32_t code = compact_norm_code(h, a.bits);
+                const int bit = lane * a.bits;
+                const int sft = bit & 31;
+                atomicOr(&sw[wave][bit >> 5], code << sft);
+                if (sft + a.bits > 32) atomicOr(&sw[wave][(bit >> 5) + 1], code >> (32 - sft));
+            }
+            wave_sync();
+            if (lane < W) static_cast<uint32_t *>(a.pool_norm)[dst * W + lane] = sw[wave][lane];
+            wave_sync();
+        }
+    }
+}
+
+__global__ void paged_clear_kernel(uint32_t *side_count, int64_t slices, int64_t num_pages, const int32_t *pages,
+                                   int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= slices * n) return;
+    const int64_t s = i / n;
+    const int32_t pg = pages[i - s * n];
+    if (pg >= 0 && pg < num_pages) side_count[s * num_pages + pg] = 0u;
+}
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Batches small enough for the single-pass select (its bitmask is in LDS).
@@ -1509,6 +1654,63 @@ hipError_t launch_pack_norms(const Geometry &g, const uint16_t *h16, uint32_t *w
     const int64_t blocks = ceil_div(total, kPackChunks);
     hipLaunchKernelGGL(pack_norms_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kPackThreads), 0, st, h16, words,
                        total, static_cast<int32_t>(__builtin_ctz(static_cast<unsigned>(g.cpt))), g.bits, g.words);
+    return hipGetLastError();
+}
+
+hipError_t launch_paged_scatter(const Geometry &g, const uint64_t *offsets, const uint32_t *out_pos,
+                                const uint16_t *out_val, const int64_t *slots, uint16_t *h16,
+                                const PagedPool &pool, uint64_t *status, hipStream_t st) {
+    if (g.slices == 0 || g.batches_per_slice == 0) return hipSuccess;
+    ScatterArgs a;
+    a.offsets = offsets;
+    a.out_pos = out_pos;
+    a.out_val = out_val;
+    a.slots = slots;
+    a.h16 = h16;
+    a.side_count = pool.side_count;
+    a.side_pos = pool.side_pos;
+    a.side_val = pool.side_val;
+    a.status = status;
+    a.slices = g.slices;
+    a.n_slice = g.n_slice;
+    a.num_pages = pool.num_pages;
+    a.bps = g.batches_per_slice;
+    a.log2_cpt = __builtin_ctz(static_cast<unsigned>(g.cpt));
+    a.log2_page = pool.log2_page;
+    a.cap = pool.cap;
+    hipLaunchKernelGGL(paged_scatter_kernel, dim3(static_cast<unsigned>(ceil_div(g.slices, 4))), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_paged_rows(const Geometry &g, const uint32_t *idx, const uint16_t *h16, const int64_t *slots,
+                             const PagedPool &pool, hipStream_t st) {
+    const int64_t rows = g.slices * g.tokens;
+    if (rows == 0) return hipSuccess;
+    RowsArgs a;
+    a.idx = idx;
+    a.h16 = h16;
+    a.slots = slots;
+    a.pool_idx = pool.idx;
+    a.pool_norm = pool.hnorm;
+    a.slices = g.slices;
+    a.tokens = g.tokens;
+    a.num_pages = pool.num_pages;
+    a.log2_page = pool.log2_page;
+    a.cpt = g.cpt;
+    a.bits = g.bits;
+    a.words = g.words;
+    a.npack = g.npack;
+    const int64_t blocks = ceil_div(rows, 4);
+    hipLaunchKernelGGL(paged_rows_kernel, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)), dim3(256), 0,
+                       st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_paged_clear(int64_t slices, const int32_t *pages, int64_t n, const PagedPool &pool,
+                              hipStream_t st) {
+    if (slices == 0 || n == 0) return hipSuccess;
+    hipLaunchKernelGGL(paged_clear_kernel, dim3(static_cast<unsigned>(ceil_div(slices * n, 256))), dim3(256), 0, st,
+                       pool.side_count, slices, pool.num_pages, pages, n);
     return hipGetLastError();
 }
 

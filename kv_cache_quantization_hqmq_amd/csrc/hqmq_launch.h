@@ -80,6 +80,7 @@ struct AttRole {
     const uint16_t *out_val;
     uint64_t capacity;
     const float *cb;           // [layers][kv_heads][S][4]
+    const uint32_t *side_count;   // paged pools: entries per (slice, page)
 };  // hnorm: binary16 half-norms, or packed compact codes (AttLaunch::npack)
 
 // Decode-step attention over one layer of an encoded cache.
@@ -95,10 +96,42 @@ struct AttLaunch {
     int64_t bps;                // Med3x batches per slice (0 = off)
     int32_t layer, heads, group, batch, nsplit, split_tokens, max_len, head_dim, S, bits, words, npack;
     float scale;
+    // paged pools (page_table != nullptr): rows at (slice * num_pages + page) * P + offset,
+    // side lists of page_cap entries per (slice, page); seq_start is not used
+    const int32_t *page_table;  // [batch][pt_stride]
+    int64_t num_pages;
+    int32_t pt_stride, log2_page;
+    uint32_t page_cap;
 };
 
 // Dynamic LDS of the attention kernel for this shape (0: unsupported head_dim).
 size_t attend_lds_bytes(int head_dim, int S);
 hipError_t launch_attend(const AttLaunch &L, hipStream_t st);
+
+// Paged pool of one role (device pointers), as the append kernels write it.
+struct PagedPool {
+    uint32_t *idx;          // [slices][num_pages * P][W]
+    void *hnorm;            // [slices][num_pages * P][cpt] u16, or [..][W] u32 (npack)
+    uint32_t *side_count;   // [slices][num_pages]
+    uint32_t *side_pos;     // [slices][num_pages][cap]
+    uint16_t *side_val;     // [slices][num_pages][cap][4]
+    int64_t num_pages;
+    int32_t log2_page;
+    uint32_t cap;
+};
+
+// Append: the call's records (the encode of its tokens with geometry g,
+// binary16 norms with flags in h16) moved into the pool at slots[t].  The
+// side entries go to the end of their pages' lists (entries past the
+// capacity are dropped and their flags cleared in h16); then the token rows
+// are written (norms packed when g.npack).
+hipError_t launch_paged_scatter(const Geometry &g, const uint64_t *offsets, const uint32_t *out_pos,
+                                const uint16_t *out_val, const int64_t *slots, uint16_t *h16,
+                                const PagedPool &pool, uint64_t *status, hipStream_t st);
+hipError_t launch_paged_rows(const Geometry &g, const uint32_t *idx, const uint16_t *h16, const int64_t *slots,
+                             const PagedPool &pool, hipStream_t st);
+// Zero the side-list counts of the n pages listed (every slice).
+hipError_t launch_paged_clear(int64_t slices, const int32_t *pages, int64_t n, const PagedPool &pool,
+                              hipStream_t st);
 
 }  // namespace hqmq

@@ -28,7 +28,7 @@ HQMQ_NORM_F16, HQMQ_NORM_PACKED = 0, 1
 # every symbol include/hqmq.h declares
 EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
            "hqmq_encode_timed", "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes",
-           "hqmq_attend")
+           "hqmq_attend", "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged")
 
 
 class HQMQError(RuntimeError):
@@ -98,6 +98,25 @@ class AttnSizes(ctypes.Structure):
                 ("split_tokens", ctypes.c_int32)]
 
 
+class PagedDesc(ctypes.Structure):
+    """hqmq_paged_desc."""
+    _fields_ = [("num_pages", ctypes.c_int64), ("page_tokens", ctypes.c_int32),
+                ("page_capacity", ctypes.c_int32)]
+
+
+class Pages(ctypes.Structure):
+    """hqmq_pages."""
+    _fields_ = [("idx", ctypes.c_void_p), ("hnorm", ctypes.c_void_p), ("side_count", ctypes.c_void_p),
+                ("side_pos", ctypes.c_void_p), ("side_val", ctypes.c_void_p)]
+
+
+class PagedSizes(ctypes.Structure):
+    """hqmq_paged_sizes_t."""
+    _fields_ = [("idx_bytes", ctypes.c_uint64), ("hnorm_bytes", ctypes.c_uint64),
+                ("side_count_bytes", ctypes.c_uint64), ("side_pos_bytes", ctypes.c_uint64),
+                ("side_val_bytes", ctypes.c_uint64), ("append_workspace_bytes", ctypes.c_uint64)]
+
+
 _lib = None
 
 
@@ -131,8 +150,21 @@ def lib():
                                   ctypes.c_void_p, ctypes.POINTER(Enc), ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.hqmq_paged_sizes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PagedDesc),
+                                       ctypes.POINTER(PagedSizes)]
+        L.hqmq_paged_clear.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PagedDesc), ctypes.POINTER(Pages),
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.hqmq_append.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PagedDesc), ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Pages), ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.hqmq_attend_paged.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PagedDesc),
+                                        ctypes.POINTER(AttnDesc), ctypes.POINTER(Pages), ctypes.c_void_p,
+                                        ctypes.POINTER(Pages), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         for f in ("hqmq_sizes", "hqmq_make_codebook", "hqmq_encode", "hqmq_encode_timed",
-                  "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes", "hqmq_attend"):
+                  "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes", "hqmq_attend",
+                  "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -224,6 +256,37 @@ def hqmq_attend(desc: Desc, adesc: AttnDesc, rec_k: "Records", codebook_k, rec_v
     _check(rc, "hqmq_attend")
 
 
+def hqmq_paged_sizes(desc: Desc, pdesc: PagedDesc) -> PagedSizes:
+    out = PagedSizes()
+    _check(lib().hqmq_paged_sizes(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(out)),
+           "hqmq_paged_sizes")
+    return out
+
+
+def hqmq_paged_clear(desc: Desc, pdesc: PagedDesc, pool: "Pool", pages, stream=None) -> None:
+    rc = lib().hqmq_paged_clear(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(pool.c), _ptr(pages),
+                                int(pages.numel()), _stream(stream))
+    _check(rc, "hqmq_paged_clear")
+
+
+def hqmq_append(desc: Desc, pdesc: PagedDesc, x, slots, codebook, pool: "Pool", status=None,
+                workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().hqmq_append(ctypes.byref(desc), ctypes.byref(pdesc), _ptr(x), _ptr(slots), _ptr(codebook),
+                           ctypes.byref(pool.c), _ptr(status), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "hqmq_append")
+
+
+def hqmq_attend_paged(desc: Desc, pdesc: PagedDesc, adesc: AttnDesc, pool_k: "Pool", codebook_k,
+                      pool_v: "Pool", codebook_v, q, page_table, seq_len, out, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().hqmq_attend_paged(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(adesc),
+                                 ctypes.byref(pool_k.c), _ptr(codebook_k), ctypes.byref(pool_v.c),
+                                 _ptr(codebook_v), _ptr(q), _ptr(page_table), int(page_table.shape[1]),
+                                 _ptr(seq_len), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "hqmq_attend_paged")
+
+
 # ------------------------------------------------------------------ buffers
 @dataclass
 class Records:
@@ -313,4 +376,74 @@ def attend(desc: Desc, layer: int, rec_k: Records, codebook_k, rec_v: Records, c
     if out is None:
         out = torch.empty((batch, hq, D), dtype=torch.float32, device=q.device)
     hqmq_attend(desc, a, rec_k, codebook_k, rec_v, codebook_v, q, seq_start, seq_len, out, ws, stream)
+    return out
+
+
+# ------------------------------------------------------------------ paged pool
+@dataclass
+class Pool:
+    """Torch buffers of one role's paged pool plus the C struct pointing at them."""
+    idx: object
+    hnorm: object
+    side_count: object
+    side_pos: object
+    side_val: object
+    c: Pages
+
+
+def allocate_pool(desc: Desc, pdesc: PagedDesc, device="cuda") -> Pool:
+    """A pool for ``desc``'s codec and ``pdesc``'s pages, every page empty."""
+    import torch
+    sz = hqmq_sizes(desc)
+    L, H, D = desc.layers, desc.kv_heads, desc.head_dim
+    NP, P, cap = pdesc.num_pages, pdesc.page_tokens, pdesc.page_capacity
+    W = sz.words_per_token
+    idx = torch.empty((L, H, NP, P, W), dtype=torch.int32, device=device)
+    if desc.norm_format == HQMQ_NORM_PACKED:
+        hnorm = torch.empty((L, H, NP, P, W), dtype=torch.int32, device=device)
+    else:
+        hnorm = torch.empty((L, H, NP, P, D // 4), dtype=torch.int16, device=device)
+    count = torch.zeros((L, H, NP), dtype=torch.int32, device=device)
+    pos = torch.empty((L, H, NP, max(cap, 1)), dtype=torch.int32, device=device)
+    val = torch.empty((L, H, NP, max(cap, 1), 4), dtype=torch.int16, device=device)
+    c = Pages(_ptr(idx), _ptr(hnorm), _ptr(count), _ptr(pos), _ptr(val))
+    return Pool(idx, hnorm, count, pos, val, c)
+
+
+def append_workspace(desc: Desc, pdesc: PagedDesc, device="cuda"):
+    """Workspace of an append of ``desc.tokens`` tokens."""
+    import torch
+    n = hqmq_paged_sizes(desc, pdesc).append_workspace_bytes
+    return torch.empty((max(int(n), 1),), dtype=torch.uint8, device=device)
+
+
+def append(desc: Desc, pdesc: PagedDesc, pool: Pool, x, slots, codebook, ws=None, status=None,
+           stream=None) -> None:
+    """Append x [layers, kv_heads, T, head_dim] to ``pool`` at ``slots`` (int64
+    device tensor of T slots); ``desc.tokens`` must be T."""
+    if ws is None:
+        ws = append_workspace(desc, pdesc, x.device)
+    hqmq_append(desc, pdesc, x, slots, codebook, pool, status, ws, stream)
+
+
+def attend_paged(desc: Desc, pdesc: PagedDesc, layer: int, pool_k: Pool, codebook_k, pool_v: Pool, codebook_v,
+                 q, page_table, seq_len, max_len: int, scale: float | None = None, out=None, ws=None,
+                 stream=None):
+    """Decode-step attention over paged pools: page_table [batch, max_pages]
+    int32 and seq_len [batch] int32 device tensors; returns out [batch,
+    kv_heads * group, head_dim] fp32."""
+    import math
+    import torch
+    batch, hq, D = q.shape
+    group = hq // desc.kv_heads
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    a = AttnDesc.make(batch, group, layer, max_len, scale)
+    if ws is None:
+        n = hqmq_attn_sizes(desc, a).workspace_bytes
+        ws = torch.empty((max(int(n), 16),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((batch, hq, D), dtype=torch.float32, device=q.device)
+    hqmq_attend_paged(desc, pdesc, a, pool_k, codebook_k, pool_v, codebook_v, q, page_table, seq_len, out, ws,
+                      stream)
     return out

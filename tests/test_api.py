@@ -36,7 +36,8 @@ def test_struct_layouts_match_header(tmp_path):
     """Field offsets and sizes of the ctypes structs equal what a C compiler
     makes of include/hqmq.h."""
     structs = {"hqmq_desc": B.Desc, "hqmq_sizes_t": B.Sizes, "hqmq_enc": B.Enc,
-               "hqmq_attn_desc": B.AttnDesc, "hqmq_attn_sizes_t": B.AttnSizes}
+               "hqmq_attn_desc": B.AttnDesc, "hqmq_attn_sizes_t": B.AttnSizes,
+               "hqmq_paged_desc": B.PagedDesc, "hqmq_pages": B.Pages, "hqmq_paged_sizes_t": B.PagedSizes}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hqmq.h"', "int main(void){"]
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -236,3 +237,59 @@ def test_attend_rejects_before_enqueueing():
     assert call(ws_bytes=100) == B.HQMQ_EINVAL
     assert call(q=18) == B.HQMQ_EINVAL          # misaligned query
     assert call(a=_attn(batch=0), q=None) == B.HQMQ_OK
+
+
+# ---------------------------------------------------------------- paged pool
+@pytest.mark.parametrize("nf", [0, 1])
+def test_paged_sizes_follow_the_layout(nf):
+    d = K.Desc.make(32, 8, 32, 128, 32, K.HQMQ_F16, 4096, 3.0, nf)
+    p = K.PagedDesc(1000, 128, 256)
+    s = K.hqmq_paged_sizes(d, p)
+    W = 10
+    rows = 32 * 8 * 1000 * 128
+    assert s.idx_bytes == rows * W * 4
+    assert s.hnorm_bytes == (rows * W * 4 if nf else rows * 32 * 2)
+    assert s.side_count_bytes == 32 * 8 * 1000 * 4
+    assert s.side_pos_bytes == 32 * 8 * 1000 * 256 * 4
+    assert s.side_val_bytes == 32 * 8 * 1000 * 256 * 8
+    # the call's records with a worst-case side list (16 outliers per token
+    # of 32 chunks), plus the encode scratch
+    c = K.hqmq_sizes(K.Desc.make(32, 8, 32, 128, 32, K.HQMQ_F16, 4096, 3.0))
+    lo = c.idx_bytes + c.hnorm_bytes + c.offsets_bytes + 12 * c.max_outliers + c.workspace_bytes
+    assert lo <= s.append_workspace_bytes <= lo + 8 * 256
+
+
+@pytest.mark.parametrize("kw", [dict(page_tokens=48), dict(page_tokens=8), dict(page_tokens=0),
+                                dict(num_pages=-1), dict(page_capacity=-1)])
+def test_paged_desc_validation(kw):
+    d = K.Desc.make(2, 2, 16, 128, 8, K.HQMQ_F16, 0, 3.0)
+    p = dict(num_pages=10, page_tokens=64, page_capacity=16)
+    p.update(kw)
+    with pytest.raises(K.HQMQError) as e:
+        K.hqmq_paged_sizes(d, K.PagedDesc(**p))
+    assert e.value.code == B.HQMQ_EINVAL
+
+
+def test_paged_calls_reject_before_enqueueing():
+    lib = B.lib()
+    d = K.Desc.make(1, 1, 4, 128, 8, K.HQMQ_F16, 4, 3.0)
+    p = K.PagedDesc(4, 64, 8)
+    pool = B.Pages()
+    # null pool pointers, slots and workspace
+    assert lib.hqmq_append(ctypes.byref(d), ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.c_void_p(16),
+                           ctypes.byref(pool), None, None, 0, None) == B.HQMQ_EINVAL
+    pool = B.Pages(16, 16, 16, 16, 16)
+    assert lib.hqmq_append(ctypes.byref(d), ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.c_void_p(16),
+                           ctypes.byref(pool), None, ctypes.c_void_p(256), 1 << 30, None) == B.HQMQ_EINVAL
+    # workspace too small
+    assert lib.hqmq_append(ctypes.byref(d), ctypes.byref(p), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                           ctypes.c_void_p(16), ctypes.byref(pool), None, ctypes.c_void_p(256), 64,
+                           None) == B.HQMQ_EINVAL
+    a = B.AttnDesc.make(1, 4, 0, 64, 0.1)
+    # page-table stride 0
+    assert lib.hqmq_attend_paged(ctypes.byref(d), ctypes.byref(p), ctypes.byref(a), ctypes.byref(pool),
+                                 ctypes.c_void_p(16), ctypes.byref(pool), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                 ctypes.c_void_p(16), 0, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                 ctypes.c_void_p(256), 1 << 20, None) == B.HQMQ_EINVAL
+    assert lib.hqmq_paged_clear(ctypes.byref(d), ctypes.byref(p), ctypes.byref(pool), None, 3,
+                                None) == B.HQMQ_EINVAL
