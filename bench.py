@@ -326,6 +326,157 @@ def decode_step_bench(args, w):
     print(json.dumps(out), flush=True)
 
 
+def paged_step_bench(args, w):
+    """Decode-step workload on paged pools, the serving form of the step: the
+    cache of ``w.sequences`` sequences is appended into K and V pools of
+    ``--page-tokens``-token pages (pages of a sequence scattered through the
+    pool; prefill calls of one Med3x batch, 4096 tokens of one sequence,
+    untimed).  One step appends the step's new token of every sequence
+    (hqmq_append, K and V, Med3x batch = the step) and runs the attention of
+    every layer over each sequence's pages including the new token
+    (hqmq_attend_paged, GQA group 4)."""
+    import math
+    import numpy as np
+    import torch
+    import kv_cache_quantization_hqmq_amd as K
+    import synth
+    torch.cuda.set_device(0)
+    sh = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    group = 4
+    nf = NORM_FORMATS[args.norm_format]
+    L, H, D, nseq = w.layers, w.heads, w.head_dim, w.sequences
+    Tc = w.tokens // nseq
+    cpt = D // 4
+    P = args.page_tokens
+    total = args.warmup + args.steps
+    pps = (Tc + total + P - 1) // P            # pages per sequence
+    NP = nseq * pps
+    cap = P * cpt // 16                         # side entries per page: 6.25% of its chunks
+    pdesc = K.PagedDesc(NP, P, cap)
+    B = w.med_batch_tokens
+    desc0 = K.Desc.make(L, H, 0, D, w.S, K.HQMQ_F16, B, w.med_C, nf)
+    desc_p = K.Desc.make(L, H, B, D, w.S, K.HQMQ_F16, B, w.med_C, nf)           # prefill call
+    desc_a = K.Desc.make(L, H, nseq, D, w.S, K.HQMQ_F16, nseq, w.med_C, nf)     # one step
+    rng = np.random.default_rng(7)
+    ptab = rng.permutation(NP).astype(np.int32).reshape(nseq, pps)
+    ptab_d = torch.from_numpy(ptab).cuda()
+    psz = K.hqmq_paged_sizes(desc0, pdesc)
+    pool_bytes = psz.idx_bytes + psz.hnorm_bytes + psz.side_count_bytes + psz.side_pos_bytes + psz.side_val_bytes
+    log(f"workload {synth.describe(w)}; paged pools: {NP} pages of {P} tokens, {cap} side entries per page, "
+        f"{pool_bytes / 1e9:.1f} GB per role")
+    pools, cbs, xa = {}, {}, {}
+    ws_p = K.append_workspace(desc_p, pdesc)
+    n_pre = {}
+    for role in w.roles:
+        t = time.perf_counter()
+        cbs[role] = torch.from_numpy(K.hqmq_make_codebook(w.codebook_seed, L, H, role, w.S)).cuda()
+        pools[role] = K.allocate_pool(desc0, pdesc)
+        x_all = synth.generate(w, role, "cuda")
+        st = torch.zeros(2, dtype=torch.int64, device="cuda")
+        st_sum = torch.zeros(2, dtype=torch.int64, device="cuda")
+        tok = torch.arange(B, dtype=torch.int64, device="cuda")
+        for q in range(nseq):
+            for k0 in range(0, Tc, B):
+                x = x_all[:, :, q * Tc + k0:q * Tc + k0 + B].contiguous()
+                t_seq = k0 + tok
+                slots = ptab_d[q].long()[t_seq // P] * P + t_seq % P
+                K.hqmq_append(desc_p, pdesc, x, slots, cbs[role], pools[role], st, ws_p, sh)
+                st_sum += st
+        del x_all, x
+        torch.cuda.synchronize()
+        n_pre[role] = st_sum.cpu().tolist()
+        log(f"role {role}: cache appended in {time.perf_counter() - t:.1f} s, {n_pre[role][0]} outliers, "
+            f"{n_pre[role][1]} dropped (page lists full)")
+        xa[role] = [synth.generate_append(w, role, i, "cuda") for i in range(total)]
+    del ws_p
+    ws_a = K.append_workspace(desc_a, pdesc)
+    seqs = torch.arange(nseq, dtype=torch.int64, device="cuda")
+    slots_i, lens_i = [], []
+    for i in range(total):
+        t = Tc + i
+        slots_i.append((ptab_d[:, t // P].long() * P + t % P).contiguous())
+        lens_i.append(torch.full((nseq,), t + 1, dtype=torch.int32, device="cuda"))
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(4242)
+    qs = torch.randn((L, nseq, H * group, D), generator=gq, device="cuda").to(torch.float16)
+    scale = 1.0 / math.sqrt(D)
+    max_len = Tc + total
+    adesc = [K.AttnDesc.make(nseq, group, l, max_len, scale) for l in range(L)]
+    asz = K.hqmq_attn_sizes(desc0, adesc[0])
+    aws = torch.empty((int(asz.workspace_bytes),), dtype=torch.uint8, device="cuda")
+    aout = torch.empty((L, nseq, H * group, D), dtype=torch.float32, device="cuda")
+    st_a = {r: torch.zeros(2, dtype=torch.int64, device="cuda") for r in w.roles}
+    torch.cuda.synchronize()
+
+    def step(i, e=None):
+        if e:
+            ev.record(e[0], sh)
+        for role in w.roles:
+            K.hqmq_append(desc_a, pdesc, xa[role][i], slots_i[i], cbs[role], pools[role], st_a[role], ws_a, sh)
+        if e:
+            ev.record(e[1], sh)
+        for l in range(L):
+            K.hqmq_attend_paged(desc0, pdesc, adesc[l], pools[0], cbs[0], pools[1], cbs[1], qs[l], ptab_d,
+                                lens_i[i], aout[l], aws, sh)
+        if e:
+            ev.record(e[2], sh)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [tuple(ev.create() for _ in range(3)) for _ in range(args.steps)]
+    log(f"timing {args.steps} paged steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    ms = 1000.0 * (time.perf_counter() - t0) / args.steps
+    app_ms = sum(ev.ms(e[0], e[1]) for e in evs) / args.steps
+    att_ms = sum(ev.ms(e[1], e[2]) for e in evs) / args.steps
+    for e in evs:
+        for x in e:
+            ev.destroy(x)
+    assert torch.isfinite(aout).all(), "attention produced non-finite values"
+    app_out = {r: st_a[r].cpu().tolist() for r in w.roles}
+
+    # one attention launch reads one layer's K and V records of every token and their side entries
+    W = K.hqmq_sizes(desc0).words_per_token
+    tok_all = nseq * (Tc + args.warmup + (args.steps + 1) / 2)   # mean over the timed steps
+    rec_tok = W * 4 + (W * 4 if nf else cpt * 2)
+    side = sum(n_pre[r][0] - n_pre[r][1] for r in w.roles) * 12 / L
+    att_bytes = 2 * H * tok_all * rec_tok + side + nseq * H * group * D * (2 + 4)
+    att_launch_ms = att_ms / L
+    att_gbps = att_bytes / (att_launch_ms * 1e-3) / 1e9
+    roles = len(w.roles)
+    work = roles * H * L * tok_all * cpt
+    out = {
+        "metric": METRIC,
+        "value": work / (ms * 1e-3),
+        "unit": "chunks/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name + "-paged", "layers": L, "kv_heads": H, "query_heads": H * group,
+                   "sequences": nseq, "cached_tokens_per_sequence": Tc, "head_dim": D, "roles": "K+V",
+                   "S": w.S, "med3_batch_tokens": B, "med3_C": w.med_C, "norm_format": args.norm_format,
+                   "page_tokens": P, "pages": NP, "page_capacity": cap,
+                   "step": "append the step's token of every sequence into the pools + attention of every "
+                           "layer over each sequence's pages", "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "attend_paged (one layer)", "achieved": att_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": att_gbps / PEAK_HBM_GBPS,
+                     "traffic": None, "algorithmic_per_launch": att_bytes, "avg_launch_ms": att_launch_ms},
+        "append_ms": app_ms,
+        "attention_ms_per_step": att_ms,
+        "prefill_outliers_dropped": {r: n_pre[r] for r in w.roles},
+        "appended_outliers_last_step": app_out,
+        "pool_bytes_per_role": pool_bytes,
+        "kernel_sha256_16": kernel_hash(),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def _int_per_token(x, bits: int):
     """Naive symmetric per-(token, head) integer quantisation of x [..., D]
     (absmax scale in fp16, round to nearest): the baseline the pages compare
@@ -455,6 +606,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="1..5 (see synth.WORKLOADS; 5 is the decode step)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--paged", action="store_true",
+                    help="workload 5 on paged pools (append + paged attention per step)")
+    ap.add_argument("--page-tokens", type=int, default=128)
     ap.add_argument("--norm-format", choices=sorted(NORM_FORMATS), default="f16",
                     help="norm records: binary16 half-norms, or packed b-bit compact codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -490,7 +644,10 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     if w.sequences > 1:
-        decode_step_bench(args, w)
+        if args.paged:
+            paged_step_bench(args, w)
+        else:
+            decode_step_bench(args, w)
         return
     dev = "cuda"
     torch.cuda.set_device(0)
