@@ -46,7 +46,8 @@
  *          range, batches numbered slice-major (slice * batches_per_slice +
  *          token_block).
  *   status [2] u64: status[0] = outliers found, status[1] = 1 when they did
- *          not fit out_capacity (entries past the capacity are dropped).
+ *          not fit out_capacity (entries past the capacity are dropped;
+ *          their chunks decode to the bulk value of their record).
  *
  * Decoding: bulk chunk y = (2 * h) * (q_p * q_s) in fp32, rounded to the
  * output type, h the binary16 half-norm (packed format: the value the code
@@ -200,8 +201,9 @@ int hqmq_encode_result(const hqmq_enc *enc, hipStream_t stream, uint64_t *n_outl
  * (packed: the binary16 value its code stands for), computed in fp32 and
  * rounded to nearest even; outlier chunks take their side-list values (the decoder
  * the pages run before or inside attention: gist.science "Memory en
- * Latentie").  enc must come from a successful hqmq_encode with the same
- * descriptor and codebook.  Asynchronous on stream.
+ * Latentie").  enc must come from hqmq_encode with the same descriptor and
+ * codebook; after a side-list overflow the chunks whose entries were dropped
+ * decode to their bulk value.  Asynchronous on stream.
  * Errors: HQMQ_EINVAL, HQMQ_EHIP. */
 int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, void *y,
                 hipStream_t stream);

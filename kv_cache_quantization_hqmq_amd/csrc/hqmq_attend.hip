@@ -64,21 +64,6 @@ struct AttArgs {
     uint32_t page_cap;          // side-list entries per (layer, head, page)
 };  // r[].hnorm: binary16 half-norms, or packed compact codes (kernel's NPACK)
 
-// Exclusive prefix sum over the wave, in lane order, of counts below 32.
-__device__ __forceinline__ uint32_t wave_excl_small(uint32_t v, uint32_t *total) {
-    uint32_t ex = 0, tot = 0;
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-        const uint64_t m = __ballot((v >> k) & 1u);
-        ex += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))
-              << k;
-        tot += static_cast<uint32_t>(__popcll(m)) << k;
-    }
-    *total = tot;
-    return ex;
-}
-
 // First entry in [lo, hi) of a position-sorted side list whose position is
 // at least p0 (hi when none): a 64-way search per round.
 __device__ uint64_t search_first(const uint32_t *out_pos, uint64_t lo, uint64_t hi, int64_t p0, int lane) {
@@ -347,14 +332,18 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
 
     // entries at and past end[r] are never used; lanes past it read a valid
     // address (the last entry, or the half-norm array when there is none)
-    uint64_t sv[2];   // side-list entries cur[r] + lane (4 x fp16 each)
+    uint64_t sv[2];   // side-list entries cur[r] + lane: values (4 x fp16)
+    uint32_t sp[2];   // and positions
     auto load_window = [&](int r) {
         const uint64_t left = end[r] - cur[r];   // entries from cur[r] on (end >= cur)
         const uint32_t last = left > 64u ? 63u : (left > 0u ? static_cast<uint32_t>(left) - 1u : 0u);
-        const uint64_t *base = left > 0u ? reinterpret_cast<const uint64_t *>(a.r[r].out_val) + cur[r]
-                                         : reinterpret_cast<const uint64_t *>(a.r[r].hnorm);
+        const bool any = left > 0u;
+        const uint64_t *vb = any ? reinterpret_cast<const uint64_t *>(a.r[r].out_val) + cur[r]
+                                 : reinterpret_cast<const uint64_t *>(a.r[r].hnorm);
+        const uint32_t *pb = any ? a.r[r].out_pos + cur[r] : reinterpret_cast<const uint32_t *>(a.r[r].hnorm);
         const uint32_t li = static_cast<uint32_t>(lane);
-        sv[r] = base[li < last ? li : last];
+        sv[r] = vb[li < last ? li : last];
+        sp[r] = pb[li < last ? li : last];
     };
     load_window(0);
     load_window(1);
@@ -390,9 +379,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
 
     // (after the tile: the cursor moves to the next page's list first when
     // the next tile starts a page, paged pools only)
-    auto decode_tile = [&](int r, const TileRegs<D, BITS, NPACK> &tr, int nvalid, unsigned char *dst, bool newpage,
-                           uint64_t nlo, uint64_t nhi) {
-        const bool valid = ti < nvalid;
+    // (plo: slice position, or page position when paged, of the tile's
+    // first chunk; rows at and past nvalid hold copies of a valid row)
+    auto decode_tile = [&](int r, const TileRegs<D, BITS, NPACK> &tr, int nvalid, unsigned char *dst, uint32_t plo,
+                           bool newpage, uint64_t nlo, uint64_t nhi) {
         uint32_t hw[CPL / 2];
         if constexpr (NPACK) {
             uint32_t nc[CPL];
@@ -400,11 +390,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
             const int nbits = BITS > 0 ? BITS : a.bits;
 #pragma unroll
             for (int v = 0; v < CPL / 2; ++v)
-                hw[v] = valid ? compact_norm_h16(nc[2 * v], nbits) | (compact_norm_h16(nc[2 * v + 1], nbits) << 16)
-                              : 0u;
+                hw[v] = compact_norm_h16(nc[2 * v], nbits) | (compact_norm_h16(nc[2 * v + 1], nbits) << 16);
         } else {
 #pragma unroll
-            for (int v = 0; v < CPL / 2; ++v) hw[v] = valid ? tr.hw[v] : 0u;
+            for (int v = 0; v < CPL / 2; ++v) hw[v] = tr.hw[v];
         }
         uint32_t code[CPL];
         extract(tr.w, code);
@@ -434,55 +423,47 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         uint2 *dp = reinterpret_cast<uint2 *>(dst + ti * ROWB + c0 * 8);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) dp[j] = val[j];
-        uint32_t fl = 0u;   // Med3x flags (bit 15 of each code), chunk order
-#pragma unroll
-        for (int v = 0; v < CPL / 2; ++v) fl |= (((hw[v] >> 15) & 1u) | ((hw[v] >> 30) & 2u)) << (2 * v);
-        // Outlier chunks take their side-list values, in position order: the
-        // tile's k-th flagged chunk is entry cur + k.  Each round writes one
-        // flagged chunk per lane over its bulk value in LDS, taking entries
-        // below 64 from the register window; a tile with more than 64 flagged
-        // chunks reads the rest in rounds of 64 (rare; those loads are used
-        // at once, inside that uniform branch).
-        if (__ballot(fl != 0u)) {
-            uint32_t tot;
-            const uint32_t ex = wave_excl_small(static_cast<uint32_t>(__popc(fl)), &tot);
+        // Outlier chunks take their side-list values.  Lane i holds entry
+        // cur + i (value and position); the list is sorted by position and cur
+        // is its first entry at or after this tile, so the tile's entries are
+        // a prefix of the window: each lane whose entry lies in the tile writes
+        // it over the bulk value in LDS.  A tile with more than 64 entries reads
+        // further windows (rare; those loads are used at once).  Chunks whose
+        // entry was dropped (side list over capacity) keep the bulk value.
+        {
+            constexpr int LCPT = CPT == 16 ? 4 : (CPT == 32 ? 5 : 6);
             const uint64_t left = end[r] - cur[r];
-            const uint32_t lim = left < 0xFFFFFFFFu ? static_cast<uint32_t>(left) : 0xFFFFFFFFu;
-            uint32_t f = fl, e = ex;
-            while (__ballot(f != 0u && e < 64u)) {
-                const bool act = f != 0u && e < 64u;
-                const int src = static_cast<int>(e & 63u);
-                const uint32_t vx = __shfl(static_cast<uint32_t>(sv[r]), src);
-                const uint32_t vy = __shfl(static_cast<uint32_t>(sv[r] >> 32), src);
-                if (act) {
-                    const int j = __builtin_ctz(f);
-                    *reinterpret_cast<uint2 *>(dst + ti * ROWB + (c0 + j) * 8) =
-                        e < lim ? make_uint2(vx, vy) : make_uint2(0u, 0u);
-                    f &= f - 1u;
-                    ++e;
-                }
+            const uint32_t span = static_cast<uint32_t>(nvalid * CPT);   // the tile's positions
+            const uint32_t lim = left < 64u ? static_cast<uint32_t>(left) : 64u;
+            const uint32_t rel0 = sp[r] - plo;
+            bool in = static_cast<uint32_t>(lane) < lim && rel0 < span;
+            if (in) {
+                const uint32_t rel = rel0;
+                *reinterpret_cast<uint2 *>(dst + (rel >> LCPT) * ROWB + (rel & (CPT - 1)) * 8) =
+                    make_uint2(static_cast<uint32_t>(sv[r]), static_cast<uint32_t>(sv[r] >> 32));
             }
-            if (tot > 64u) {
-                for (uint32_t base = 64u; base < tot; base += 64u) {
-                    const uint32_t li = base + static_cast<uint32_t>(lane);
-                    const uint64_t w = reinterpret_cast<const uint64_t *>(a.r[r].out_val)[cur[r] + (li < lim ? li : lim - 1u)];
+            uint32_t n = static_cast<uint32_t>(__popcll(__ballot(in)));
+            if (n == 64u) {
+                for (uint64_t base = 64u; left > base; base += 64u) {
+                    const uint64_t rest = left - base;
+                    const uint32_t l2 = rest < 64u ? static_cast<uint32_t>(rest) : 64u;
+                    const uint32_t li = static_cast<uint32_t>(lane) < l2 ? static_cast<uint32_t>(lane) : l2 - 1u;
+                    const uint64_t e = cur[r] + base + li;
+                    const uint32_t pos = a.r[r].out_pos[e];
+                    const uint64_t w = reinterpret_cast<const uint64_t *>(a.r[r].out_val)[e];
                     __builtin_amdgcn_s_waitcnt(0);
-                    while (__ballot(f != 0u && e < base + 64u)) {
-                        const bool act = f != 0u && e < base + 64u;
-                        const int src = static_cast<int>((e - base) & 63u);
-                        const uint32_t vx = __shfl(static_cast<uint32_t>(w), src);
-                        const uint32_t vy = __shfl(static_cast<uint32_t>(w >> 32), src);
-                        if (act) {
-                            const int j = __builtin_ctz(f);
-                            *reinterpret_cast<uint2 *>(dst + ti * ROWB + (c0 + j) * 8) =
-                                e < lim ? make_uint2(vx, vy) : make_uint2(0u, 0u);
-                            f &= f - 1u;
-                            ++e;
-                        }
+                    const uint32_t rel = pos - plo;
+                    in = static_cast<uint32_t>(lane) < l2 && rel < span;
+                    if (in) {
+                        *reinterpret_cast<uint2 *>(dst + (rel >> LCPT) * ROWB + (rel & (CPT - 1)) * 8) =
+                            make_uint2(static_cast<uint32_t>(w), static_cast<uint32_t>(w >> 32));
                     }
+                    const uint32_t c = static_cast<uint32_t>(__popcll(__ballot(in)));
+                    n += c;
+                    if (c < 64u) break;
                 }
             }
-            cur[r] += tot;
+            cur[r] += n;
         }
         if (PAGED && newpage) {
             cur[r] = nlo;
@@ -505,6 +486,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         const int64_t tb1 = tile_row(nv1 > 0 ? t1 : w_lo);
         load_tile(0, tb1, nv1, nxt_t[0]);
         load_tile(1, tb1, nv1, nxt_t[1]);
+        const uint32_t plo = static_cast<uint32_t>((PAGED ? (t0 & page_mask) : start + t0) * CPT);
         // paged: the side lists of the page the next tile starts
         const bool newpage = PAGED && nv1 > 0 && (t1 & page_mask) == 0;
         uint64_t nlo[2] = {0, 0}, nhi[2] = {0, 0};
@@ -515,7 +497,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
                 page_list(a.r[1], ps, a.page_cap, &nlo[1], &nhi[1]);
             }
         }
-        decode_tile(0, cur_t[0], nvalid, tt, newpage, nlo[0], nhi[0]);
+        decode_tile(0, cur_t[0], nvalid, tt, plo, newpage, nlo[0], nhi[0]);
         wave_sync();
 
         // S[token 4 g + i][head n]: A[m = token n][k = 4 g + j] = K[token n][16 kb + 4 g + j]
@@ -535,20 +517,22 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         if (__ballot(tmax > m_run + kLazy)) {
             const float m_new = tmax > m_run + kLazy ? tmax : m_run;
-            const float alpha = exp2f(m_run - m_new);   // 1 where unchanged, 0 from -inf
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 where unchanged, 0 from -inf
             l_run *= alpha;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) o[kb] *= alpha;
             m_run = m_new;
         }
         wave_sync();   // the K tile has been read: V goes into the same place
-        decode_tile(1, cur_t[1], nvalid, tt, newpage, nlo[1], nhi[1]);
+        decode_tile(1, cur_t[1], nvalid, tt, plo, newpage, nlo[1], nhi[1]);
         wave_sync();
         f16x4 ph;
         float psum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const _Float16 p = static_cast<_Float16>(exp2f(s[i] - m_run + kPScale));
+            // v_exp_f32 alone: arguments are at most kPScale + kLazy, and
+            // results below the binary16 range become 0 either way
+            const _Float16 p = static_cast<_Float16>(__builtin_amdgcn_exp2f(s[i] - m_run + kPScale));
             ph[i] = p;
             psum += static_cast<float>(p);
         }

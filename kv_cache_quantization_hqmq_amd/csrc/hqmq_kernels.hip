@@ -1288,8 +1288,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
                 pd[u].h = compact_norm_h16(k0, a.bits) | (compact_norm_h16(k1, a.bits) << 16);
             }
         }
-        // side-list values of this iteration's flagged chunks, in order
+        // side-list values of this iteration's flagged chunks, in order (a
+        // chunk whose entry was dropped, past the capacity, keeps its bulk value)
         uint2 ov[kDecUnroll][2];
+        bool oh[kDecUnroll][2];
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
             const bool f0 = (pd[u].h & 0x8000u) != 0;
@@ -1301,8 +1303,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m1), 0u));
             const uint64_t e0 = e_next + below;
             const uint64_t e1 = e0 + (f0 ? 1 : 0);
-            ov[u][0] = f0 && e0 < e_end ? sval[e0] : make_uint2(0u, 0u);
-            ov[u][1] = f1 && e1 < e_end ? sval[e1] : make_uint2(0u, 0u);
+            oh[u][0] = f0 && e0 < e_end;
+            oh[u][1] = f1 && e1 < e_end;
+            ov[u][0] = oh[u][0] ? sval[e0] : make_uint2(0u, 0u);
+            ov[u][1] = oh[u][1] ? sval[e1] : make_uint2(0u, 0u);
             e_next += static_cast<uint64_t>(__popcll(m0) + __popcll(m1));
         }
 #pragma unroll
@@ -1328,7 +1332,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
                     cw = codeword_f32(qa, static_cast<int>(k) - 24 * s);
                 }
                 out[i] = r * cw;
-                if (hi & 0x8000u) {
+                if (oh[u][i]) {
                     const uint2 v = ov[u][i];
                     const f32x4 f = {f16_bits_to_f32(static_cast<uint16_t>(v.x)), f16_bits_to_f32(static_cast<uint16_t>(v.x >> 16)),
                                      f16_bits_to_f32(static_cast<uint16_t>(v.y)), f16_bits_to_f32(static_cast<uint16_t>(v.y >> 16))};

@@ -277,6 +277,65 @@ def test_capacity_overflow_reports_needed_count():
     G.compare(desc, x, cb_host, rec2, y2)
 
 
+def test_capacity_overflow_decodes_dropped_chunks_to_bulk_values():
+    """With the side list cut at the capacity, the outlier chunks whose entries
+    were dropped decode to the bulk value of their record (nearest codeword
+    times the half-norm), kept entries exactly, and attention reads the same
+    values as the decoder."""
+    import math
+    from tests import attend_cases as A
+    x = _x((1, 2, 2048, 128), torch.float16, seed=12)
+    x[:, :, :, 7] *= 60
+    cb_host, cb = _cb(1, 2, 32)
+    desc = K.Desc.make(1, 2, 2048, 128, 32, K.HQMQ_F16, 512, 3.0)
+    cap = 700
+    rec = K.allocate_records(desc, capacity=cap)
+    K.hqmq_encode(desc, x, cb, rec, K.workspace(desc))
+    with pytest.raises(K.CapacityError) as ei:
+        K.hqmq_encode_result(rec)
+    assert ei.value.needed > cap
+    y = K.decode(desc, rec, cb)
+    torch.cuda.synchronize()
+    offs = rec.batch_offsets.cpu().numpy().view(np.uint64)
+    pos = rec.out_pos[:cap].cpu().numpy().view(np.uint32)
+    nb = 4
+    b = O.code_bits(32)
+    dropped_any = 0
+    for h in range(2):
+        codes = P_unpack(rec.idx[0, h].cpu().numpy().view(np.uint32), 32, b).reshape(-1)
+        hn = rec.hnorm[0, h].cpu().numpy().view(np.uint16).reshape(-1)
+        flagged = (hn & 0x8000) != 0
+        kept = np.zeros(hn.shape, bool)
+        e0, e1 = min(int(offs[h * nb]), cap), min(int(offs[(h + 1) * nb]), cap)
+        kept[pos[e0:e1]] = True
+        dropped = flagged & ~kept
+        dropped_any += int(dropped.sum())
+        bulk = A.f16_values(O.decode_range(codes, hn & 0x7FFF, 2048, 128, cb_host[0, h])).reshape(-1, 4)
+        yg = y[0, h].float().cpu().numpy().astype(np.float64).reshape(-1, 4)
+        rhat = 2.0 * (hn & 0x7FFF).view(np.float16).astype(np.float64)
+        err = np.abs(yg - bulk).max(axis=1)
+        lim = np.maximum(1e-3 * rhat, 2.0 ** -24)
+        assert np.all(err[~kept] <= lim[~kept])
+        xs = x[0, h].float().cpu().numpy().reshape(-1, 4).astype(np.float16).astype(np.float64)
+        np.testing.assert_array_equal(yg[kept], xs[kept])
+    assert dropped_any > 0
+    # attention over the same records reads the decoder's values
+    q = A.make_queries(1, 8, 128, 5)
+    out = K.attend(desc, 0, rec, cb, rec, cb, q, torch.zeros(1, dtype=torch.int64, device="cuda"),
+                   torch.full((1,), 2048, dtype=torch.int32, device="cuda"), 2048)
+    torch.cuda.synchronize()
+    qn = q.float().cpu().numpy().astype(np.float64)
+    for h in range(2):
+        v = y[0, h].float().cpu().numpy().astype(np.float64)
+        ref = O.attend(v, v, qn[0, 4 * h:4 * h + 4], 1.0 / math.sqrt(128))
+        assert A.compare_out(out.cpu().numpy()[0, 4 * h:4 * h + 4], ref, v) <= 1.0
+
+
+def P_unpack(words, cpt, b):
+    from tests.parity import unpack_words
+    return unpack_words(words, cpt, b)
+
+
 def test_invalid_arguments_enqueue_nothing():
     x = _x((1, 1, 64, 128), torch.float16, seed=1)
     cb_host, cb = _cb(1, 1, 8)
