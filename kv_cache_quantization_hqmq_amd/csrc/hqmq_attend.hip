@@ -45,6 +45,22 @@ constexpr int kTile = 16;            // tokens per wave step (one MFMA tile)
 constexpr float kPScale = 8.0f;
 constexpr float kLazy = 7.0f;
 constexpr int kAttTableMaxS = 64;    // the 24 S codewords of K and V in LDS up to here
+// Dword 3 of the buffer resources of the record loads (gfx9 raw buffer:
+// 32-bit data format, no swizzle); loads past num_records return 0.
+constexpr int kBufWord3 = 0x00020000;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Code width of S secondary codewords (b = ceil(log2(24 S))) and the width
+// the kernel is specialised for (0: any width).
+inline int attend_code_bits(int S) {
+    int b = 0;
+    while ((1 << b) < 24 * S) ++b;
+    return b;
+}
+inline int attend_kernel_bits(int S, bool table) {
+    const int b = attend_code_bits(S);
+    return table && (b == 10 || b == 8) ? b : 0;
+}
 
 struct AttArgs {
     AttRole r[2];               // K, V
@@ -151,7 +167,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     constexpr int CPT = Sh::CPT, CPL = Sh::CPL, KB = Sh::KB, NU = Sh::NU, ROWB = Sh::ROWB, TILEB = Sh::TILEB;
 
     extern __shared__ f32x4 smem[];
-    const int ntab = TABLE ? 24 * a.S : a.S;
+    // codeword tables: TABLE kernels of a fixed code width hold all 2^BITS
+    // codes (zeros past 24 S), so a code read from the records needs no clamp
+    const int ntab = TABLE ? (BITS > 0 ? (1 << BITS) : 24 * a.S) : a.S;
     f32x4 *tab = smem;                                                     // [2][ntab]
     unsigned char *tiles = reinterpret_cast<unsigned char *>(smem + 2 * ntab);   // [waves][TILEB]
 
@@ -194,6 +212,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         const float *q = a.r[r].cb + sl * a.S * 4;
         for (int k = threadIdx.x; k < ntab; k += kAttThreads) {
             if constexpr (TABLE) {
+                if (k >= 24 * a.S) {
+                    tab[r * ntab + k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    continue;
+                }
                 const int s = k / 24;
                 const float qe[4] = {double_f16(q[4 * s]), double_f16(q[4 * s + 1]), double_f16(q[4 * s + 2]),
                                      double_f16(q[4 * s + 3])};
@@ -288,43 +310,54 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     auto load_tile = [&](int r, int64_t tb, int nvalid, TileRegs<D, BITS, NPACK> &tr) {
         const AttRole &R = a.r[r];
         const uint32_t ri = static_cast<uint32_t>(nvalid > 0 ? (ti < nvalid ? ti : nvalid - 1) : 0);
-        const uint16_t *hp = (R.hnorm + tb * CPT) + (ri * static_cast<uint32_t>(CPT) + static_cast<uint32_t>(c0));
+        // buffer resources over the tile's rows (wave-uniform bases; lanes
+        // add 32-bit offsets, fixed word offsets go in the instructions)
+        const int words = a.words;
+        const __amdgpu_buffer_rsrc_t ir = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(R.idx + tb * words), 0, kTile * words * 4, kBufWord3);
         if constexpr (NPACK) {
             // the norm words at the index words' places (loaded below)
-        } else if constexpr (CPL == 4) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(hp);
-            tr.hw[0] = u.x;
-            tr.hw[1] = u.y;
         } else {
+            const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(R.hnorm + tb * CPT), 0, kTile * CPT * 2, kBufWord3);
+            const int ho = static_cast<int>((__umul24(ri, static_cast<uint32_t>(CPT)) + static_cast<uint32_t>(c0)) * 2u);
+            if constexpr (CPL == 4) {
+                const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(hr, ho, 0, 0);
+                tr.hw[0] = u[0];
+                tr.hw[1] = u[1];
+            } else {
 #pragma unroll
-            for (int v = 0; v < CPL / 8; ++v) {
-                const uint4 u = reinterpret_cast<const uint4 *>(hp)[v];
-                tr.hw[4 * v] = u.x;
-                tr.hw[4 * v + 1] = u.y;
-                tr.hw[4 * v + 2] = u.z;
-                tr.hw[4 * v + 3] = u.w;
+                for (int v = 0; v < CPL / 8; ++v) {
+                    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(hr, ho + 16 * v, 0, 0);
+                    tr.hw[4 * v] = u[0];
+                    tr.hw[4 * v + 1] = u[1];
+                    tr.hw[4 * v + 2] = u[2];
+                    tr.hw[4 * v + 3] = u[3];
+                }
             }
         }
-        const uint32_t *ib = R.idx + tb * a.words;   // the tile's first row
-        const uint32_t *nb = reinterpret_cast<const uint32_t *>(R.hnorm) + tb * a.words;
-        const uint32_t ro = ri * static_cast<uint32_t>(a.words);
+        const __amdgpu_buffer_rsrc_t nr = NPACK ? __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(reinterpret_cast<const uint32_t *>(R.hnorm) + tb * words), 0, kTile * words * 4,
+            kBufWord3) : ir;
+        const uint32_t ro = __umul24(ri, static_cast<uint32_t>(words));
         if constexpr (BITS > 0) {
+            const int lo = static_cast<int>((ro + static_cast<uint32_t>(w0)) * 4u);
 #pragma unroll
             for (int k = 0; k < TileRegs<D, BITS, NPACK>::NW; ++k) {
-                tr.w[k] = ib[ro + static_cast<uint32_t>(w0 + k)];
-                if constexpr (NPACK) tr.hw[k] = nb[ro + static_cast<uint32_t>(w0 + k)];
+                tr.w[k] = __builtin_amdgcn_raw_buffer_load_b32(ir, lo + 4 * k, 0, 0);
+                if constexpr (NPACK) tr.hw[k] = __builtin_amdgcn_raw_buffer_load_b32(nr, lo + 4 * k, 0, 0);
             }
         } else {
 #pragma unroll
             for (int j = 0; j < CPL; j += 2) {
                 const int w = ((c0 + j) * a.bits) >> 5;
-                const uint32_t o0 = ro + static_cast<uint32_t>(w);
-                const uint32_t o1 = ro + static_cast<uint32_t>(w + 1 < last_word ? w + 1 : last_word);
-                tr.w[j] = ib[o0];
-                tr.w[j + 1] = ib[o1];
+                const int o0 = static_cast<int>((ro + static_cast<uint32_t>(w)) * 4u);
+                const int o1 = static_cast<int>((ro + static_cast<uint32_t>(w + 1 < last_word ? w + 1 : last_word)) * 4u);
+                tr.w[j] = __builtin_amdgcn_raw_buffer_load_b32(ir, o0, 0, 0);
+                tr.w[j + 1] = __builtin_amdgcn_raw_buffer_load_b32(ir, o1, 0, 0);
                 if constexpr (NPACK) {
-                    tr.hw[j] = nb[o0];
-                    tr.hw[j + 1] = nb[o1];
+                    tr.hw[j] = __builtin_amdgcn_raw_buffer_load_b32(nr, o0, 0, 0);
+                    tr.hw[j + 1] = __builtin_amdgcn_raw_buffer_load_b32(nr, o1, 0, 0);
                 }
             }
         }
@@ -397,8 +430,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         }
         uint32_t code[CPL];
         extract(tr.w, code);
+        if constexpr (!(TABLE && BITS > 0)) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) code[j] = code[j] < kmax ? code[j] : kmax;
+            for (int j = 0; j < CPL; ++j) code[j] = code[j] < kmax ? code[j] : kmax;
+        }
         f32x4 cw[CPL];   // TABLE: 2 (a_p * q_s); else a_p * q_s
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -439,7 +474,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
             bool in = static_cast<uint32_t>(lane) < lim && rel0 < span;
             if (in) {
                 const uint32_t rel = rel0;
-                *reinterpret_cast<uint2 *>(dst + (rel >> LCPT) * ROWB + (rel & (CPT - 1)) * 8) =
+                *reinterpret_cast<uint2 *>(dst + __umul24(rel >> LCPT, static_cast<uint32_t>(ROWB)) + (rel & (CPT - 1)) * 8) =
                     make_uint2(static_cast<uint32_t>(sv[r]), static_cast<uint32_t>(sv[r] >> 32));
             }
             uint32_t n = static_cast<uint32_t>(__popcll(__ballot(in)));
@@ -502,11 +537,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
 
         // S[token 4 g + i][head n]: A[m = token n][k = 4 g + j] = K[token n][16 kb + 4 g + j]
         f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        uint2 ka[KB];   // all reads first, so their latencies overlap
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const f16x4 ka = __builtin_bit_cast(f16x4, *reinterpret_cast<const uint2 *>(tt + n * ROWB + (4 * kb + g) * 8));
-            s = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, qv[kb], s, 0, 0, 0);
-        }
+        for (int kb = 0; kb < KB; ++kb) ka[kb] = *reinterpret_cast<const uint2 *>(tt + n * ROWB + (4 * kb + g) * 8);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ka[kb]), qv[kb], s, 0, 0, 0);
         float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -634,7 +669,8 @@ __global__ __launch_bounds__(D) void attend_combine_kernel(const float *part, in
 
 template <int D>
 size_t attend_lds(int S, bool table) {
-    const int ntab = table ? 24 * S : S;
+    const int bits = attend_kernel_bits(S, table);
+    const int ntab = table ? (bits > 0 ? (1 << bits) : 24 * S) : S;
     const size_t loop = 2 * static_cast<size_t>(ntab) * sizeof(f32x4) + kAttWaves * static_cast<size_t>(AttShape<D>::TILEB);
     const size_t merge = kAttWaves * static_cast<size_t>(AttShape<D>::MERGEB);
     return loop > merge ? loop : merge;
