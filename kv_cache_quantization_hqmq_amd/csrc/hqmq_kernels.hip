@@ -589,7 +589,7 @@ __device__ void med3_after_tile(const EncArgs &a, const TileCoords &tc, uint32_t
     }
 }
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 512;
 constexpr int kCandCap = 4096;
 
 struct SelArgs {
@@ -793,16 +793,17 @@ __global__ __launch_bounds__(kSelThreads) void med3_select_kernel(SelArgs a) {
     uint32_t *mrow = a.mask + bid * a.mask_words;
     uint32_t cnt = 0;
     constexpr int U = 8;
-    for (int64_t g0 = 64 * wave; g0 < n; g0 += 64 * 4 * U) {
+    constexpr int kWv = kSelThreads / 64;
+    for (int64_t g0 = 64 * wave; g0 < n; g0 += 64 * kWv * U) {
         uint32_t cv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t i = g0 + 64 * 4 * u + lane;
+            const int64_t i = g0 + 64 * kWv * u + lane;
             cv[u] = i < n ? codes[i] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t gb = g0 + 64 * 4 * u;
+            const int64_t gb = g0 + 64 * kWv * u;
             const int64_t i = gb + lane;
             bool f = i < n && cv[u] > hthr;
             if (i < n && cv[u] == hthr) f = chunk_s2(a, gbase + i) > thr;
