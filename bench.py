@@ -35,6 +35,8 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 NORM_FORMATS = {"f16": 0, "packed": 1}   # hqmq_desc.norm_format
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-70b-kv-128k.json")
+ATTEND_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_attend.hip")
+ATTEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-8b-decode-32x32k.json")
 
 
 def log(*a):
@@ -83,6 +85,18 @@ def traffic_per_launch(key: str = "search_bytes_per_launch"):
     if t.get("kernel_sha256_16") != kernel_hash():
         return None
     return t.get(key)
+
+
+def attend_traffic_per_launch():
+    """HBM bytes per attention launch (one layer of the decode-step workload)
+    from the committed counter summary, or None when it is missing or was
+    taken from another attention kernel source."""
+    if not os.path.exists(ATTEND_TRAFFIC_FILE):
+        return None
+    t = json.load(open(ATTEND_TRAFFIC_FILE))
+    if t.get("attend_sha256_16") != hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()[:16]:
+        return None
+    return t.get("attend_bytes_per_launch")
 
 
 def cpu_baseline(w, xs, cbs, seconds: float):
@@ -306,7 +320,9 @@ def decode_step_bench(args, w):
                    "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": "attend (one layer)", "achieved": att_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": att_gbps / PEAK_HBM_GBPS,
-                     "traffic": None, "algorithmic_per_launch": att_bytes, "avg_launch_ms": att_launch_ms},
+                     # counters were taken on the binary16-norm configuration
+                     "traffic": attend_traffic_per_launch() if args.norm_format == "f16" else None,
+                     "algorithmic_per_launch": att_bytes, "avg_launch_ms": att_launch_ms},
         "encode_appended_ms": enc_ms,
         "attention_ms_per_step": att_ms,
         "fakequant": {"ms_per_step": fq_ms, "decode_ms": dec_ms, "torch_attention_ms": fq_att_ms,
