@@ -903,17 +903,21 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
                     const uint32_t w = e < 2 ? v[u].x : v[u].y;
                     const uint32_t c = (w >> (16 * (e & 1))) & 0xFFFFu;
                     const int i = 4 * q + e;
+                    // positions (< 2^17) keep their code's low bits beside
+                    // them, so the later phases read no code back from HBM
                     if ((c >> 4) == d1) {
                         atomicAdd(&hist[c & 15u], 1u);
                         if (keep) {
                             const uint32_t slot = atomicAdd(ncand, 1u);
-                            if (slot < static_cast<uint32_t>(kCand1Cap)) cand[slot] = static_cast<uint32_t>(i);
+                            if (slot < static_cast<uint32_t>(kCand1Cap))
+                                cand[slot] = (static_cast<uint32_t>(i) << 4) | (c & 15u);
                         }
                     }
                     if (c > hhi) nib |= 1u << e;
                     else if (c >= hlo) {
                         const uint32_t slot = atomicAdd(nunc, 1u);
-                        if (slot < static_cast<uint32_t>(kUnc1Cap)) unc[slot] = static_cast<uint32_t>(i);
+                        if (slot < static_cast<uint32_t>(kUnc1Cap))
+                            unc[slot] = (static_cast<uint32_t>(i) << 15) | (c - hlo);
                     }
                 }
                 if (nib) {
@@ -940,8 +944,8 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
         if (threadIdx.x == 0) *ncand = 0;
         __syncthreads();
         for (uint32_t i = threadIdx.x; i < m1; i += kSelThreads) {
-            const uint32_t off = min(cand[i], static_cast<uint32_t>(n - 1));
-            if (codes[off] == hmed) {
+            const uint32_t off = min(cand[i] >> 4, static_cast<uint32_t>(n - 1));
+            if ((cand[i] & 15u) == (hmed & 15u)) {
                 const uint32_t slot = atomicAdd(ncand, 1u);
                 if (slot < static_cast<uint32_t>(kCand1Cap)) candv[slot] = chunk_s2(a, gbase + off);
             }
@@ -988,8 +992,8 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     const uint32_t nu = *nunc;
     if (nu <= static_cast<uint32_t>(kUnc1Cap)) {
         for (uint32_t j = threadIdx.x; j < nu; j += kSelThreads) {
-            const int i = static_cast<int>(unc[j]);
-            decide(i, codes[i]);
+            const int i = static_cast<int>(unc[j] >> 15);
+            decide(i, hlo + (unc[j] & 0x7FFFu));
         }
     } else {
         for (int i = threadIdx.x; i < n; i += kSelThreads) {
