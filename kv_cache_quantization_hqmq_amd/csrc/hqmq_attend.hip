@@ -45,10 +45,6 @@ constexpr int kTile = 16;            // tokens per wave step (one MFMA tile)
 constexpr float kPScale = 8.0f;
 constexpr float kLazy = 7.0f;
 constexpr int kAttTableMaxS = 64;    // the 24 S codewords of K and V in LDS up to here
-// Dword 3 of the buffer resources of the record loads (gfx9 raw buffer:
-// 32-bit data format, no swizzle); loads past num_records return 0.
-constexpr int kBufWord3 = 0x00020000;
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Code width of S secondary codewords (b = ceil(log2(24 S))) and the width
 // the kernel is specialised for (0: any width).

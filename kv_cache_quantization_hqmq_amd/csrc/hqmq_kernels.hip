@@ -64,16 +64,17 @@ __device__ __forceinline__ float sqrt_rn(float a) {
 }
 
 // binary16 half-norm code fp16_rn(sqrt_rn(s2) / 2).  v_sqrt_f32 is within one
-// ulp, so its half rounds to the same binary16 as the exact value unless it
-// lies within one fp32 ulp of a binary16 rounding boundary; only then (about
-// 3 in 8192 chunks) is the correctly rounded root computed.
+// ulp, so h = v_sqrt_f32(s2) / 2 and the exact half-root round to the same
+// binary16 unless a rounding midpoint lies within one fp32 ulp of h: in the
+// normal binary16 range [2^-14, 2^16) the midpoints are the fp32 values whose
+// low 13 mantissa bits are 0x1000, so h is safe unless those bits are
+// 0x0FFF..0x1001.  Only the others (about 3 in 8192 chunks, and any h outside
+// that range) take the correctly rounded root.
 __device__ __forceinline__ uint16_t half_norm_code(float s2) {
     const float h = __builtin_amdgcn_sqrtf(s2) * 0.5f;
-    const uint16_t c = f32_to_f16_bits(h);
     const uint32_t hb = __float_as_uint(h);
-    if (s2 > 0x1p-100f && f32_to_f16_bits(__uint_as_float(hb + 1u)) == c &&
-        f32_to_f16_bits(__uint_as_float(hb - 1u)) == c)
-        return c;
+    const bool safe = (hb - 0x38800000u) < (0x47800000u - 0x38800000u) && ((hb & 0x1FFFu) - 0x0FFFu) > 2u;
+    if (safe) return f32_to_f16_bits(h);
     return f32_to_f16_bits(sqrt_rn(s2) * 0.5f);
 }
 
@@ -90,7 +91,8 @@ __device__ __forceinline__ float best_primary(f32x4 d) {
 // Index p of the best 2T element for secondary codeword qs: t = (<x, e_m q_s>)_m
 // in fp32; a unit +-e_m (p = 2 m + sign) wins when |t|_inf >= |t|_1 / 2
 // (lowest m, + before -), otherwise the half-unit with s_m = sign t_m
-// (p = 8 + sum of (t_m < 0) 2^m; 0 counts as +).
+// (p = 8 + sum of (t_m < 0) 2^m; 0 counts as +).  Branch-free: the sign
+// nibble comes from the top bits of t_m + 0 (which turns -0 into +0).
 __device__ __forceinline__ int primary_index(const float *qs, float x0, float x1, float x2, float x3) {
     const float q0 = qs[0], q1 = qs[1], q2 = qs[2], q3 = qs[3];
     const float t0 = __builtin_fmaf(q3, x3, __builtin_fmaf(q2, x2, __builtin_fmaf(q1, x1, q0 * x0)));
@@ -98,15 +100,16 @@ __device__ __forceinline__ int primary_index(const float *qs, float x0, float x1
     const float t2 = __builtin_fmaf(-q1, x3, __builtin_fmaf(q0, x2, __builtin_fmaf(q3, x1, -q2 * x0)));
     const float t3 = __builtin_fmaf(q0, x3, __builtin_fmaf(q1, x2, __builtin_fmaf(-q2, x1, -q3 * x0)));
     const float e0 = fabsf(t0), e1 = fabsf(t1), e2 = fabsf(t2), e3 = fabsf(t3);
-    float linf = e0;
-    int mi = 0;
-    float tm = t0;
-    if (e1 > linf) { linf = e1; mi = 1; tm = t1; }
-    if (e2 > linf) { linf = e2; mi = 2; tm = t2; }
-    if (e3 > linf) { linf = e3; mi = 3; tm = t3; }
+    const float linf = fmaxf(fmaxf(fmaxf(e0, e1), e2), e3);
     const float l1 = (e0 + e1) + (e2 + e3);
-    if (linf + linf >= l1) return 2 * mi + (tm < 0.0f ? 1 : 0);
-    return 8 + (t0 < 0.0f ? 1 : 0) + (t1 < 0.0f ? 2 : 0) + (t2 < 0.0f ? 4 : 0) + (t3 < 0.0f ? 8 : 0);
+    const uint32_t m = e0 == linf ? 0u : (e1 == linf ? 1u : (e2 == linf ? 2u : 3u));
+    // top bytes of the four signed values side by side, then their sign bits
+    // moved to bits 28..31 by one multiply (no two partial products overlap)
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t1 + 0.0f), __float_as_uint(t0 + 0.0f), 0x0c0c0703u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t3 + 0.0f), __float_as_uint(t2 + 0.0f), 0x07030c0cu);
+    const uint32_t nib = (((lo | hi) & 0x80808080u) * 0x00204081u) >> 28;
+    const uint32_t unit = 2u * m + ((nib >> m) & 1u);
+    return static_cast<int>(linf + linf >= l1 ? unit : 8u + nib);
 }
 
 // Strict order of (score, s) candidates: higher score, then lower s.
@@ -427,16 +430,28 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
     const int wpg = (64 >> a.log2_cpt) * a.words;
     const int p_tt = lane / a.words;
     const int p_ww = lane - p_tt * a.words;
-    uint32_t *idx_slice = a.idx + slice * a.tokens * a.words;
-    const uint2 *xs = static_cast<const uint2 *>(a.x) + slice * a.n_slice;
+    // block-relative buffer resources: the block's chunks [c_begin, c_end)
+    // start on a token row and number at most 8192, so offsets are 32-bit and
+    // the resources' sizes do the range checks (loads past the end read 0,
+    // stores there are dropped)
+    const uint32_t n = c_end > c_begin ? static_cast<uint32_t>(c_end - c_begin) : 0u;
+    const uint32_t tok_lim = (n + static_cast<uint32_t>(a.cpt) - 1u) >> a.log2_cpt;   // token rows of the block
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(static_cast<const void *>(static_cast<const uint2 *>(a.x) + slice * a.n_slice + c_begin)), 0,
+        static_cast<int>(n * 8u), kBufWord3);
+    const __amdgpu_buffer_rsrc_t hrs =
+        __builtin_amdgcn_make_buffer_rsrc(a.hnorm + slice * a.n_slice + c_begin, 0, static_cast<int>(n * 2u), kBufWord3);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        a.idx + (slice * a.tokens + (c_begin >> a.log2_cpt)) * a.words, 0,
+        static_cast<int>(tok_lim * static_cast<uint32_t>(a.words) * 4u), kBufWord3);
 
-    for (int64_t g0 = c_begin + 64 * wave; g0 < c_end; g0 += 64 * 4) {
-        // B operands: chunk g0 + 32 b + col of both column blocks
+    for (uint32_t o0 = 64u * wave; o0 < n; o0 += 64u * 4u) {
+        // B operands: chunk o0 + 32 b + col of both column blocks
         uint2 xr[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int64_t c = g0 + 32 * b + col;
-            xr[b] = c < c_end ? xs[c] : make_uint2(0u, 0u);
+            const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(xrs, static_cast<int>((o0 + 32u * b + col) * 8u), 0, 0);
+            xr[b] = make_uint2(u[0], u[1]);
         }
         float bsc[2];
         int bsi[2];
@@ -477,21 +492,21 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
             bsi[b] = 8 * bt + 2 * g + hh;
         }
 
-        // the two lane halves hold the other parity of s for the same
-        // chunks; exchanging one block each leaves lane l with chunk g0 + l
+        // lane l < 32 holds parity 0 of chunks l and l + 32, lane l + 32
+        // parity 1 of the same chunks; swapping the upper half of block 0 with
+        // the lower half of block 1 leaves every lane l with both parities of
+        // chunk o0 + l (v_permlane32_swap)
         int s_best;
         {
-            const float ss = hh ? bsc[0] : bsc[1];
-            const int si = hh ? bsi[0] : bsi[1];
-            float ks = hh ? bsc[1] : bsc[0];
-            int ki = hh ? bsi[1] : bsi[0];
-            const float rs = __shfl_xor(ss, 32);
-            const int ri = __shfl_xor(si, 32);
-            if (better(rs, ri, ks, ki)) { ks = rs; ki = ri; }
-            s_best = min(ki, 8 * NT - 1);
+            const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(bsc[0]), __float_as_uint(bsc[1]), false, false);
+            const auto pi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(bsi[0]), static_cast<uint32_t>(bsi[1]),
+                                                             false, false);
+            const float s0 = __uint_as_float(ps[0]), s1 = __uint_as_float(ps[1]);
+            const int i0 = static_cast<int>(pi[0]), i1 = static_cast<int>(pi[1]);
+            s_best = min(better(s1, i1, s0, i0) ? i1 : i0, 8 * NT - 1);
         }
-        const int64_t c = g0 + lane;
-        const bool valid = c < c_end;
+        const uint32_t o = o0 + lane;
+        const bool valid = o < n;
         const uint2 own = hh ? xr[1] : xr[0];
         const float v0 = f16_bits_to_f32(static_cast<uint16_t>(own.x));
         const float v1 = f16_bits_to_f32(static_cast<uint16_t>(own.x >> 16));
@@ -505,10 +520,11 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
         s2 = __builtin_fmaf(v3, v3, s2);
         const uint16_t hn = half_norm_code(s2);
 
-        const uint32_t code = s2 > 0.0f ? static_cast<uint32_t>(24 * s_best + primary_index(&sq[4 * s_best], v0, v1, v2, v3)) : 0u;
-        if (valid) {
-            a.hnorm[slice * a.n_slice + c] = hn;
-            if constexpr (MED) atomicAdd(&shist[hn >> 4], 1u);
+        const int pidx = primary_index(&sq[4 * s_best], v0, v1, v2, v3);
+        const uint32_t code = s2 > 0.0f ? static_cast<uint32_t>(24 * s_best + pidx) : 0u;
+        __builtin_amdgcn_raw_buffer_store_b16(hn, hrs, static_cast<int>(o * 2u), 0, 0);
+        if constexpr (MED) {
+            if (valid) atomicAdd(&shist[hn >> 4], 1u);
         }
         // pack the group's codes into its token rows' words: every code is
         // ORed into the one or two words it spans, then lane w < wpg stores
@@ -524,8 +540,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
         }
         wave_sync();
         if (lane < wpg) {
-            const int64_t tok = (g0 >> a.log2_cpt) + p_tt;
-            if ((tok << a.log2_cpt) < c_end) idx_slice[tok * a.words + p_ww] = sword[wave][lane];
+            const uint32_t tok = (o0 >> a.log2_cpt) + static_cast<uint32_t>(p_tt);
+            __builtin_amdgcn_raw_buffer_store_b32(sword[wave][lane], wrs,
+                                                  static_cast<int>((tok * static_cast<uint32_t>(a.words) + static_cast<uint32_t>(p_ww)) * 4u), 0, 0);
         }
         wave_sync();
     }
@@ -1465,37 +1482,43 @@ struct RowsArgs {
     int32_t log2_page, cpt, bits, words, npack;
 };
 
-// One wave per (slice, call token): its index words and norms to the pool
-// row of its slot (norms packed into b-bit compact codes when npack).
+// Token rows of the call to the pool rows of their slots: one thread per
+// output dword (a row is W index words, then cpt / 2 binary16 norm pairs or
+// W packed norm words); blockIdx.y walks the slices.  Packed words are
+// formed from the compact codes of the (at most five) chunks they hold.
 __global__ __launch_bounds__(256) void paged_rows_kernel(RowsArgs a) {
-    __shared__ uint32_t sw[4][64];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t rows = a.slices * a.tokens;
-    const int64_t nslot = a.num_pages << a.log2_page;
     const int W = a.words;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave; r < rows; r += static_cast<int64_t>(gridDim.x) * 4) {
-        const int64_t s = r / a.tokens;
-        const int64_t slot = a.slots[r - s * a.tokens];
-        if (slot < 0 || slot >= nslot) continue;   // uniform in the wave
-        const int64_t dst = s * nslot + slot;
-        if (lane < W) a.pool_idx[dst * W + lane] = a.idx[r * W + lane];
-        const uint32_t h = lane < a.cpt ? a.h16[r * a.cpt + lane] : 0u;
-        if (!a.npack) {
-            if (lane < a.cpt) static_cast<uint16_t *>(a.pool_norm)[dst * a.cpt + lane] = static_cast<uint16_t>(h);
-        } else {
-            if (lane < W) sw[wave][lane] = 0u;
-            wave_sync();
-            if (lane < a.cpt) {
-                const uint32_t code = compact_norm_code(h, a.bits);
-                const int bit = lane * a.bits;
-                const int sft = bit & 31;
-                atomicOr(&sw[wave][bit >> 5], code << sft);
-                if (sft + a.bits > 32) atomicOr(&sw[wave][(bit >> 5) + 1], code >> (32 - sft));
+    const int NH = a.npack ? W : a.cpt / 2;   // norm dwords per row
+    const uint32_t per = static_cast<uint32_t>(W + NH);
+    const uint32_t total = static_cast<uint32_t>(a.tokens) * per;   // dwords per slice (< 2^32)
+    const int64_t nslot = a.num_pages << a.log2_page;
+    for (int64_t s = blockIdx.y; s < a.slices; s += gridDim.y) {
+        for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += gridDim.x * 256) {
+            const uint32_t t = static_cast<uint32_t>(e) / per;
+            const int w = static_cast<int>(static_cast<uint32_t>(e) - t * per);
+            const int64_t slot = a.slots[t];
+            if (slot < 0 || slot >= nslot) continue;
+            const int64_t src = s * a.tokens + t;   // the call's row
+            const int64_t dst = s * nslot + slot;   // the pool's row
+            if (w < W) {
+                a.pool_idx[dst * W + w] = a.idx[src * W + w];
+            } else if (!a.npack) {
+                const int j = w - W;
+                reinterpret_cast<uint32_t *>(a.pool_norm)[dst * NH + j] =
+                    reinterpret_cast<const uint32_t *>(a.h16)[src * NH + j];
+            } else {
+                const int j = w - W;
+                const int b = a.bits;
+                const uint16_t *hr = a.h16 + src * a.cpt;
+                const int c_lo = (32 * j) / b, c_hi = min((32 * j + 31) / b, a.cpt - 1);
+                uint32_t word = 0u;
+                for (int c = c_lo; c <= c_hi; ++c) {
+                    const uint32_t code = compact_norm_code(hr[c], b);
+                    const int sft = c * b - 32 * j;
+                    word |= sft >= 0 ? code << sft : code >> (-sft);
+                }
+                reinterpret_cast<uint32_t *>(a.pool_norm)[dst * W + j] = word;
             }
-            wave_sync();
-            if (lane < W) static_cast<uint32_t *>(a.pool_norm)[dst * W + lane] = sw[wave][lane];
-            wave_sync();
         }
     }
 }
@@ -1709,9 +1732,11 @@ hipError_t launch_paged_rows(const Geometry &g, const uint32_t *idx, const uint1
     a.bits = g.bits;
     a.words = g.words;
     a.npack = g.npack;
-    const int64_t blocks = ceil_div(rows, 4);
-    hipLaunchKernelGGL(paged_rows_kernel, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)), dim3(256), 0,
-                       st, a);
+    const int64_t per = g.words + (g.npack ? g.words : g.cpt / 2);
+    const int64_t bx = ceil_div(g.tokens * per, 256);
+    const dim3 grid(static_cast<unsigned>(bx < 65536 ? bx : 65536),
+                    static_cast<unsigned>(g.slices < 65535 ? g.slices : 65535));
+    hipLaunchKernelGGL(paged_rows_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
