@@ -894,16 +894,20 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     __syncthreads();
 
     // the one pass: 4 codes per 8-byte load (a batch is a whole number of
-    // token rows, so n is a multiple of 4), eight loads per thread in flight;
-    // definite outliers are ORed into the batch's bitmask (zeroed before the
-    // search) and get their flag in the same 8 bytes written back
+    // token rows, so n is a multiple of 4), eight loads per thread in flight.
+    // Definite outliers: the 8 lanes holding one bitmask word (32 chunks)
+    // combine their nibbles and store the word (the mask is zeroed before the
+    // search and no other thread writes it in this pass), and when any of its
+    // 32 codes is flagged the 8 lanes write back their whole 64-byte line of
+    // codes with the flags set
     uint32_t *mrow = a.mask + bid * a.mask_words;
     uint32_t cnt = 0;
     {
+        const int lane = threadIdx.x & 63;
         uint2 *c4 = reinterpret_cast<uint2 *>(codes);
         const int n4 = n >> 2;
         constexpr int U = 8;
-        for (int i0 = threadIdx.x; i0 < n4; i0 += kSelThreads * U) {
+        for (int i0 = threadIdx.x; i0 - lane < n4; i0 += kSelThreads * U) {
             uint2 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -913,10 +917,10 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int q = i0 + kSelThreads * u;
-                if (q >= n4) continue;
                 uint32_t nib = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
+                    if (q >= n4) break;
                     const uint32_t w = e < 2 ? v[u].x : v[u].y;
                     const uint32_t c = (w >> (16 * (e & 1))) & 0xFFFFu;
                     const int i = 4 * q + e;
@@ -937,8 +941,13 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
                             unc[slot] = (static_cast<uint32_t>(i) << 15) | (c - hlo);
                     }
                 }
-                if (nib) {
-                    atomicOr(&mrow[q >> 3], nib << (4 * (q & 7)));
+                // q & 7 == lane & 7: lanes 8 j .. 8 j + 7 hold the word's 8 nibbles
+                uint32_t wv = nib << (4 * (lane & 7));
+                wv |= __shfl_xor(wv, 1);
+                wv |= __shfl_xor(wv, 2);
+                wv |= __shfl_xor(wv, 4);
+                if (wv != 0u && q < n4) {
+                    if ((lane & 7) == 0) mrow[q >> 3] = wv;
                     cnt += static_cast<uint32_t>(__popc(nib));
                     uint2 f = v[u];
                     f.x |= ((nib & 1u) ? 0x8000u : 0u) | ((nib & 2u) ? 0x80000000u : 0u);
@@ -1061,49 +1070,85 @@ struct GatherArgs {
     int32_t set_flags;   // 0 when the select kernel has already flagged hnorm
 };
 
-// Ordered outlier write: one block per batch walks the batch's bitmask in
-// order, a block scan of the word popcounts ranks every outlier, and its
-// entry lands at batch_offsets[batch] + rank (dropped past the capacity).
-// The chunk's half-norm record gets the outlier flag (bit 15) unless the
-// select kernel has set it.
+// Ordered outlier write: one block per batch walks the batch's bitmask, 256
+// words (8192 chunks) per round with the next round's words already in
+// flight; a block-wide scan of the words' popcounts places each outlier's
+// chunk offset in an LDS list in position order.  The list is written out
+// when the next round might not fit and at the end: every thread then loads
+// the inputs of four entries before storing any, so a batch's side-list
+// writes wait on a few rounds of loads rather than one per outlier.
+constexpr int kGatherList = 32 * kFlagThreads;   // one round's worth of entries
+
 __global__ __launch_bounds__(kFlagThreads) void med3_gather_kernel(GatherArgs a) {
     __shared__ uint32_t sh[kFlagThreads / 64 + 1];
+    __shared__ uint32_t list[kGatherList];
     const int64_t bid = blockIdx.x;
     const int64_t slice = bid / a.bps;
     const int64_t lo = (bid - slice * a.bps) * a.batch_chunks;
     const int64_t n = min(a.batch_chunks, a.n_slice - lo);
     const int64_t nw = (n + 31) >> 5;
-    const int64_t sbase = slice * a.n_slice;
+    const int64_t bbase = slice * a.n_slice + lo;   // the batch's first chunk
     const uint32_t *mrow = a.mask + bid * a.mask_words;
     uint64_t running = a.offsets[bid];
+    uint32_t fill = 0;   // list entries not yet written (uniform)
+
+    auto flush = [&]() {
+        constexpr int U = 4;
+        for (uint32_t i0 = threadIdx.x; i0 < fill; i0 += kFlagThreads * U) {
+            uint32_t cs[U];
+            uint2 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + kFlagThreads * u;
+                cs[u] = i < fill ? list[i] : 0u;
+                v[u] = make_uint2(0u, 0u);
+                if (i < fill) {
+                    if (a.f32) {
+                        const float4 xf = static_cast<const float4 *>(a.x)[bbase + cs[u]];
+                        v[u].x = static_cast<uint32_t>(f32_to_f16_bits(xf.x)) |
+                                 (static_cast<uint32_t>(f32_to_f16_bits(xf.y)) << 16);
+                        v[u].y = static_cast<uint32_t>(f32_to_f16_bits(xf.z)) |
+                                 (static_cast<uint32_t>(f32_to_f16_bits(xf.w)) << 16);
+                    } else {
+                        v[u] = static_cast<const uint2 *>(a.x)[bbase + cs[u]];
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = i0 + kFlagThreads * u;
+                if (i >= fill) continue;
+                const uint64_t pos = running + i;
+                if (pos < a.capacity) {
+                    a.out_pos[pos] = static_cast<uint32_t>(lo + cs[u]);
+                    reinterpret_cast<uint2 *>(a.out_val)[pos] = v[u];
+                }
+                if (a.set_flags) a.hnorm[bbase + cs[u]] = static_cast<uint16_t>(a.hnorm[bbase + cs[u]] | 0x8000u);
+            }
+        }
+        running += fill;
+        fill = 0;
+        __syncthreads();   // the list is refilled next
+    };
+
+    uint32_t next = threadIdx.x < nw ? mrow[threadIdx.x] : 0u;
     for (int64_t w0 = 0; w0 < nw; w0 += kFlagThreads) {
         const int64_t w = w0 + threadIdx.x;
-        uint32_t word = w < nw ? mrow[w] : 0u;
+        uint32_t word = next;
+        next = w + kFlagThreads < nw ? mrow[w + kFlagThreads] : 0u;
         uint32_t tot;
         const uint32_t ex = block_exclusive_scan<uint32_t, kFlagThreads>(static_cast<uint32_t>(__popc(word)), &tot, sh);
-        uint64_t pos = running + ex;
+        if (fill + tot > static_cast<uint32_t>(kGatherList)) flush();
+        uint32_t p = fill + ex;
         while (word) {
             const int b = __ffs(word) - 1;
             word &= word - 1u;
-            const int64_t cs = lo + 32 * w + b;   // chunk position in the slice
-            const int64_t gc = sbase + cs;
-            if (pos < a.capacity) {
-                a.out_pos[pos] = static_cast<uint32_t>(cs);
-                uint2 v;
-                if (a.f32) {
-                    const float4 xf = static_cast<const float4 *>(a.x)[gc];
-                    v.x = static_cast<uint32_t>(f32_to_f16_bits(xf.x)) | (static_cast<uint32_t>(f32_to_f16_bits(xf.y)) << 16);
-                    v.y = static_cast<uint32_t>(f32_to_f16_bits(xf.z)) | (static_cast<uint32_t>(f32_to_f16_bits(xf.w)) << 16);
-                } else {
-                    v = static_cast<const uint2 *>(a.x)[gc];
-                }
-                reinterpret_cast<uint2 *>(a.out_val)[pos] = v;
-            }
-            if (a.set_flags) a.hnorm[gc] = static_cast<uint16_t>(a.hnorm[gc] | 0x8000u);
-            ++pos;
+            list[p++] = static_cast<uint32_t>(32 * w + b);
         }
-        running += tot;
+        fill += tot;
+        __syncthreads();
     }
+    if (fill > 0) flush();
 }
 
 __global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t v) {
@@ -1248,7 +1293,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     const int64_t w1 = min(w0 + wlen, r1);
     const uint2 *sval = reinterpret_cast<const uint2 *>(a.out_val);
 
-    // first side-list entry with position >= w0 (64-way search per round)
+    // first side-list entry with position >= w0: one probe of 64 entries
+    // around the index interpolated from w0's place in its batches (enough
+    // when the outliers are spread evenly), then 64-way search rounds
     uint64_t e_next = 0, e_end = 0;
     if (a.bps > 0 && w0 < w1) {
         const int64_t bl = w0 / a.batch_chunks;
@@ -1258,6 +1305,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
         hi = hi < a.capacity ? hi : a.capacity;
         lo = lo < hi ? lo : hi;
         e_end = hi;
+        if (hi - lo > 64) {
+            const int64_t p0 = bl * a.batch_chunks;
+            const int64_t p1 = min((bh + 1) * a.batch_chunks, a.n_slice);
+            const double f = static_cast<double>(w0 - p0) / static_cast<double>(p1 - p0);
+            const uint64_t guess = lo + static_cast<uint64_t>(f * static_cast<double>(hi - lo));
+            const uint64_t g0 = min(max(guess, lo + 32) - 32, hi - 64);
+            const bool below = static_cast<int64_t>(a.out_pos[g0 + lane]) < w0;
+            const int cnt = __popcll(__ballot(below));
+            if (cnt == 0) hi = g0;                       // the answer is at or before g0
+            else if (cnt == 64) lo = g0 + 64;            // after the window
+            else lo = hi = g0 + static_cast<uint64_t>(cnt);
+        }
         while (hi > lo) {
             const uint64_t len = hi - lo;
             const uint64_t step = (len + 63) / 64;
@@ -1754,9 +1813,9 @@ hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const void *hno
     const int64_t total = g.slices * g.n_slice;
     if (total == 0) return hipSuccess;
     // block ranges: multiples of 512 chunks (4 waves x 128), enough blocks
-    // to fill the chip, at most 32768 chunks
+    // to fill the chip, at most 16384 chunks
     int64_t wgc = round_up(ceil_div(total, 4096), 2 * kDecThreads);
-    wgc = wgc < 2 * kDecThreads ? 2 * kDecThreads : (wgc > 32768 ? 32768 : wgc);
+    wgc = wgc < 2 * kDecThreads ? 2 * kDecThreads : (wgc > 16384 ? 16384 : wgc);
     DecArgs a;
     a.idx = idx;
     a.hnorm = hnorm;
