@@ -72,6 +72,47 @@ class HipEvents:
         self.rt.hipEventDestroy(e)
 
 
+def measure_ceilings(src, dst, stream: int, ev) -> dict:
+    """This GPU's measured ceilings (context beside the published peaks):
+    streaming read, write and copy over 4 GiB of device memory (src and dst:
+    device tensors of at least that size, overwritten), non-packed fp32 FMA on
+    the VALU, and the fp32 and f16 matrix cores.  Each figure is the median
+    of 3 timed launches after one untimed."""
+    import torch
+    import kv_cache_quantization_hqmq_amd as K
+    nbytes = 4 << 30
+    assert src.numel() * src.element_size() >= nbytes and dst.numel() * dst.element_size() >= nbytes
+    e0, e1 = ev.create(), ev.create()
+
+    def timed(launch):
+        ts = []
+        for rep in range(4):
+            ev.record(e0, stream)
+            launch()
+            ev.record(e1, stream)
+            torch.cuda.synchronize()
+            if rep > 0:
+                ts.append(ev.ms(e0, e1))
+        return sorted(ts)[1]
+
+    out = {}
+    for name, kind, moved in (("hbm_read_GBps", K.HQMQ_CEIL_READ, nbytes),
+                              ("hbm_write_GBps", K.HQMQ_CEIL_WRITE, nbytes),
+                              ("hbm_copy_GBps", K.HQMQ_CEIL_COPY, 2 * nbytes)):
+        t = timed(lambda: K.hqmq_ceiling_stream(kind, src, dst, nbytes, stream))
+        out[name] = moved / (t * 1e-3) / 1e9
+    sink = torch.zeros(1, dtype=torch.float32, device=src.device)
+    for name, kind, iters in (("valu_fma_f32_TFLOPs", K.HQMQ_CEIL_FMA_F32, 100000),
+                              ("mfma_f32_16x16x4_TFLOPs", K.HQMQ_CEIL_MFMA_F32, 20000),
+                              ("mfma_f16_32x32x8_TFLOPs", K.HQMQ_CEIL_MFMA_F16, 40000)):
+        fl = []
+        t = timed(lambda: fl.append(K.hqmq_ceiling_compute(kind, iters, sink, stream)))
+        out[name] = fl[-1] / (t * 1e-3) / 1e12
+    ev.destroy(e0)
+    ev.destroy(e1)
+    return out
+
+
 def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
@@ -804,6 +845,16 @@ def main():
         "kernel_sha256_16": kernel_hash(),
     }
     del ws
+    if len(w.roles) == 2 and ys[w.roles[0]].numel() * 2 >= (4 << 30):
+        # measured ceilings (context; the decode outputs serve as scratch)
+        c = measure_ceilings(ys[w.roles[0]], ys[w.roles[1]], sh, ev)
+        dec_read = rec_bytes + 12 * (sum(n_out.values()) / len(w.roles)) + sz.offsets_bytes
+        dec_write = chunks_role * 8
+        mix = (dec_read + dec_write) / (dec_read / c["hbm_read_GBps"] + dec_write / c["hbm_write_GBps"])
+        out["ceilings"] = dict(c, decode_mix_GBps=mix)
+        out["roofline"]["frac_of_measured_mfma_f32"] = achieved_tf / c["mfma_f32_16x16x4_TFLOPs"]
+        out["roofline_decode"]["frac_of_measured_mix"] = dec_gbps / mix
+        out["roofline_decode"]["frac_of_measured_copy"] = dec_gbps / c["hbm_copy_GBps"]
     if not args.no_cpu_baseline:
         log("timing the oracle on a host sample")
         out["cpu_baseline"] = cpu_baseline(w, xs, cbs_host, args.cpu_seconds)

@@ -28,7 +28,12 @@ HQMQ_NORM_F16, HQMQ_NORM_PACKED = 0, 1
 # every symbol include/hqmq.h declares
 EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
            "hqmq_encode_timed", "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes",
-           "hqmq_attend", "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged")
+           "hqmq_attend", "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged",
+           "hqmq_ceiling_stream", "hqmq_ceiling_compute")
+
+# include/hqmq_ceiling.h
+HQMQ_CEIL_READ, HQMQ_CEIL_WRITE, HQMQ_CEIL_COPY = 0, 1, 2
+HQMQ_CEIL_FMA_F32, HQMQ_CEIL_MFMA_F32, HQMQ_CEIL_MFMA_F16 = 0, 1, 2
 
 
 class HQMQError(RuntimeError):
@@ -162,9 +167,14 @@ def lib():
                                         ctypes.POINTER(Pages), ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.hqmq_ceiling_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p]
+        L.hqmq_ceiling_compute.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_double)]
         for f in ("hqmq_sizes", "hqmq_make_codebook", "hqmq_encode", "hqmq_encode_timed",
                   "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes", "hqmq_attend",
-                  "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged"):
+                  "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged",
+                  "hqmq_ceiling_stream", "hqmq_ceiling_compute"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,6 +199,19 @@ def _stream(stream) -> int:
 # ------------------------------------------------------------------ C calls
 def hqmq_strerror(code: int) -> str:
     return lib().hqmq_strerror(int(code)).decode()
+
+
+def hqmq_ceiling_stream(kind: int, src, dst, nbytes: int, stream=None) -> None:
+    """One streaming pass (read, write or copy) of nbytes over device tensors."""
+    _check(lib().hqmq_ceiling_stream(kind, _ptr(src), _ptr(dst), nbytes, _stream(stream)), "hqmq_ceiling_stream")
+
+
+def hqmq_ceiling_compute(kind: int, iterations: int, sink, stream=None) -> float:
+    """Launch an arithmetic ceiling loop; returns the flops it performs."""
+    fl = ctypes.c_double(0.0)
+    _check(lib().hqmq_ceiling_compute(kind, iterations, _ptr(sink), _stream(stream), ctypes.byref(fl)),
+           "hqmq_ceiling_compute")
+    return fl.value
 
 
 def hqmq_sizes(desc: Desc) -> Sizes:
