@@ -283,14 +283,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
     const uint32_t kmax = static_cast<uint32_t>(24 * a.S - 1);
     const int last_word = a.words - 1;
 
-    // Lane l decodes token l / 4 of a 16-token tile, chunks (l % 4) CPL ..
-    // + CPL - 1, so lane order is position order and a tile's flagged chunks
-    // rank with one wave prefix sum.  The records of tile t + 1 are loaded
-    // while tile t is decoded and used (two register sets, used in turn), and
-    // each role keeps the next 64 side-list entries in registers (one per
-    // lane), loaded one tile ahead.
-    const int ti = lane >> 2;
-    const int c0 = (lane & 3) * CPL;
+    // Lane l decodes token l % 16 of a 16-token tile, chunks (l / 16) CPL ..
+    // + CPL - 1: the 16 lanes that store together write 16 different rows,
+    // so their stores fall on distinct LDS banks.  The records of tile t + 1
+    // are loaded while tile t is decoded and used (two register sets, used in
+    // turn), and each role keeps the next 64 side-list entries in registers
+    // (one per lane), loaded one tile ahead.
+    const int ti = lane & 15;
+    const int c0 = (lane >> 4) * CPL;
     const int cbits = BITS > 0 ? BITS : a.bits;
     const uint32_t sh0 = static_cast<uint32_t>(c0 * cbits) & 31u;
     const int w0 = (c0 * cbits) >> 5;
