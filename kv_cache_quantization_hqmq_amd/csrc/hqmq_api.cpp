@@ -370,7 +370,8 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
     if (search_end && hipEventRecord(search_end, stream) != hipSuccess) return HQMQ_EHIP;
     if (med) {
         if (nb > 0) {
-            e = hqmq::launch_med3_select(g, x, h16, ws, stream);
+            e = hqmq::launch_med3_select(g, x, h16, ws, g.npack ? static_cast<uint32_t *>(enc->hnorm) : nullptr,
+                                         stream);
             if (e == hipSuccess)
                 e = hqmq::launch_med3_scan(nb, ws.counts, enc->batch_offsets, enc->out_capacity, enc->status, stream);
             if (e == hipSuccess)
@@ -383,7 +384,9 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
     } else if (enc->status) {
         e = hqmq::launch_fill_u64(enc->status, 2, 0, stream);
     }
-    if (e == hipSuccess && g.npack && chunks > 0)
+    // packed norms: the single-pass select has packed its batches already
+    const bool packed_by_select = med && nb > 0 && hqmq::med3_single_pass(g);
+    if (e == hipSuccess && g.npack && chunks > 0 && !packed_by_select)
         e = hqmq::launch_pack_norms(g, h16, static_cast<uint32_t *>(enc->hnorm), stream);
     return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
 }

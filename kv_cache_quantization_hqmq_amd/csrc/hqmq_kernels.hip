@@ -621,6 +621,11 @@ struct SelArgs {
     int64_t bps;
     float C;
     int32_t f32;
+    // packed norm format, single-pass select: the select packs its batch's
+    // final codes into the record's norm words (nullptr: a separate pass does)
+    uint32_t *pwords;       // [slices][tokens][words]
+    int64_t tokens;
+    int32_t log2_cpt, bits, words;
 };
 
 // Declared fp32 squared norm of chunk gc (the search kernel's operations).
@@ -1030,6 +1035,42 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     uint32_t tot;
     block_exclusive_scan<uint32_t, kSelThreads>(cnt, &tot, sh);
     if (threadIdx.x == 0) a.counts[bid] = tot + *nout;
+
+    // packed norm format: the batch's codes are final now (flags included),
+    // so pack them into the record's norm words here, 2048 chunks (whole
+    // token rows) per round with the words ORed together in LDS
+    if (a.pwords != nullptr) {
+        __syncthreads();   // every decision has been written to codes[]
+        uint32_t *sw = cand;   // rows * words <= 2048 * 15 / 32 + 32 <= kCand1Cap
+        const int cpt = 1 << a.log2_cpt;
+        const int W = a.words;
+        uint32_t *out = a.pwords + (slice * a.tokens + (lo >> a.log2_cpt)) * W;
+        constexpr int kRound = 4 * kSelThreads;
+        for (int r0 = 0; r0 < n; r0 += kRound) {
+            const int rows = min(kRound, n - r0) >> a.log2_cpt;
+            for (int i = threadIdx.x; i < rows * W; i += kSelThreads) sw[i] = 0u;
+            __syncthreads();
+            const int c = r0 + 4 * static_cast<int>(threadIdx.x);
+            if (c < n) {   // n and c are multiples of 4
+                const uint2 u = *reinterpret_cast<const uint2 *>(codes + c);
+                const uint32_t h[4] = {u.x & 0xFFFFu, u.x >> 16, u.y & 0xFFFFu, u.y >> 16};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int lc = 4 * static_cast<int>(threadIdx.x) + j;
+                    const uint32_t code = compact_norm_code(h[j], a.bits);
+                    const int bit = (lc & (cpt - 1)) * a.bits;
+                    uint32_t *wr = &sw[(lc >> a.log2_cpt) * W + (bit >> 5)];
+                    const int sft = bit & 31;
+                    atomicOr(wr, code << sft);
+                    if (sft + a.bits > 32) atomicOr(wr + 1, code >> (32 - sft));
+                }
+            }
+            __syncthreads();
+            uint32_t *dst = out + (r0 >> a.log2_cpt) * W;
+            for (int i = threadIdx.x; i < rows * W; i += kSelThreads) dst[i] = sw[i];
+            __syncthreads();
+        }
+    }
 }
 
 __global__ __launch_bounds__(kScanThreads) void med3_scan_kernel(int64_t nb, const uint32_t *counts,
@@ -1594,10 +1635,11 @@ __global__ void paged_clear_kernel(uint32_t *side_count, int64_t slices, int64_t
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Batches small enough for the single-pass select (its bitmask is in LDS).
-bool med3_single_pass(const Geometry &g) { return g.batch_chunks <= kSel1MaxChunks; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 }  // namespace
+
+bool med3_single_pass(const Geometry &g) { return g.batch_chunks <= kSel1MaxChunks; }
 
 // --------------------------------------------------------------------------
 // Launchers.
@@ -1682,10 +1724,15 @@ hipError_t launch_med3_scan(int64_t batches, const uint32_t *counts, uint64_t *o
 }
 
 hipError_t launch_med3_select(const Geometry &g, const void *x, uint16_t *hnorm, const Med3Work &med,
-                              hipStream_t st) {
+                              uint32_t *pwords, hipStream_t st) {
     const int64_t nb = g.slices * g.batches_per_slice;
     if (nb == 0) return hipSuccess;
     SelArgs a;
+    a.pwords = med3_single_pass(g) ? pwords : nullptr;
+    a.tokens = g.tokens;
+    a.log2_cpt = __builtin_ctz(static_cast<unsigned>(g.cpt));
+    a.bits = g.bits;
+    a.words = g.words;
     a.x = x;
     a.hnorm = hnorm;
     a.hist = med.hist;

@@ -41,9 +41,14 @@ hipError_t launch_encode_search(const Geometry &g, const void *x, const float *c
                                 uint32_t *idx, uint16_t *hnorm, const Med3Work *med, hipStream_t st);
 
 // Med3x: per batch, exact median, threshold, outlier count and bitmask (and,
-// for batches of at most 131072 chunks, the outlier flags in hnorm).
+// for batches of at most 131072 chunks, the outlier flags in hnorm).  With
+// pwords != nullptr and single-pass batches (med3_single_pass), the select
+// also packs the batch's final codes into the record's norm words.
 hipError_t launch_med3_select(const Geometry &g, const void *x, uint16_t *hnorm, const Med3Work &med,
-                              hipStream_t st);
+                              uint32_t *pwords, hipStream_t st);
+
+// Whether Med3x batches of this geometry take the single-pass select.
+bool med3_single_pass(const Geometry &g);
 
 // Exclusive scan of the per-batch counts into batch_offsets, total and
 // overflow flag into status.
