@@ -503,7 +503,8 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
                                                              false, false);
             const float s0 = __uint_as_float(ps[0]), s1 = __uint_as_float(ps[1]);
             const int i0 = static_cast<int>(pi[0]), i1 = static_cast<int>(pi[1]);
-            s_best = min(better(s1, i1, s0, i0) ? i1 : i0, 8 * NT - 1);
+            const bool take1 = (s1 > s0) | ((s1 == s0) & (i1 < i0));
+            s_best = min(take1 ? i1 : i0, 8 * NT - 1);
         }
         const uint32_t o = o0 + lane;
         const bool valid = o < n;
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
         const uint16_t hn = half_norm_code(s2);
 
         const int pidx = primary_index(&sq[4 * s_best], v0, v1, v2, v3);
-        const uint32_t code = s2 > 0.0f ? static_cast<uint32_t>(24 * s_best + pidx) : 0u;
+        const uint32_t code = s2 > 0.0f ? __umul24(24u, static_cast<uint32_t>(s_best)) + static_cast<uint32_t>(pidx) : 0u;
         __builtin_amdgcn_raw_buffer_store_b16(hn, hrs, static_cast<int>(o * 2u), 0, 0);
         if constexpr (MED) {
             if (valid) atomicAdd(&shist[hn >> 4], 1u);
