@@ -260,6 +260,25 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         return sl * a.num_pages + pg;
     };
 
+    // paged: the slot of the page the next tile lies on, and the slot and
+    // side-list bounds of the page after it (requested a page ahead, so no
+    // tile waits on the page table or a page's entry count)
+    int64_t ps_now = 0, ps_ahead = 0;
+    uint64_t ahead_lo[2] = {0, 0}, ahead_hi[2] = {0, 0};
+    auto fetch_ahead = [&](int64_t t) {   // t: the first token of a page
+        if (t < w_hi) {
+            ps_ahead = page_slot(t);
+            page_list(a.r[0], ps_ahead, a.page_cap, &ahead_lo[0], &ahead_hi[0]);
+            page_list(a.r[1], ps_ahead, a.page_cap, &ahead_lo[1], &ahead_hi[1]);
+        }
+    };
+    if constexpr (PAGED) {
+        if (w_lo < w_hi) {
+            ps_now = page_slot(w_lo);
+            fetch_ahead((w_lo | page_mask) + 1);
+        }
+    }
+
     // side-list cursors of K and V for this wave's tokens
     uint64_t cur[2] = {0, 0}, end[2] = {0, 0};
     if constexpr (PAGED) {
@@ -517,20 +536,27 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
         const int nvalid = static_cast<int>(w_hi - t0 < kTile ? w_hi - t0 : kTile);
         const int64_t t1 = t0 + kTile;
         const int nv1 = t1 < w_hi ? static_cast<int>(w_hi - t1 < kTile ? w_hi - t1 : kTile) : 0;
-        const int64_t tb1 = tile_row(nv1 > 0 ? t1 : w_lo);
+        // paged: when the next tile starts a page, its slot and side lists
+        // are the ones loaded a page ahead; then the page after is requested
+        const bool newpage = PAGED && nv1 > 0 && (t1 & page_mask) == 0;
+        uint64_t nlo[2] = {0, 0}, nhi[2] = {0, 0};
+        int64_t tb1;
+        if constexpr (PAGED) {
+            if (newpage) {
+                ps_now = ps_ahead;
+                for (int r = 0; r < 2; ++r) {
+                    nlo[r] = ahead_lo[r];
+                    nhi[r] = ahead_hi[r];
+                }
+                fetch_ahead(t1 + (page_mask + 1));
+            }
+            tb1 = (ps_now << a.log2_page) + ((nv1 > 0 ? t1 : w_lo) & page_mask);
+        } else {
+            tb1 = tile_row(nv1 > 0 ? t1 : w_lo);
+        }
         load_tile(0, tb1, nv1, nxt_t[0]);
         load_tile(1, tb1, nv1, nxt_t[1]);
         const uint32_t plo = static_cast<uint32_t>((PAGED ? (t0 & page_mask) : start + t0) * CPT);
-        // paged: the side lists of the page the next tile starts
-        const bool newpage = PAGED && nv1 > 0 && (t1 & page_mask) == 0;
-        uint64_t nlo[2] = {0, 0}, nhi[2] = {0, 0};
-        if constexpr (PAGED) {
-            if (newpage) {
-                const int64_t ps = tb1 >> a.log2_page;
-                page_list(a.r[0], ps, a.page_cap, &nlo[0], &nhi[0]);
-                page_list(a.r[1], ps, a.page_cap, &nlo[1], &nhi[1]);
-            }
-        }
         decode_tile(0, cur_t[0], nvalid, tt, plo, newpage, nlo[0], nhi[0]);
         wave_sync();
 
