@@ -899,69 +899,138 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     if (threadIdx.x == 0) { *ncand = 0; *nunc = 0; *nout = 0; }
     __syncthreads();
 
-    // the one pass: 4 codes per 8-byte load (a batch is a whole number of
-    // token rows, so n is a multiple of 4), eight loads per thread in flight.
-    // Definite outliers: the 8 lanes holding one bitmask word (32 chunks)
-    // combine their nibbles and store the word (the mask is zeroed before the
-    // search and no other thread writes it in this pass), and when any of its
-    // 32 codes is flagged the 8 lanes write back their whole 64-byte line of
-    // codes with the flags set
+    // the one pass over the batch's codes, 4 codes per 8-byte load (a batch
+    // is a whole number of token rows, so n is a multiple of 32), eight loads
+    // per thread in flight, without per-code branches:
+    //  - definite outliers (code > hhi) are flagged with packed 16-bit
+    //    arithmetic; the 8 lanes holding one bitmask word (32 chunks) combine
+    //    their nibbles by DPP and, when any is set, store the word (the mask
+    //    is zeroed before the search and no other thread writes it here) and
+    //    write back their 64-byte line of codes with the flags set;
+    //  - loads holding a code of the median's bin or an undecided code (in
+    //    [hlo, hhi]), about 1% of them, are listed per wave in LDS (no
+    //    atomics: the wave's count is uniform) and visited in a second step.
     uint32_t *mrow = a.mask + bid * a.mask_words;
     uint32_t cnt = 0;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    constexpr int kWaves = kSelThreads / 64;
+    constexpr uint32_t kEntPerWave = kCand1Cap / kWaves;
+    // the lists use candv, which is free until the median step below
+    uint32_t *ent = reinterpret_cast<uint32_t *>(candv);
+    uint32_t went = 0;
+    uint2 *c4 = reinterpret_cast<uint2 *>(codes);
+    const int n4 = n >> 2;
     {
-        const int lane = threadIdx.x & 63;
-        uint2 *c4 = reinterpret_cast<uint2 *>(codes);
-        const int n4 = n >> 2;
+        const u16x2 v_hhi = {static_cast<uint16_t>(hhi), static_cast<uint16_t>(hhi)};
+        const u16x2 v_7fff = {0x7FFFu, 0x7FFFu};
+        const u16x2 v_cl = {static_cast<uint16_t>(cl), static_cast<uint16_t>(cl)};
+        const u16x2 v_hlo = {static_cast<uint16_t>(hlo), static_cast<uint16_t>(hlo)};
+        const uint32_t band_w = hhi - hlo;   // hlo <= hhi: vlo < vhi
+        const uint32_t wshift = 4u * static_cast<uint32_t>(lane & 7);
         constexpr int U = 8;
         for (int i0 = threadIdx.x; i0 - lane < n4; i0 += kSelThreads * U) {
             uint2 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int q = i0 + kSelThreads * u;
-                v[u] = q < n4 ? c4[q] : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+                v[u] = q < n4 ? c4[q] : make_uint2(0u, 0u);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int q = i0 + kSelThreads * u;
-                uint32_t nib = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (q >= n4) break;
-                    const uint32_t w = e < 2 ? v[u].x : v[u].y;
-                    const uint32_t c = (w >> (16 * (e & 1))) & 0xFFFFu;
-                    const int i = 4 * q + e;
-                    // positions (< 2^17) keep their code's low bits beside
-                    // them, so the later phases read no code back from HBM
-                    if ((c >> 4) == d1) {
-                        atomicAdd(&hist[c & 15u], 1u);
-                        if (keep) {
-                            const uint32_t slot = atomicAdd(ncand, 1u);
-                            if (slot < static_cast<uint32_t>(kCand1Cap))
-                                cand[slot] = (static_cast<uint32_t>(i) << 4) | (c & 15u);
-                        }
-                    }
-                    if (c > hhi) nib |= 1u << e;
-                    else if (c >= hlo) {
-                        const uint32_t slot = atomicAdd(nunc, 1u);
-                        if (slot < static_cast<uint32_t>(kUnc1Cap))
-                            unc[slot] = (static_cast<uint32_t>(i) << 15) | (c - hlo);
-                    }
-                }
+                const bool valid = q < n4;
+                const u16x2 wx = __builtin_bit_cast(u16x2, v[u].x);
+                const u16x2 wy = __builtin_bit_cast(u16x2, v[u].y);
+                // bit 15 of each halfword set iff its code exceeds hhi
+                const uint32_t fx = __builtin_bit_cast(uint32_t, __builtin_elementwise_add_sat(
+                                        __builtin_elementwise_sub_sat(wx, v_hhi), v_7fff)) & 0x80008000u;
+                const uint32_t fy = __builtin_bit_cast(uint32_t, __builtin_elementwise_add_sat(
+                                        __builtin_elementwise_sub_sat(wy, v_hhi), v_7fff)) & 0x80008000u;
+                const uint32_t t = (fx >> 15) | (fy >> 13);       // codes 0, 2 at bits 0, 2; 1, 3 at 16, 18
+                const uint32_t nib = (t | (t >> 15)) & 15u;
                 // q & 7 == lane & 7: lanes 8 j .. 8 j + 7 hold the word's 8 nibbles
-                uint32_t wv = nib << (4 * (lane & 7));
-                wv |= __shfl_xor(wv, 1);
-                wv |= __shfl_xor(wv, 2);
-                wv |= __shfl_xor(wv, 4);
-                if (wv != 0u && q < n4) {
+                uint32_t wv = nib << wshift;
+                wv |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(wv), 0xB1, 0xF, 0xF, false));
+                wv |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(wv), 0x4E, 0xF, 0xF, false));
+                wv |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(wv), 0x141, 0xF, 0xF, false));
+                if (wv != 0u) {   // a group is all valid or all invalid (n4 % 8 == 0)
                     if ((lane & 7) == 0) mrow[q >> 3] = wv;
                     cnt += static_cast<uint32_t>(__popc(nib));
-                    uint2 f = v[u];
-                    f.x |= ((nib & 1u) ? 0x8000u : 0u) | ((nib & 2u) ? 0x80000000u : 0u);
-                    f.y |= ((nib & 4u) ? 0x8000u : 0u) | ((nib & 8u) ? 0x80000000u : 0u);
-                    c4[q] = f;
+                    c4[q] = make_uint2(v[u].x | fx, v[u].y | fy);
+                }
+                // median's bin: (c - cl) mod 2^16 < 16; undecided: (c - hlo) mod 2^16 <= hhi - hlo
+                const u16x2 tm = __builtin_elementwise_min(wx - v_cl, wy - v_cl);
+                const u16x2 tb = __builtin_elementwise_min(wx - v_hlo, wy - v_hlo);
+                const bool listed = valid && (min(static_cast<uint32_t>(tm.x), static_cast<uint32_t>(tm.y)) < 16u ||
+                                              min(static_cast<uint32_t>(tb.x), static_cast<uint32_t>(tb.y)) <= band_w);
+                const uint64_t bal = __ballot(listed);
+                if (bal != 0u) {
+                    const uint32_t slot = went + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                                           __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
+                    if (listed && slot < kEntPerWave) ent[wave * kEntPerWave + slot] = static_cast<uint32_t>(q);
+                    went += static_cast<uint32_t>(__popcll(bal));
                 }
             }
         }
+    }
+    if (lane == 0) unc[kUnc1Cap - kWaves + wave] = went;   // the lists' lengths, read below
+    __syncthreads();
+    uint32_t wcnt[kWaves];
+    bool overflow = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        wcnt[w] = unc[kUnc1Cap - kWaves + w];
+        overflow |= wcnt[w] > kEntPerWave;
+    }
+    __syncthreads();
+
+    // second step: the codes of the listed loads (or, if a list overflowed,
+    // of the whole batch): the median bin's sub-histogram and candidates,
+    // and the undecided codes
+    auto visit = [&](int i, uint32_t c) {
+        // positions (< 2^17) keep their code's low bits beside them, so the
+        // later phases read no code back from HBM
+        if ((c >> 4) == d1) {
+            atomicAdd(&hist[c & 15u], 1u);
+            if (keep) {
+                const uint32_t slot = atomicAdd(ncand, 1u);
+                if (slot < static_cast<uint32_t>(kCand1Cap))
+                    cand[slot] = (static_cast<uint32_t>(i) << 4) | (c & 15u);
+            }
+        }
+        // (both when the median's bin starts at 0: then hlo = 0)
+        if (c >= hlo && c <= hhi) {
+            const uint32_t slot = atomicAdd(nunc, 1u);
+            if (slot < static_cast<uint32_t>(kUnc1Cap - kWaves))
+                unc[slot] = (static_cast<uint32_t>(i) << 15) | (c - hlo);
+        }
+    };
+    if (!overflow) {
+        uint32_t total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) total += wcnt[w];
+        for (uint32_t j0 = threadIdx.x; j0 < total; j0 += 4 * kSelThreads) {
+            int qs[4];
+            uint2 vs[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t j = j0 + r * kSelThreads, w = 0;
+                while (w + 1 < kWaves && j >= wcnt[w]) j -= wcnt[w++];
+                qs[r] = j0 + r * kSelThreads < total ? static_cast<int>(ent[w * kEntPerWave + j]) : -1;
+                vs[r] = qs[r] >= 0 ? c4[qs[r]] : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (qs[r] < 0) continue;
+                visit(4 * qs[r], vs[r].x & 0xFFFFu);
+                visit(4 * qs[r] + 1, vs[r].x >> 16);
+                visit(4 * qs[r] + 2, vs[r].y & 0xFFFFu);
+                visit(4 * qs[r] + 3, vs[r].y >> 16);
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < n; i += kSelThreads) visit(i, codes[i]);
     }
     __syncthreads();
     select_digit(hist, 16, k1, found, sh);
@@ -1022,7 +1091,7 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
         }
     };
     const uint32_t nu = *nunc;
-    if (nu <= static_cast<uint32_t>(kUnc1Cap)) {
+    if (nu <= static_cast<uint32_t>(kUnc1Cap - kSelThreads / 64)) {
         for (uint32_t j = threadIdx.x; j < nu; j += kSelThreads) {
             const int i = static_cast<int>(unc[j] >> 15);
             decide(i, hlo + (unc[j] & 0x7FFFu));
