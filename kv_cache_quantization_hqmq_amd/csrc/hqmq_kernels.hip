@@ -400,7 +400,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform (a scalar register), so the loop and the block-relative
+    // offsets below are scalar work
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int col = lane & 31;
     const int hh = lane >> 5;            // K block: 0 = hi parts, 1 = lo parts
     const int m_row = col & 3;
@@ -428,29 +430,31 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
 
     const f32x16 zero = {};
     const int wpg = (64 >> a.log2_cpt) * a.words;
-    const int p_tt = lane / a.words;
-    const int p_ww = lane - p_tt * a.words;
-    // block-relative buffer resources: the block's chunks [c_begin, c_end)
-    // start on a token row and number at most 8192, so offsets are 32-bit and
-    // the resources' sizes do the range checks (loads past the end read 0,
-    // stores there are dropped)
+    // buffer resources over the wave's current 64 chunks onward (rebuilt per
+    // step from uniform values, so scalar work): the block's chunks
+    // [c_begin, c_end) start on a token row and number at most 8192, so
+    // offsets are 32-bit and the resources' sizes do the range checks (loads
+    // past the end read 0, stores there are dropped)
     const uint32_t n = c_end > c_begin ? static_cast<uint32_t>(c_end - c_begin) : 0u;
     const uint32_t tok_lim = (n + static_cast<uint32_t>(a.cpt) - 1u) >> a.log2_cpt;   // token rows of the block
-    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void *>(static_cast<const void *>(static_cast<const uint2 *>(a.x) + slice * a.n_slice + c_begin)), 0,
-        static_cast<int>(n * 8u), kBufWord3);
-    const __amdgpu_buffer_rsrc_t hrs =
-        __builtin_amdgcn_make_buffer_rsrc(a.hnorm + slice * a.n_slice + c_begin, 0, static_cast<int>(n * 2u), kBufWord3);
-    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-        a.idx + (slice * a.tokens + (c_begin >> a.log2_cpt)) * a.words, 0,
-        static_cast<int>(tok_lim * static_cast<uint32_t>(a.words) * 4u), kBufWord3);
+    const uint2 *xb = static_cast<const uint2 *>(a.x) + slice * a.n_slice + c_begin;
+    uint16_t *hb = a.hnorm + slice * a.n_slice + c_begin;
+    uint32_t *wb = a.idx + (slice * a.tokens + (c_begin >> a.log2_cpt)) * a.words;
 
     for (uint32_t o0 = 64u * wave; o0 < n; o0 += 64u * 4u) {
+        const uint32_t r0 = o0 >> a.log2_cpt;   // the step's first token row
+        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void *>(static_cast<const void *>(xb + o0)), 0, static_cast<int>((n - o0) * 8u), kBufWord3);
+        const __amdgpu_buffer_rsrc_t hrs =
+            __builtin_amdgcn_make_buffer_rsrc(hb + o0, 0, static_cast<int>((n - o0) * 2u), kBufWord3);
+        const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+            wb + r0 * static_cast<uint32_t>(a.words), 0,
+            static_cast<int>((tok_lim - r0) * static_cast<uint32_t>(a.words) * 4u), kBufWord3);
         // B operands: chunk o0 + 32 b + col of both column blocks
         uint2 xr[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(xrs, static_cast<int>((o0 + 32u * b + col) * 8u), 0, 0);
+            const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(xrs, static_cast<int>((32u * b + col) * 8u), 0, 0);
             xr[b] = make_uint2(u[0], u[1]);
         }
         float bsc[2];
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
 
         const int pidx = primary_index(&sq[4 * s_best], v0, v1, v2, v3);
         const uint32_t code = s2 > 0.0f ? __umul24(24u, static_cast<uint32_t>(s_best)) + static_cast<uint32_t>(pidx) : 0u;
-        __builtin_amdgcn_raw_buffer_store_b16(hn, hrs, static_cast<int>(o * 2u), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(hn, hrs, lane * 2, 0, 0);
         if constexpr (MED) {
             if (valid) atomicAdd(&shist[hn >> 4], 1u);
         }
@@ -541,9 +545,8 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
         }
         wave_sync();
         if (lane < wpg) {
-            const uint32_t tok = (o0 >> a.log2_cpt) + static_cast<uint32_t>(p_tt);
-            __builtin_amdgcn_raw_buffer_store_b32(sword[wave][lane], wrs,
-                                                  static_cast<int>((tok * static_cast<uint32_t>(a.words) + static_cast<uint32_t>(p_ww)) * 4u), 0, 0);
+            // word lane % words of token row r0 + lane / words
+            __builtin_amdgcn_raw_buffer_store_b32(sword[wave][lane], wrs, lane * 4, 0, 0);
         }
         wave_sync();
     }
