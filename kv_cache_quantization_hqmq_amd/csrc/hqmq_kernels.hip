@@ -858,14 +858,20 @@ __global__ __launch_bounds__(kSelThreads) void med3_select_kernel(SelArgs a) {
 // undecided list overflows, one more pass decides the codes in [hlo, hhi].
 // A batch is a whole number of token rows (n a multiple of 4).
 constexpr int kSel1MaxChunks = 131072;
-constexpr int kCand1Cap = 3000;   // with the other LDS arrays: 4 blocks per CU
+constexpr int kCand1Cap = 3000;
 constexpr int kUnc1Cap = 2048;
+// listed loads whose 8 bytes the single-pass select keeps in LDS, per wave:
+// 12 KB of their own (with the other arrays 52.7 KB, 3 blocks per CU, which
+// the kernel's 74 VGPRs allow anyway) plus the histogram's bins 16..2047
+constexpr uint32_t kValPerWave = 192;
+constexpr uint32_t kHistVal = (2048 - 16) / 2 / (kSelThreads / 64);
 
 __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t cand[kCand1Cap];
     __shared__ float candv[kCand1Cap];
     __shared__ uint32_t unc[kUnc1Cap];
+    __shared__ uint2 lval[kSelThreads / 64 * kValPerWave];
     __shared__ uint32_t sh[kSelThreads / 64 + 6];
     uint32_t *found = sh + kSelThreads / 64 + 1;
     uint32_t *ncand = sh + kSelThreads / 64 + 3;
@@ -919,8 +925,12 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     const int wave = threadIdx.x >> 6;
     constexpr int kWaves = kSelThreads / 64;
     constexpr uint32_t kEntPerWave = kCand1Cap / kWaves;
-    // the lists use candv, which is free until the median step below
+    // the lists use candv, which is free until the median step below; the
+    // values of a wave's first kValPerWave listed loads are kept in lval, the
+    // next kHistVal in the histogram's bins 16.. (unused from here until the
+    // second step has read them), and later ones are re-read from memory
     uint32_t *ent = reinterpret_cast<uint32_t *>(candv);
+    uint2 *hval = reinterpret_cast<uint2 *>(hist + 16);
     uint32_t went = 0;
     uint2 *c4 = reinterpret_cast<uint2 *>(codes);
     const int n4 = n >> 2;
@@ -971,7 +981,11 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
                 if (bal != 0u) {
                     const uint32_t slot = went + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
                                                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
-                    if (listed && slot < kEntPerWave) ent[wave * kEntPerWave + slot] = static_cast<uint32_t>(q);
+                    if (listed && slot < kEntPerWave) {
+                        ent[wave * kEntPerWave + slot] = static_cast<uint32_t>(q);
+                        if (slot < kValPerWave) lval[wave * kValPerWave + slot] = v[u];
+                        else if (slot < kValPerWave + kHistVal) hval[wave * kHistVal + (slot - kValPerWave)] = v[u];
+                    }
                     went += static_cast<uint32_t>(__popcll(bal));
                 }
             }
@@ -1021,7 +1035,12 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
                 uint32_t j = j0 + r * kSelThreads, w = 0;
                 while (w + 1 < kWaves && j >= wcnt[w]) j -= wcnt[w++];
                 qs[r] = j0 + r * kSelThreads < total ? static_cast<int>(ent[w * kEntPerWave + j]) : -1;
-                vs[r] = qs[r] >= 0 ? c4[qs[r]] : make_uint2(0u, 0u);
+                vs[r] = make_uint2(0u, 0u);
+                if (qs[r] >= 0) {
+                    if (j < kValPerWave) vs[r] = lval[w * kValPerWave + j];
+                    else if (j < kValPerWave + kHistVal) vs[r] = hval[w * kHistVal + (j - kValPerWave)];
+                    else vs[r] = c4[qs[r]];
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {

@@ -168,6 +168,28 @@ def test_med3_many_chunks_at_the_threshold():
     assert rep["outliers"] > 0
 
 
+def test_med3_crowded_median_bin():
+    """One 131072-chunk batch whose median's code is shared by 2650 chunks at
+    random positions (norm 1; 64000 chunks of norm 0.5 below them, the rest of
+    norm 2 and 40 of norm 10 above): the single-pass select lists about 330
+    loads per wave, more than it keeps in LDS (319), so some of their bytes are
+    read again from memory, and the exact median is ranked among 2650 equal
+    values."""
+    T, D, B = 4096, 128, 4096
+    n = T * D // 4
+    rng = np.random.default_rng(17)
+    x = np.full((n, 4), 1.0, np.float16)                  # norm 2
+    idx = rng.permutation(n)
+    x[idx[:64000]] = np.float16(0.25)                      # norm 0.5
+    x[idx[64000:66650]] = np.float16(0.5)                  # norm 1: the median's code
+    x[idx[66650:66690]] = np.float16(5.0)                  # norm 10 > 3 x 1: outliers
+    xt = torch.from_numpy(x.reshape(1, 1, T, D)).cuda()
+    cb_host, cb = _cb(1, 1, 32)
+    desc = K.Desc.make(1, 1, T, D, 32, K.HQMQ_F16, B, 3.0)
+    rep, rec, _ = _check(desc, xt, cb_host, cb)
+    assert rep["outliers"] == 40
+
+
 def test_empty_inputs():
     cb_host, cb = _cb(1, 1, 8)
     for T in (0,):
