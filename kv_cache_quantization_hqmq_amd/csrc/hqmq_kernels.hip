@@ -909,7 +909,7 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     __syncthreads();
 
     // the one pass over the batch's codes, 4 codes per 8-byte load (a batch
-    // is a whole number of token rows, so n is a multiple of 32), eight loads
+    // is a whole number of token rows, so n is a multiple of 4), eight loads
     // per thread in flight, without per-code branches:
     //  - definite outliers (code > hhi) are flagged with packed 16-bit
     //    arithmetic; the 8 lanes holding one bitmask word (32 chunks) combine
@@ -967,10 +967,15 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
                 wv |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(wv), 0xB1, 0xF, 0xF, false));
                 wv |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(wv), 0x4E, 0xF, 0xF, false));
                 wv |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(wv), 0x141, 0xF, 0xF, false));
-                if (wv != 0u) {   // a group is all valid or all invalid (n4 % 8 == 0)
+                // a group's lanes past the batch's end (n4 need not be a
+                // multiple of 8) hold no codes: they write nothing; lane 8 j
+                // is valid whenever any lane of its group is
+                if (wv != 0u) {
                     if ((lane & 7) == 0) mrow[q >> 3] = wv;
-                    cnt += static_cast<uint32_t>(__popc(nib));
-                    c4[q] = make_uint2(v[u].x | fx, v[u].y | fy);
+                    if (valid) {
+                        cnt += static_cast<uint32_t>(__popc(nib));
+                        c4[q] = make_uint2(v[u].x | fx, v[u].y | fy);
+                    }
                 }
                 // median's bin: (c - cl) mod 2^16 < 16; undecided: (c - hlo) mod 2^16 <= hhi - hlo
                 const u16x2 tm = __builtin_elementwise_min(wx - v_cl, wy - v_cl);

@@ -190,6 +190,39 @@ def test_med3_crowded_median_bin():
     assert rep["outliers"] == 40
 
 
+def test_med3_select_writes_stay_inside_each_batch():
+    """Head dim 16 (4 chunks per token row) and batches of 3 tokens: every
+    batch ends inside a group of 8 code loads of the select, and each holds an
+    outlier, so a group with a flag is only partly inside its batch.  The
+    half-norm plane of the last slice is followed by sentinel chunks that must
+    survive the encode (a write past a batch's end lands there for the last
+    batch), and the records match the oracle."""
+    L, H, T, D, S, B = 2, 1, 37, 16, 8, 3
+    cpt = D // 4
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((L, H, T, cpt, 4)) * 0.1).astype(np.float16)
+    for l in range(L):
+        for t0 in range(0, T, B):
+            x[l, 0, t0, rng.integers(cpt)] = np.float16(4.0)   # one outlier per batch
+    xt = torch.from_numpy(x.reshape(L, H, T, D)).cuda()
+    cb_host, cb = _cb(L, H, S)
+    desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F16, B, 3.0)
+    rec = K.allocate_records(desc)
+    n = L * H * T * cpt
+    guard = torch.full((n + 256,), 0x5A5A, dtype=torch.int16, device="cuda")
+    rec.hnorm = guard[:n].view(L, H, T, cpt)
+    rec.c.hnorm = guard.data_ptr()
+    ws = K.workspace(desc)
+    K.hqmq_encode(desc, xt, cb, rec, ws, torch.cuda.current_stream().cuda_stream)
+    n_out = K.hqmq_encode_result(rec, torch.cuda.current_stream().cuda_stream)
+    y = K.decode(desc, rec, cb)
+    torch.cuda.synchronize()
+    assert torch.all(guard[n:] == 0x5A5A), "the select wrote past the last batch"
+    rep = G.compare(desc, xt, cb_host, rec, y)
+    print(dict(rep), flush=True)
+    assert n_out >= L * ((T + B - 1) // B)
+
+
 def test_empty_inputs():
     cb_host, cb = _cb(1, 1, 8)
     for T in (0,):
