@@ -98,6 +98,40 @@ def test_attend_empty_batch_and_zero_tokens():
     assert not out.any()
 
 
+def _guarded(t: torch.Tensor, pad_bytes: int = 4096):
+    nbytes = t.numel() * t.element_size()
+    buf = torch.full((nbytes + pad_bytes,), 0xA5, dtype=torch.uint8, device=t.device)
+    return buf[:nbytes].view(t.dtype).view(t.shape), buf, nbytes
+
+
+@pytest.mark.parametrize("norm", [K.HQMQ_NORM_F16, K.HQMQ_NORM_PACKED])
+def test_attend_writes_stay_inside_out_and_workspace(norm):
+    """The output and the split workspace sit at the front of buffers with a
+    patterned tail: after attention over ragged sequences the tails are
+    unchanged and the output equals that of a call with plain buffers."""
+    w = BASE.scaled(tokens=700)
+    desc = GC.desc_for(w, norm_format=norm)
+    recs, cbs = {}, {}
+    for role in (0, 1):
+        x = synth.generate(w, role, "cuda")
+        _, cbs[role] = GC.codebook(w, role)
+        recs[role] = K.encode(desc, x, cbs[role])
+    q = A.make_queries(3, 8, 128, 5)
+    s = torch.tensor([0, 100, 651], dtype=torch.int64, device="cuda")
+    n = torch.tensor([700, 333, 49], dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(128)
+    ref = K.attend(desc, 1, recs[0], cbs[0], recs[1], cbs[1], q, s, n, 700, scale)
+    a = K.AttnDesc.make(3, 4, 1, 700, scale)
+    ws, wbuf, wnb = _guarded(torch.empty((max(int(K.hqmq_attn_sizes(desc, a).workspace_bytes), 16),),
+                                         dtype=torch.uint8, device="cuda"))
+    out, obuf, onb = _guarded(torch.empty_like(ref))
+    got = K.attend(desc, 1, recs[0], cbs[0], recs[1], cbs[1], q, s, n, 700, scale, out=out, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.all(wbuf[wnb:] == 0xA5), "workspace written past its end"
+    assert torch.all(obuf[onb:] == 0xA5), "output written past its end"
+    assert torch.equal(got, ref)
+
+
 def test_attend_rejects_invalid_requests():
     w = BASE.scaled(tokens=256)
     desc = GC.desc_for(w)

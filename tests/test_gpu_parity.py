@@ -223,6 +223,55 @@ def test_med3_select_writes_stay_inside_each_batch():
     assert n_out >= L * ((T + B - 1) // B)
 
 
+def _guarded(t: torch.Tensor, pad_bytes: int = 4096):
+    """A tensor of t's shape and dtype at the front of a larger buffer whose
+    tail holds a byte pattern: writes past the tensor's end change the tail."""
+    nbytes = t.numel() * t.element_size()
+    buf = torch.full((nbytes + pad_bytes,), 0xA5, dtype=torch.uint8, device=t.device)
+    return buf[:nbytes].view(t.dtype).view(t.shape), buf, nbytes
+
+
+@pytest.mark.parametrize("L,H,T,D,S,dt,B,norm", [
+    (2, 3, 41, 16, 8, "f16", 3, "f16"),
+    (1, 2, 77, 64, 40, "f16", 5, "packed"),
+    (2, 1, 33, 16, 100, "f32", 7, "f16"),
+    (1, 1, 130, 128, 32, "f16", 64, "packed"),
+])
+def test_outputs_stay_inside_their_buffers(L, H, T, D, S, dt, B, norm):
+    """Every record plane, the side list, its offsets and the decoded tensor
+    sit at the front of buffers with a patterned tail: after encode and decode
+    on ragged shapes (small head dims, partial batches and token rows, packed
+    and binary16 norms, fp16 and fp32 input) every tail is unchanged and the
+    result matches the oracle."""
+    dtype = torch.float16 if dt == "f16" else torch.float32
+    x = _x((L, H, T, D), dtype, seed=T * 7 + S)
+    x[:, :, :, 5] *= 40                      # hot channel: outliers in every batch
+    cb_host, cb = _cb(L, H, S)
+    nf = K.HQMQ_NORM_PACKED if norm == "packed" else K.HQMQ_NORM_F16
+    desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F32 if dt == "f32" else K.HQMQ_F16, B, 3.0, nf)
+    rec = K.allocate_records(desc, K.hqmq_sizes(desc).max_outliers)
+    guards = []
+    for name, field in (("idx", "idx"), ("hnorm", "hnorm"), ("batch_offsets", "batch_offsets"),
+                        ("out_pos", "out_pos"), ("out_val", "out_val")):
+        t = getattr(rec, name)
+        g, buf, nb = _guarded(t)
+        setattr(rec, name, g)
+        setattr(rec.c, field, buf.data_ptr())
+        guards.append((name, buf, nb))
+    ws = K.workspace(desc)
+    st = torch.cuda.current_stream().cuda_stream
+    K.hqmq_encode(desc, x, cb, rec, ws, st)
+    rec.n_outliers = K.hqmq_encode_result(rec, st)
+    y, ybuf, ynb = _guarded(torch.empty(desc.shape, dtype=dtype, device="cuda"))
+    K.hqmq_decode(desc, rec, cb, y, st)
+    torch.cuda.synchronize()
+    for name, buf, nb in guards + [("y", ybuf, ynb)]:
+        assert torch.all(buf[nb:] == 0xA5), f"{name}: written past its end"
+    rep = G.compare(desc, x, cb_host, rec, y)
+    print(dict(rep), flush=True)
+    assert rep["outliers"] > 0
+
+
 def test_empty_inputs():
     cb_host, cb = _cb(1, 1, 8)
     for T in (0,):
