@@ -135,10 +135,30 @@ class Replay:
     page_lists: dict      # sequence -> its pages in order
     lengths: dict         # sequence -> tokens
     statuses: list
+    guards: list = field(default_factory=list)   # (name, buffer, used bytes) when guarded
 
 
-def replay(sc: Scenario) -> Replay:
-    """Run every call on the GPU (K and V pools) and in the model."""
+GUARD_BYTE = 0xA5
+
+
+def _guard_pool(pool: K.Pool, role: int, guards: list) -> None:
+    """Move every plane of ``pool`` to the front of a buffer whose tail holds
+    GUARD_BYTE (page counts start at zero as in a fresh pool)."""
+    for name in ("idx", "hnorm", "side_count", "side_pos", "side_val"):
+        t = getattr(pool, name)
+        nbytes = t.numel() * t.element_size()
+        buf = torch.full((nbytes + 4096,), GUARD_BYTE, dtype=torch.uint8, device=t.device)
+        view = buf[:nbytes].view(t.dtype).view(t.shape)
+        if name == "side_count":
+            view.zero_()
+        setattr(pool, name, view)
+        setattr(pool.c, name, buf.data_ptr())
+        guards.append((f"role {role} {name}", buf, nbytes))
+
+
+def replay(sc: Scenario, guard: bool = False) -> Replay:
+    """Run every call on the GPU (K and V pools) and in the model.  guard:
+    the pools' planes are followed by patterned bytes (see ``_guard_pool``)."""
     pdesc = _pdesc(sc)
     desc0 = _desc(sc, 0)
     rng = np.random.default_rng(sc.seed)
@@ -151,6 +171,10 @@ def replay(sc: Scenario) -> Replay:
         pools[role] = K.allocate_pool(desc0, pdesc)
         models[role] = PoolModel(sc, cbh[role])
     statuses = []
+    guards = []
+    if guard:
+        for role in (0, 1):
+            _guard_pool(pools[role], role, guards)
     for i, call in enumerate(sc.calls):
         slots = []
         for seq, n in call:
@@ -175,7 +199,7 @@ def replay(sc: Scenario) -> Replay:
             models[role].apply(x.float().cpu().numpy(), slots)
             st.append(status.cpu().numpy().tolist())
         statuses.append(st)
-    return Replay(sc, desc0, pdesc, pools, cbh, cbd, models, page_lists, lengths, statuses)
+    return Replay(sc, desc0, pdesc, pools, cbh, cbd, models, page_lists, lengths, statuses, guards)
 
 
 def compare_records(rp: Replay) -> dict:

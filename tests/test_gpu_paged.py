@@ -31,6 +31,17 @@ def test_append_prefill_and_decode_steps():
     assert rep["entries"] > 0
 
 
+def test_pool_writes_stay_inside_their_planes():
+    """The default scenario on pools whose planes are followed by patterned
+    bytes: the appends leave every tail unchanged and the records match the
+    model."""
+    rp = PC.replay(PC.Scenario(seed=3), guard=True)
+    torch.cuda.synchronize()
+    for name, buf, nbytes in rp.guards:
+        assert torch.all(buf[nbytes:] == PC.GUARD_BYTE), f"{name}: written past its end"
+    _records_ok(rp, "guarded")
+
+
 def test_append_drops_entries_past_page_capacity():
     rp = PC.replay(PC.Scenario(page_capacity=3, seed=1, outlier_channels=2))
     _records_ok(rp, "capacity 3")
