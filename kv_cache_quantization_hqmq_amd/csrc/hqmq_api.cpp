@@ -146,7 +146,7 @@ float double_f16(float q) {
 
 // Validation and split plan of a decode-step attention request: enough
 // (sequence, head, split) blocks to fill the chip several times, splits of a
-// multiple of 64 tokens (4 waves x 16-token tiles).
+// multiple of 128 tokens (8 waves x 16-token tiles).
 static int attn_plan(const hqmq_desc *d, const hqmq::Geometry &g, const hqmq_attn_desc *a, int32_t *nsplit,
               int32_t *stok) {
     if (!a) return HQMQ_EINVAL;
@@ -159,11 +159,11 @@ static int attn_plan(const hqmq_desc *d, const hqmq::Geometry &g, const hqmq_att
     if (hqmq::attend_lds_bytes(static_cast<int>(d->head_dim), g.S) > 160 * 1024) return HQMQ_ENOTSUP;
     if (d->kv_heads > 4096) return HQMQ_ENOTSUP;
     const int64_t pairs = std::max<int64_t>(1, static_cast<int64_t>(a->batch) * d->kv_heads);
-    int64_t want = (2048 + pairs - 1) / pairs;
-    const int64_t most = std::max<int64_t>(1, (static_cast<int64_t>(a->max_len) + 63) / 64);
+    int64_t want = (1024 + pairs - 1) / pairs;
+    const int64_t most = std::max<int64_t>(1, (static_cast<int64_t>(a->max_len) + 127) / 128);
     want = std::min(std::max<int64_t>(want, 1), most);
-    int64_t st = ((a->max_len + want - 1) / want + 63) / 64 * 64;
-    if (st < 64) st = 64;
+    int64_t st = ((a->max_len + want - 1) / want + 127) / 128 * 128;
+    if (st < 128) st = 128;
     const int64_t ns = std::max<int64_t>(1, (a->max_len + st - 1) / st);
     if (pairs * ns > (int64_t{1} << 31) - 1) return HQMQ_ENOTSUP;
     *nsplit = static_cast<int32_t>(ns);

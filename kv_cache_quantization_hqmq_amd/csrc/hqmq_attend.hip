@@ -16,7 +16,7 @@
 // compact code; Med3x outlier chunks their side-list values).
 //
 // Layout of the work.  A block takes one (sequence, KV head, token split);
-// each of its 4 waves walks a contiguous quarter of the split in tiles of 16
+// each of its 8 waves walks a contiguous eighth of the split in tiles of 16
 // tokens: it decodes the tile's K and V chunks from the records into LDS
 // (the same arithmetic as the decode kernel, so the values are bit-identical),
 // computes the 16 x 16 score tile S[token][query head] with
@@ -34,7 +34,9 @@
 namespace hqmq {
 namespace {
 
-constexpr int kAttThreads = 256;
+// 8 waves per block share the block's codeword tables: 66.6 KB of LDS, two
+// blocks (16 waves) per CU, which the kernel's 128-VGPR budget allows
+constexpr int kAttThreads = 512;
 constexpr int kAttWaves = kAttThreads / 64;
 constexpr int kTile = 16;            // tokens per wave step (one MFMA tile)
 // Softmax weights enter the value sum as binary16 2^(s - m + kPScale), m a
@@ -161,7 +163,8 @@ struct TileRegs {
 };
 
 template <int D, bool TABLE, int BITS, bool NPACK, bool PAGED>
-__global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
+__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void attend_split_kernel(AttArgs a) {
     using Sh = AttShape<D>;
     constexpr int CPT = Sh::CPT, CPL = Sh::CPL, KB = Sh::KB, NU = Sh::NU, ROWB = Sh::ROWB, TILEB = Sh::TILEB;
 
@@ -452,30 +455,35 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
 #pragma unroll
             for (int j = 0; j < CPL; ++j) code[j] = code[j] < kmax ? code[j] : kmax;
         }
-        f32x4 cw[CPL];   // TABLE: 2 (a_p * q_s); else a_p * q_s
+        // two halves of the lane's chunks: lookups, products and stores of
+        // one half at a time keep fewer values live
+        uint2 *dp = reinterpret_cast<uint2 *>(dst + ti * ROWB + c0 * 8);
+        constexpr int HC = CPL >= 8 ? CPL / 2 : CPL;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            if constexpr (TABLE) {
-                cw[j] = tab[r * ntab + code[j]];
-            } else {
-                const int s = static_cast<int>(code[j] / 24u);
-                const f32x4 qs = tab[r * ntab + s];
-                const float qa[4] = {qs[0], qs[1], qs[2], qs[3]};
-                cw[j] = codeword_f32(qa, static_cast<int>(code[j]) - 24 * s);
+        for (int j0 = 0; j0 < CPL; j0 += HC) {
+            f32x4 cw[HC];   // TABLE: 2 (a_p * q_s); else a_p * q_s
+#pragma unroll
+            for (int jj = 0; jj < HC; ++jj) {
+                const int j = j0 + jj;
+                if constexpr (TABLE) {
+                    cw[jj] = tab[r * ntab + code[j]];
+                } else {
+                    const int s = static_cast<int>(code[j] / 24u);
+                    const f32x4 qs = tab[r * ntab + s];
+                    const float qa[4] = {qs[0], qs[1], qs[2], qs[3]};
+                    cw[jj] = codeword_f32(qa, static_cast<int>(code[j]) - 24 * s);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < HC; ++jj) {
+                const int j = j0 + jj;
+                const float hv = f16_bits_to_f32(static_cast<uint16_t>((hw[j >> 1] >> (16 * (j & 1))) & 0x7FFFu));
+                const f32x4 y = TABLE ? hv * cw[jj] : (2.0f * hv) * cw[jj];
+                const f16x4 hy = {static_cast<_Float16>(y[0]), static_cast<_Float16>(y[1]), static_cast<_Float16>(y[2]),
+                                  static_cast<_Float16>(y[3])};
+                dp[j] = __builtin_bit_cast(uint2, hy);
             }
         }
-        uint2 val[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const float hv = f16_bits_to_f32(static_cast<uint16_t>((hw[j >> 1] >> (16 * (j & 1))) & 0x7FFFu));
-            const f32x4 y = TABLE ? hv * cw[j] : (2.0f * hv) * cw[j];
-            const f16x4 hy = {static_cast<_Float16>(y[0]), static_cast<_Float16>(y[1]), static_cast<_Float16>(y[2]),
-                              static_cast<_Float16>(y[3])};
-            val[j] = __builtin_bit_cast(uint2, hy);
-        }
-        uint2 *dp = reinterpret_cast<uint2 *>(dst + ti * ROWB + c0 * 8);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) dp[j] = val[j];
         // Outlier chunks take their side-list values.  Lane i holds entry
         // cur + i (value and position); the list is sorted by position and cur
         // is its first entry at or after this tile, so the tile's entries are
@@ -562,11 +570,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
 
         // S[token 4 g + i][head n]: A[m = token n][k = 4 g + j] = K[token n][16 kb + 4 g + j]
         f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-        uint2 ka[KB];   // all reads first, so their latencies overlap
+        constexpr int KH = KB >= 8 ? KB / 2 : KB;   // reads in two halves: fewer live registers
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) ka[kb] = *reinterpret_cast<const uint2 *>(tt + n * ROWB + (4 * kb + g) * 8);
+        for (int k0 = 0; k0 < KB; k0 += KH) {
+            uint2 ka[KH];   // the half's reads first, so their latencies overlap
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ka[kb]), qv[kb], s, 0, 0, 0);
+            for (int kk = 0; kk < KH; ++kk)
+                ka[kk] = *reinterpret_cast<const uint2 *>(tt + n * ROWB + (4 * (k0 + kk) + g) * 8);
+#pragma unroll
+            for (int kk = 0; kk < KH; ++kk)
+                s = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, ka[kk]), qv[k0 + kk], s, 0, 0, 0);
+        }
         float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -600,20 +614,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_split_kernel(AttArgs a) {
 
         // O^T += V^T P^T: A[m = n][k = 4 g + j] = V[token 4 g + j][dim 4 (n + 16 u) + c],
         // B[k = 4 g + j][n] = P[head n][token 4 g + j] (this lane's own weights)
-        uint2 vv[4][NU];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int u = 0; u < NU; ++u)
-                vv[j][u] = *reinterpret_cast<const uint2 *>(tt + (4 * g + j) * ROWB + (n + 16 * u) * 8);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
+            uint2 vv[4][1];   // one chunk group at a time: fewer live registers
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vv[j][0] = *reinterpret_cast<const uint2 *>(tt + (4 * g + j) * ROWB + (n + 16 * u) * 8);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 // halves c of tokens 4 g + 0..3: byte selectors of v_perm_b32
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-                const uint32_t x0 = c < 2 ? vv[0][u].x : vv[0][u].y, x1 = c < 2 ? vv[1][u].x : vv[1][u].y;
-                const uint32_t x2 = c < 2 ? vv[2][u].x : vv[2][u].y, x3 = c < 2 ? vv[3][u].x : vv[3][u].y;
+                const uint32_t x0 = c < 2 ? vv[0][0].x : vv[0][0].y, x1 = c < 2 ? vv[1][0].x : vv[1][0].y;
+                const uint32_t x2 = c < 2 ? vv[2][0].x : vv[2][0].y, x3 = c < 2 ? vv[3][0].x : vv[3][0].y;
                 const uint2 pk = make_uint2(__builtin_amdgcn_perm(x1, x0, sel), __builtin_amdgcn_perm(x3, x2, sel));
                 o[4 * u + c] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, pk), ph, o[4 * u + c], 0, 0, 0);
             }
