@@ -236,7 +236,7 @@ typedef struct hqmq_attn_desc {
 typedef struct hqmq_attn_sizes_t {
     uint64_t workspace_bytes;   /* batch * kv_heads * group * splits * (head_dim + 2) * 4 */
     int32_t splits;             /* token splits per sequence */
-    int32_t split_tokens;       /* tokens per split, a multiple of 64 */
+    int32_t split_tokens;       /* tokens per split, a multiple of 128 */
 } hqmq_attn_sizes_t;
 
 /* Workspace size and split plan of hqmq_attend for cache d and request a.
