@@ -193,7 +193,7 @@ def test_attn_plan_covers_every_token():
     d = K.Desc.make(**_CACHE)
     for batch, max_len in [(32, 32768), (1, 1), (3, 1000), (1, 200000), (64, 4096), (5, 0)]:
         s = B.hqmq_attn_sizes(d, _attn(batch=batch, max_len=max_len))
-        assert s.split_tokens % 64 == 0 and s.split_tokens >= 64
+        assert s.split_tokens % 128 == 0 and s.split_tokens >= 128
         assert s.splits >= 1 and s.splits * s.split_tokens >= max_len
         assert (s.splits - 1) * s.split_tokens < max(max_len, 1)
         assert s.workspace_bytes == batch * 8 * 4 * s.splits * (128 + 2) * 4
