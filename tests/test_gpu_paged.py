@@ -101,7 +101,7 @@ def test_clear_empties_listed_pages_only():
     assert torch.equal(after[:, :, ~mask], before[:, :, ~mask])
 
 
-@pytest.mark.parametrize("group", [4, 1])
+@pytest.mark.parametrize("group", [4, 1, 16])
 def test_attend_paged(group):
     rp = PC.replay(PC.Scenario(seed=7))
     _records_ok(rp, "attend records")
