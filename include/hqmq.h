@@ -53,6 +53,15 @@
  * output type, h the binary16 half-norm (packed format: the value the code
  * stands for); outlier chunk y = its side-list values.
  *
+ * Codebook values.  Every call that takes a codebook (encode, decode,
+ * attend, append, attend_paged) uses each fp32 value q on the
+ * double-binary16 grid: q' = hi + lo with hi = binary16(q) and
+ * lo = binary16(q - hi), both rounded to nearest even (q - hi and hi + lo
+ * are exact in fp32; |q' - q| <= 2^-22 |q|).  The search splits each value
+ * into exactly these two binary16 parts for the f16 matrix cores, so a
+ * codebook off that grid encodes, decodes and attends exactly like its
+ * rounded copy.  hqmq_make_codebook returns values already on the grid.
+ *
  * Threading: every entry point is stateless and re-entrant; device work is
  * enqueued on the caller's stream and nothing is allocated.  Calls on
  * different streams that share output buffers race.
@@ -116,7 +125,8 @@ typedef struct hqmq_sizes_t {
     int32_t words_per_token;    /* ceil(b * head_dim / 4 / 32) */
     int64_t chunks;             /* layers * kv_heads * tokens * head_dim / 4 */
     int64_t batches;            /* Med3x batches (0 when Med3x is off) */
-    int64_t max_outliers;       /* sum over batches of floor(n_batch / 2) */
+    int64_t max_outliers;       /* sum over batches of floor(n_batch / 2) (every
+                                   chunk when fl(med_C * med_C) < 1) */
     uint64_t input_bytes;       /* x (and y) */
     uint64_t idx_bytes;
     uint64_t hnorm_bytes;       /* chunks * 2 (binary16), or idx_bytes (packed) */
@@ -155,16 +165,18 @@ int hqmq_sizes(const hqmq_desc *d, hqmq_sizes_t *out);
  * HOST buffer out_host.  Uniform on S^3: Philox4x64-10 (Salmon et al., SC'11)
  * keyed (seed, layer << 32 | head << 8 | role), candidate j from counter
  * (j, 0, 0, 0), coordinates v_m = (2 (w_m >> 40) - 2^24 + 1) 2^-24, kept when
- * sum v^2 <= 1, q = v / sqrt(sum v^2) in fp64 rounded to fp32.  Bit-identical
- * on every IEEE-754 host.  Host only.
+ * sum v^2 <= 1, q = v / sqrt(sum v^2) in fp64, rounded to fp32 and then to
+ * the double-binary16 grid described above (q = hi + lo, 22 significant
+ * bits), so that the stored values are the ones every kernel uses.
+ * Bit-identical on every IEEE-754 host.  Host only.
  * Errors: HQMQ_EINVAL if out_host is NULL, layers or kv_heads < 0 or
  * >= 2^24, role not 0/1, or S outside [1, 1024]. */
 int hqmq_make_codebook(uint64_t seed, int32_t layers, int32_t kv_heads, int32_t role,
                        int32_t S, float *out_host);
 
 /* Encode x (device, [layers][kv_heads][tokens][head_dim] in d->dtype,
- * 16-byte aligned) with codebook (device, [layers][kv_heads][S][4] fp32)
- * into enc.  Steps: per chunk the fp32 norm and its binary16 half-norm code,
+ * 16-byte aligned) with codebook (device, [layers][kv_heads][S][4] fp32,
+ * used on the double-binary16 grid) into enc.  Steps: per chunk the fp32 norm and its binary16 half-norm code,
  * the nearest of the 24 S codewords <x, q_p q_s> (gist.science Methodologie
  * 1; the identity <x, q_p q_s> = <conj(q_p) x, q_s> of the isometry argument,
  * abstract), then, when Med3x is on, the exact lower median of s2 per batch,
@@ -202,8 +214,9 @@ int hqmq_encode_result(const hqmq_enc *enc, hipStream_t stream, uint64_t *n_outl
  * rounded to nearest even; outlier chunks take their side-list values (the decoder
  * the pages run before or inside attention: gist.science "Memory en
  * Latentie").  enc must come from hqmq_encode with the same descriptor and
- * codebook; after a side-list overflow the chunks whose entries were dropped
- * decode to their bulk value.  Asynchronous on stream.
+ * codebook (used on the double-binary16 grid, as in the encode); after a
+ * side-list overflow the chunks whose entries were dropped decode to their
+ * bulk value.  Asynchronous on stream.
  * Errors: HQMQ_EINVAL, HQMQ_EHIP. */
 int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, void *y,
                 hipStream_t stream);
@@ -247,7 +260,7 @@ int hqmq_attn_sizes(const hqmq_desc *d, const hqmq_attn_desc *a, hqmq_attn_sizes
 
 /* Attention of one decode step over layer a->layer of the cache encoded as
  * k (role K, codebook_k) and v (role V, codebook_v), both from hqmq_encode
- * with descriptor d.  Device arrays: q [batch][kv_heads * group][head_dim]
+ * with descriptor d (codebooks used on the double-binary16 grid).  Device arrays: q [batch][kv_heads * group][head_dim]
  * binary16 (8-byte aligned); seq_start [batch] int64 and seq_len [batch]
  * int32 (token ranges within each slice; a range is clipped to the slice
  * and to max_len, a negative length counts as 0); out [batch][kv_heads *

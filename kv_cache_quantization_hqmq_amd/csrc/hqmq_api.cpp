@@ -267,9 +267,13 @@ int hqmq_sizes(const hqmq_desc *d, hqmq_sizes_t *out) {
     out->batches = g.slices * g.batches_per_slice;
     int64_t mo = 0;
     if (g.batch_chunks > 0) {
+        // s2 > fl(fl(C C) med) leaves at most floor(n / 2) chunks of a batch
+        // above its lower median when fl(C C) >= 1; with a smaller multiplier
+        // the median itself and everything above it can be outliers
         const int64_t full = g.n_slice / g.batch_chunks;
         const int64_t tail = g.n_slice - full * g.batch_chunks;
-        mo = g.slices * (full * (g.batch_chunks / 2) + tail / 2);
+        const float cc = g.med_C * g.med_C;
+        mo = cc >= 1.0f ? g.slices * (full * (g.batch_chunks / 2) + tail / 2) : g.slices * g.n_slice;
     }
     out->max_outliers = mo;
     out->input_bytes = static_cast<uint64_t>(out->chunks) * 4 * (g.f32 ? 4 : 2);

@@ -700,7 +700,8 @@ __device__ float kth_s2(const SelArgs &a, const uint16_t *codes, int64_t gbase, 
             }
         } else {
             for (int64_t i = threadIdx.x; i < n; i += kSelThreads) {
-                if (codes[i] != hsel) continue;
+                // (a flag set by the single-pass select is not part of the code)
+                if ((codes[i] & 0x7FFFu) != hsel) continue;
                 const uint32_t key = __float_as_uint(chunk_s2(a, gbase + i));
                 if ((key >> above) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
             }
@@ -796,7 +797,7 @@ __global__ __launch_bounds__(kSelThreads) void med3_select_kernel(SelArgs a) {
         __syncthreads();
         for (uint32_t i = threadIdx.x; i < m1; i += kSelThreads) {
             const uint32_t off = min(cand[i], static_cast<uint32_t>(n - 1));
-            if (codes[off] == hmed) {
+            if ((codes[off] & 0x7FFFu) == hmed) {
                 const uint32_t slot = atomicAdd(&sh[kSelThreads / 64 + 3], 1u);
                 if (slot < static_cast<uint32_t>(kCandCap)) candv[slot] = chunk_s2(a, gbase + off);
             }
@@ -1011,6 +1012,10 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     // of the whole batch): the median bin's sub-histogram and candidates,
     // and the undecided codes
     auto visit = [&](int i, uint32_t c) {
+        // a code re-read from memory may carry the flag the pass above set
+        // (with C < 1 even a code of the median's bin exceeds hhi): the
+        // median and the undecided band are about the code without it
+        c &= 0x7FFFu;
         // positions (< 2^17) keep their code's low bits beside them, so the
         // later phases read no code back from HBM
         if ((c >> 4) == d1) {
@@ -1021,7 +1026,8 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
                     cand[slot] = (static_cast<uint32_t>(i) << 4) | (c & 15u);
             }
         }
-        // (both when the median's bin starts at 0: then hlo = 0)
+        // (both when the median's bin starts at 0: then hlo = 0; a code above
+        // hhi is a definite outlier, flagged and counted by the pass)
         if (c >= hlo && c <= hhi) {
             const uint32_t slot = atomicAdd(nunc, 1u);
             if (slot < static_cast<uint32_t>(kUnc1Cap - kWaves))
@@ -1065,8 +1071,8 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     const uint32_t k2 = found[1];
     __syncthreads();
 
-    // exact median among the chunks with code hmed (never flagged: a code
-    // in the median's bin is at most hhi)
+    // exact median among the chunks with code hmed (their positions and
+    // unflagged low code bits are in cand)
     float med;
     if (keep) {
         if (threadIdx.x == 0) *ncand = 0;

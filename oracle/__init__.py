@@ -111,6 +111,19 @@ def _configure(L):
     L.or_compact_to_h16.argtypes = [ctypes.c_uint32, ctypes.c_int]
     L.or_compact_to_h16.restype = ctypes.c_uint16
     L.or_compact_norms.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int, _u32p]
+    L.or_exact_m.argtypes = [ctypes.c_int]
+    L.or_exact_m.restype = ctypes.c_int
+    L.or_exact_level_pattern.argtypes = [ctypes.c_uint32, ctypes.c_int]
+    L.or_exact_level_pattern.restype = ctypes.c_uint32
+    L.or_exact_norm.argtypes = [ctypes.c_uint16, ctypes.c_int]
+    L.or_exact_norm.restype = ctypes.c_uint32
+    L.or_exact_norm_to_h16.argtypes = [ctypes.c_uint32, ctypes.c_int]
+    L.or_exact_norm_to_h16.restype = ctypes.c_uint16
+    L.or_exact_norms.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int, _u32p]
+    L.or_exact_group_words.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.or_exact_group_words.restype = ctypes.c_int
+    L.or_pack_exact_group.argtypes = [_i32p, _u32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u32p]
+    L.or_unpack_exact_group.argtypes = [_u32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _u32p]
     L.or_attend.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int, _f64p, ctypes.c_int,
                             ctypes.c_double, _f64p]
     return L
@@ -246,7 +259,8 @@ def encode_range(x, q, t0: int = 0, B: int = 0, C: float = 3.0) -> dict:
     hnorm = np.empty(n, np.uint16)
     gap = np.empty(n, np.float64)
     s2 = np.empty(n, np.float32)
-    cap = n // 2 + 1
+    # at most floor(n / 2) outliers per batch when fl(C C) >= 1, every chunk otherwise
+    cap = n // 2 + 1 if np.float32(C) * np.float32(C) >= np.float32(1.0) else n
     side_pos = np.empty(cap, np.uint32)
     side_val = np.empty((cap, 4), np.uint16)
     nb = (T + B - 1) // B if B > 0 else 0
@@ -300,6 +314,77 @@ def compact_to_h16(codes, b: int) -> np.ndarray:
     """Half-norm records (binary16 pattern, or the flag) of compact codes."""
     c = np.asarray(codes, dtype=np.uint32).ravel()
     return np.array([lib().or_compact_to_h16(int(v), int(b)) for v in c], np.uint16).reshape(np.shape(codes))
+
+
+EXACT_ROWS = 4   # token rows per exact-rate group
+
+
+def exact_m(S: int) -> int:
+    """m with 24 S = 3 2^m (-1 when S is not a power of two up to 1024)."""
+    return int(lib().or_exact_m(int(S)))
+
+
+def exact_level_pattern(n: int, S: int) -> int:
+    return int(lib().or_exact_level_pattern(int(n), int(S)))
+
+
+def exact_norm(h16: int, S: int) -> int:
+    return int(lib().or_exact_norm(int(h16), int(S)))
+
+
+def exact_norms(h16, S: int) -> np.ndarray:
+    """Exact-rate norm codes (24 S levels) of binary16 half-norm records."""
+    h = np.ascontiguousarray(h16, dtype=np.uint16)
+    out = np.empty(h.shape, np.uint32)
+    lib().or_exact_norms(_p(h, _u16p), h.size, int(S), _p(out, _u32p))
+    return out
+
+
+def exact_norm_to_h16(codes, S: int) -> np.ndarray:
+    """Half-norm records (binary16 pattern, or the flag) of exact-rate norm codes."""
+    c = np.asarray(codes, dtype=np.uint32).ravel()
+    return np.array([lib().or_exact_norm_to_h16(int(v), int(S)) for v in c],
+                    np.uint16).reshape(np.shape(codes))
+
+
+def exact_group_words(cpt: int, S: int) -> int:
+    return int(lib().or_exact_group_words(int(cpt), int(S)))
+
+
+def pack_exact(codes, ncodes, S: int) -> np.ndarray:
+    """Exact-rate records of T token rows: codes, ncodes [T, cpt] ->
+    [ceil(T / 4), group words] u32 (one group per 4 rows, the last one
+    zero-filled past row T)."""
+    codes = np.ascontiguousarray(codes, dtype=np.int32)
+    ncodes = np.ascontiguousarray(ncodes, dtype=np.uint32)
+    T, cpt = codes.shape
+    gw = exact_group_words(cpt, S)
+    ng = (T + EXACT_ROWS - 1) // EXACT_ROWS
+    out = np.zeros((ng, gw), np.uint32)
+    for g in range(ng):
+        rows = min(EXACT_ROWS, T - EXACT_ROWS * g)
+        c = np.ascontiguousarray(codes[EXACT_ROWS * g:EXACT_ROWS * g + rows])
+        n = np.ascontiguousarray(ncodes[EXACT_ROWS * g:EXACT_ROWS * g + rows])
+        w = np.zeros(gw, np.uint32)
+        lib().or_pack_exact_group(_p(c, _i32p), _p(n, _u32p), rows, cpt, int(S), _p(w, _u32p))
+        out[g] = w
+    return out
+
+
+def unpack_exact(words, T: int, cpt: int, S: int):
+    """Inverse of pack_exact: (codes, ncodes), each [T, cpt]."""
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    codes = np.zeros((T, cpt), np.int32)
+    ncodes = np.zeros((T, cpt), np.uint32)
+    for g in range((T + EXACT_ROWS - 1) // EXACT_ROWS):
+        rows = min(EXACT_ROWS, T - EXACT_ROWS * g)
+        w = np.ascontiguousarray(words[g])
+        c = np.zeros((rows, cpt), np.int32)
+        n = np.zeros((rows, cpt), np.uint32)
+        lib().or_unpack_exact_group(_p(w, _u32p), rows, cpt, int(S), _p(c, _i32p), _p(n, _u32p))
+        codes[EXACT_ROWS * g:EXACT_ROWS * g + rows] = c
+        ncodes[EXACT_ROWS * g:EXACT_ROWS * g + rows] = n
+    return codes, ncodes
 
 
 def attend(k, v, q, scale: float) -> np.ndarray:

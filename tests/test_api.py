@@ -171,6 +171,18 @@ def test_codebook_matches_oracle_bit_for_bit(seed, L, H, role, S):
     assert a.tobytes() == b.tobytes()
 
 
+def test_library_codebook_is_on_the_double_binary16_grid():
+    """hqmq_make_codebook returns every value as hi + lo with hi = fp16(q),
+    lo = fp16(q - hi) (numpy's float16 rounding here, independent of both the
+    library and the oracle), i.e. a value the kernels use unchanged."""
+    q = K.hqmq_make_codebook(9, 3, 4, 1, 100).ravel()
+    hi = q.astype(np.float16)
+    lo = (q - hi.astype(np.float32)).astype(np.float16)
+    assert np.array_equal(hi.astype(np.float32) + lo.astype(np.float32), q)
+    # and not merely fp32: most values need the low part
+    assert (lo != 0).mean() > 0.9
+
+
 def test_codebook_validation():
     with pytest.raises(K.HQMQError):
         K.hqmq_make_codebook(0, 1, 1, 2, 8)

@@ -190,6 +190,78 @@ def test_med3_crowded_median_bin():
     assert rep["outliers"] == 40
 
 
+def test_med3_multiplier_below_one():
+    """C = 0.5 on the crowded-median batch: the threshold s2 > 0.25 med puts
+    the threshold code below the median's bin, so the single-pass select
+    flags every code of that bin during its pass, and loads it visits again
+    from memory (more than the 319 per wave it keeps in LDS) carry the flag;
+    the median must still be ranked among the 2650 chunks of norm 1.  Every
+    chunk of norm >= 1 is an outlier (67072, more than half the batch); the
+    64000 chunks of norm 0.5 sit exactly at the threshold (s2 = 0.25 med) and
+    stay in the bulk (strict >), decided by the pass over the whole batch
+    since they overflow the undecided list."""
+    T, D, B = 4096, 128, 4096
+    n = T * D // 4
+    rng = np.random.default_rng(17)
+    x = np.full((n, 4), 1.0, np.float16)
+    idx = rng.permutation(n)
+    x[idx[:64000]] = np.float16(0.25)
+    x[idx[64000:66650]] = np.float16(0.5)
+    x[idx[66650:66690]] = np.float16(5.0)
+    xt = torch.from_numpy(x.reshape(1, 1, T, D)).cuda()
+    cb_host, cb = _cb(1, 1, 32)
+    desc = K.Desc.make(1, 1, T, D, 32, K.HQMQ_F16, B, 0.5)
+    assert K.hqmq_sizes(desc).max_outliers == n
+    rep, rec, _ = _check(desc, xt, cb_host, cb)
+    assert rep["outliers"] == n - 64000
+
+
+@pytest.mark.parametrize("C", [0.5, 0.99, 1.0, 1.7])
+def test_med3_other_multipliers_random(C):
+    """Random heavy-tailed data with Med3x multipliers around 1 (binary16 and
+    packed norms): outlier sets, codes and decoded values against the oracle."""
+    L, H, T, D = 1, 2, 4100, 128
+    x = _x((L, H, T, D), torch.float16, seed=int(C * 1000))
+    x[:, :, :, 9] *= 30
+    cb_host, cb = _cb(L, H, 32)
+    for nf in (K.HQMQ_NORM_F16, K.HQMQ_NORM_PACKED):
+        desc = K.Desc.make(L, H, T, D, 32, K.HQMQ_F16, 4096, C, nf)
+        rep, _, _ = _check(desc, x, cb_host, cb)
+        assert rep["outliers"] > 0
+
+
+def test_off_grid_codebook_encodes_like_its_rounded_copy():
+    """The kernels use every codebook value on the double-binary16 grid
+    (hi + lo binary16 parts): a codebook off the grid gives bit-identical
+    records, decoded values and attention outputs to its rounded copy."""
+    L, H, T, D, S = 2, 2, 1500, 128, 32
+    x = _x((L, H, T, D), torch.float16, seed=77)
+    x[:, :, :, 3] *= 25
+    base = K.hqmq_make_codebook(5, L, H, 0, S)
+    rng = np.random.default_rng(5)
+    # nudge every value by a few fp32 ulps (off the 22-bit grid)
+    off = (base * (1 + rng.integers(-6, 7, base.shape) * 2.0 ** -23)).astype(np.float32)
+    assert (off != base).mean() > 0.5
+    rounded = np.vectorize(O.codebook_value)(off).astype(np.float32)
+    desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F16, 512, 3.0)
+    q = _x((1, H * 2, D), torch.float16, seed=78)
+    st = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ln = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    outs = []
+    for cb_host in (off, rounded):
+        cb = torch.from_numpy(cb_host).cuda()
+        rec, y = G.run(desc, x, cb)
+        att = K.attend(desc, 1, rec, cb, rec, cb, q, st, ln, T)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (rec.idx, rec.hnorm, rec.out_pos[:rec.n_outliers],
+                                        rec.out_val[:rec.n_outliers], y, att)])
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    # and the records are the oracle's for the rounded codebook
+    rec, y = G.run(desc, x, torch.from_numpy(off).cuda())
+    G.compare(desc, x, rounded, rec, y)
+
+
 def test_med3_select_writes_stay_inside_each_batch():
     """Head dim 16 (4 chunks per token row) and batches of 3 tokens: every
     batch ends inside a group of 8 code loads of the select, and each holds an
