@@ -11,10 +11,15 @@ single-GPU configuration, and the one that exercises every step.
 
 Prints one JSON line.  ``value`` counts chunks (4-element groups) per second,
 each chunk encoded and decoded once per step.  ``roofline`` is the encode
-search kernel against the fp32 matrix-core peak, timed with HIP events
-recorded by the library around that kernel on the launch stream.
-``cpu_baseline`` is the plain C oracle timed on a bounded sample of the same
-workload on this host.
+search kernel, timed with HIP events recorded by the library around that
+kernel on the launch stream, against the dense f16 peak of the matrix-core
+instruction it issues (with the committed VALU counters beside it: the
+epilogue on the vector ALUs is what binds it); ``roofline_decode`` is the
+decode kernel against HBM bandwidth.  ``cpu_baseline`` is the plain C oracle
+timed on a bounded sample of the same workload on this host.  By default the
+line also carries the same step in the other norm formats (``formats``) and
+the decode-step workload's figures (``decode_step``: attention read from the
+records against decoding the whole cache each step).
 """
 from __future__ import annotations
 
@@ -30,11 +35,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "HQMQ encode & decode chunks/s and GB/s (fp16 in) on 1 MI355X; % of roofline"
-PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
+PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense f16 matrix cores
+PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 NORM_FORMATS = {"f16": 0, "packed": 1}   # hqmq_desc.norm_format
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-70b-kv-128k.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_llama3-70b-kv-128k.json")
 ATTEND_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_attend.hip")
 ATTEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-8b-decode-32x32k.json")
 
@@ -349,7 +356,8 @@ def decode_step_bench(args, w):
         "value": work / (fused_ms * 1e-3),
         "unit": "chunks/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": fused_ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16xf16->f32 mfma attention, f32 decode",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "kv_heads": H, "query_heads": H * group,
                    "sequences": nseq, "cached_tokens_per_sequence": Tc,
@@ -380,7 +388,7 @@ def decode_step_bench(args, w):
         "kernel_sha256_16": kernel_hash(),
         "cpu_baseline": None,
     }
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def paged_step_bench(args, w):
@@ -512,7 +520,8 @@ def paged_step_bench(args, w):
         "value": work / (ms * 1e-3),
         "unit": "chunks/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16xf16->f32 mfma attention, f32 decode",
         "data": "synthetic",
         "config": {"workload": w.name + "-paged", "layers": L, "kv_heads": H, "query_heads": H * group,
                    "sequences": nseq, "cached_tokens_per_sequence": Tc, "head_dim": D, "roles": "K+V",
@@ -531,7 +540,7 @@ def paged_step_bench(args, w):
         "kernel_sha256_16": kernel_hash(),
         "cpu_baseline": None,
     }
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def _int_per_token(x, bits: int):
@@ -656,6 +665,132 @@ def quality_report(args):
     print(json.dumps(rep), flush=True)
 
 
+def codec_bench(w, norm_format: str, xs, cbs, ev, sh, steps: int, warmup: int, ws=None, ys=None) -> dict:
+    """Time `steps` steps of the codec on workload w's resident inputs xs
+    (dict role -> device tensor) in one norm format: per role hqmq_encode
+    (search kernel bracketed by HIP events the library records on the launch
+    stream) then per role hqmq_decode.  Returns the figures and keeps the
+    records and decode outputs in the result ('_recs', '_ys')."""
+    import torch
+    import kv_cache_quantization_hqmq_amd as K
+    desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, w.S,
+                       K.HQMQ_F32 if w.dtype == "f32" else K.HQMQ_F16, w.med_batch_tokens, w.med_C,
+                       NORM_FORMATS[norm_format])
+    sz = K.hqmq_sizes(desc)
+    if ws is None or (sz.workspace_bytes and ws.numel() < sz.workspace_bytes):
+        ws = K.workspace(desc, "cuda")
+    recs = {}
+    ys = {} if ys is None else ys
+    for role in w.roles:
+        # size the side list from a first encode (re-allocated on overflow)
+        recs[role] = K.encode(desc, xs[role], cbs[role], ws=ws)
+        if recs[role].capacity > 0 and recs[role].n_outliers > 0:
+            cap = int(recs[role].n_outliers)
+            if cap < recs[role].capacity // 2:
+                recs[role] = K.encode(desc, xs[role], cbs[role], capacity=cap, ws=ws)
+        if role not in ys:
+            ys[role] = torch.empty(desc.shape, dtype=w.torch_dtype, device="cuda")
+        log(f"{norm_format} norms, role {role}: {recs[role].n_outliers} outliers "
+            f"({recs[role].n_outliers / sz.chunks:.4%})")
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for role in w.roles:
+            e = events[("enc", role)] if events else (None, None, None, None)
+            if events:
+                ev.record(e[0], sh)
+            K.hqmq_encode_timed(desc, xs[role], cbs[role], recs[role], ws, sh,
+                                e[1] if events else None, e[2] if events else None)
+            if events:
+                ev.record(e[3], sh)
+        for role in w.roles:
+            if events:
+                d = events[("dec", role)]
+                ev.record(d[0], sh)
+            K.hqmq_decode(desc, recs[role], cbs[role], ys[role], sh)
+            if events:
+                ev.record(d[1], sh)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    all_events = [{**{("enc", r): tuple(ev.create() for _ in range(4)) for r in w.roles},
+                   **{("dec", r): tuple(ev.create() for _ in range(2)) for r in w.roles}}
+                  for _ in range(steps)]
+    log(f"timing {steps} steps ({norm_format} norms)")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(all_events[i])
+    torch.cuda.synchronize()
+    ms_step = 1000.0 * (time.perf_counter() - t0) / steps
+
+    search_ms = {r: [] for r in w.roles}
+    enc_ms = {r: [] for r in w.roles}
+    dec_ms = {r: [] for r in w.roles}
+    for evs in all_events:
+        for r in w.roles:
+            a, b, c, d = evs[("enc", r)]
+            search_ms[r].append(ev.ms(b, c))
+            enc_ms[r].append(ev.ms(a, d))
+            e0, e1 = evs[("dec", r)]
+            dec_ms[r].append(ev.ms(e0, e1))
+        for v in evs.values():
+            for e in v:
+                ev.destroy(e)
+    mean = lambda v: sum(v) / len(v)
+    flat = lambda d: [x for r in w.roles for x in d[r]]
+
+    # every launch must still be valid after the timed steps
+    n_out = {r: K.hqmq_encode_result(recs[r], sh) for r in w.roles}
+    chunks_role = sz.chunks
+    total_chunks = chunks_role * len(w.roles)
+    rec_bytes = sz.idx_bytes + (0 if norm_format == "exact" else sz.hnorm_bytes)
+    comp_bytes = sum(rec_bytes + 12 * n_out[r] + sz.offsets_bytes + sz.codebook_bytes for r in w.roles)
+    dec_bytes = {r: rec_bytes + chunks_role * (16 if w.dtype == "f32" else 8) + 12 * n_out[r] + sz.offsets_bytes
+                 for r in w.roles}
+    res = {
+        "ms_per_step": ms_step,
+        "search_ms": mean(flat(search_ms)),
+        "search_ms_per_role": {str(r): mean(search_ms[r]) for r in w.roles},
+        "encode_ms_per_role": {str(r): mean(enc_ms[r]) for r in w.roles},
+        "med3_ms_per_role": {str(r): mean(enc_ms[r]) - mean(search_ms[r]) for r in w.roles},
+        "decode_ms_per_role": {str(r): mean(dec_ms[r]) for r in w.roles},
+        "decode_GBps_per_role": {str(r): dec_bytes[r] / (mean(dec_ms[r]) * 1e-3) / 1e9 for r in w.roles},
+        "decode_bytes_per_launch": mean([dec_bytes[r] for r in w.roles]),
+        "decode_ms": mean(flat(dec_ms)),
+        "encode_chunks_per_s": total_chunks / (sum(flat(enc_ms)) / steps * 1e-3),
+        "decode_chunks_per_s": total_chunks / (sum(flat(dec_ms)) / steps * 1e-3),
+        "encode_GBps_fp16_in": total_chunks * 8 / (sum(flat(enc_ms)) / steps * 1e-3) / 1e9,
+        "decode_GBps_fp16_out": total_chunks * 8 / (sum(flat(dec_ms)) / steps * 1e-3) / 1e9,
+        "value": total_chunks / (ms_step * 1e-3),
+        "outlier_fraction": sum(n_out.values()) / total_chunks,
+        "outliers_per_role": {str(r): n_out[r] for r in w.roles},
+        "fp16_bytes": total_chunks * 8,
+        "compressed_bytes": comp_bytes,
+        "compression_ratio": total_chunks * 8 / comp_bytes,
+        "bits_per_element": 8 * comp_bytes / (total_chunks * 4),
+        "bulk_bits_per_element": 8 * rec_bytes / (chunks_role * 4),
+        "_recs": recs, "_ys": ys, "_ws": ws, "_sz": sz,
+    }
+    return res
+
+
+def public(d: dict) -> dict:
+    return {k: v for k, v in d.items() if not k.startswith("_")}
+
+
+def counters_for(kernel: str):
+    """Counter averages of one kernel from the committed summary, or None
+    when it is missing or was taken from another kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    t = json.load(open(COUNTERS_FILE))
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("kernels", {}).get(kernel)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -669,6 +804,10 @@ def main():
     ap.add_argument("--norm-format", choices=sorted(NORM_FORMATS), default="f16",
                     help="norm records: binary16 half-norms, or packed b-bit compact codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the main line: skip the other norm formats and the decode-step figures")
+    ap.add_argument("--extra-steps", type=int, default=3, help="timed steps of each extra figure")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--quality", action="store_true", help="print the synthetic quality report instead")
     ap.add_argument("--summarize", metavar="ROCPD_DB", help="print a kernel table of a rocprofv3 database")
@@ -702,24 +841,18 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if w.sequences > 1:
         if args.paged:
-            paged_step_bench(args, w)
+            out = paged_step_bench(args, w)
         else:
-            decode_step_bench(args, w)
+            out = decode_step_bench(args, w)
+        print(json.dumps(out), flush=True)
         return
     dev = "cuda"
     torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
+    sh = torch.cuda.current_stream().cuda_stream
     ev = HipEvents()
+    log(f"workload {synth.describe(w)}")
 
-    desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, w.S,
-                       K.HQMQ_F32 if w.dtype == "f32" else K.HQMQ_F16, w.med_batch_tokens, w.med_C,
-                       NORM_FORMATS[args.norm_format])
-    sz = K.hqmq_sizes(desc)
-    log(f"workload {synth.describe(w)}; {sz.chunks} chunks per role")
-
-    xs, cbs_host, cbs, recs, ys = {}, {}, {}, {}, {}
-    ws = K.workspace(desc, dev)
+    xs, cbs_host, cbs = {}, {}, {}
     for role in w.roles:
         t = time.perf_counter()
         xs[role] = synth.generate(w, role, dev)
@@ -727,132 +860,77 @@ def main():
         cbs[role] = torch.from_numpy(cbs_host[role]).to(dev)
         torch.cuda.synchronize()
         log(f"role {role}: input generated in {time.perf_counter() - t:.1f} s")
-        # size the side list from a first encode (re-allocated on overflow)
-        recs[role] = K.encode(desc, xs[role], cbs[role], ws=ws)
-        if recs[role].capacity > 0 and recs[role].n_outliers > 0:
-            cap = int(recs[role].n_outliers)
-            if cap < recs[role].capacity // 2:
-                recs[role] = K.encode(desc, xs[role], cbs[role], capacity=cap, ws=ws)
-        ys[role] = torch.empty(desc.shape, dtype=w.torch_dtype, device=dev)
-        log(f"role {role}: {recs[role].n_outliers} outliers "
-            f"({recs[role].n_outliers / sz.chunks:.4%})")
-    torch.cuda.synchronize()
 
-    def step(events=None):
-        for role in w.roles:
-            e = events[("enc", role)] if events else (None, None, None, None)
-            if events:
-                ev.record(e[0], sh)
-            K.hqmq_encode_timed(desc, xs[role], cbs[role], recs[role], ws, sh,
-                                e[1] if events else None, e[2] if events else None)
-            if events:
-                ev.record(e[3], sh)
-        for role in w.roles:
-            if events:
-                d = events[("dec", role)]
-                ev.record(d[0], sh)
-            K.hqmq_decode(desc, recs[role], cbs[role], ys[role], sh)
-            if events:
-                ev.record(d[1], sh)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    all_events = [{**{("enc", r): tuple(ev.create() for _ in range(4)) for r in w.roles},
-                   **{("dec", r): tuple(ev.create() for _ in range(2)) for r in w.roles}}
-                  for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(all_events[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = 1000.0 * elapsed / args.steps
-
-    search_ms, enc_ms, dec_ms = [], [], []
-    for evs in all_events:
-        for r in w.roles:
-            a, b, c, d = evs[("enc", r)]
-            search_ms.append(ev.ms(b, c))
-            enc_ms.append(ev.ms(a, d))
-            e0, e1 = evs[("dec", r)]
-            dec_ms.append(ev.ms(e0, e1))
-        for v in evs.values():
-            for e in v:
-                ev.destroy(e)
-    mean = lambda v: sum(v) / len(v)
-
-    # every launch must still be valid after the timed steps
-    n_out = {}
-    for r in w.roles:
-        n_out[r] = K.hqmq_encode_result(recs[r], sh)
+    main_res = codec_bench(w, args.norm_format, xs, cbs, ev, sh, args.steps, args.warmup)
+    sz = main_res["_sz"]
     chunks_role = sz.chunks
     total_chunks = chunks_role * len(w.roles)
-    f_out = sum(n_out.values()) / total_chunks
-    in_bytes_chunk = 16 if w.dtype == "f32" else 8
-    rec_bytes = sz.idx_bytes + sz.hnorm_bytes
-    comp_bytes = sum(rec_bytes + 12 * n_out[r] + sz.offsets_bytes + sz.codebook_bytes for r in w.roles)
-    fp16_bytes = total_chunks * 8
 
-    flops_launch = 32 * w.S * chunks_role           # 16 S FMA per chunk (the method's minimum)
-    s_ms = mean(search_ms)
+    # encode search: the method's arithmetic is 16 S FMA per chunk; it runs on
+    # the f16 matrix cores (v_mfma_f32_32x32x8_f16 with the codebook split into
+    # two binary16 parts, so the instructions issue twice those flops); the
+    # contraction's roofline is that instruction's dense f16 peak, and the
+    # counters show the VALU epilogue is what binds
+    flops_launch = 32 * w.S * chunks_role
+    s_ms = main_res["search_ms"]
     achieved_tf = flops_launch / (s_ms * 1e-3) / 1e12
+    search_bytes = chunks_role * (16 if w.dtype == "f32" else 8) + sz.idx_bytes + sz.hnorm_bytes
     # counters were taken on the binary16-norm configuration
-    traffic = traffic_per_launch() if (w.wid == 4 and args.norm_format == "f16") else None
-    d_ms = mean(dec_ms)
-    dec_bytes_launch = rec_bytes + chunks_role * 8 + 12 * (sum(n_out.values()) / len(w.roles)) + \
-        sz.offsets_bytes
+    is_ref_cfg = w.wid == 4 and args.norm_format == "f16"
+    traffic = traffic_per_launch() if is_ref_cfg else None
+    cnt = counters_for("encode_search_h_kernel") if is_ref_cfg else None
+    d_ms = main_res["decode_ms"]
+    dec_bytes_launch = main_res["decode_bytes_per_launch"]
     dec_gbps = dec_bytes_launch / (d_ms * 1e-3) / 1e9
-
+    roofline = {"bound": "mfma", "kernel": "encode_search", "instruction": "v_mfma_f32_32x32x8_f16",
+                "achieved": achieved_tf, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved_tf / PEAK_F16_MFMA_TFLOPS, "traffic": traffic,
+                "algorithmic_per_launch": flops_launch, "avg_launch_ms": s_ms,
+                "issued_mfma_flops_per_launch": 2 * 16384 * ((w.S + 7) // 8) * (chunks_role // 64)
+                if w.dtype == "f16" else None,
+                "hbm_bytes_per_launch": search_bytes,
+                "hbm_frac": search_bytes / (s_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                "frac_of_fp32_peak": achieved_tf / PEAK_FP32_TFLOPS}
+    if cnt:
+        roofline["valu"] = {k: cnt[k] for k in ("valu_insts_per_chunk", "mfma_insts_per_chunk",
+                                                 "valu_busy", "source") if k in cnt}
     out = {
         "metric": METRIC,
-        "value": total_chunks / (ms_step * 1e-3),
+        "value": main_res["value"],
         "unit": "chunks/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16xf16->f32 mfma search, f32 decode" if w.dtype == "f16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.heads,
                    "tokens": w.tokens, "head_dim": w.head_dim, "roles": "K+V" if len(w.roles) == 2 else "K",
                    "input": w.dtype, "S": w.S, "med3_batch_tokens": w.med_batch_tokens,
                    "med3_C": w.med_C, "norm_format": args.norm_format, "parallelism": "none"},
-        "roofline": {"bound": "mfma", "kernel": "encode_search", "achieved": achieved_tf,
-                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tf / PEAK_FP32_MFMA_TFLOPS, "traffic": traffic,
-                     "algorithmic_per_launch": flops_launch, "avg_launch_ms": s_ms},
+        "roofline": roofline,
         "roofline_decode": {"bound": "hbm", "kernel": "decode", "achieved": dec_gbps,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
-                            "traffic": traffic_per_launch("decode_bytes_per_launch")
-                            if (w.wid == 4 and args.norm_format == "f16") else None,
-                            "algorithmic_per_launch": dec_bytes_launch, "avg_launch_ms": d_ms},
-        "encode_chunks_per_s": total_chunks / (sum(enc_ms) / args.steps * 1e-3),
-        "decode_chunks_per_s": total_chunks / (sum(dec_ms) / args.steps * 1e-3),
-        "encode_GBps_fp16_in": total_chunks * 8 / (sum(enc_ms) / args.steps * 1e-3) / 1e9,
-        "decode_GBps_fp16_out": total_chunks * 8 / (sum(dec_ms) / args.steps * 1e-3) / 1e9,
-        "encode_ms_per_role": mean(enc_ms),
-        "med3_ms_per_role": mean(enc_ms) - s_ms,
-        "outlier_fraction": f_out,
-        "fp16_bytes": fp16_bytes,
-        "compressed_bytes": comp_bytes,
-        "compression_ratio": fp16_bytes / comp_bytes,
-        "bits_per_element": 8 * comp_bytes / (total_chunks * 4),
+                            "traffic": traffic_per_launch("decode_bytes_per_launch") if is_ref_cfg else None,
+                            "algorithmic_per_launch": dec_bytes_launch, "avg_launch_ms": d_ms,
+                            "avg_launch_ms_per_role": main_res["decode_ms_per_role"],
+                            "GBps_per_role": main_res["decode_GBps_per_role"]},
+        **{k: v for k, v in public(main_res).items()
+           if k not in ("ms_per_step", "value", "decode_ms", "decode_bytes_per_launch")},
         "kernel_sha256_16": kernel_hash(),
     }
-    del ws
-    if len(w.roles) == 2 and ys[w.roles[0]].numel() * 2 >= (4 << 30):
+    if not args.no_ceilings and len(w.roles) == 2 and main_res["_ys"][w.roles[0]].numel() * 2 >= (4 << 30):
         # measured ceilings (context; the decode outputs serve as scratch)
+        ys = main_res["_ys"]
         c = measure_ceilings(ys[w.roles[0]], ys[w.roles[1]], sh, ev)
-        dec_read = rec_bytes + 12 * (sum(n_out.values()) / len(w.roles)) + sz.offsets_bytes
+        dec_read = dec_bytes_launch - chunks_role * 8
         dec_write = chunks_role * 8
         mix = (dec_read + dec_write) / (dec_read / c["hbm_read_GBps"] + dec_write / c["hbm_write_GBps"])
         out["ceilings"] = dict(c, decode_mix_GBps=mix)
-        out["roofline"]["frac_of_measured_mfma_f32"] = achieved_tf / c["mfma_f32_16x16x4_TFLOPs"]
+        out["roofline"]["frac_of_measured_mfma_f16"] = achieved_tf / c["mfma_f16_32x32x8_TFLOPs"]
         out["roofline_decode"]["frac_of_measured_mix"] = dec_gbps / mix
         out["roofline_decode"]["frac_of_measured_copy"] = dec_gbps / c["hbm_copy_GBps"]
     if not args.no_cpu_baseline:
@@ -860,6 +938,35 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, xs, cbs_host, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+
+    if not args.no_extras and w.wid == 4:
+        # the same step with the other norm formats, on the same inputs
+        ws, ys = main_res["_ws"], main_res["_ys"]
+        del main_res
+        out["formats"] = {}
+        for fmt in sorted(NORM_FORMATS):
+            if fmt == args.norm_format:
+                continue
+            torch.cuda.empty_cache()
+            r = codec_bench(w, fmt, xs, cbs, ev, sh, args.extra_steps, 1, ws=None, ys=ys)
+            keep = ("ms_per_step", "search_ms", "med3_ms_per_role", "decode_ms_per_role", "decode_GBps_per_role",
+                    "compression_ratio", "bits_per_element", "bulk_bits_per_element", "compressed_bytes")
+            out["formats"][fmt] = {k: r[k] for k in keep}
+            out["formats"][fmt]["decode_frac_of_hbm_peak"] = \
+                r["decode_bytes_per_launch"] / (r["decode_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS
+            out["formats"][fmt]["steps"] = args.extra_steps
+            del r
+        del xs, ys, ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        # the decode-step workload (attention read from the records)
+        a5 = argparse.Namespace(**vars(args))
+        a5.steps, a5.warmup, a5.norm_format = args.extra_steps, 1, "f16"
+        d = decode_step_bench(a5, synth.WORKLOADS[5])
+        out["decode_step"] = {k: d[k] for k in ("ms_per_step", "value", "unit", "config", "roofline",
+                                                "encode_appended_ms", "attention_ms_per_step", "fakequant",
+                                                "fused_speedup_vs_fakequant", "cache_bits_per_element")}
+        out["decode_step"]["steps"] = a5.steps
     print(json.dumps(out), flush=True)
 
 

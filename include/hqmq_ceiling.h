@@ -27,7 +27,10 @@ enum {
     HQMQ_CEIL_COPY = 2    /* copy src to dst (bytes read + bytes written) */
 };
 
-/* One streaming pass over `bytes` bytes.  src and dst are device pointers,
+/* One streaming pass over `bytes` bytes, shaped like the codec's
+ * bandwidth-bound kernels: each thread has 8 independent 16-byte accesses in
+ * flight and each access instruction of a wave covers 1 KB of consecutive
+ * bytes (non-temporal loads and stores).  src and dst are device pointers,
  * 16-byte aligned; bytes is a positive multiple of 16 (src is unused for
  * WRITE, dst is unused for READ except for one 4-byte word that keeps the
  * read live; the caller owns both).  Asynchronous on `stream`.

@@ -162,8 +162,15 @@ struct TileRegs {
     uint32_t w[NW];
 };
 
+// Waves per SIMD the register budget is set for: two 8-wave blocks per CU
+// (128 VGPRs) where the LDS of two blocks fits, i.e. head_dim <= 128 with the
+// 2^BITS-entry tables of a fixed code width; one block (256 VGPRs, no
+// spills) otherwise.
+constexpr int attend_waves_per_eu(int D, bool table, int bits) { return D <= 128 && table && bits > 0 ? 4 : 2; }
+
 template <int D, bool TABLE, int BITS, bool NPACK, bool PAGED>
-__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ __launch_bounds__(kAttThreads)
+__attribute__((amdgpu_waves_per_eu(attend_waves_per_eu(D, TABLE, BITS), attend_waves_per_eu(D, TABLE, BITS))))
 void attend_split_kernel(AttArgs a) {
     using Sh = AttShape<D>;
     constexpr int CPT = Sh::CPT, CPL = Sh::CPL, KB = Sh::KB, NU = Sh::NU, ROWB = Sh::ROWB, TILEB = Sh::TILEB;

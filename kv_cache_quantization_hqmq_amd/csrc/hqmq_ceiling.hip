@@ -15,28 +15,54 @@ using hqmq::f32x4;
 using hqmq::u32x4;
 
 constexpr int kCeilThreads = 256;
-constexpr unsigned kStreamBlocks = 16384;   // enough 16-byte lanes in flight to cover HBM latency
 constexpr uint32_t kNever = 0x9E3779B9u;    // a result the loops are not expected to produce
 
+// Streaming loops shaped like the codec's bandwidth-bound kernels: every
+// thread issues kStreamUnroll independent 16-byte accesses before using any,
+// and a block covers kStreamUnroll * 256 consecutive 16-byte elements
+// (element u * 256 + thread of the block's range, so each access
+// instruction of a wave touches 1 KB of consecutive bytes).  One pass, no
+// grid-stride loop: the grid has one block per range.
+constexpr int kStreamUnroll = 8;
+constexpr size_t kStreamBlockElems = static_cast<size_t>(kStreamUnroll) * kCeilThreads;
+
 __global__ __launch_bounds__(kCeilThreads) void ceil_read_kernel(const u32x4 *a, size_t n, uint32_t *out) {
-    u32x4 acc = {0u, 0u, 0u, 0u};
-    for (size_t i = static_cast<size_t>(blockIdx.x) * kCeilThreads + threadIdx.x; i < n;
-         i += static_cast<size_t>(gridDim.x) * kCeilThreads)
-        acc ^= a[i];
+    const size_t base = static_cast<size_t>(blockIdx.x) * kStreamBlockElems + threadIdx.x;
+    u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+        const size_t i = base + static_cast<size_t>(u) * kCeilThreads;
+        v[u] = i < n ? __builtin_nontemporal_load(a + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x4 acc = v[0];
+#pragma unroll
+    for (int u = 1; u < kStreamUnroll; ++u) acc ^= v[u];
     if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == kNever) out[0] = 1u;
 }
 
 __global__ __launch_bounds__(kCeilThreads) void ceil_write_kernel(u32x4 *b, size_t n) {
+    const size_t base = static_cast<size_t>(blockIdx.x) * kStreamBlockElems + threadIdx.x;
     const u32x4 v = {threadIdx.x, blockIdx.x, 1u, 2u};
-    for (size_t i = static_cast<size_t>(blockIdx.x) * kCeilThreads + threadIdx.x; i < n;
-         i += static_cast<size_t>(gridDim.x) * kCeilThreads)
-        __builtin_nontemporal_store(v, b + i);
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+        const size_t i = base + static_cast<size_t>(u) * kCeilThreads;
+        if (i < n) __builtin_nontemporal_store(v, b + i);
+    }
 }
 
 __global__ __launch_bounds__(kCeilThreads) void ceil_copy_kernel(const u32x4 *a, u32x4 *b, size_t n) {
-    for (size_t i = static_cast<size_t>(blockIdx.x) * kCeilThreads + threadIdx.x; i < n;
-         i += static_cast<size_t>(gridDim.x) * kCeilThreads)
-        __builtin_nontemporal_store(a[i], b + i);
+    const size_t base = static_cast<size_t>(blockIdx.x) * kStreamBlockElems + threadIdx.x;
+    u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+        const size_t i = base + static_cast<size_t>(u) * kCeilThreads;
+        v[u] = i < n ? __builtin_nontemporal_load(a + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+        const size_t i = base + static_cast<size_t>(u) * kCeilThreads;
+        if (i < n) __builtin_nontemporal_store(v[u], b + i);
+    }
 }
 
 // 16 independent FMA chains per lane (32 flops per lane per round).
@@ -90,8 +116,9 @@ extern "C" int hqmq_ceiling_stream(int kind, const void *src, void *dst, size_t 
     if (kind != HQMQ_CEIL_WRITE && (src == nullptr || reinterpret_cast<uintptr_t>(src) % 16 != 0)) return HQMQ_EINVAL;
     if (dst == nullptr || reinterpret_cast<uintptr_t>(dst) % 16 != 0) return HQMQ_EINVAL;
     const size_t n = bytes / 16;
-    const size_t want = (n + kCeilThreads - 1) / kCeilThreads;
-    const dim3 grid(static_cast<unsigned>(want < kStreamBlocks ? want : kStreamBlocks));
+    const size_t blocks = (n + kStreamBlockElems - 1) / kStreamBlockElems;
+    if (blocks >= (size_t{1} << 31)) return HQMQ_EINVAL;
+    const dim3 grid(static_cast<unsigned>(blocks));
     if (kind == HQMQ_CEIL_READ)
         hipLaunchKernelGGL(ceil_read_kernel, grid, dim3(kCeilThreads), 0, stream, static_cast<const u32x4 *>(src), n,
                            static_cast<uint32_t *>(dst));
