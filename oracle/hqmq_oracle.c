@@ -50,6 +50,14 @@
  *   or_compact_norm ............... pinned (brute-force nearest value of the
  *                                   format over every binary16 input; flag,
  *                                   identity at b = 15, error bound)
+ *   or_exact_norm ................. pinned (nearest level of the grid by an
+ *                                   independent vectorised search over every
+ *                                   binary16 input; binade boundaries on the
+ *                                   grid; flag; cap)
+ *   or_pack_exact_group ........... pinned (an independent unpacker: numpy
+ *                                   bit unpacking and base-3 digits; the
+ *                                   information bound on the group size;
+ *                                   planted slips)
  *   or_attend ..................... pinned (closed forms: uniform scores,
  *                                   one token, dominant key; scipy softmax
  *                                   on random inputs; token permutation)
@@ -601,6 +609,168 @@ void or_compact_norms(const uint16_t *h16, int64_t n, int b, uint32_t *out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = or_compact_norm(h16[i], b);
+}
+
+/* ------------------------------------------------------------------ */
+/* Exact-rate record (reading).  The pages' rate -- about 3.79 bits per */
+/* element at S = 8 and about 5 at S = 32 ([ABS], [FR-MEC]) -- is two   */
+/* codes of log2(24 S) bits per 4-element chunk: an index with 24 S     */
+/* values and a norm code with as many.  Reading: the norm code has     */
+/* R = 24 S levels (the last one is the Med3x flag) and both codes of   */
+/* every chunk are stored at that exact rate up to a small packing      */
+/* loss.  With S a power of two, R = 3 2^m (m = log2 S + 3): a code is  */
+/* m plain bits plus one ternary digit (code = 2^m t + l, t in {0,1,2}), */
+/* the digits packed five to a byte (3^5 = 243 <= 256).                */
+/* ------------------------------------------------------------------ */
+
+/* m with 24 S = 3 2^m, or -1 when S is not a power of two in [1, 1024]. */
+int or_exact_m(int S)
+{
+    int m = 3;
+    for (int s = 1; s <= 1024; s *= 2, ++m)
+        if (s == S)
+            return m;
+    return -1;
+}
+
+/* binary16 pattern of norm level n (0 <= n < R - 1): the integer nearest to
+ * n 2^15 / R, i.e. the levels divide the 32 binades of the binary16
+ * pattern range evenly (R / 32 levels per binade, 6 at S = 8, 24 at
+ * S = 32).  Levels whose pattern is not finite (>= 0x7C00) are unused. */
+uint32_t or_exact_level_pattern(uint32_t n, int S)
+{
+    const uint64_t R = 24u * (uint64_t)S;
+    return (uint32_t)((2u * (uint64_t)n * 32768u + R) / (2u * R));
+}
+
+/* Exact-rate norm code of a binary16 half-norm record h16: the flag bit
+ * gives R - 1; otherwise the level whose value is nearest to the value of
+ * h16, a tie going to the even level, among the levels below R - 1 with
+ * finite patterns (so larger norms take the top level).  Brute force over
+ * every level. */
+uint32_t or_exact_norm(uint16_t h16, int S)
+{
+    const uint32_t R = 24u * (uint32_t)S;
+    if (h16 & 0x8000u)
+        return R - 1u;
+    const double v = or_f16_value(h16);
+    uint32_t best = 0;
+    double bd = INFINITY;
+    for (uint32_t n = 0; n + 1u < R; ++n) {
+        const uint32_t p = or_exact_level_pattern(n, S);
+        if (p >= 0x7C00u)
+            break;
+        const double d = fabs(or_f16_value((uint16_t)p) - v);
+        if (d < bd || (d == bd && (n & 1u) == 0u)) {
+            bd = d;
+            best = n;
+        }
+    }
+    return best;
+}
+
+/* The binary16 half-norm record an exact-rate norm code stands for (the
+ * flag 0x8000 for R - 1). */
+uint16_t or_exact_norm_to_h16(uint32_t n, int S)
+{
+    if (n == 24u * (uint32_t)S - 1u)
+        return 0x8000u;
+    return (uint16_t)or_exact_level_pattern(n, S);
+}
+
+/* Words of one group of 4 token rows: per row ceil(cpt m / 32) words of
+ * index low parts and as many of norm low parts, and ceil(2 cpt / 5) bytes
+ * of ternary digits per row (4 rows: a whole number of words). */
+int or_exact_group_words(int cpt, int S)
+{
+    const int m = or_exact_m(S);
+    if (m < 0)
+        return -1;
+    const int wl = (cpt * m + 31) / 32;
+    const int tb = (2 * cpt + 4) / 5;
+    return 8 * wl + tb;
+}
+
+/* Pack rows 0 .. rows-1 (rows <= 4) of a group: codes[r][c] (index) and
+ * ncodes[r][c] (norm), both in [0, R).  Layout of the group's words:
+ *   [0, 4 wl)      index low parts: row r's stream at words r wl ..; the low
+ *                  m bits of chunk c's code are stream bits c m .. c m + m - 1
+ *                  (stream bit j = bit j % 32 of word j / 32)
+ *   [4 wl, 8 wl)   norm low parts, the same way
+ *   [8 wl, GW)     digit bytes: row r's at bytes r tb .. r tb + tb - 1 of
+ *                  the area (byte i of the area is byte i % 4 of word
+ *                  8 wl + i / 4, little-endian); digit j of a row (j = c for
+ *                  chunk c's index, cpt + c for its norm) is digit j % 5 of
+ *                  byte j / 5, a byte holding sum_i d_i 3^i.
+ * Missing rows and unused bits are 0.  Written bit by bit and digit by
+ * digit. */
+void or_pack_exact_group(const int32_t *codes, const uint32_t *ncodes, int rows, int cpt, int S,
+                         uint32_t *words)
+{
+    const int m = or_exact_m(S);
+    const int wl = (cpt * m + 31) / 32;
+    const int tb = (2 * cpt + 4) / 5;
+    const int gw = 8 * wl + tb;
+    memset(words, 0, sizeof(uint32_t) * (size_t)gw);
+    for (int r = 0; r < rows; ++r) {
+        for (int c = 0; c < cpt; ++c) {
+            const uint32_t k = (uint32_t)codes[r * cpt + c];
+            const uint32_t n = ncodes[r * cpt + c];
+            const uint32_t parts[2] = {k, n};
+            for (int pl = 0; pl < 2; ++pl) {
+                const uint32_t low = parts[pl] % (1u << m);
+                const uint32_t digit = parts[pl] / (1u << m);
+                uint32_t *plane = words + (pl * 4 + r) * wl;
+                for (int i = 0; i < m; ++i)
+                    if ((low >> i) & 1u) {
+                        const long bit = (long)c * m + i;
+                        plane[bit / 32] |= 1u << (bit % 32);
+                    }
+                const int j = pl * cpt + c;
+                const int byte = r * tb + j / 5;
+                uint32_t weight = 1;
+                for (int d = 0; d < j % 5; ++d)
+                    weight *= 3u;
+                words[8 * wl + byte / 4] += (digit * weight) << (8 * (byte % 4));
+            }
+        }
+    }
+}
+
+/* Inverse of or_pack_exact_group for rows 0 .. rows-1. */
+void or_unpack_exact_group(const uint32_t *words, int rows, int cpt, int S, int32_t *codes, uint32_t *ncodes)
+{
+    const int m = or_exact_m(S);
+    const int wl = (cpt * m + 31) / 32;
+    const int tb = (2 * cpt + 4) / 5;
+    for (int r = 0; r < rows; ++r) {
+        for (int c = 0; c < cpt; ++c) {
+            uint32_t parts[2];
+            for (int pl = 0; pl < 2; ++pl) {
+                const uint32_t *plane = words + (pl * 4 + r) * wl;
+                uint32_t low = 0;
+                for (int i = 0; i < m; ++i) {
+                    const long bit = (long)c * m + i;
+                    low |= ((plane[bit / 32] >> (bit % 32)) & 1u) << i;
+                }
+                const int j = pl * cpt + c;
+                const int byte = r * tb + j / 5;
+                uint32_t v = (words[8 * wl + byte / 4] >> (8 * (byte % 4))) & 0xFFu;
+                for (int d = 0; d < j % 5; ++d)
+                    v /= 3u;
+                parts[pl] = (v % 3u) * (1u << m) + low;
+            }
+            codes[r * cpt + c] = (int32_t)parts[0];
+            ncodes[r * cpt + c] = parts[1];
+        }
+    }
+}
+
+void or_exact_norms(const uint16_t *h16, int64_t n, int S, uint32_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = or_exact_norm(h16[i], S);
 }
 
 /* Decode-step attention of G query rows over T cached tokens ([NL-LAT]):

@@ -17,6 +17,7 @@ import oracle as O
 from tests import test_oracle_algebra as A
 from tests import test_oracle_attend as T
 from tests import test_oracle_compact_norm as CN
+from tests import test_oracle_exact as EX
 from tests import test_oracle_f16_codebook as F
 from tests import test_oracle_med3_codec as M
 from tests import test_oracle_quantizer as Q
@@ -93,6 +94,27 @@ MUTANTS = [
     ("compact-norm-no-cap",
      "    const double hi = (f + 1.0) * q < vmax ? (f + 1.0) * q : vmax;", "    const double hi = (f + 1.0) * q;",
      lambda: CN.test_monotone_bounded_and_flagged(8)),
+    ("exact-digit-weight",
+     "                    weight *= 3u;", "                    weight *= 4u;",
+     lambda: EX.test_pack_exact_round_trips_through_an_independent_unpacker(8, 32, 9)),
+    ("exact-digit-order",
+     "for (int d = 0; d < j % 5; ++d)\n                    weight *= 3u;",
+     "for (int d = 0; d < 4 - j % 5; ++d)\n                    weight *= 3u;",
+     lambda: EX.test_pack_exact_round_trips_through_an_independent_unpacker(32, 32, 4)),
+    ("exact-planes-interleaved",
+     "                uint32_t *plane = words + (pl * 4 + r) * wl;",
+     "                uint32_t *plane = words + (r * 2 + pl) * wl;",
+     lambda: EX.test_pack_exact_round_trips_through_an_independent_unpacker(8, 32, 9)),
+    ("exact-grid-rounds-down",
+     "return (uint32_t)((2u * (uint64_t)n * 32768u + R) / (2u * R));",
+     "return (uint32_t)((2u * (uint64_t)n * 32768u) / (2u * R));",
+     lambda: EX.test_level_grid_divides_the_binades_evenly(8)),
+    ("exact-norm-ties-odd",
+     "if (d < bd || (d == bd && (n & 1u) == 0u)) {", "if (d < bd || (d == bd && (n & 1u) == 1u)) {",
+     lambda: EX.test_exact_norm_is_the_nearest_level_for_every_binary16_input(8)),
+    ("exact-norm-flag-level",
+     "    if (h16 & 0x8000u)\n        return R - 1u;", "    if (h16 & 0x8000u)\n        return R - 2u;",
+     lambda: EX.test_exact_norm_is_the_nearest_level_for_every_binary16_input(32)),
     ("side-pos-drops-offset",
      "side_pos[n_out] = (uint32_t)((t0 + t) * cpt + c);", "side_pos[n_out] = (uint32_t)(t * cpt + c);",
      M.test_batches_and_partial_tail),
