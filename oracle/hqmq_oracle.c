@@ -620,7 +620,7 @@ void or_compact_norms(const uint16_t *h16, int64_t n, int b, uint32_t *out)
 /* every chunk are stored at that exact rate up to a small packing      */
 /* loss.  With S a power of two, R = 3 2^m (m = log2 S + 3): a code is  */
 /* m plain bits plus one ternary digit (code = 2^m t + l, t in {0,1,2}), */
-/* the digits packed five to a byte (3^5 = 243 <= 256).                */
+/* the digits packed eight to a 13-bit field (3^8 = 6561 <= 2^13).    */
 /* ------------------------------------------------------------------ */
 
 /* m with 24 S = 3 2^m, or -1 when S is not a power of two in [1, 1024]. */
@@ -678,60 +678,70 @@ uint16_t or_exact_norm_to_h16(uint32_t n, int S)
     return (uint16_t)or_exact_level_pattern(n, S);
 }
 
+/* Ternary digits per field and bits per field: 3^8 = 6561 <= 2^13. */
+#define OR_DIGITS_PER_FIELD 8
+#define OR_FIELD_BITS 13
+
 /* Words of one group of 4 token rows: per row ceil(cpt m / 32) words of
- * index low parts and as many of norm low parts, and ceil(2 cpt / 5) bytes
- * of ternary digits per row (4 rows: a whole number of words). */
+ * index low parts and as many of norm low parts, then the digit area: per
+ * row F = 2 ceil(cpt / 8) fields of 13 bits (the index digits' fields, then
+ * the norm digits'), rounded up to whole words for the 4 rows. */
 int or_exact_group_words(int cpt, int S)
 {
     const int m = or_exact_m(S);
     if (m < 0)
         return -1;
     const int wl = (cpt * m + 31) / 32;
-    const int tb = (2 * cpt + 4) / 5;
-    return 8 * wl + tb;
+    const int F = 2 * ((cpt + OR_DIGITS_PER_FIELD - 1) / OR_DIGITS_PER_FIELD);
+    return 8 * wl + (4 * F * OR_FIELD_BITS + 31) / 32;
 }
 
 /* Pack rows 0 .. rows-1 (rows <= 4) of a group: codes[r][c] (index) and
- * ncodes[r][c] (norm), both in [0, R).  Layout of the group's words:
- *   [0, 4 wl)      index low parts: row r's stream at words r wl ..; the low
- *                  m bits of chunk c's code are stream bits c m .. c m + m - 1
- *                  (stream bit j = bit j % 32 of word j / 32)
+ * ncodes[r][c] (norm), both in [0, R), R = 3 2^m; a code is 2^m d + l with
+ * d its ternary digit and l its m low bits.  Layout of the group's words
+ * (bit j of a stream is bit j % 32 of word j / 32):
+ *   [0, 4 wl)      index low parts: row r's stream starts at word r wl; the
+ *                  low bits of chunk c are stream bits c m .. c m + m - 1
  *   [4 wl, 8 wl)   norm low parts, the same way
- *   [8 wl, GW)     digit bytes: row r's at bytes r tb .. r tb + tb - 1 of
- *                  the area (byte i of the area is byte i % 4 of word
- *                  8 wl + i / 4, little-endian); digit j of a row (j = c for
- *                  chunk c's index, cpt + c for its norm) is digit j % 5 of
- *                  byte j / 5, a byte holding sum_i d_i 3^i.
- * Missing rows and unused bits are 0.  Written bit by bit and digit by
- * digit. */
+ *   [8 wl, GW)     one stream of digit fields: row r's F fields start at
+ *                  bit 13 F r; field f < F / 2 holds the index digits of
+ *                  chunks 8 f .. 8 f + 7, field F / 2 + f their norm digits,
+ *                  as the 13-bit number sum_i d_i 3^i (d_i of chunk 8 f + i,
+ *                  0 past the row's end).
+ * Missing rows and unused bits are 0.  Written bit by bit. */
 void or_pack_exact_group(const int32_t *codes, const uint32_t *ncodes, int rows, int cpt, int S,
                          uint32_t *words)
 {
     const int m = or_exact_m(S);
     const int wl = (cpt * m + 31) / 32;
-    const int tb = (2 * cpt + 4) / 5;
-    const int gw = 8 * wl + tb;
+    const int fh = (cpt + OR_DIGITS_PER_FIELD - 1) / OR_DIGITS_PER_FIELD;   /* fields per plane */
+    const int gw = or_exact_group_words(cpt, S);
     memset(words, 0, sizeof(uint32_t) * (size_t)gw);
+    uint32_t *digits = words + 8 * wl;
     for (int r = 0; r < rows; ++r) {
-        for (int c = 0; c < cpt; ++c) {
-            const uint32_t k = (uint32_t)codes[r * cpt + c];
-            const uint32_t n = ncodes[r * cpt + c];
-            const uint32_t parts[2] = {k, n};
-            for (int pl = 0; pl < 2; ++pl) {
-                const uint32_t low = parts[pl] % (1u << m);
-                const uint32_t digit = parts[pl] / (1u << m);
-                uint32_t *plane = words + (pl * 4 + r) * wl;
+        for (int pl = 0; pl < 2; ++pl) {
+            const uint32_t *src = pl == 0 ? (const uint32_t *)(codes + r * cpt) : ncodes + r * cpt;
+            uint32_t *plane = words + (pl * 4 + r) * wl;
+            for (int c = 0; c < cpt; ++c) {
+                const uint32_t low = src[c] % (1u << m);
                 for (int i = 0; i < m; ++i)
                     if ((low >> i) & 1u) {
                         const long bit = (long)c * m + i;
                         plane[bit / 32] |= 1u << (bit % 32);
                     }
-                const int j = pl * cpt + c;
-                const int byte = r * tb + j / 5;
-                uint32_t weight = 1;
-                for (int d = 0; d < j % 5; ++d)
+            }
+            for (int f = 0; f < fh; ++f) {
+                uint32_t value = 0, weight = 1;
+                for (int i = 0; i < OR_DIGITS_PER_FIELD; ++i) {
+                    const int c = OR_DIGITS_PER_FIELD * f + i;
+                    if (c < cpt)
+                        value += (src[c] / (1u << m)) * weight;
                     weight *= 3u;
-                words[8 * wl + byte / 4] += (digit * weight) << (8 * (byte % 4));
+                }
+                const long base = (long)OR_FIELD_BITS * (2 * fh * r + pl * fh + f);
+                for (int i = 0; i < OR_FIELD_BITS; ++i)
+                    if ((value >> i) & 1u)
+                        digits[(base + i) / 32] |= 1u << ((base + i) % 32);
             }
         }
     }
@@ -742,26 +752,29 @@ void or_unpack_exact_group(const uint32_t *words, int rows, int cpt, int S, int3
 {
     const int m = or_exact_m(S);
     const int wl = (cpt * m + 31) / 32;
-    const int tb = (2 * cpt + 4) / 5;
+    const int fh = (cpt + OR_DIGITS_PER_FIELD - 1) / OR_DIGITS_PER_FIELD;
+    const uint32_t *digits = words + 8 * wl;
     for (int r = 0; r < rows; ++r) {
-        for (int c = 0; c < cpt; ++c) {
-            uint32_t parts[2];
-            for (int pl = 0; pl < 2; ++pl) {
-                const uint32_t *plane = words + (pl * 4 + r) * wl;
+        for (int pl = 0; pl < 2; ++pl) {
+            const uint32_t *plane = words + (pl * 4 + r) * wl;
+            for (int c = 0; c < cpt; ++c) {
                 uint32_t low = 0;
                 for (int i = 0; i < m; ++i) {
                     const long bit = (long)c * m + i;
                     low |= ((plane[bit / 32] >> (bit % 32)) & 1u) << i;
                 }
-                const int j = pl * cpt + c;
-                const int byte = r * tb + j / 5;
-                uint32_t v = (words[8 * wl + byte / 4] >> (8 * (byte % 4))) & 0xFFu;
-                for (int d = 0; d < j % 5; ++d)
-                    v /= 3u;
-                parts[pl] = (v % 3u) * (1u << m) + low;
+                const long base = (long)OR_FIELD_BITS * (2 * fh * r + pl * fh + c / OR_DIGITS_PER_FIELD);
+                uint32_t value = 0;
+                for (int i = 0; i < OR_FIELD_BITS; ++i)
+                    value |= ((digits[(base + i) / 32] >> ((base + i) % 32)) & 1u) << i;
+                for (int i = 0; i < c % OR_DIGITS_PER_FIELD; ++i)
+                    value /= 3u;
+                const uint32_t code = (value % 3u) * (1u << m) + low;
+                if (pl == 0)
+                    codes[r * cpt + c] = (int32_t)code;
+                else
+                    ncodes[r * cpt + c] = code;
             }
-            codes[r * cpt + c] = (int32_t)parts[0];
-            ncodes[r * cpt + c] = parts[1];
         }
     }
 }

@@ -6,7 +6,7 @@ S = 8 and about 5 at S = 32 (signal-ia-rouge.vercel.app, "La mecanique";
 the abstract), i.e. two codes of log2(24 S) bits per 4-element chunk.  The
 oracle's reading: a norm code with 24 S levels beside the 24 S-valued
 index, each split into m plain bits and one ternary digit (24 S = 3 2^m),
-digits packed five to a byte, groups of 4 token rows.  These tests check
+digits packed eight to a 13-bit field, groups of 4 token rows.  These tests check
 the oracle against things written independently of it: the defining
 property of a nearest-level quantiser (a vectorised search over every
 binary16 input), closed forms of the level grid, an unpacker written with
@@ -117,29 +117,31 @@ def test_exact_norm_relative_error_bound(S):
 
 def _unpack_independent(words, T, cpt, S):
     """An unpacker written from the layout description only: numpy bit
-    unpacking for the plain parts, integer base-3 digits for the bytes."""
+    unpacking for the plain parts and the 13-bit digit fields, integer
+    base-3 digits of each field."""
     m = int(round(math.log2(24 * S / 3)))
     wl = -(-cpt * m // 32)
-    tb = -(-2 * cpt // 5)
+    fh = -(-cpt // 8)
     codes = np.zeros((T, cpt), np.int64)
     norms = np.zeros((T, cpt), np.int64)
     for g in range(words.shape[0]):
         w = np.ascontiguousarray(words[g], np.uint32)
-        digit_bytes = w[8 * wl:].view(np.uint8)
+        dbits = np.unpackbits(w[8 * wl:].view(np.uint8), bitorder="little").astype(np.int64)
+        fields = dbits[:4 * 2 * fh * 13].reshape(4, 2, fh, 13) @ (1 << np.arange(13))
         for r in range(min(4, T - 4 * g)):
             for plane, out in ((0, codes), (1, norms)):
                 stream = np.unpackbits(w[(plane * 4 + r) * wl:(plane * 4 + r + 1) * wl].view(np.uint8),
                                        bitorder="little")
                 lows = stream[:cpt * m].reshape(cpt, m).astype(np.int64) @ (1 << np.arange(m))
-                for c in range(cpt):
-                    j = plane * cpt + c
-                    b = int(digit_bytes[r * tb + j // 5])
-                    assert b < 243
-                    digits = []
-                    for _ in range(5):
-                        b, d = divmod(b, 3)
-                        digits.append(d)
-                    out[4 * g + r, c] = digits[j % 5] * 2 ** m + lows[c]
+                for f in range(fh):
+                    v = int(fields[r, plane, f])
+                    assert v < 3 ** 8
+                    for i in range(8):
+                        v, d = divmod(v, 3)
+                        if 8 * f + i < cpt:
+                            out[4 * g + r, 8 * f + i] = d * 2 ** m + lows[8 * f + i]
+                        else:
+                            assert d == 0
     return codes, norms
 
 
@@ -186,13 +188,14 @@ def test_pack_exact_is_injective_on_single_changes():
 @pytest.mark.parametrize("cpt", (4, 16, 32, 64))
 def test_group_size_against_the_information_bound(S, cpt):
     """A group of 4 rows holds 8 cpt values of log2(24 S) bits each: its
-    size can not be smaller, and the packing loses little (digits at 1.6
-    bits instead of log2 3, and word padding)."""
+    size can not be smaller, and the packing loses little (digits at 13 / 8
+    bits instead of log2 3, fields of 8 digits, and word padding)."""
     bits = 32 * O.exact_group_words(cpt, S)
     info = 8 * cpt * math.log2(24 * S)
     assert bits >= info
     m = O.exact_m(S)
-    assert bits <= 8 * cpt * (m + 1.6) + 8 * 31 + 31
+    fields = 8 * -(-cpt // 8)
+    assert bits <= 8 * cpt * m + fields * 13 + 8 * 31 + 31
 
 
 def test_rates_at_the_pages_settings():

@@ -97,13 +97,13 @@ MUTANTS = [
     ("exact-digit-weight",
      "                    weight *= 3u;", "                    weight *= 4u;",
      lambda: EX.test_pack_exact_round_trips_through_an_independent_unpacker(8, 32, 9)),
-    ("exact-digit-order",
-     "for (int d = 0; d < j % 5; ++d)\n                    weight *= 3u;",
-     "for (int d = 0; d < 4 - j % 5; ++d)\n                    weight *= 3u;",
+    ("exact-digit-field-order",
+     "const long base = (long)OR_FIELD_BITS * (2 * fh * r + pl * fh + f);",
+     "const long base = (long)OR_FIELD_BITS * (2 * fh * r + (1 - pl) * fh + f);",
      lambda: EX.test_pack_exact_round_trips_through_an_independent_unpacker(32, 32, 4)),
     ("exact-planes-interleaved",
-     "                uint32_t *plane = words + (pl * 4 + r) * wl;",
-     "                uint32_t *plane = words + (r * 2 + pl) * wl;",
+     "            uint32_t *plane = words + (pl * 4 + r) * wl;\n            for (int c = 0; c < cpt; ++c) {\n                const uint32_t low",
+     "            uint32_t *plane = words + (r * 2 + pl) * wl;\n            for (int c = 0; c < cpt; ++c) {\n                const uint32_t low",
      lambda: EX.test_pack_exact_round_trips_through_an_independent_unpacker(8, 32, 9)),
     ("exact-grid-rounds-down",
      "return (uint32_t)((2u * (uint64_t)n * 32768u + R) / (2u * R));",
