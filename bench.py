@@ -40,10 +40,9 @@ PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 NORM_FORMATS = {"f16": 0, "packed": 1}   # hqmq_desc.norm_format
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-70b-kv-128k.json")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_llama3-70b-kv-128k.json")
+COUNTERS5_FILE = os.path.join(ROOT, "profiles", "counters_llama3-8b-decode-32x32k.json")
 ATTEND_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_attend.hip")
-ATTEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3-8b-decode-32x32k.json")
 
 
 def log(*a):
@@ -124,27 +123,41 @@ def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def traffic_per_launch(key: str = "search_bytes_per_launch"):
-    """HBM bytes per launch from the committed counter summary, or None when
-    it is missing or was taken from another kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _counters(path: str, hash_key: str, src: str):
+    """A committed counter summary, or None when it is missing or was taken
+    from another kernel source."""
+    if not os.path.exists(path):
         return None
-    t = json.load(open(TRAFFIC_FILE))
-    if t.get("kernel_sha256_16") != kernel_hash():
+    t = json.load(open(path))
+    if t.get(hash_key) != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
         return None
-    return t.get(key)
+    return t
+
+
+def counters_for(kernel: str, path: str = None):
+    """Counter summary of one kernel of the 128k workload (or of `path`)."""
+    t = _counters(path or COUNTERS_FILE, "kernel_sha256_16", KERNEL_SRC)
+    return None if t is None else t.get("kernels", {}).get(kernel)
+
+
+def traffic_per_launch(kernel: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated, average over
+    the K and V launches) from the committed counters, or None."""
+    c = counters_for(kernel)
+    if not c or "fetch_bytes" not in c or "write_bytes" not in c:
+        return None
+    return c["fetch_bytes"]["avg"] + c["write_bytes"]["avg"]
 
 
 def attend_traffic_per_launch():
     """HBM bytes per attention launch (one layer of the decode-step workload)
-    from the committed counter summary, or None when it is missing or was
-    taken from another attention kernel source."""
-    if not os.path.exists(ATTEND_TRAFFIC_FILE):
+    from the committed counters, or None when they were taken from another
+    attention kernel source."""
+    t = _counters(COUNTERS5_FILE, "attend_sha256_16", ATTEND_SRC)
+    c = None if t is None else t.get("kernels", {}).get("attend_split_kernel")
+    if not c or "fetch_bytes" not in c or "write_bytes" not in c:
         return None
-    t = json.load(open(ATTEND_TRAFFIC_FILE))
-    if t.get("attend_sha256_16") != hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()[:16]:
-        return None
-    return t.get("attend_bytes_per_launch")
+    return c["fetch_bytes"]["avg"] + c["write_bytes"]["avg"]
 
 
 def cpu_baseline(w, xs, cbs, seconds: float):
@@ -223,6 +236,69 @@ def summarize_pmc(db: str):
     for r in rows:
         print(json.dumps({"kernel": r[0].replace("(anonymous namespace)::", "").split("(")[0],
                           "counter": r[1], "dispatches": r[2], "avg": r[3], "min": r[4], "max": r[5]}))
+
+
+def _kernel_key(name: str) -> str:
+    """'void hqmq::decode_kernel<false, true, false>' -> 'decode_kernel'."""
+    n = name.split("(")[0].split("<")[0].replace("void ", "").strip()
+    return n.split("::")[-1]
+
+
+def summarize_counters(run_dir: str, workload: int):
+    """Counter summary of one workload from the per-pass outputs of
+    `bench.py --summarize-pmc` (files pA.jsonl: instruction counts, pB.jsonl:
+    busy metrics, pF.jsonl / pW.jsonl: FETCH_SIZE / WRITE_SIZE, pFc.jsonl /
+    pWc.jsonl: the same two counters on --copy-calibration) in run_dir.
+    Prints the JSON kept under profiles/: per kernel the counters' average,
+    minimum and maximum over its dispatches (the minimum and maximum of the
+    codec kernels are its V and K launches), instructions per chunk, and
+    HBM bytes per dispatch scaled by the copy calibration."""
+    import synth
+    w = synth.WORKLOADS[workload]
+
+    def load(tag):
+        path = os.path.join(run_dir, f"{tag}.jsonl")
+        out = {}
+        if not os.path.exists(path):
+            return out
+        for line in open(path):
+            r = json.loads(line)
+            out.setdefault(r["kernel"], {})[r["counter"]] = r
+        return out
+
+    inst, busy, fetch, write = load("pA"), load("pB"), load("pF"), load("pW")
+    cal_f = load("pFc").get("__amd_rocclr_copyBuffer", {}).get("FETCH_SIZE")
+    cal_w = load("pWc").get("__amd_rocclr_copyBuffer", {}).get("WRITE_SIZE")
+    moved_kib = 4 * 1024 * 1024          # the calibration copies 4 GiB each way
+    fscale = moved_kib / cal_f["avg"] if cal_f else None
+    wscale = moved_kib / cal_w["avg"] if cal_w else None
+    chunks = w.layers * w.heads * w.tokens * w.head_dim // 4     # one role
+    kernels = {}
+    for name in sorted(set(inst) | set(busy)):
+        if "hqmq" not in name:
+            continue
+        k = _kernel_key(name)
+        e = kernels.setdefault(k, {"kernel": name})
+        for src in (inst.get(name, {}), busy.get(name, {})):
+            for c, r in src.items():
+                e[c] = {"avg": r["avg"], "min": r["min"], "max": r["max"], "dispatches": r["dispatches"]}
+        if name in fetch and fscale:
+            e["fetch_bytes"] = {q: fetch[name]["FETCH_SIZE"][q] * 1024 * fscale for q in ("avg", "min", "max")}
+        if name in write and wscale:
+            e["write_bytes"] = {q: write[name]["WRITE_SIZE"][q] * 1024 * wscale for q in ("avg", "min", "max")}
+        if k in ("encode_search_h_kernel", "encode_search_kernel", "decode_kernel") and "SQ_INSTS_VALU" in e:
+            e["valu_insts_per_chunk"] = e["SQ_INSTS_VALU"]["avg"] / chunks
+            e["valu_insts_per_wave_step_64_chunks"] = 64 * e["SQ_INSTS_VALU"]["avg"] / chunks
+            e["mfma_insts_per_chunk"] = e["SQ_INSTS_MFMA"]["avg"] / chunks
+            e["salu_insts_per_chunk"] = e["SQ_INSTS_SALU"]["avg"] / chunks
+        if "VALUBusy" in e:
+            e["valu_busy"] = e["VALUBusy"]["avg"] / 100.0
+            e["source"] = "VALUBusy = 100 sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE) (rocprofv3's definition)"
+    print(json.dumps({"workload": synth.describe(w), "chunks_per_role": chunks,
+                      "fetch_scale": fscale, "write_scale": wscale,
+                      "kernel_sha256_16": kernel_hash(),
+                      "attend_sha256_16": hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()[:16],
+                      "kernels": kernels}, indent=1))
 
 
 def decode_step_bench(args, w):
@@ -780,17 +856,6 @@ def public(d: dict) -> dict:
     return {k: v for k, v in d.items() if not k.startswith("_")}
 
 
-def counters_for(kernel: str):
-    """Counter averages of one kernel from the committed summary, or None
-    when it is missing or was taken from another kernel source."""
-    if not os.path.exists(COUNTERS_FILE):
-        return None
-    t = json.load(open(COUNTERS_FILE))
-    if t.get("kernel_sha256_16") != kernel_hash():
-        return None
-    return t.get("kernels", {}).get(kernel)
-
-
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -812,9 +877,14 @@ def main():
     ap.add_argument("--quality", action="store_true", help="print the synthetic quality report instead")
     ap.add_argument("--summarize", metavar="ROCPD_DB", help="print a kernel table of a rocprofv3 database")
     ap.add_argument("--summarize-pmc", metavar="ROCPD_DB", help="print per-kernel counter averages")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="JSON counter summary of --workload from the --summarize-pmc outputs in DIR")
     args = ap.parse_args()
     if args.summarize:
         summarize_rocpd(args.summarize)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
@@ -877,7 +947,7 @@ def main():
     search_bytes = chunks_role * (16 if w.dtype == "f32" else 8) + sz.idx_bytes + sz.hnorm_bytes
     # counters were taken on the binary16-norm configuration
     is_ref_cfg = w.wid == 4 and args.norm_format == "f16"
-    traffic = traffic_per_launch() if is_ref_cfg else None
+    traffic = traffic_per_launch("encode_search_h_kernel") if is_ref_cfg else None
     cnt = counters_for("encode_search_h_kernel") if is_ref_cfg else None
     d_ms = main_res["decode_ms"]
     dec_bytes_launch = main_res["decode_bytes_per_launch"]
@@ -892,8 +962,10 @@ def main():
                 "hbm_frac": search_bytes / (s_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                 "frac_of_fp32_peak": achieved_tf / PEAK_FP32_TFLOPS}
     if cnt:
-        roofline["valu"] = {k: cnt[k] for k in ("valu_insts_per_chunk", "mfma_insts_per_chunk",
+        roofline["valu"] = {k: cnt[k] for k in ("valu_insts_per_wave_step_64_chunks", "mfma_insts_per_chunk",
                                                  "valu_busy", "source") if k in cnt}
+        if "MfmaUtil" in cnt:
+            roofline["valu"]["mfma_util"] = cnt["MfmaUtil"]["avg"] / 100.0
     out = {
         "metric": METRIC,
         "value": main_res["value"],
@@ -914,7 +986,7 @@ def main():
         "roofline": roofline,
         "roofline_decode": {"bound": "hbm", "kernel": "decode", "achieved": dec_gbps,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
-                            "traffic": traffic_per_launch("decode_bytes_per_launch") if is_ref_cfg else None,
+                            "traffic": traffic_per_launch("decode_kernel") if is_ref_cfg else None,
                             "algorithmic_per_launch": dec_bytes_launch, "avg_launch_ms": d_ms,
                             "avg_launch_ms_per_role": main_res["decode_ms_per_role"],
                             "GBps_per_role": main_res["decode_GBps_per_role"]},
