@@ -273,6 +273,22 @@ int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, 
                 const int32_t *seq_len, float *out, void *workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/* hqmq_attend for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and results, with the split partials
+ * kept in a library-owned device array of HQMQ_ATTEND_SCRATCH_BYTES per GPU
+ * (a file-scope array each GPU holds until the process ends) instead of a
+ * caller workspace.  The call allocates nothing; its first call on a device
+ * looks the array's address up once.  stream must belong to the current
+ * device.  Calls that overlap on one GPU share the array and race: order
+ * them on one stream (or with events).  Errors: as hqmq_attend, and
+ * HQMQ_ENOTSUP when hqmq_attn_sizes() gives a workspace larger than
+ * HQMQ_ATTEND_SCRATCH_BYTES (nothing enqueued). */
+#define HQMQ_ATTEND_SCRATCH_BYTES ((size_t)16 << 20)
+int hqmq_attend_noalloc(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k,
+                        const float *codebook_k, const hqmq_enc *v, const float *codebook_v, const void *q,
+                        const int64_t *seq_start, const int32_t *seq_len, float *out, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Paged cache with streaming append.  A serving loop keeps each role's
  * records in a pool of fixed-size pages, appends every step's new tokens

@@ -2,8 +2,8 @@
 
     python -m kv_cache_quantization_hqmq_amd.build
 
-compiles csrc/hqmq_kernels.hip, csrc/hqmq_attend.hip, csrc/hqmq_ceiling.hip and
-csrc/hqmq_api.cpp with hipcc into
+compiles csrc/hqmq_kernels.hip, csrc/hqmq_attend.hip, csrc/hqmq_ceiling.hip,
+csrc/hqmq_noalloc.hip and csrc/hqmq_api.cpp with hipcc into
 kv_cache_quantization_hqmq_amd/libhqmq.so.  Every HIP translation unit is
 built with packed FP32 disabled and fp contraction off (each fused
 multiply-add in the kernels is written out).
@@ -54,7 +54,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    for src in ("hqmq_kernels.hip", "hqmq_attend.hip", "hqmq_ceiling.hip", "hqmq_api.cpp"):
+    for src in ("hqmq_kernels.hip", "hqmq_attend.hip", "hqmq_ceiling.hip", "hqmq_noalloc.hip", "hqmq_api.cpp"):
         obj = os.path.join(bdir, src + ".o")
         extra = ["-x", "hip", *KERNEL_FLAGS] if src.endswith(".hip") else []
         _run([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)

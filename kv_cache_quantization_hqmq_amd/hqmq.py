@@ -28,7 +28,8 @@ HQMQ_NORM_F16, HQMQ_NORM_PACKED = 0, 1
 # every symbol include/hqmq.h declares
 EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
            "hqmq_encode_timed", "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes",
-           "hqmq_attend", "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged",
+           "hqmq_attend", "hqmq_attend_noalloc", "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append",
+           "hqmq_attend_paged",
            "hqmq_ceiling_stream", "hqmq_ceiling_compute")
 
 # include/hqmq_ceiling.h
@@ -155,6 +156,10 @@ def lib():
                                   ctypes.c_void_p, ctypes.POINTER(Enc), ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.hqmq_attend_noalloc.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(AttnDesc), ctypes.POINTER(Enc),
+                                          ctypes.c_void_p, ctypes.POINTER(Enc), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]
         L.hqmq_paged_sizes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PagedDesc),
                                        ctypes.POINTER(PagedSizes)]
         L.hqmq_paged_clear.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PagedDesc), ctypes.POINTER(Pages),
@@ -172,7 +177,7 @@ def lib():
         L.hqmq_ceiling_compute.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.POINTER(ctypes.c_double)]
         for f in ("hqmq_sizes", "hqmq_make_codebook", "hqmq_encode", "hqmq_encode_timed",
-                  "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes", "hqmq_attend",
+                  "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes", "hqmq_attend", "hqmq_attend_noalloc",
                   "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged",
                   "hqmq_ceiling_stream", "hqmq_ceiling_compute"):
             getattr(L, f).restype = ctypes.c_int
@@ -277,6 +282,18 @@ def hqmq_attend(desc: Desc, adesc: AttnDesc, rec_k: "Records", codebook_k, rec_v
                            _ptr(seq_start), _ptr(seq_len), _ptr(out), _ptr(workspace), ws_bytes,
                            _stream(stream))
     _check(rc, "hqmq_attend")
+
+
+HQMQ_ATTEND_SCRATCH_BYTES = 16 << 20   # include/hqmq.h
+
+
+def hqmq_attend_noalloc(desc: Desc, adesc: AttnDesc, rec_k: "Records", codebook_k, rec_v: "Records",
+                        codebook_v, q, seq_start, seq_len, out, stream=None) -> None:
+    """hqmq_attend with the library's own per-GPU scratch (no workspace)."""
+    rc = lib().hqmq_attend_noalloc(ctypes.byref(desc), ctypes.byref(adesc), ctypes.byref(rec_k.c),
+                                   _ptr(codebook_k), ctypes.byref(rec_v.c), _ptr(codebook_v), _ptr(q),
+                                   _ptr(seq_start), _ptr(seq_len), _ptr(out), _stream(stream))
+    _check(rc, "hqmq_attend_noalloc")
 
 
 def hqmq_paged_sizes(desc: Desc, pdesc: PagedDesc) -> PagedSizes:
