@@ -49,6 +49,30 @@
  *          not fit out_capacity (entries past the capacity are dropped;
  *          their chunks decode to the bulk value of their record).
  *
+ * Exact-rate records (norm_format HQMQ_NORM_EXACT, S a power of two): the
+ * pages' rate of two log2(24 S)-bit codes per chunk (about 3.79 bits per
+ * element at S = 8 and 4.79 at S = 32; the abstract, and the
+ * signal-ia-rouge.vercel.app article, "La mecanique") without whole-bit
+ * rounding.  The index k keeps its meaning; the norm code n has R = 24 S
+ * levels: n = R - 1 is the Med3x flag, level n < R - 1 stands for the
+ * binary16 half-norm pattern nearest n 2^15 / R (R / 32 levels per binade),
+ * and n is the level whose value is nearest the binary16 half-norm h16 (a
+ * tie to the even level, capped at the top finite level).  With R = 3 2^m
+ * every code is 2^m d + l: m low bits l and a ternary digit d.  idx then
+ * holds [layers][kv_heads][ceil(tokens / 4)][group_words] u32 (hnorm is
+ * unused and may be NULL): one group per 4 token rows (rows past the end
+ * are zero), wl = ceil(head_dim / 4 * m / 32), fh = ceil(head_dim / 32):
+ *   words [0, 4 wl)      index low bits, row r's stream at word r wl, chunk c's
+ *                        bits at stream bits c m .. c m + m - 1 (stream bit j is
+ *                        bit j % 32 of word j / 32)
+ *   words [4 wl, 8 wl)   norm low bits, the same way
+ *   words [8 wl, end)    a stream of 13-bit fields: row r's 2 fh fields start
+ *                        at bit 26 fh r; field f < fh holds the index digits of
+ *                        chunks 8 f .. 8 f + 7, field fh + f their norm digits,
+ *                        as sum_i d_i 3^i (3^8 <= 2^13).
+ * At head_dim 128 a group is 61 words at S = 8 (3.8125 bits per element)
+ * and 77 words at S = 32 (4.8125).
+ *
  * Decoding: bulk chunk y = (2 * h) * (q_p * q_s) in fp32, rounded to the
  * output type, h the binary16 half-norm (packed format: the value the code
  * stands for); outlier chunk y = its side-list values.
@@ -93,8 +117,8 @@ enum { HQMQ_F16 = 0, HQMQ_F32 = 1 };
 /* Roles: which cache tensor a codebook belongs to. */
 enum { HQMQ_ROLE_K = 0, HQMQ_ROLE_V = 1 };
 
-/* Norm record formats (see hnorm above). */
-enum { HQMQ_NORM_F16 = 0, HQMQ_NORM_PACKED = 1 };
+/* Norm record formats (see hnorm above; HQMQ_NORM_EXACT: see below). */
+enum { HQMQ_NORM_F16 = 0, HQMQ_NORM_PACKED = 1, HQMQ_NORM_EXACT = 2 };
 
 /* Problem descriptor (a plain value, read only during the call).
  *   layers, kv_heads, tokens >= 0 (any of them 0 = empty input)
@@ -106,7 +130,8 @@ enum { HQMQ_NORM_F16 = 0, HQMQ_NORM_PACKED = 1 };
  *       current batch", gist.science/nl Methodologie 3).
  *   med_C: Med3x multiplier, the pages fix 3 (finite, > 0 when Med3x is on)
  *   dtype: HQMQ_F16 or HQMQ_F32 for x (and y)
- *   norm_format: HQMQ_NORM_F16 or HQMQ_NORM_PACKED. */
+ *   norm_format: HQMQ_NORM_F16, HQMQ_NORM_PACKED or HQMQ_NORM_EXACT (S a
+ *       power of two, else HQMQ_ENOTSUP; not for paged pools). */
 typedef struct hqmq_desc {
     int64_t layers;
     int64_t kv_heads;
@@ -128,13 +153,16 @@ typedef struct hqmq_sizes_t {
     int64_t max_outliers;       /* sum over batches of floor(n_batch / 2) (every
                                    chunk when fl(med_C * med_C) < 1) */
     uint64_t input_bytes;       /* x (and y) */
-    uint64_t idx_bytes;
-    uint64_t hnorm_bytes;       /* chunks * 2 (binary16), or idx_bytes (packed) */
+    uint64_t idx_bytes;         /* exact: slices * ceil(tokens / 4) * group_words * 4 */
+    uint64_t hnorm_bytes;       /* chunks * 2 (binary16), idx_bytes (packed), 0 (exact) */
     uint64_t offsets_bytes;     /* (batches + 1) * 8, 0 when Med3x is off */
     uint64_t side_entry_bytes;  /* 12 bytes per outlier (4 pos + 8 values) */
-    uint64_t workspace_bytes;   /* encode scratch: Med3x histograms and bitmasks, and
-                                   the binary16 half-norms when packed (0 if neither) */
+    uint64_t workspace_bytes;   /* encode scratch: Med3x histograms and bitmasks, the
+                                   binary16 half-norms when packed or exact, and the
+                                   whole-bit codes when exact (0 if none) */
     uint64_t codebook_bytes;    /* layers * kv_heads * S * 16 */
+    int32_t group_rows;         /* HQMQ_NORM_EXACT: 4 token rows per record group, else 0 */
+    int32_t group_words;        /* HQMQ_NORM_EXACT: u32 words per group, else 0 */
 } hqmq_sizes_t;
 
 /* Encoded records: device pointers owned by the caller (see layout above).

@@ -11,7 +11,7 @@ from .hqmq import (AttnDesc, AttnSizes, CapacityError, Desc, HQMQError, PagedDes
                    attend_paged, decode, encode, hqmq_append, hqmq_attend, hqmq_attend_paged,
                    hqmq_attn_sizes, hqmq_decode, hqmq_paged_clear, hqmq_paged_sizes,
                    hqmq_encode, hqmq_encode_result, hqmq_encode_timed, hqmq_make_codebook, hqmq_sizes,
-                   hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_NORM_F16, HQMQ_NORM_PACKED,
+                   hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_NORM_F16, HQMQ_NORM_PACKED, HQMQ_NORM_EXACT,
                    HQMQ_ROLE_K, HQMQ_ROLE_V, hqmq_ceiling_compute, hqmq_ceiling_stream, HQMQ_CEIL_READ,
                    HQMQ_CEIL_WRITE, HQMQ_CEIL_COPY, HQMQ_CEIL_FMA_F32, HQMQ_CEIL_MFMA_F32, HQMQ_CEIL_MFMA_F16)
 
@@ -21,6 +21,6 @@ __all__ = ["AttnDesc", "AttnSizes", "CapacityError", "Desc", "HQMQError", "Paged
            "hqmq_attend_paged", "hqmq_attn_sizes", "hqmq_paged_clear", "hqmq_paged_sizes",
            "hqmq_decode", "hqmq_encode", "hqmq_encode_result", "hqmq_encode_timed",
            "hqmq_make_codebook", "hqmq_sizes", "hqmq_strerror", "workspace", "HQMQ_F16",
-           "HQMQ_F32", "HQMQ_NORM_F16", "HQMQ_NORM_PACKED", "HQMQ_ROLE_K", "HQMQ_ROLE_V",
+           "HQMQ_F32", "HQMQ_NORM_F16", "HQMQ_NORM_PACKED", "HQMQ_NORM_EXACT", "HQMQ_ROLE_K", "HQMQ_ROLE_V",
            "hqmq_ceiling_compute", "hqmq_ceiling_stream", "HQMQ_CEIL_READ", "HQMQ_CEIL_WRITE", "HQMQ_CEIL_COPY",
            "HQMQ_CEIL_FMA_F32", "HQMQ_CEIL_MFMA_F32", "HQMQ_CEIL_MFMA_F16"]

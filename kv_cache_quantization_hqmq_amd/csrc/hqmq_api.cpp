@@ -33,7 +33,8 @@ int make_geometry(const hqmq_desc *d, hqmq::Geometry *g) {
     if (!head_dim_ok(d->head_dim)) return HQMQ_EINVAL;
     if (d->S < 1 || d->S > kMaxS) return HQMQ_EINVAL;
     if (d->dtype != HQMQ_F16 && d->dtype != HQMQ_F32) return HQMQ_EINVAL;
-    if (d->norm_format != HQMQ_NORM_F16 && d->norm_format != HQMQ_NORM_PACKED) return HQMQ_EINVAL;
+    if (d->norm_format != HQMQ_NORM_F16 && d->norm_format != HQMQ_NORM_PACKED && d->norm_format != HQMQ_NORM_EXACT)
+        return HQMQ_EINVAL;
     if (d->med_batch_tokens < 0) return HQMQ_EINVAL;
     if (d->med_batch_tokens > 0 && !(std::isfinite(d->med_C) && d->med_C > 0.0f)) return HQMQ_EINVAL;
     const int64_t cpt = d->head_dim / 4;
@@ -58,20 +59,36 @@ int make_geometry(const hqmq_desc *d, hqmq::Geometry *g) {
     }
     g->med_C = d->med_C;
     g->npack = d->norm_format == HQMQ_NORM_PACKED ? 1 : 0;
+    g->exact = d->norm_format == HQMQ_NORM_EXACT ? 1 : 0;
+    if (g->exact) {
+        // 24 S = 3 2^m needs S a power of two
+        if ((d->S & (d->S - 1)) != 0) return HQMQ_ENOTSUP;
+        const int m = 3 + __builtin_ctz(static_cast<unsigned>(d->S));
+        g->em = m;
+        g->ewl = static_cast<int32_t>((cpt * m + 31) / 32);
+        g->efh = static_cast<int32_t>((cpt + 7) / 8);
+        g->egw = 8 * g->ewl + (4 * 2 * g->efh * 13 + 31) / 32;
+        g->egps = (d->tokens + 3) / 4;
+        // levels n < R - 1 whose pattern floor((n 2^(15 - m) + 1) / 3) is below 0x7C00
+        const uint32_t top = 95230u >> (15 - m);
+        g->enmax = std::min((3u << m) - 2u, top);
+        g->estep = static_cast<float>(std::ldexp(1.0, 15 - m) / 3.0);
+    }
     // grids are one-dimensional: keep the block count well inside 2^31
     if (g->slices > 0 && g->n_slice / 256 + 1 > (int64_t{1} << 31) / g->slices) return HQMQ_ENOTSUP;
     return HQMQ_OK;
 }
 
 // Encode workspace.  Med3x: hist [batches][2048] u32 | counts [batches] u32 |
-// mask [batches][mask_words] u32 (one bit per chunk).  Packed norms: the
-// binary16 half-norm plane [chunks] u16 that the search writes, Med3x flags,
-// and the pack kernel reads.
+// mask [batches][mask_words] u32 (one bit per chunk).  Packed and exact
+// norms: the binary16 half-norm plane [chunks] u16 that the search writes,
+// Med3x flags, and the pack kernel reads.  Exact format: also the whole-bit
+// code plane [slices][tokens][words] u32 of the search.
 int64_t mask_words(const hqmq::Geometry &g) { return 2 * ((g.batch_chunks + 63) / 64); }
 
 uint64_t workspace_layout(const hqmq::Geometry &g, void *base, hqmq::Med3Work *w) {
     uint64_t off = 0;
-    uint64_t o_hist = 0, o_cnt = 0, o_mask = 0, o_h16 = 0;
+    uint64_t o_hist = 0, o_cnt = 0, o_mask = 0, o_h16 = 0, o_idx = 0;
     const uint64_t mw = static_cast<uint64_t>(mask_words(g));
     if (g.batch_chunks > 0) {
         const uint64_t nb = static_cast<uint64_t>(g.slices * g.batches_per_slice);
@@ -82,9 +99,13 @@ uint64_t workspace_layout(const hqmq::Geometry &g, void *base, hqmq::Med3Work *w
         o_mask = off;
         off = align_up(off + nb * mw * 4, kWsAlign);
     }
-    if (g.npack) {
+    if (g.npack || g.exact) {
         o_h16 = off;
         off = align_up(off + static_cast<uint64_t>(g.slices * g.n_slice) * 2, kWsAlign);
+    }
+    if (g.exact) {
+        o_idx = off;
+        off = align_up(off + static_cast<uint64_t>(g.slices * g.tokens) * g.words * 4, kWsAlign);
     }
     if (w) {
         char *b = static_cast<char *>(base);
@@ -95,7 +116,8 @@ uint64_t workspace_layout(const hqmq::Geometry &g, void *base, hqmq::Med3Work *w
             w->mask = reinterpret_cast<uint32_t *>(b + o_mask);
             w->mask_words = static_cast<int64_t>(mw);
         }
-        if (g.npack) w->h16 = reinterpret_cast<uint16_t *>(b + o_h16);
+        if (g.npack || g.exact) w->h16 = reinterpret_cast<uint16_t *>(b + o_h16);
+        if (g.exact) w->idx32 = reinterpret_cast<uint32_t *>(b + o_idx);
     }
     return off;
 }
@@ -155,8 +177,8 @@ static int attn_plan(const hqmq_desc *d, const hqmq::Geometry &g, const hqmq_att
         return HQMQ_EINVAL;
     if (a->layer < 0 || (a->layer >= d->layers && !(d->layers == 0 && a->batch == 0))) return HQMQ_EINVAL;
     if (d->dtype != HQMQ_F16) return HQMQ_ENOTSUP;
-    if (hqmq::attend_lds_bytes(static_cast<int>(d->head_dim), g.S) == 0) return HQMQ_ENOTSUP;
-    if (hqmq::attend_lds_bytes(static_cast<int>(d->head_dim), g.S) > 160 * 1024) return HQMQ_ENOTSUP;
+    if (hqmq::attend_lds_bytes(static_cast<int>(d->head_dim), g.S, g.exact) == 0) return HQMQ_ENOTSUP;
+    if (hqmq::attend_lds_bytes(static_cast<int>(d->head_dim), g.S, g.exact) > 160 * 1024) return HQMQ_ENOTSUP;
     if (d->kv_heads > 4096) return HQMQ_ENOTSUP;
     const int64_t pairs = std::max<int64_t>(1, static_cast<int64_t>(a->batch) * d->kv_heads);
     int64_t want = (1024 + pairs - 1) / pairs;
@@ -174,6 +196,7 @@ static int attn_plan(const hqmq_desc *d, const hqmq::Geometry &g, const hqmq_att
 // Paged pool geometry: validate p against the codec geometry g.
 static int paged_geometry(const hqmq::Geometry &g, const hqmq_paged_desc *p, int32_t *log2_page) {
     if (!p) return HQMQ_EINVAL;
+    if (g.exact) return HQMQ_ENOTSUP;   // pools keep whole-bit token rows
     const int64_t P = p->page_tokens;
     if (p->num_pages < 0 || p->page_capacity < 0 || P < 16 || (P & (P - 1)) != 0) return HQMQ_EINVAL;
     if (p->num_pages >= (int64_t{1} << 31) || P * g.cpt >= (int64_t{1} << 31)) return HQMQ_ENOTSUP;
@@ -277,8 +300,15 @@ int hqmq_sizes(const hqmq_desc *d, hqmq_sizes_t *out) {
     }
     out->max_outliers = mo;
     out->input_bytes = static_cast<uint64_t>(out->chunks) * 4 * (g.f32 ? 4 : 2);
-    out->idx_bytes = static_cast<uint64_t>(g.slices * g.tokens) * g.words * 4;
-    out->hnorm_bytes = g.npack ? out->idx_bytes : static_cast<uint64_t>(out->chunks) * 2;
+    if (g.exact) {
+        out->idx_bytes = static_cast<uint64_t>(g.slices * g.egps) * g.egw * 4;
+        out->hnorm_bytes = 0;
+        out->group_rows = 4;
+        out->group_words = g.egw;
+    } else {
+        out->idx_bytes = static_cast<uint64_t>(g.slices * g.tokens) * g.words * 4;
+        out->hnorm_bytes = g.npack ? out->idx_bytes : static_cast<uint64_t>(out->chunks) * 2;
+    }
     out->offsets_bytes = g.batch_chunks > 0 ? static_cast<uint64_t>(out->batches + 1) * 8 : 0;
     out->side_entry_bytes = 12;
     out->workspace_bytes = workspace_layout(g, nullptr, nullptr);
@@ -334,8 +364,9 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
     const bool med = g.batch_chunks > 0;
     const int64_t nb = g.slices * g.batches_per_slice;
     if (chunks > 0) {
-        if (!x || !codebook || !enc->idx || !enc->hnorm) return HQMQ_EINVAL;
-        if (!aligned(x, 16) || !aligned(codebook, 16) || !aligned(enc->idx, 4) || !aligned(enc->hnorm, 8))
+        if (!x || !codebook || !enc->idx || (!enc->hnorm && !g.exact)) return HQMQ_EINVAL;
+        if (!aligned(x, 16) || !aligned(codebook, 16) || !aligned(enc->idx, 4) ||
+            (!g.exact && !aligned(enc->hnorm, 8)))
             return HQMQ_EINVAL;
     }
     hqmq::Med3Work ws{};
@@ -353,9 +384,11 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
             return HQMQ_EINVAL;
         if (need > 0) workspace_layout(g, workspace, &ws);
     }
-    // the binary16 half-norms: the record itself, or (packed) the scratch
-    // plane the pack kernel turns into compact codes at the end
-    uint16_t *h16 = g.npack ? ws.h16 : static_cast<uint16_t *>(enc->hnorm);
+    // the binary16 half-norms: the record itself, or (packed, exact) the
+    // scratch plane the pack kernels turn into norm codes at the end; the
+    // whole-bit codes: the record, or (exact) a scratch plane
+    uint16_t *h16 = (g.npack || g.exact) ? ws.h16 : static_cast<uint16_t *>(enc->hnorm);
+    uint32_t *idx32 = g.exact ? ws.idx32 : enc->idx;
 
     hipError_t e = hipSuccess;
     if (med && nb > 0) {
@@ -368,7 +401,7 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
     }
     if (search_begin && hipEventRecord(search_begin, stream) != hipSuccess) return HQMQ_EHIP;
     if (chunks > 0) {
-        e = hqmq::launch_encode_search(g, x, codebook, enc->idx, h16, med && nb > 0 ? &ws : nullptr, stream);
+        e = hqmq::launch_encode_search(g, x, codebook, idx32, h16, med && nb > 0 ? &ws : nullptr, stream);
         if (e != hipSuccess) return HQMQ_EHIP;
     }
     if (search_end && hipEventRecord(search_end, stream) != hipSuccess) return HQMQ_EHIP;
@@ -392,6 +425,7 @@ int hqmq_encode_timed(const hqmq_desc *d, const void *x, const float *codebook, 
     const bool packed_by_select = med && nb > 0 && hqmq::med3_single_pass(g);
     if (e == hipSuccess && g.npack && chunks > 0 && !packed_by_select)
         e = hqmq::launch_pack_norms(g, h16, static_cast<uint32_t *>(enc->hnorm), stream);
+    if (e == hipSuccess && g.exact && chunks > 0) e = hqmq::launch_pack_exact(g, idx32, h16, enc->idx, stream);
     return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
 }
 
@@ -414,8 +448,8 @@ int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, 
     if (!enc) return HQMQ_EINVAL;
     const int64_t chunks = g.slices * g.n_slice;
     if (chunks == 0) return HQMQ_OK;
-    if (!y || !codebook || !enc->idx || !enc->hnorm) return HQMQ_EINVAL;
-    if (!aligned(y, 16) || !aligned(codebook, 16) || !aligned(enc->idx, 4) || !aligned(enc->hnorm, 8))
+    if (!y || !codebook || !enc->idx || (!enc->hnorm && !g.exact)) return HQMQ_EINVAL;
+    if (!aligned(y, 16) || !aligned(codebook, 16) || !aligned(enc->idx, 4) || (!g.exact && !aligned(enc->hnorm, 8)))
         return HQMQ_EINVAL;
     if (g.batch_chunks > 0) {
         if (!enc->batch_offsets) return HQMQ_EINVAL;
@@ -465,8 +499,8 @@ int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, 
     for (int r = 0; r < 2; ++r) {
         const hqmq_enc *e = enc[r];
         const bool data = g.tokens > 0;
-        if (data && (!e->idx || !e->hnorm || !cb[r] || !aligned(e->idx, 4) || !aligned(e->hnorm, 16) ||
-                     !aligned(cb[r], 16)))
+        if (data && (!e->idx || (!g.exact && (!e->hnorm || !aligned(e->hnorm, 16))) || !cb[r] ||
+                     !aligned(e->idx, 4) || !aligned(cb[r], 16)))
             return HQMQ_EINVAL;
         if (data && g.batch_chunks > 0) {
             if (!e->batch_offsets || !aligned(e->batch_offsets, 8)) return HQMQ_EINVAL;
@@ -500,6 +534,13 @@ int hqmq_attend(const hqmq_desc *d, const hqmq_attn_desc *a, const hqmq_enc *k, 
     L.bits = g.bits;
     L.words = g.words;
     L.npack = g.npack;
+    L.exact = g.exact;
+    L.em = g.em;
+    L.ewl = g.ewl;
+    L.efh = g.efh;
+    L.egw = g.egw;
+    L.egps = g.egps;
+    L.estep = g.estep;
     L.scale = a->scale;
     return hqmq::launch_attend(L, stream) == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
 }

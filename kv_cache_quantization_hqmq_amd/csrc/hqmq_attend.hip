@@ -76,7 +76,14 @@ struct AttArgs {
     int64_t num_pages;
     int32_t pt_stride, log2_page;
     uint32_t page_cap;          // side-list entries per (layer, head, page)
-};  // r[].hnorm: binary16 half-norms, or packed compact codes (kernel's NPACK)
+    // exact-rate records (NF == kNormExact): idx holds [slices][gps][gw] groups
+    int64_t gps;
+    int32_t m, wl, fh, gw;
+    float step;
+};  // r[].hnorm: binary16 half-norms, or packed compact codes (NF == kNormPacked)
+
+// Norm formats: binary16 half-norms, packed compact codes, exact-rate groups.
+constexpr int kNormF16 = 0, kNormPacked = 1, kNormExact = 2;
 
 // First entry in [lo, hi) of a position-sorted side list whose position is
 // at least p0 (hi when none): a 64-way search per round.
@@ -153,13 +160,22 @@ constexpr bool words_in_row(int cpl, int bits, int nw) {
     return true;
 }
 
-template <int D, int BITS, bool NPACK>
+template <int D, int BITS, int NF>
 struct TileRegs {
     static constexpr int CPL = D / 16;
-    static constexpr int NW = BITS > 0 ? (max_code_shift(CPL, BITS) + CPL * BITS + 31) / 32 : CPL;
-    static_assert(BITS == 0 || words_in_row(CPL, BITS, NW), "a lane's words must stay in its row");
-    uint32_t hw[NPACK ? NW : CPL / 2];   // binary16 code pairs, or packed norm words
-    uint32_t w[NW];
+    static constexpr bool EXACT = NF == kNormExact;
+    // exact-rate records: BITS is m (0: any m up to 13); a window of NWL
+    // words holds the lane's low bits of one plane, 2 words its digit fields
+    static constexpr int NWL = BITS > 0 ? (max_code_shift(CPL, BITS) + CPL * BITS + 31) / 32
+                                        : (31 + CPL * 13 + 31) / 32;
+    static constexpr int NW = EXACT ? NWL + 2
+                                    : (BITS > 0 ? (max_code_shift(CPL, BITS) + CPL * BITS + 31) / 32 : CPL);
+    static_assert(EXACT || BITS == 0 || words_in_row(CPL, BITS, NW), "a lane's words must stay in its row");
+    // binary16 code pairs, packed norm words, or (exact) the norm plane's
+    // low-bit and digit windows
+    uint32_t hw[NF == kNormF16 ? CPL / 2 : NW];
+    uint32_t w[NW];   // index words (exact: low-bit window, then digit window)
+    uint32_t dsh[EXACT ? 1 : 0];   // exact: bit offsets of the index | norm << 8 digit fields
 };
 
 // Waves per SIMD the register budget is set for: two 8-wave blocks per CU
@@ -168,17 +184,20 @@ struct TileRegs {
 // spills) otherwise.
 constexpr int attend_waves_per_eu(int D, bool table, int bits) { return D <= 128 && table && bits > 0 ? 4 : 2; }
 
-template <int D, bool TABLE, int BITS, bool NPACK, bool PAGED>
+template <int D, bool TABLE, int BITS, int NF, bool PAGED>
 __global__ __launch_bounds__(kAttThreads)
 __attribute__((amdgpu_waves_per_eu(attend_waves_per_eu(D, TABLE, BITS), attend_waves_per_eu(D, TABLE, BITS))))
 void attend_split_kernel(AttArgs a) {
     using Sh = AttShape<D>;
     constexpr int CPT = Sh::CPT, CPL = Sh::CPL, KB = Sh::KB, NU = Sh::NU, ROWB = Sh::ROWB, TILEB = Sh::TILEB;
+    constexpr bool NPACK = NF == kNormPacked;
+    constexpr bool EXACT = NF == kNormExact;   // BITS is then m (0: any)
+    static_assert(!(EXACT && PAGED), "paged pools keep whole-bit token rows");
 
     extern __shared__ f32x4 smem[];
     // codeword tables: TABLE kernels of a fixed code width hold all 2^BITS
     // codes (zeros past 24 S), so a code read from the records needs no clamp
-    const int ntab = TABLE ? (BITS > 0 ? (1 << BITS) : 24 * a.S) : a.S;
+    const int ntab = TABLE ? ((BITS > 0 && !EXACT) ? (1 << BITS) : 24 * a.S) : a.S;
     f32x4 *tab = smem;                                                     // [2][ntab]
     unsigned char *tiles = reinterpret_cast<unsigned char *>(smem + 2 * ntab);   // [waves][TILEB]
 
@@ -320,6 +339,7 @@ void attend_split_kernel(AttArgs a) {
     // (one per lane), loaded one tile ahead.
     const int ti = lane & 15;
     const int c0 = (lane >> 4) * CPL;
+    const int em = BITS > 0 ? BITS : a.m;   // exact-rate records: low bits per code
     const int cbits = BITS > 0 ? BITS : a.bits;
     const uint32_t sh0 = static_cast<uint32_t>(c0 * cbits) & 31u;
     const int w0 = (c0 * cbits) >> 5;
@@ -335,9 +355,43 @@ void attend_split_kernel(AttArgs a) {
     // valid row and are masked when decoded) and address a tile base common
     // to the wave plus a per-lane offset, so that the compiler keeps them in
     // flight across the decode of the current tile.
-    auto load_tile = [&](int r, int64_t tb, int nvalid, TileRegs<D, BITS, NPACK> &tr) {
+    auto load_tile = [&](int r, int64_t tb, int nvalid, TileRegs<D, BITS, NF> &tr) {
         const AttRole &R = a.r[r];
         const uint32_t ri = static_cast<uint32_t>(nvalid > 0 ? (ti < nvalid ? ti : nvalid - 1) : 0);
+        if constexpr (EXACT) {
+            // the tile's rows lie in at most 5 groups from the one holding
+            // slice token tb - sl * tokens; lane token ri is row (st & 3) of
+            // group st / 4 (the buffer resource's range spans those groups)
+            using TR = TileRegs<D, BITS, NF>;
+            const int64_t st0 = tb - sl * a.tokens;
+            const uint32_t st = static_cast<uint32_t>(st0 & 3) + ri;   // token relative to the first group
+            // (the range ends at the slice's last group: window words past it read 0)
+            const int64_t ng = a.gps - (st0 >> 2) < 5 ? a.gps - (st0 >> 2) : 5;
+            const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint32_t *>(R.idx + (sl * a.gps + (st0 >> 2)) * a.gw), 0,
+                static_cast<int>(ng * a.gw * 4), kBufWord3);
+            const uint32_t rr = st & 3u;
+            const uint32_t gbase = __umul24(st >> 2, static_cast<uint32_t>(a.gw));
+            const uint32_t lbit = static_cast<uint32_t>(c0 * em);
+            const uint32_t lk = gbase + __umul24(rr, static_cast<uint32_t>(a.wl)) + (lbit >> 5);
+            const uint32_t ln = lk + 4u * static_cast<uint32_t>(a.wl);
+            const uint32_t fk = static_cast<uint32_t>(kFieldBits) *
+                                (__umul24(2u * static_cast<uint32_t>(a.fh), rr) + static_cast<uint32_t>(c0 / kDigitsPerField));
+            const uint32_t fn = fk + static_cast<uint32_t>(kFieldBits * a.fh);
+            const uint32_t dbase = gbase + 8u * static_cast<uint32_t>(a.wl);
+            tr.dsh[0] = (fk & 31u) | ((fn & 31u) << 8);
+#pragma unroll
+            for (int k = 0; k < TR::NWL; ++k) {
+                tr.w[k] = __builtin_amdgcn_raw_buffer_load_b32(gr, static_cast<int>((lk + k) * 4u), 0, 0);
+                tr.hw[k] = __builtin_amdgcn_raw_buffer_load_b32(gr, static_cast<int>((ln + k) * 4u), 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                tr.w[TR::NWL + k] = __builtin_amdgcn_raw_buffer_load_b32(gr, static_cast<int>((dbase + (fk >> 5) + k) * 4u), 0, 0);
+                tr.hw[TR::NWL + k] = __builtin_amdgcn_raw_buffer_load_b32(gr, static_cast<int>((dbase + (fn >> 5) + k) * 4u), 0, 0);
+            }
+            return;
+        }
         // buffer resources over the tile's rows (wave-uniform bases; lanes
         // add 32-bit offsets, fixed word offsets go in the instructions)
         const int words = a.words;
@@ -371,7 +425,7 @@ void attend_split_kernel(AttArgs a) {
         if constexpr (BITS > 0) {
             const int lo = static_cast<int>((ro + static_cast<uint32_t>(w0)) * 4u);
 #pragma unroll
-            for (int k = 0; k < TileRegs<D, BITS, NPACK>::NW; ++k) {
+            for (int k = 0; k < TileRegs<D, BITS, NF>::NW; ++k) {
                 tr.w[k] = __builtin_amdgcn_raw_buffer_load_b32(ir, lo + 4 * k, 0, 0);
                 if constexpr (NPACK) tr.hw[k] = __builtin_amdgcn_raw_buffer_load_b32(nr, lo + 4 * k, 0, 0);
             }
@@ -392,7 +446,9 @@ void attend_split_kernel(AttArgs a) {
     };
 
     // entries at and past end[r] are never used; lanes past it read a valid
-    // address (the last entry, or the half-norm array when there is none)
+    // address (the last entry, or, when there is none, the first 8 bytes of
+    // the block's query rows, which every launch with work has: the exact
+    // format has no norm plane to point at)
     uint64_t sv[2];   // side-list entries cur[r] + lane: values (4 x fp16)
     uint32_t sp[2];   // and positions
     auto load_window = [&](int r) {
@@ -400,8 +456,8 @@ void attend_split_kernel(AttArgs a) {
         const uint32_t last = left > 64u ? 63u : (left > 0u ? static_cast<uint32_t>(left) - 1u : 0u);
         const bool any = left > 0u;
         const uint64_t *vb = any ? reinterpret_cast<const uint64_t *>(a.r[r].out_val) + cur[r]
-                                 : reinterpret_cast<const uint64_t *>(a.r[r].hnorm);
-        const uint32_t *pb = any ? a.r[r].out_pos + cur[r] : reinterpret_cast<const uint32_t *>(a.r[r].hnorm);
+                                 : reinterpret_cast<const uint64_t *>(a.q);
+        const uint32_t *pb = any ? a.r[r].out_pos + cur[r] : reinterpret_cast<const uint32_t *>(a.q);
         const uint32_t li = static_cast<uint32_t>(lane);
         sv[r] = vb[li < last ? li : last];
         sp[r] = pb[li < last ? li : last];
@@ -412,10 +468,10 @@ void attend_split_kernel(AttArgs a) {
     // Decode a loaded tile of role r into dst[token][chunk] (fp16), with the
     // decoder's arithmetic: 2 hnorm (a_p * q_s) in fp32, rounded to binary16.
     // the lane's CPL codes from its record words (index or packed norm)
-    using Words = uint32_t[TileRegs<D, BITS, NPACK>::NW];
+    using Words = uint32_t[TileRegs<D, BITS, NF>::NW];
     auto extract = [&](const Words &tw, uint32_t (&out)[CPL]) {
         if constexpr (BITS > 0) {
-            constexpr int NW = TileRegs<D, BITS, NPACK>::NW;
+            constexpr int NW = TileRegs<D, BITS, NF>::NW;
             uint32_t nw[NW];   // the lane's codes from bit 0
 #pragma unroll
             for (int k = 0; k + 1 < NW; ++k) nw[k] = __builtin_amdgcn_alignbit(tw[k + 1], tw[k], sh0);
@@ -438,27 +494,97 @@ void attend_split_kernel(AttArgs a) {
         }
     };
 
+    // exact-rate records: the lane's CPL full codes of one plane from its
+    // low-bit window (words 0 .. NWL-1, chunk c0's bits first) and digit
+    // window (words NWL, NWL+1): code = 2^m d + l
+    auto extract_exact = [&](const Words &tw, uint32_t dsh, uint32_t (&out)[CPL]) {
+        using TR = TileRegs<D, BITS, NF>;
+        constexpr int NWL = TR::NWL;
+        const uint32_t sh = static_cast<uint32_t>(c0 * em) & 31u;
+        const uint32_t lmask = (1u << em) - 1u;
+        if constexpr (BITS > 0) {
+            // the window from the lane's first bit, then fields at fixed places
+            uint32_t nw[NWL];
+#pragma unroll
+            for (int k = 0; k + 1 < NWL; ++k) nw[k] = __builtin_amdgcn_alignbit(tw[k + 1], tw[k], sh);
+            nw[NWL - 1] = tw[NWL - 1] >> sh;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int p = j * BITS, k = p >> 5, sft = p & 31;
+                if (sft + BITS <= 32) out[j] = (nw[k] >> sft) & lmask;
+                else out[j] = __builtin_amdgcn_alignbit(nw[k + 1], nw[k], sft) & lmask;
+            }
+        } else {
+            // any m: each field's two words picked from the window
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const uint32_t p = sh + static_cast<uint32_t>(j * em);
+                const uint32_t k = p >> 5;
+                uint32_t wlo = tw[0], whi = NWL > 1 ? tw[1] : 0u;
+#pragma unroll
+                for (int q = 1; q < NWL; ++q) {
+                    wlo = k == static_cast<uint32_t>(q) ? tw[q] : wlo;
+                    whi = k + 1 == static_cast<uint32_t>(q) ? tw[q] : whi;
+                }
+                out[j] = __builtin_amdgcn_alignbit(whi, wlo, p & 31u) & lmask;
+            }
+        }
+        // digit fields: CPL / 8 whole fields (CPL >= 8), or half of one
+        uint32_t v = __builtin_amdgcn_alignbit(tw[NWL + 1], tw[NWL], dsh);
+        if constexpr (CPL >= kDigitsPerField) {
+#pragma unroll
+            for (int f = 0; f < CPL / kDigitsPerField; ++f) {
+                uint32_t q = (v >> (kFieldBits * f)) & 0x1FFFu;
+#pragma unroll
+                for (int i = 0; i < kDigitsPerField; ++i) {
+                    const uint32_t q3 = div3_small(q);
+                    out[f * kDigitsPerField + i] |= (q - 3u * q3) << em;
+                    q = q3;
+                }
+            }
+        } else {
+            uint32_t q = v & 0x1FFFu;
+            if (c0 & 4) q = __umul24(q, 207127u) >> 24;   // skip digits 0..3: q / 81
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const uint32_t q3 = div3_small(q);
+                out[i] |= (q - 3u * q3) << em;
+                q = q3;
+            }
+        }
+    };
+
     // (after the tile: the cursor moves to the next page's list first when
     // the next tile starts a page, paged pools only)
     // (plo: slice position, or page position when paged, of the tile's
     // first chunk; rows at and past nvalid hold copies of a valid row)
-    auto decode_tile = [&](int r, const TileRegs<D, BITS, NPACK> &tr, int nvalid, unsigned char *dst, uint32_t plo,
+    auto decode_tile = [&](int r, const TileRegs<D, BITS, NF> &tr, int nvalid, unsigned char *dst, uint32_t plo,
                            bool newpage, uint64_t nlo, uint64_t nhi) {
         uint32_t hw[CPL / 2];
-        if constexpr (NPACK) {
+        uint32_t code[CPL];
+        if constexpr (EXACT) {
             uint32_t nc[CPL];
-            extract(tr.hw, nc);
-            const int nbits = BITS > 0 ? BITS : a.bits;
+            extract_exact(tr.hw, (tr.dsh[0] >> 8) & 31u, nc);
+            const uint32_t flag = (3u << em) - 1u;
 #pragma unroll
             for (int v = 0; v < CPL / 2; ++v)
-                hw[v] = compact_norm_h16(nc[2 * v], nbits) | (compact_norm_h16(nc[2 * v + 1], nbits) << 16);
+                hw[v] = exact_norm_h16(nc[2 * v], flag, a.step) | (exact_norm_h16(nc[2 * v + 1], flag, a.step) << 16);
+            extract_exact(tr.w, tr.dsh[0] & 31u, code);
         } else {
+            if constexpr (NPACK) {
+                uint32_t nc[CPL];
+                extract(tr.hw, nc);
+                const int nbits = BITS > 0 ? BITS : a.bits;
 #pragma unroll
-            for (int v = 0; v < CPL / 2; ++v) hw[v] = tr.hw[v];
+                for (int v = 0; v < CPL / 2; ++v)
+                    hw[v] = compact_norm_h16(nc[2 * v], nbits) | (compact_norm_h16(nc[2 * v + 1], nbits) << 16);
+            } else {
+#pragma unroll
+                for (int v = 0; v < CPL / 2; ++v) hw[v] = tr.hw[v];
+            }
+            extract(tr.w, code);
         }
-        uint32_t code[CPL];
-        extract(tr.w, code);
-        if constexpr (!(TABLE && BITS > 0)) {
+        if constexpr (!(TABLE && BITS > 0) || EXACT) {
 #pragma unroll
             for (int j = 0; j < CPL; ++j) code[j] = code[j] < kmax ? code[j] : kmax;
         }
@@ -547,7 +673,7 @@ void attend_split_kernel(AttArgs a) {
     for (int kb = 0; kb < KB; ++kb) o[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // one 16-token tile: prefetch the next into nxt, decode cur, attend
-    auto step = [&](int64_t t0, TileRegs<D, BITS, NPACK>(&cur_t)[2], TileRegs<D, BITS, NPACK>(&nxt_t)[2]) {
+    auto step = [&](int64_t t0, TileRegs<D, BITS, NF>(&cur_t)[2], TileRegs<D, BITS, NF>(&nxt_t)[2]) {
         const int nvalid = static_cast<int>(w_hi - t0 < kTile ? w_hi - t0 : kTile);
         const int64_t t1 = t0 + kTile;
         const int nv1 = t1 < w_hi ? static_cast<int>(w_hi - t1 < kTile ? w_hi - t1 : kTile) : 0;
@@ -639,7 +765,7 @@ void attend_split_kernel(AttArgs a) {
         wave_sync();
     };
 
-    TileRegs<D, BITS, NPACK> ta[2], tb[2];
+    TileRegs<D, BITS, NF> ta[2], tb[2];
     if (w_lo < w_hi) {
         const int nv = static_cast<int>(w_hi - w_lo < kTile ? w_hi - w_lo : kTile);
         const int64_t tb0 = tile_row(w_lo);
@@ -711,20 +837,30 @@ __global__ __launch_bounds__(D) void attend_combine_kernel(const float *part, in
 }
 
 template <int D>
-size_t attend_lds(int S, bool table) {
-    const int bits = attend_kernel_bits(S, table);
+size_t attend_lds(int S, bool table, bool exact) {
+    const int bits = exact ? 0 : attend_kernel_bits(S, table);
     const int ntab = table ? (bits > 0 ? (1 << bits) : 24 * S) : S;
     const size_t loop = 2 * static_cast<size_t>(ntab) * sizeof(f32x4) + kAttWaves * static_cast<size_t>(AttShape<D>::TILEB);
     const size_t merge = kAttWaves * static_cast<size_t>(AttShape<D>::MERGEB);
     return loop > merge ? loop : merge;
 }
 
-template <int D, bool NPACK, bool PAGED>
+template <int D, int NF, bool PAGED>
 const void *split_kernel_for(bool table, int bits) {
-    if (table && bits == 10) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 10, NPACK, PAGED>);
-    if (table && bits == 8) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 8, NPACK, PAGED>);
-    if (table) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0, NPACK, PAGED>);
-    return reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0, NPACK, PAGED>);
+    if (table && bits == 10) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 10, NF, PAGED>);
+    if (table && bits == 8) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 8, NF, PAGED>);
+    if (table) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0, NF, PAGED>);
+    return reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0, NF, PAGED>);
+}
+
+// Exact-rate records: kernels of a fixed m for S = 8 (m = 6) and S = 32
+// (m = 8), the general one for any other power of two.
+template <int D>
+const void *exact_kernel_for(bool table, int m) {
+    if (table && m == 8) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 8, kNormExact, false>);
+    if (table && m == 6) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 6, kNormExact, false>);
+    if (table) return reinterpret_cast<const void *>(&attend_split_kernel<D, true, 0, kNormExact, false>);
+    return reinterpret_cast<const void *>(&attend_split_kernel<D, false, 0, kNormExact, false>);
 }
 
 template <int D>
@@ -750,7 +886,13 @@ hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
     a.words = L.words;
     a.qscale = L.scale * 1.4426950408889634f;
     const bool table = L.S <= kAttTableMaxS;
-    const size_t lds = attend_lds<D>(L.S, table);
+    const size_t lds = attend_lds<D>(L.S, table, L.exact != 0);
+    a.gps = L.egps;
+    a.m = L.em;
+    a.wl = L.ewl;
+    a.fh = L.efh;
+    a.gw = L.egw;
+    a.step = L.estep;
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(L.batch) * L.heads * L.nsplit));
     // code widths of the common codebooks (S = 8: 8 bits, S = 32: 10) get
     // extraction at fixed bit positions; any other width the general path
@@ -760,10 +902,11 @@ hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
     a.log2_page = L.log2_page;
     a.page_cap = L.page_cap;
     const bool paged = L.page_table != nullptr;
-    const void *kern = paged ? (L.npack ? split_kernel_for<D, true, true>(table, L.bits)
-                                        : split_kernel_for<D, false, true>(table, L.bits))
-                             : (L.npack ? split_kernel_for<D, true, false>(table, L.bits)
-                                        : split_kernel_for<D, false, false>(table, L.bits));
+    const void *kern = L.exact ? exact_kernel_for<D>(table, L.em)
+                       : paged ? (L.npack ? split_kernel_for<D, kNormPacked, true>(table, L.bits)
+                                          : split_kernel_for<D, kNormF16, true>(table, L.bits))
+                               : (L.npack ? split_kernel_for<D, kNormPacked, false>(table, L.bits)
+                                          : split_kernel_for<D, kNormF16, false>(table, L.bits));
     // more than the default 64 KB of dynamic LDS must be asked for
     hipError_t e = hipSuccess;
     if (lds > 64 * 1024) {
@@ -782,12 +925,12 @@ hipError_t launch_attend_d(const AttLaunch &L, hipStream_t st) {
 
 }  // namespace
 
-size_t attend_lds_bytes(int head_dim, int S) {
+size_t attend_lds_bytes(int head_dim, int S, bool exact) {
     const bool table = S <= kAttTableMaxS;
     switch (head_dim) {
-        case 64: return attend_lds<64>(S, table);
-        case 128: return attend_lds<128>(S, table);
-        case 256: return attend_lds<256>(S, table);
+        case 64: return attend_lds<64>(S, table, exact);
+        case 128: return attend_lds<128>(S, table, exact);
+        case 256: return attend_lds<256>(S, table, exact);
         default: return 0;
     }
 }

@@ -104,5 +104,48 @@ __device__ __forceinline__ uint32_t compact_norm_h16(uint32_t c, int bits) {
     return c == (1u << bits) - 1u ? 0x8000u : c << (15 - bits);
 }
 
+// Exact-rate records (HQMQ_NORM_EXACT, S a power of two): the index and the
+// norm code both have R = 24 S = 3 2^m values; a code is 2^m d + l with l
+// its m low bits and d a ternary digit.  Digits are stored eight to a
+// 13-bit field as sum_i d_i 3^i.
+constexpr int kExactRows = 4;          // token rows per group
+constexpr int kDigitsPerField = 8;
+constexpr int kFieldBits = 13;
+
+// binary16 pattern of norm level n < R - 1: the integer nearest
+// n 2^15 / R = n 2^(15 - m) / 3 (never a tie).  n 2^(15 - m) / 3 is at most
+// 2^15 and its fraction is 0, 1/3 or 2/3, so the fp32 product with the
+// rounded constant (error below 0.01) plus 1/2 truncates to the nearest
+// integer.
+__device__ __forceinline__ uint32_t exact_level_pattern(uint32_t n, float level_step) {
+    return static_cast<uint32_t>(__builtin_fmaf(static_cast<float>(n), level_step, 0.5f));
+}
+
+// The binary16 half-norm record an exact-rate norm code stands for: the
+// flag for R - 1, else the level's pattern.
+__device__ __forceinline__ uint32_t exact_norm_h16(uint32_t n, uint32_t flag_code, float level_step) {
+    return n == flag_code ? 0x8000u : exact_level_pattern(n, level_step);
+}
+
+// Exact-rate norm code of a binary16 half-norm record h: R - 1 for a flagged
+// record; otherwise the level with the nearest value (a tie to the even
+// level), at most nmax (the top finite level).  h lies between the patterns
+// of levels floor(3 h / 2^(15 - m)) and the next, so those two are compared
+// (differences of nearby binary16 values are exact in fp32).
+__device__ __forceinline__ uint32_t exact_norm_code(uint32_t h, int m, uint32_t nmax, float level_step) {
+    if (h & 0x8000u) return (3u << m) - 1u;
+    const uint32_t n0 = (3u * h) >> (15 - m);
+    if (n0 >= nmax) return nmax;
+    const float v = f16_bits_to_f32(static_cast<uint16_t>(h));
+    const float d0 = v - f16_bits_to_f32(static_cast<uint16_t>(exact_level_pattern(n0, level_step)));
+    const float d1 = f16_bits_to_f32(static_cast<uint16_t>(exact_level_pattern(n0 + 1u, level_step))) - v;
+    return d0 < d1 ? n0 : (d1 < d0 ? n0 + 1u : n0 + (n0 & 1u));
+}
+
+// floor(q / 3) for q < 2^13 with a full-rate 24-bit multiply:
+// ceil(2^16 / 3) = 21846 overestimates 1/3 by 2/3 2^-16, which moves q / 3
+// by less than 1/12, and the fraction of q / 3 is at most 2/3.
+__device__ __forceinline__ uint32_t div3_small(uint32_t q) { return __umul24(q, 21846u) >> 16; }
+
 }  // namespace
 }  // namespace hqmq

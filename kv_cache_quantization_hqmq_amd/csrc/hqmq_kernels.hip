@@ -25,6 +25,8 @@
 // scores differ by less than fp32 rounding (near ties).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "hqmq_device.h"
 #include "hqmq_launch.h"
 
@@ -1346,6 +1348,94 @@ __global__ __launch_bounds__(kPackThreads) void pack_norms_kernel(const uint16_t
 }
 
 // --------------------------------------------------------------------------
+// Exact-rate records: whole-bit codes and binary16 half-norms (flags set)
+// turned into groups of 4 token rows.  A block takes kPackExChunks chunks
+// (whole groups) of one slice: every thread first forms the index and norm
+// codes of 8 chunks into LDS, then builds whole output words from them (the
+// low-bit planes and the 13-bit digit fields), so each word is stored once.
+// --------------------------------------------------------------------------
+constexpr int kPackExThreads = 256;
+constexpr int kPackExChunks = 2048;   // 4 rows x cpt chunks divides it for every head_dim
+
+struct PackExArgs {
+    const uint32_t *idx;    // [slices][tokens][words] whole-bit codes
+    const uint16_t *h16;    // [slices][tokens][cpt]
+    uint32_t *out;          // [slices][gps][gw]
+    int64_t tokens, gps, blocks_per_slice;
+    int32_t log2_cpt, bits, words, m, wl, fh, gw;
+    uint32_t nmax;
+    float step;
+};
+
+__global__ __launch_bounds__(kPackExThreads) void pack_exact_kernel(PackExArgs a) {
+    __shared__ uint16_t kc[kPackExChunks];
+    __shared__ uint16_t nc[kPackExChunks];
+    const int64_t slice = blockIdx.x / a.blocks_per_slice;
+    const int64_t gb = blockIdx.x - slice * a.blocks_per_slice;
+    const int cpt = 1 << a.log2_cpt;
+    const int gpb = kPackExChunks >> (a.log2_cpt + 2);   // groups per block
+    const int64_t g0 = gb * gpb;
+    const int64_t t0 = g0 * kExactRows;
+    const uint32_t kmask = (1u << a.bits) - 1u;
+    for (int i = threadIdx.x; i < kPackExChunks; i += kPackExThreads) {
+        const int64_t t = t0 + (i >> a.log2_cpt);
+        const int c = i & (cpt - 1);
+        uint32_t k = 0u, n = 0u;   // rows past the slice's end pack as zeros
+        if (t < a.tokens) {
+            const uint32_t *row = a.idx + (slice * a.tokens + t) * a.words;
+            const int bit = c * a.bits;
+            const int w = bit >> 5;
+            const uint64_t win = (static_cast<uint64_t>(w + 1 < a.words ? row[w + 1] : 0u) << 32) | row[w];
+            k = static_cast<uint32_t>(win >> (bit & 31)) & kmask;
+            n = exact_norm_code(a.h16[(slice * a.tokens + t) * cpt + c], a.m, a.nmax, a.step);
+        }
+        kc[i] = static_cast<uint16_t>(k);
+        nc[i] = static_cast<uint16_t>(n);
+    }
+    __syncthreads();
+    const int groups = static_cast<int>(min(static_cast<int64_t>(gpb), a.gps - g0));
+    const uint32_t lmask = (1u << a.m) - 1u;
+    const int lw = 8 * a.wl;   // words of the two low-bit planes
+    for (int w = threadIdx.x; w < groups * a.gw; w += kPackExThreads) {
+        const int gi = w / a.gw, ww = w - gi * a.gw;
+        const uint16_t *gk = kc + gi * kExactRows * cpt;
+        const uint16_t *gn = nc + gi * kExactRows * cpt;
+        uint32_t v = 0u;
+        if (ww < lw) {
+            // plane pl, row r, word wi of the row's stream of m-bit low parts
+            const int pr = ww / a.wl, wi = ww - pr * a.wl;
+            const uint16_t *src = (pr >= kExactRows ? gn : gk) + (pr & 3) * cpt;
+            const int b0 = 32 * wi;
+            const int c_hi = min(cpt - 1, (b0 + 31) / a.m);
+            for (int c = b0 / a.m; c <= c_hi; ++c) {
+                const int sft = c * a.m - b0;   // -(m - 1) .. 31
+                const uint32_t low = src[c] & lmask;
+                v |= sft >= 0 ? (low << sft) : (low >> -sft);
+            }
+        } else {
+            // 13-bit digit fields: field f of the stream is (row f / 2fh,
+            // plane (f / fh) % 2, field f % fh of that plane)
+            const int b0 = 32 * (ww - lw);
+            const int nf = kExactRows * 2 * a.fh;
+            const int f_hi = min(nf - 1, (b0 + 31) / kFieldBits);
+            for (int f = b0 / kFieldBits; f <= f_hi; ++f) {
+                const int r = f / (2 * a.fh), pl = (f / a.fh) & 1, ff = f - (f / a.fh) * a.fh;
+                const uint16_t *src = (pl ? gn : gk) + r * cpt;
+                uint32_t val = 0u;
+#pragma unroll
+                for (int i = kDigitsPerField - 1; i >= 0; --i) {
+                    const int c = ff * kDigitsPerField + i;
+                    val = 3u * val + (c < cpt ? static_cast<uint32_t>(src[c]) >> a.m : 0u);
+                }
+                const int sft = f * kFieldBits - b0;   // -12 .. 31
+                v |= sft >= 0 ? (val << sft) : (val >> -sft);
+            }
+        }
+        a.out[(slice * a.gps + g0 + gi) * a.gw + ww] = v;
+    }
+}
+
+// --------------------------------------------------------------------------
 // Decode kernel: one block per contiguous chunk range of one slice.
 // --------------------------------------------------------------------------
 struct DecArgs {
@@ -1368,6 +1458,10 @@ struct DecArgs {
     int32_t log2_cpt;
     int32_t bits;
     int32_t words;
+    // exact-rate records (NF == 2): idx holds [slices][gps][gw] group words
+    int64_t gps;
+    int32_t m, wl, fh, gw;
+    float step;
 };
 
 template <bool F32OUT>
@@ -1384,14 +1478,37 @@ __device__ __forceinline__ void store_chunk(void *y, int64_t gc, f32x4 v) {
 
 // Codes and half-norms of the 2 chunks c, c+1 of one token row.
 struct DecPair {
-    uint32_t w0, w1;   // the row words holding the 2 codes
+    uint32_t w0, w1;   // the row words holding the 2 codes (exact: their low bits)
     uint32_t sh;       // bit offset of the first code in w0
     uint32_t h;        // 2 binary16 half-norm codes
-    uint32_t n0, n1;   // NPACK: the norm row words at the index words' places
+    uint32_t n0, n1;   // NF 1: the norm row words at the index words' places; NF 2: the norm low bits
+    uint32_t dk0, dk1, dn0, dn1;   // NF 2: words holding the index and norm digit fields
+    uint32_t dsh;      // NF 2: bit offsets of the two fields (index | norm << 8)
 };
 
-template <bool F32OUT, bool TABLE, bool NPACK>
+// Norm formats of the decode and attention kernels: binary16 half-norms,
+// packed compact codes, exact-rate groups.
+constexpr int kNormF16 = 0, kNormPacked = 1, kNormExact = 2;
+
+// Ternary digits i0 and i0 + 1 of a 13-bit digit field v, i0 = 2 sel in
+// {0, 2, 4, 6}: v / 3^i0 by a 24-bit multiply and shift (exact for v < 2^13),
+// then two base-3 digits of the quotient.
+__device__ __forceinline__ void digit_pair(uint32_t v, uint32_t sel, uint32_t *d0, uint32_t *d1) {
+    const uint32_t mul = sel == 1u ? 116509u : (sel == 2u ? 207127u : 23015u);
+    const uint32_t sft = sel == 1u ? 20u : 24u;
+    const uint32_t q = sel == 0u ? v : (__umul24(v, mul) >> sft);
+    const uint32_t q3 = div3_small(q);
+    *d0 = q - 3u * q3;
+    *d1 = q3 - 3u * div3_small(q3);
+}
+
+template <bool F32OUT, bool TABLE, int NF>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
+    constexpr bool NPACK = NF == kNormPacked;
+    constexpr bool EXACT = NF == kNormExact;
+    // steps whose loads a thread issues together (an exact-rate step holds
+    // twice the record words, so half as many keep the register count)
+    constexpr int kUnroll = EXACT ? kDecUnroll / 2 : kDecUnroll;
     extern __shared__ f32x4 tab[];   // TABLE: the 24 S codewords; else the S q_s
     const int64_t slice = blockIdx.x / a.wg_per_slice;
     const int64_t r0 = (blockIdx.x - slice * a.wg_per_slice) * a.wg_chunks;
@@ -1416,7 +1533,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     }
     __syncthreads();
 
-    const uint32_t *idx_s = a.idx + slice * a.tokens * a.words;
+    const uint32_t *idx_s = EXACT ? a.idx + slice * a.gps * a.gw : a.idx + slice * a.tokens * a.words;
     // half-norm code pairs (u32 per 2 chunks), or the packed norm rows
     const uint32_t *hn_s = NPACK ? static_cast<const uint32_t *>(a.hnorm) + slice * a.tokens * a.words
                                  : static_cast<const uint32_t *>(a.hnorm) + (sbase >> 1);
@@ -1478,6 +1595,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
 
     auto load = [&](int64_t c) {
         DecPair d;
+        if constexpr (EXACT) {
+            // row r of group row / 4: the low bits of chunks cc, cc + 1 in both
+            // planes, and the 13-bit index and norm digit fields holding
+            // their digits (each read as a 2-word window)
+            const int64_t row = c >> a.log2_cpt;
+            const int cc = static_cast<int>(c & cmask);
+            const int r = static_cast<int>(row & 3);
+            const uint32_t *gp = idx_s + (row >> 2) * a.gw;
+            const int ob = cc * a.m, w = ob >> 5;
+            const int w1 = min(w + 1, a.wl - 1);
+            d.w0 = gp[r * a.wl + w];
+            d.w1 = gp[r * a.wl + w1];
+            d.n0 = gp[(4 + r) * a.wl + w];
+            d.n1 = gp[(4 + r) * a.wl + w1];
+            d.sh = static_cast<uint32_t>(ob & 31);
+            const int dbase = 8 * a.wl, dlast = a.gw - 1;
+            const int fk = kFieldBits * (2 * a.fh * r + (cc >> 3));
+            const int fn = fk + kFieldBits * a.fh;
+            d.dk0 = gp[dbase + (fk >> 5)];
+            d.dk1 = gp[min(dbase + (fk >> 5) + 1, dlast)];
+            d.dn0 = gp[dbase + (fn >> 5)];
+            d.dn1 = gp[min(dbase + (fn >> 5) + 1, dlast)];
+            d.dsh = static_cast<uint32_t>(fk & 31) | (static_cast<uint32_t>(fn & 31) << 8) |
+                    (static_cast<uint32_t>((cc >> 1) & 3) << 16);
+            d.h = 0u;
+            return d;
+        }
         const int64_t row = c >> a.log2_cpt;
         const int o = static_cast<int>(c & cmask) * a.bits;
         const int w = o >> 5;
@@ -1497,28 +1641,51 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
         return d;
     };
     constexpr int kWaveStep = 128;   // chunks per wave step
-    for (int64_t c0 = w0 + 2 * lane; c0 < w1; c0 += static_cast<int64_t>(kWaveStep) * kDecUnroll) {
-        DecPair pd[kDecUnroll];
+    for (int64_t c0 = w0 + 2 * lane; c0 < w1; c0 += static_cast<int64_t>(kWaveStep) * kUnroll) {
+        DecPair pd[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
+        for (int u = 0; u < kUnroll; ++u) {
             const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
             pd[u] = c < w1 ? load(c) : DecPair{};
         }
         if constexpr (NPACK) {
 #pragma unroll
-            for (int u = 0; u < kDecUnroll; ++u) {
+            for (int u = 0; u < kUnroll; ++u) {
                 const uint64_t nwin = ((static_cast<uint64_t>(pd[u].n1) << 32) | pd[u].n0) >> pd[u].sh;
                 const uint32_t k0 = static_cast<uint32_t>(nwin) & kmask;
                 const uint32_t k1 = static_cast<uint32_t>(nwin >> a.bits) & kmask;
                 pd[u].h = compact_norm_h16(k0, a.bits) | (compact_norm_h16(k1, a.bits) << 16);
             }
         }
+        if constexpr (EXACT) {
+            // full codes 2^m d + l of the two chunks: indices into w0 / w1
+            // (read below with a zero shift), norm codes to half-norm records
+            const uint32_t lmask = (1u << a.m) - 1u;
+            const uint32_t flag = (3u << a.m) - 1u;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                DecPair &p = pd[u];
+                const uint32_t sel = (p.dsh >> 16) & 3u;
+                const uint32_t vk = static_cast<uint32_t>(((static_cast<uint64_t>(p.dk1) << 32) | p.dk0) >> (p.dsh & 31u)) & 0x1FFFu;
+                const uint32_t vn = static_cast<uint32_t>(((static_cast<uint64_t>(p.dn1) << 32) | p.dn0) >> ((p.dsh >> 8) & 31u)) & 0x1FFFu;
+                uint32_t ka, kb, na, nb;
+                digit_pair(vk, sel, &ka, &kb);
+                digit_pair(vn, sel, &na, &nb);
+                const uint32_t lk = static_cast<uint32_t>(((static_cast<uint64_t>(p.w1) << 32) | p.w0) >> p.sh);
+                const uint32_t ln = static_cast<uint32_t>(((static_cast<uint64_t>(p.n1) << 32) | p.n0) >> p.sh);
+                p.w0 = (ka << a.m) | (lk & lmask);
+                p.w1 = (kb << a.m) | ((lk >> a.m) & lmask);
+                p.sh = 0u;
+                const uint32_t n0 = (na << a.m) | (ln & lmask), n1 = (nb << a.m) | ((ln >> a.m) & lmask);
+                p.h = exact_norm_h16(n0, flag, a.step) | (exact_norm_h16(n1, flag, a.step) << 16);
+            }
+        }
         // side-list values of this iteration's flagged chunks, in order (a
         // chunk whose entry was dropped, past the capacity, keeps its bulk value)
-        uint2 ov[kDecUnroll][2];
-        bool oh[kDecUnroll][2];
+        uint2 ov[kUnroll][2];
+        bool oh[kUnroll][2];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
+        for (int u = 0; u < kUnroll; ++u) {
             const bool f0 = (pd[u].h & 0x8000u) != 0;
             const bool f1 = (pd[u].h & 0x80000000u) != 0;
             const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
@@ -1535,7 +1702,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
             e_next += static_cast<uint64_t>(__popcll(m0) + __popcll(m1));
         }
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
+        for (int u = 0; u < kUnroll; ++u) {
             const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
             if (c >= w1) break;
             const DecPair &cur = pd[u];
@@ -1543,7 +1710,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
             f32x4 out[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                uint32_t k = static_cast<uint32_t>(win >> (i * a.bits)) & kmask;
+                uint32_t k = EXACT ? (i ? cur.w1 : cur.w0) : static_cast<uint32_t>(win >> (i * a.bits)) & kmask;
                 k = min(k, static_cast<uint32_t>(ncw - 1));
                 const uint16_t hi = static_cast<uint16_t>(cur.h >> (16 * i));
                 const float r = 2.0f * f16_bits_to_f32(static_cast<uint16_t>(hi & 0x7FFFu));
@@ -1957,6 +2124,31 @@ hipError_t launch_paged_clear(int64_t slices, const int32_t *pages, int64_t n, c
     return hipGetLastError();
 }
 
+hipError_t launch_pack_exact(const Geometry &g, const uint32_t *idx32, const uint16_t *h16, uint32_t *groups,
+                             hipStream_t st) {
+    if (g.slices == 0 || g.tokens == 0) return hipSuccess;
+    PackExArgs a;
+    a.idx = idx32;
+    a.h16 = h16;
+    a.out = groups;
+    a.tokens = g.tokens;
+    a.gps = g.egps;
+    a.log2_cpt = __builtin_ctz(static_cast<unsigned>(g.cpt));
+    const int gpb = kPackExChunks >> (a.log2_cpt + 2);
+    a.blocks_per_slice = ceil_div(g.egps, static_cast<int64_t>(gpb));
+    a.bits = g.bits;
+    a.words = g.words;
+    a.m = g.em;
+    a.wl = g.ewl;
+    a.fh = g.efh;
+    a.gw = g.egw;
+    a.nmax = g.enmax;
+    a.step = g.estep;
+    hipLaunchKernelGGL(pack_exact_kernel, dim3(static_cast<unsigned>(g.slices * a.blocks_per_slice)),
+                       dim3(kPackExThreads), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const void *hnorm,
                          const uint64_t *offsets, const uint32_t *out_pos, const uint16_t *out_val,
                          uint64_t capacity, const float *codebook, void *y, hipStream_t st) {
@@ -1988,23 +2180,33 @@ hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const void *hno
     a.words = g.words;
     const dim3 grid(static_cast<unsigned>(g.slices * a.wg_per_slice));
     const dim3 block(kDecThreads);
+    a.gps = g.egps;
+    a.m = g.em;
+    a.wl = g.ewl;
+    a.fh = g.efh;
+    a.gw = g.egw;
+    a.step = g.estep;
     const bool table = g.S <= kTableMaxS;
     const size_t lds = (table ? 24 * static_cast<size_t>(g.S) : static_cast<size_t>(g.S)) * sizeof(f32x4);
-    if (g.npack) {
-        if (g.f32) {
-            if (table) hipLaunchKernelGGL((decode_kernel<true, true, true>), grid, block, lds, st, a);
-            else hipLaunchKernelGGL((decode_kernel<true, false, true>), grid, block, lds, st, a);
-        } else {
-            if (table) hipLaunchKernelGGL((decode_kernel<false, true, true>), grid, block, lds, st, a);
-            else hipLaunchKernelGGL((decode_kernel<false, false, true>), grid, block, lds, st, a);
-        }
-    } else if (g.f32) {
-        if (table) hipLaunchKernelGGL((decode_kernel<true, true, false>), grid, block, lds, st, a);
-        else hipLaunchKernelGGL((decode_kernel<true, false, false>), grid, block, lds, st, a);
-    } else {
-        if (table) hipLaunchKernelGGL((decode_kernel<false, true, false>), grid, block, lds, st, a);
-        else hipLaunchKernelGGL((decode_kernel<false, false, false>), grid, block, lds, st, a);
-    }
+    const int nf = g.exact ? kNormExact : (g.npack ? kNormPacked : kNormF16);
+    const void *k = nullptr;
+    auto pick = [&](auto f32out) {
+        constexpr bool F = decltype(f32out)::value;
+        if (nf == kNormExact)
+            k = table ? reinterpret_cast<const void *>(&decode_kernel<F, true, kNormExact>)
+                      : reinterpret_cast<const void *>(&decode_kernel<F, false, kNormExact>);
+        else if (nf == kNormPacked)
+            k = table ? reinterpret_cast<const void *>(&decode_kernel<F, true, kNormPacked>)
+                      : reinterpret_cast<const void *>(&decode_kernel<F, false, kNormPacked>);
+        else
+            k = table ? reinterpret_cast<const void *>(&decode_kernel<F, true, kNormF16>)
+                      : reinterpret_cast<const void *>(&decode_kernel<F, false, kNormF16>);
+    };
+    if (g.f32) pick(std::true_type{});
+    else pick(std::false_type{});
+    void *args[] = {&a};
+    const hipError_t e = hipLaunchKernel(k, grid, block, args, lds, st);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -23,6 +23,16 @@ struct Geometry {
     int64_t batches_per_slice;
     float med_C;
     int32_t npack;           // 1: norms as packed compact codes (b bits per chunk)
+    // exact-rate records (norm_format HQMQ_NORM_EXACT; S a power of two):
+    // groups of 4 token rows, each code m low bits plus a ternary digit
+    int32_t exact;
+    int32_t em;              // 24 S = 3 2^m
+    int32_t ewl;             // words of low bits per row and plane: ceil(cpt m / 32)
+    int32_t efh;             // digit fields per row and plane: ceil(cpt / 8)
+    int32_t egw;             // words per group
+    int64_t egps;            // groups per slice: ceil(tokens / 4)
+    uint32_t enmax;          // top finite norm level
+    float estep;             // fp32(2^(15 - m) / 3): norm level n sits at pattern round(n estep)
 };
 
 // Encode scratch (inside the caller's workspace).
@@ -31,7 +41,8 @@ struct Med3Work {
     uint32_t *counts;    // [batches] outliers per batch
     uint32_t *mask;      // [batches][mask_words] outlier bitmasks
     int64_t mask_words;
-    uint16_t *h16;       // packed norm format: the binary16 half-norm plane
+    uint16_t *h16;       // packed and exact formats: the binary16 half-norm plane
+    uint32_t *idx32;     // exact format: the whole-bit code plane the search writes
 };
 
 // Encode: nearest codeword and norm code per chunk; with med != nullptr the
@@ -70,8 +81,13 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
 // bit -> all-ones code), packed per token row like the index codes.
 hipError_t launch_pack_norms(const Geometry &g, const uint16_t *h16, uint32_t *words, hipStream_t st);
 
+// Exact-rate format: the group records of the whole-bit codes idx32 and the
+// binary16 half-norms h16 (flags included).
+hipError_t launch_pack_exact(const Geometry &g, const uint32_t *idx32, const uint16_t *h16, uint32_t *groups,
+                             hipStream_t st);
+
 // Decode: bulk gather-multiply plus outlier re-insertion (hnorm: the norm
-// plane in the geometry's format).
+// plane in the geometry's format; exact format: idx holds the groups).
 hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const void *hnorm,
                          const uint64_t *offsets, const uint32_t *out_pos, const uint16_t *out_val,
                          uint64_t capacity, const float *codebook, void *y, hipStream_t st);
@@ -100,6 +116,10 @@ struct AttLaunch {
     int64_t batch_chunks;       // Med3x batch length in chunks (0 = off)
     int64_t bps;                // Med3x batches per slice (0 = off)
     int32_t layer, heads, group, batch, nsplit, split_tokens, max_len, head_dim, S, bits, words, npack;
+    // exact-rate records (see Geometry)
+    int32_t exact, em, ewl, efh, egw;
+    int64_t egps;
+    float estep;
     float scale;
     // paged pools (page_table != nullptr): rows at (slice * num_pages + page) * P + offset,
     // side lists of page_cap entries per (slice, page); seq_start is not used
@@ -110,7 +130,7 @@ struct AttLaunch {
 };
 
 // Dynamic LDS of the attention kernel for this shape (0: unsupported head_dim).
-size_t attend_lds_bytes(int head_dim, int S);
+size_t attend_lds_bytes(int head_dim, int S, bool exact);
 hipError_t launch_attend(const AttLaunch &L, hipStream_t st);
 
 // Paged pool of one role (device pointers), as the append kernels write it.

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libhqmq.so")
 HQMQ_OK, HQMQ_EINVAL, HQMQ_ENOTSUP, HQMQ_ECAPACITY, HQMQ_EHIP = 0, -1, -2, -3, -4
 HQMQ_F16, HQMQ_F32 = 0, 1
 HQMQ_ROLE_K, HQMQ_ROLE_V = 0, 1
-HQMQ_NORM_F16, HQMQ_NORM_PACKED = 0, 1
+HQMQ_NORM_F16, HQMQ_NORM_PACKED, HQMQ_NORM_EXACT = 0, 1, 2
 
 # every symbol include/hqmq.h declares
 EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
@@ -74,7 +74,8 @@ class Sizes(ctypes.Structure):
                 ("max_outliers", ctypes.c_int64), ("input_bytes", ctypes.c_uint64),
                 ("idx_bytes", ctypes.c_uint64), ("hnorm_bytes", ctypes.c_uint64),
                 ("offsets_bytes", ctypes.c_uint64), ("side_entry_bytes", ctypes.c_uint64),
-                ("workspace_bytes", ctypes.c_uint64), ("codebook_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("codebook_bytes", ctypes.c_uint64),
+                ("group_rows", ctypes.c_int32), ("group_words", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -348,10 +349,14 @@ def allocate_records(desc: Desc, capacity: int | None = None, device="cuda") -> 
     sz = hqmq_sizes(desc)
     T, W, cpt = desc.tokens, sz.words_per_token, desc.head_dim // 4
     L, H = desc.layers, desc.kv_heads
-    idx = torch.empty((L, H, T, W), dtype=torch.int32, device=device)
+    if desc.norm_format == HQMQ_NORM_EXACT:   # groups of 4 token rows, no norm plane
+        idx = torch.empty((L, H, (T + 3) // 4, sz.group_words), dtype=torch.int32, device=device)
+        hnorm = None
+    else:
+        idx = torch.empty((L, H, T, W), dtype=torch.int32, device=device)
     if desc.norm_format == HQMQ_NORM_PACKED:   # u32 words laid out like idx
         hnorm = torch.empty((L, H, T, W), dtype=torch.int32, device=device)
-    else:
+    elif desc.norm_format == HQMQ_NORM_F16:
         hnorm = torch.empty((L, H, T, cpt), dtype=torch.int16, device=device)
     med = desc.med_batch_tokens > 0
     if capacity is None:

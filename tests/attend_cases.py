@@ -37,16 +37,20 @@ def f16_values(y64: np.ndarray) -> np.ndarray:
     return O.round_f16(y64).view(np.float16).astype(np.float64)
 
 
-def oracle_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float, npack: bool = False):
+def oracle_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float, npack: bool = False,
+                 exact: bool = False):
     """Oracle records and binary16 decoded values of tokens [t0, t0+T) of one
     slice (t0 a multiple of the Med3x batch).  r["hrec"] is the norm record
-    as the GPU stores it: binary16 codes, or (npack) compact codes, whose
-    half-norms the decode then uses."""
+    as the GPU stores it: binary16 codes, or (npack) compact codes, or
+    (exact) exact-rate norm codes, whose half-norms the decode then uses."""
     T, D = x.shape
     r = O.encode_range(x, q, t0, B, C)
     hn = r["hnorm"]
     r["hrec"] = hn
-    if npack:
+    if exact:
+        r["hrec"] = O.exact_norms(hn, q.shape[0])
+        hn = O.exact_norm_to_h16(r["hrec"], q.shape[0])
+    elif npack:
         b = O.code_bits(q.shape[0])
         r["hrec"] = O.compact_norms(hn, b)
         hn = O.compact_to_h16(r["hrec"], b)
@@ -60,8 +64,16 @@ def gpu_slice_records(desc: K.Desc, rec, l: int, h: int, t0: int, T: int):
     L, H, Tt, D = desc.shape
     cpt = D // 4
     b = O.code_bits(int(desc.S))
-    codes = P.unpack_words(rec.idx[l, h, t0:t0 + T].cpu().numpy().view(np.uint32), cpt, b).reshape(-1)
-    if desc.norm_format == K.HQMQ_NORM_PACKED:
+    if desc.norm_format == K.HQMQ_NORM_EXACT:
+        assert t0 % 4 == 0
+        words = rec.idx[l, h, t0 // 4:(t0 + T + 3) // 4].cpu().numpy().view(np.uint32)
+        codes, hn = O.unpack_exact(words, T, cpt, int(desc.S))
+        codes, hn = codes.reshape(-1), hn.reshape(-1)
+    else:
+        codes = P.unpack_words(rec.idx[l, h, t0:t0 + T].cpu().numpy().view(np.uint32), cpt, b).reshape(-1)
+    if desc.norm_format == K.HQMQ_NORM_EXACT:
+        pass
+    elif desc.norm_format == K.HQMQ_NORM_PACKED:
         hn = P.unpack_words(rec.hnorm[l, h, t0:t0 + T].cpu().numpy().view(np.uint32), cpt, b).reshape(-1)
     else:
         hn = rec.hnorm[l, h, t0:t0 + T].cpu().numpy().view(np.uint16).reshape(-1)
@@ -117,6 +129,7 @@ def run_case(w: synth.Workload, seqs, group: int, scale: float, layers=None, max
     (must be 0)."""
     desc = GC.desc_for(w, norm_format=norm_format)
     npack = norm_format == K.HQMQ_NORM_PACKED
+    exact = norm_format == K.HQMQ_NORM_EXACT
     L, H, Tt, D = desc.shape
     xs, cbh, cbd, recs = {}, {}, {}, {}
     for role in (0, 1):
@@ -139,7 +152,7 @@ def run_case(w: synth.Workload, seqs, group: int, scale: float, layers=None, max
             dec = {}
             for role in (0, 1):
                 x = xs[role][l, h].float().cpu().numpy()
-                r, dec[role] = oracle_slice(x, cbh[role][l, h], 0, w.med_batch_tokens, w.med_C, npack)
+                r, dec[role] = oracle_slice(x, cbh[role][l, h], 0, w.med_batch_tokens, w.med_C, npack, exact)
                 near, bad = record_mismatches(r, gpu_slice_records(desc, recs[role], l, h, 0, Tt))
                 rep["near_tie_codes"] += near
                 rep["record_mismatch"] += bad

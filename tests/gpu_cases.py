@@ -44,8 +44,13 @@ def compare(desc: K.Desc, x: torch.Tensor, cb_host: np.ndarray, rec, y: torch.Te
         if T == 0:
             continue
         xs = x[l, h, t0:t0 + T].float().cpu().numpy()
-        words = rec.idx[l, h, t0:t0 + T].cpu().numpy()
-        hn = rec.hnorm[l, h, t0:t0 + T].cpu().numpy()
+        exact = desc.norm_format == K.HQMQ_NORM_EXACT
+        if exact:   # the groups holding tokens [t0, t0 + T)
+            words = rec.idx[l, h, t0 // 4:(t0 + T + 3) // 4].cpu().numpy()
+            hn = None
+        else:
+            words = rec.idx[l, h, t0:t0 + T].cpu().numpy()
+            hn = rec.hnorm[l, h, t0:t0 + T].cpu().numpy()
         ys = y[l, h, t0:t0 + T].cpu().numpy()
         pos = val = None
         if B > 0:
@@ -56,6 +61,7 @@ def compare(desc: K.Desc, x: torch.Tensor, cb_host: np.ndarray, rec, y: torch.Te
             pos = rec.out_pos[e0:e1].cpu().numpy()
             val = rec.out_val[e0:e1].cpu().numpy()
         r = P.compare_slice(xs, cb_host[l, h], t0, Bc, float(desc.med_C), words, hn, pos, val, ys,
-                            int(desc.S), desc.dtype == K.HQMQ_F32, desc.norm_format == K.HQMQ_NORM_PACKED)
+                            int(desc.S), desc.dtype == K.HQMQ_F32, desc.norm_format == K.HQMQ_NORM_PACKED,
+                            exact)
         rep.merge(r)
     return rep

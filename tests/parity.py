@@ -10,6 +10,8 @@ The bar (from the method's definition and the build's contract):
   * packed index words: bit-exact on every token row whose codes all match;
   * packed norm format: the compact norm codes, and so their words, bit-exact
     (they follow from the half-norm codes, which are exact);
+  * exact-rate format: every norm code bit-exact, every group word bit-exact
+    in groups whose index codes all match;
   * decoded values: |y_gpu - y_oracle| <= 1e-3 * r^ per element (r^ the
     decoded chunk norm), outlier chunks exact.
 """
@@ -53,11 +55,13 @@ class Report(dict):
 def compare_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float,
                   g_words: np.ndarray, g_hnorm: np.ndarray, g_pos: np.ndarray | None,
                   g_val: np.ndarray | None, g_y: np.ndarray | None, S: int,
-                  out_f32: bool, npack: bool = False) -> Report:
+                  out_f32: bool, npack: bool = False, exact: bool = False) -> Report:
     """Compare the GPU records of tokens [t0, t0+T) of one slice with the
     oracle.  x: [T, D] input values; g_*: the GPU's records for the same
     tokens (g_pos/g_val: the side-list entries of those batches; g_hnorm:
-    [T, cpt] binary16 codes, or with npack the [T, W] packed norm words)."""
+    [T, cpt] binary16 codes, or with npack the [T, W] packed norm words;
+    with exact, g_words are the [ceil(T / 4), group words] groups (t0 a
+    multiple of 4) and g_hnorm is unused)."""
     T, D = x.shape
     cpt = D // 4
     b = O.code_bits(S)
@@ -68,7 +72,19 @@ def compare_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float,
     hn_o = ref["hnorm"].reshape(T, cpt)
     gap = ref["gap"].reshape(T, cpt)
 
-    if npack:
+    exact_groups = None
+    if exact:
+        # norm codes (24 S levels) bit-exact; the decode below then uses the
+        # half-norm records those codes stand for
+        assert t0 % O.EXACT_ROWS == 0
+        nc_o = O.exact_norms(hn_o, S)
+        exact_groups = np.asarray(g_words).view(np.uint32).reshape(-1, O.exact_group_words(cpt, S))
+        codes_g, nc_g = O.unpack_exact(exact_groups, T, cpt, S)
+        bad = np.argwhere(nc_g != nc_o)
+        assert bad.size == 0, \
+            f"exact norm code differs at {bad[:5].tolist()}: gpu {nc_g[tuple(bad[0])]} oracle {nc_o[tuple(bad[0])]}"
+        hn_o = O.exact_norm_to_h16(nc_o, S)
+    elif npack:
         # compact norm codes (and their packed words): bit-exact; the decode
         # below then uses the half-norm records those codes stand for
         nc_o = O.compact_norms(hn_o, b)
@@ -95,7 +111,8 @@ def compare_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float,
         np.testing.assert_array_equal(np.asarray(g_val).view(np.uint16).reshape(-1, 4), ref["side_val"])
 
     # codes: exact outside near ties; near ties must be near-optimal
-    codes_g = unpack_words(np.asarray(g_words).view(np.uint32).reshape(T, W), cpt, b)
+    if not exact:
+        codes_g = unpack_words(np.asarray(g_words).view(np.uint32).reshape(T, W), cpt, b)
     assert codes_g.max(initial=0) < 24 * S
     diff = codes_g != codes_o
     exempt = gap < GAP_EXEMPT
@@ -115,11 +132,20 @@ def compare_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float,
             best = cw[codes_o[t, c]] @ u
             mine = cw[codes_g[t, c]] @ u
             assert mine >= best - GAP_EXEMPT, f"near-tie code not near-optimal at {t0 + t},{c}"
-    # packed words bit-exact on rows whose codes match
-    rows_ok = ~diff.any(axis=1)
-    words_o = np.stack([O.pack_row(codes_o[t], b, W) for t in np.flatnonzero(rows_ok)]) if rows_ok.any() else None
-    if words_o is not None:
-        np.testing.assert_array_equal(np.asarray(g_words).view(np.uint32).reshape(T, W)[rows_ok], words_o)
+    if exact:
+        # group words bit-exact in groups whose index codes all match
+        ng = exact_groups.shape[0]
+        pad = ng * O.EXACT_ROWS - T
+        dpad = np.concatenate([diff, np.zeros((pad, cpt), bool)]) if pad else diff
+        groups_ok = ~dpad.reshape(ng, -1).any(axis=1)
+        words_o = O.pack_exact(codes_o, O.exact_norms(ref["hnorm"].reshape(T, cpt), S), S)
+        np.testing.assert_array_equal(exact_groups[groups_ok], words_o[groups_ok])
+    else:
+        # packed words bit-exact on rows whose codes match
+        rows_ok = ~diff.any(axis=1)
+        words_o = np.stack([O.pack_row(codes_o[t], b, W) for t in np.flatnonzero(rows_ok)]) if rows_ok.any() else None
+        if words_o is not None:
+            np.testing.assert_array_equal(np.asarray(g_words).view(np.uint32).reshape(T, W)[rows_ok], words_o)
 
     # decoded values
     if g_y is not None:
@@ -138,7 +164,8 @@ def compare_slice(x: np.ndarray, q: np.ndarray, t0: int, B: int, C: float,
         else:
             yo = O.round_f16(yo).view(np.float16).astype(np.float64).reshape(T, cpt, 4)
         rhat = 2.0 * (hn_o & 0x7FFF).view(np.float16).astype(np.float64)
-        err = np.abs(yg - yo).max(axis=2)
+        # (identical values, infinities of the binary16 overflow included, differ by 0)
+        err = np.where(yg == yo, 0.0, np.abs(yg - yo)).max(axis=2)
         flagged = (hn_o & 0x8000) != 0
         # 1e-3 of the chunk norm; binary16 outputs below the normal range
         # cannot resolve finer than one subnormal step (2^-24)

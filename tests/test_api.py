@@ -68,7 +68,7 @@ def test_strerror():
 
 @pytest.mark.parametrize("field,value", [
     ("head_dim", 96), ("head_dim", 0), ("head_dim", 512), ("S", 0), ("S", 1025),
-    ("dtype", 2), ("layers", -1), ("tokens", -5), ("med_batch_tokens", -1), ("norm_format", 2),
+    ("dtype", 2), ("layers", -1), ("tokens", -5), ("med_batch_tokens", -1), ("norm_format", 3),
     ("norm_format", -1)])
 def test_descriptor_validation(field, value):
     d = K.Desc.make(2, 2, 64, 128, 8, K.HQMQ_F16, 16, 3.0)
@@ -181,6 +181,29 @@ def test_library_codebook_is_on_the_double_binary16_grid():
     assert np.array_equal(hi.astype(np.float32) + lo.astype(np.float32), q)
     # and not merely fp32: most values need the low part
     assert (lo != 0).mean() > 0.9
+
+
+def test_exact_format_sizes_and_limits():
+    """Exact-rate records: groups of 4 token rows whose word count is the
+    oracle's; S not a power of two (24 S is then not 3 2^m) and paged pools
+    are refused."""
+    for S, D in ((8, 128), (32, 128), (1, 16), (1024, 256), (16, 64)):
+        d = K.Desc.make(2, 3, 1001, D, S, K.HQMQ_F16, 0, 3.0, K.HQMQ_NORM_EXACT)
+        sz = K.hqmq_sizes(d)
+        assert sz.group_rows == 4 and sz.group_words == O.exact_group_words(D // 4, S)
+        assert sz.idx_bytes == 2 * 3 * 251 * sz.group_words * 4 and sz.hnorm_bytes == 0
+    assert K.hqmq_sizes(K.Desc.make(1, 1, 4, 128, 8, K.HQMQ_F16, 0, 3.0, K.HQMQ_NORM_EXACT)).group_words == 61
+    assert K.hqmq_sizes(K.Desc.make(1, 1, 4, 128, 32, K.HQMQ_F16, 0, 3.0, K.HQMQ_NORM_EXACT)).group_words == 77
+    for S in (3, 13, 100):
+        with pytest.raises(K.HQMQError) as e:
+            K.hqmq_sizes(K.Desc.make(1, 1, 16, 128, S, K.HQMQ_F16, 0, 3.0, K.HQMQ_NORM_EXACT))
+        assert e.value.code == B.HQMQ_ENOTSUP
+    with pytest.raises(K.HQMQError) as e:
+        K.hqmq_paged_sizes(K.Desc.make(1, 1, 16, 128, 32, K.HQMQ_F16, 0, 3.0, K.HQMQ_NORM_EXACT),
+                           B.PagedDesc(4, 16, 8))
+    assert e.value.code == B.HQMQ_ENOTSUP
+    # the other formats report no groups
+    assert K.hqmq_sizes(K.Desc.make(1, 1, 16, 128, 32)).group_words == 0
 
 
 def test_codebook_validation():

@@ -71,6 +71,32 @@ def test_attend_packed_norms_d64_s8_and_general_width():
            "packed D=256 S=100")
 
 
+@pytest.mark.parametrize("group", [4, 1])
+def test_attend_exact_records_d128_s32(group):
+    """Exact-rate records (m = 8: 4.81 bits per element with outliers aside)
+    read by the attention kernel; sequences start at tokens that are not
+    multiples of the 4-row group, so tiles straddle groups."""
+    _check(A.run_case(BASE, SEQS, group, 1.0 / math.sqrt(128), norm_format=K.HQMQ_NORM_EXACT),
+           f"exact G={group}")
+
+
+def test_attend_exact_records_other_shapes():
+    """Exact-rate records at S = 8 (m = 6) with head_dim 64 (a lane decodes
+    half a digit field), S = 16 (m = 7, the any-m kernel) and S = 128 with
+    head_dim 256 (no codeword table)."""
+    w = synth.WORKLOADS[2].scaled(layers=1, heads=2, tokens=3001, data_seed=2306)
+    _check(A.run_case(w, [(0, 3001), (17, 1500), (2990, 11), (5, 3)], 4, 0.125,
+                      norm_format=K.HQMQ_NORM_EXACT), "exact D=64 S=8")
+    w = synth.WORKLOADS[3].scaled(layers=1, heads=2, tokens=1301, S=16, med_batch_tokens=512,
+                                  data_seed=2307)
+    _check(A.run_case(w, [(0, 1301), (3, 700), (650, 651)], 4, 1.0 / math.sqrt(128),
+                      norm_format=K.HQMQ_NORM_EXACT), "exact D=128 S=16")
+    w = synth.WORKLOADS[3].scaled(layers=1, heads=1, tokens=1500, head_dim=256, S=128,
+                                  med_batch_tokens=512, data_seed=2308)
+    _check(A.run_case(w, [(0, 1500), (513, 513)], 2, 1.0 / 16.0, norm_format=K.HQMQ_NORM_EXACT),
+           "exact D=256 S=128")
+
+
 def test_attend_clips_ranges():
     """Lengths beyond max_len, ranges past the slice end, a negative start and
     a negative length: the kernel attends over the clipped range (zeros when
@@ -104,7 +130,7 @@ def _guarded(t: torch.Tensor, pad_bytes: int = 4096):
     return buf[:nbytes].view(t.dtype).view(t.shape), buf, nbytes
 
 
-@pytest.mark.parametrize("norm", [K.HQMQ_NORM_F16, K.HQMQ_NORM_PACKED])
+@pytest.mark.parametrize("norm", [K.HQMQ_NORM_F16, K.HQMQ_NORM_PACKED, K.HQMQ_NORM_EXACT])
 def test_attend_writes_stay_inside_out_and_workspace(norm):
     """The output and the split workspace sit at the front of buffers with a
     patterned tail: after attention over ragged sequences the tails are

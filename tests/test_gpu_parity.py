@@ -308,6 +308,9 @@ def _guarded(t: torch.Tensor, pad_bytes: int = 4096):
     (1, 2, 77, 64, 40, "f16", 5, "packed"),
     (2, 1, 33, 16, 100, "f32", 7, "f16"),
     (1, 1, 130, 128, 32, "f16", 64, "packed"),
+    (2, 3, 43, 16, 8, "f16", 4, "exact"),
+    (1, 2, 131, 128, 32, "f32", 64, "exact"),
+    (1, 1, 70, 256, 1024, "f16", 16, "exact"),
 ])
 def test_outputs_stay_inside_their_buffers(L, H, T, D, S, dt, B, norm):
     """Every record plane, the side list, its offsets and the decoded tensor
@@ -319,13 +322,15 @@ def test_outputs_stay_inside_their_buffers(L, H, T, D, S, dt, B, norm):
     x = _x((L, H, T, D), dtype, seed=T * 7 + S)
     x[:, :, :, 5] *= 40                      # hot channel: outliers in every batch
     cb_host, cb = _cb(L, H, S)
-    nf = K.HQMQ_NORM_PACKED if norm == "packed" else K.HQMQ_NORM_F16
+    nf = {"packed": K.HQMQ_NORM_PACKED, "exact": K.HQMQ_NORM_EXACT}.get(norm, K.HQMQ_NORM_F16)
     desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F32 if dt == "f32" else K.HQMQ_F16, B, 3.0, nf)
     rec = K.allocate_records(desc, K.hqmq_sizes(desc).max_outliers)
     guards = []
     for name, field in (("idx", "idx"), ("hnorm", "hnorm"), ("batch_offsets", "batch_offsets"),
                         ("out_pos", "out_pos"), ("out_val", "out_val")):
         t = getattr(rec, name)
+        if t is None:   # the exact format has no norm plane
+            continue
         g, buf, nb = _guarded(t)
         setattr(rec, name, g)
         setattr(rec.c, field, buf.data_ptr())
