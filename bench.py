@@ -38,7 +38,7 @@ METRIC = "HQMQ encode & decode chunks/s and GB/s (fp16 in) on 1 MI355X; % of roo
 PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense f16 matrix cores
 PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
-NORM_FORMATS = {"f16": 0, "packed": 1}   # hqmq_desc.norm_format
+NORM_FORMATS = {"f16": 0, "packed": 1, "exact": 2}   # hqmq_desc.norm_format
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_kernels.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_llama3-70b-kv-128k.json")
 COUNTERS5_FILE = os.path.join(ROOT, "profiles", "counters_llama3-8b-decode-32x32k.json")
@@ -301,7 +301,7 @@ def summarize_counters(run_dir: str, workload: int):
                       "kernels": kernels}, indent=1))
 
 
-def decode_step_bench(args, w):
+def decode_step_bench(args, w, fakequant: bool = True):
     """Decode-step workload: the cache of ``w.sequences`` sequences (stacked on
     the token axis of every (layer, head)) is encoded once, untimed.  One step
     encodes the step's appended tokens (one per sequence, a Med3x batch of
@@ -412,8 +412,11 @@ def decode_step_bench(args, w):
     log(f"timing {args.steps} fused steps")
     fused_ms, (enc_ms, att_ms) = timed(fused_step, 3)
     assert torch.isfinite(aout).all(), "attention produced non-finite values"
-    log(f"timing {args.steps} fake-quant steps")
-    fq_ms, (fq_dec_ms, fq_att_ms) = timed(fakequant_step, 3)
+    if fakequant:
+        log(f"timing {args.steps} fake-quant steps")
+        fq_ms, (fq_dec_ms, fq_att_ms) = timed(fakequant_step, 3)
+    else:
+        fq_ms = fq_dec_ms = fq_att_ms = float("nan")
     app_out = {r: K.hqmq_encode_result(reca[r], sh) for r in w.roles}
 
     rec_bytes = sz.idx_bytes + sz.hnorm_bytes
@@ -867,7 +870,7 @@ def main():
                     help="workload 5 on paged pools (append + paged attention per step)")
     ap.add_argument("--page-tokens", type=int, default=128)
     ap.add_argument("--norm-format", choices=sorted(NORM_FORMATS), default="f16",
-                    help="norm records: binary16 half-norms, or packed b-bit compact codes")
+                    help="norm records: binary16 half-norms, packed b-bit compact codes, or exact-rate groups")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -1039,6 +1042,13 @@ def main():
                                                 "encode_appended_ms", "attention_ms_per_step", "fakequant",
                                                 "fused_speedup_vs_fakequant", "cache_bits_per_element")}
         out["decode_step"]["steps"] = a5.steps
+        del d
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        a5.norm_format = "exact"
+        d = decode_step_bench(a5, synth.WORKLOADS[5], fakequant=False)
+        out["decode_step"]["exact_records"] = {k: d[k] for k in ("ms_per_step", "roofline", "attention_ms_per_step",
+                                                                 "cache_bits_per_element")}
     print(json.dumps(out), flush=True)
 
 

@@ -1350,88 +1350,244 @@ __global__ __launch_bounds__(kPackThreads) void pack_norms_kernel(const uint16_t
 // --------------------------------------------------------------------------
 // Exact-rate records: whole-bit codes and binary16 half-norms (flags set)
 // turned into groups of 4 token rows.  A block takes kPackExChunks chunks
-// (whole groups) of one slice: every thread first forms the index and norm
-// codes of 8 chunks into LDS, then builds whole output words from them (the
-// low-bit planes and the 13-bit digit fields), so each word is stored once.
+// (whole groups) of one slice, in three steps without atomics:
+//  1. every thread forms the index and norm codes of two runs of 4
+//     consecutive chunks (the loads of both runs issued before either is
+//     used: an 8-byte half-norm load and the code words per run) into LDS;
+//  2. one thread per low-bit word ORs the (at most 11) codes it holds, and
+//     one thread per 13-bit digit field sums its 8 digits;
+//  3. the digit words are gathered from up to four fields each, and every
+//     word of the block's groups is stored once.
 // --------------------------------------------------------------------------
 constexpr int kPackExThreads = 256;
 constexpr int kPackExChunks = 2048;   // 4 rows x cpt chunks divides it for every head_dim
+constexpr int kPackExRuns = kPackExChunks / (4 * kPackExThreads);   // 4-chunk runs per thread
+// a block's low-bit words (8 ceil(cpt m / 32) per group) and digit fields
+// (8 ceil(cpt / 8) per group), at most over head_dim 16..256 and m <= 13
+constexpr int kPackExLowWords = 2048;
+constexpr int kPackExFields = 1024;
 
 struct PackExArgs {
     const uint32_t *idx;    // [slices][tokens][words] whole-bit codes
     const uint16_t *h16;    // [slices][tokens][cpt]
     uint32_t *out;          // [slices][gps][gw]
     int64_t tokens, gps, blocks_per_slice;
-    int32_t log2_cpt, bits, words, m, wl, fh, gw;
+    int32_t log2_cpt, log2_fh, bits, words, m, wl, fh, gw;
+    uint32_t gw_magic;      // ceil(2^24 / gw): w / gw for the block's word indices
+    uint32_t wl_magic;      // ceil(2^20 / wl): w / wl for the block's low-bit words
+    uint32_t m_recip;       // ceil(2^16 / m): b / m for bit offsets b < 2^11
     uint32_t nmax;
     float step;
 };
 
 __global__ __launch_bounds__(kPackExThreads) void pack_exact_kernel(PackExArgs a) {
-    __shared__ uint16_t kc[kPackExChunks];
-    __shared__ uint16_t nc[kPackExChunks];
+    __shared__ uint16_t codes[2 * kPackExChunks];   // [plane][chunk of the block]
+    __shared__ uint32_t lows[kPackExLowWords];
+    __shared__ uint32_t fields[kPackExFields];
     const int64_t slice = blockIdx.x / a.blocks_per_slice;
     const int64_t gb = blockIdx.x - slice * a.blocks_per_slice;
     const int cpt = 1 << a.log2_cpt;
     const int gpb = kPackExChunks >> (a.log2_cpt + 2);   // groups per block
     const int64_t g0 = gb * gpb;
     const int64_t t0 = g0 * kExactRows;
-    const uint32_t kmask = (1u << a.bits) - 1u;
-    for (int i = threadIdx.x; i < kPackExChunks; i += kPackExThreads) {
-        const int64_t t = t0 + (i >> a.log2_cpt);
-        const int c = i & (cpt - 1);
-        uint32_t k = 0u, n = 0u;   // rows past the slice's end pack as zeros
-        if (t < a.tokens) {
-            const uint32_t *row = a.idx + (slice * a.tokens + t) * a.words;
-            const int bit = c * a.bits;
-            const int w = bit >> 5;
-            const uint64_t win = (static_cast<uint64_t>(w + 1 < a.words ? row[w + 1] : 0u) << 32) | row[w];
-            k = static_cast<uint32_t>(win >> (bit & 31)) & kmask;
-            n = exact_norm_code(a.h16[(slice * a.tokens + t) * cpt + c], a.m, a.nmax, a.step);
+    const int lw = 8 * a.wl;                   // low-bit words per group
+    const int log2_nfg = 3 + a.log2_fh;        // digit fields per group: 8 fh
+    uint16_t *kc = codes, *nc = codes + kPackExChunks;
+
+    // step 1
+    {
+        const uint32_t kmask = (1u << a.bits) - 1u;
+        uint2 hv[kPackExRuns];
+        uint32_t cw[kPackExRuns][3];
+        int bit0[kPackExRuns];
+        bool ok[kPackExRuns];
+#pragma unroll
+        for (int u = 0; u < kPackExRuns; ++u) {
+            const int i = 4 * (threadIdx.x + u * kPackExThreads);   // first chunk of the run
+            const int lr = i >> a.log2_cpt, c = i & (cpt - 1);
+            const int64_t t = t0 + lr;
+            ok[u] = t < a.tokens;                                    // rows past the end pack as zeros
+            const int64_t tr = ok[u] ? t : a.tokens - 1;
+            const int64_t rowi = slice * a.tokens + tr;
+            hv[u] = *reinterpret_cast<const uint2 *>(a.h16 + rowi * cpt + c);
+            const uint32_t *row = a.idx + rowi * a.words;
+            bit0[u] = c * a.bits;
+            const int w = bit0[u] >> 5;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) cw[u][k] = row[min(w + k, a.words - 1)];
         }
-        kc[i] = static_cast<uint16_t>(k);
-        nc[i] = static_cast<uint16_t>(n);
+#pragma unroll
+        for (int u = 0; u < kPackExRuns; ++u) {
+            const int i = 4 * (threadIdx.x + u * kPackExThreads);
+            const uint32_t h[4] = {hv[u].x & 0xFFFFu, hv[u].x >> 16, hv[u].y & 0xFFFFu, hv[u].y >> 16};
+            const uint32_t sh = static_cast<uint32_t>(bit0[u] & 31);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // code j starts at bit q of the 3 loaded words and ends inside
+                // them (sh + 4 b <= 96): its two-word window by alignbit
+                const uint32_t q = sh + static_cast<uint32_t>(j * a.bits);
+                const uint32_t wj = q >> 5;
+                const uint32_t lo = wj == 0u ? cw[u][0] : (wj == 1u ? cw[u][1] : cw[u][2]);
+                const uint32_t hi = wj == 0u ? cw[u][1] : cw[u][2];
+                const uint32_t k = __builtin_amdgcn_alignbit(hi, lo, q & 31u) & kmask;
+                kc[i + j] = static_cast<uint16_t>(ok[u] ? k : 0u);
+                nc[i + j] = static_cast<uint16_t>(ok[u] ? exact_norm_code(h[j], a.m, a.nmax, a.step) : 0u);
+            }
+        }
     }
     __syncthreads();
-    const int groups = static_cast<int>(min(static_cast<int64_t>(gpb), a.gps - g0));
+
+    // step 2: low-bit words (w = (stream s, word wi), s = (group, plane, row))
     const uint32_t lmask = (1u << a.m) - 1u;
-    const int lw = 8 * a.wl;   // words of the two low-bit planes
-    for (int w = threadIdx.x; w < groups * a.gw; w += kPackExThreads) {
-        const int gi = w / a.gw, ww = w - gi * a.gw;
-        const uint16_t *gk = kc + gi * kExactRows * cpt;
-        const uint16_t *gn = nc + gi * kExactRows * cpt;
+    for (int w = threadIdx.x; w < gpb * lw; w += kPackExThreads) {
+        const int s = static_cast<int>(__umul24(static_cast<uint32_t>(w), a.wl_magic) >> 20);
+        const int wi = w - s * a.wl;
+        const int gi = s >> 3, pl = (s >> 2) & 1, r = s & 3;
+        const uint16_t *src = (pl ? nc : kc) + ((gi * kExactRows + r) << a.log2_cpt);
+        const int b0 = 32 * wi;
+        const int c_lo = static_cast<int>(__umul24(static_cast<uint32_t>(b0), a.m_recip) >> 16);
+        const int c_hi = min(cpt - 1, static_cast<int>(__umul24(static_cast<uint32_t>(b0 + 31), a.m_recip) >> 16));
         uint32_t v = 0u;
-        if (ww < lw) {
-            // plane pl, row r, word wi of the row's stream of m-bit low parts
-            const int pr = ww / a.wl, wi = ww - pr * a.wl;
-            const uint16_t *src = (pr >= kExactRows ? gn : gk) + (pr & 3) * cpt;
-            const int b0 = 32 * wi;
-            const int c_hi = min(cpt - 1, (b0 + 31) / a.m);
-            for (int c = b0 / a.m; c <= c_hi; ++c) {
-                const int sft = c * a.m - b0;   // -(m - 1) .. 31
-                const uint32_t low = src[c] & lmask;
-                v |= sft >= 0 ? (low << sft) : (low >> -sft);
-            }
-        } else {
-            // 13-bit digit fields: field f of the stream is (row f / 2fh,
-            // plane (f / fh) % 2, field f % fh of that plane)
-            const int b0 = 32 * (ww - lw);
-            const int nf = kExactRows * 2 * a.fh;
-            const int f_hi = min(nf - 1, (b0 + 31) / kFieldBits);
-            for (int f = b0 / kFieldBits; f <= f_hi; ++f) {
-                const int r = f / (2 * a.fh), pl = (f / a.fh) & 1, ff = f - (f / a.fh) * a.fh;
-                const uint16_t *src = (pl ? gn : gk) + r * cpt;
-                uint32_t val = 0u;
+        for (int c = c_lo; c <= c_hi; ++c) {
+            const int sft = c * a.m - b0;   // -(m - 1) .. 31
+            const uint32_t low = src[c] & lmask;
+            v |= sft >= 0 ? (low << sft) : (low >> -sft);
+        }
+        lows[w] = v;
+    }
+    // digit fields: field f of a group is (row f / 2fh, plane (f / fh) % 2, f % fh)
+    for (int f = threadIdx.x; f < (gpb << log2_nfg); f += kPackExThreads) {
+        const int gi = f >> log2_nfg, ff = f & ((1 << log2_nfg) - 1);
+        const int r = ff >> (a.log2_fh + 1), pl = (ff >> a.log2_fh) & 1, fi = ff & (a.fh - 1);
+        const uint16_t *src = (pl ? nc : kc) + ((gi * kExactRows + r) << a.log2_cpt);
+        uint32_t val = 0u;
 #pragma unroll
-                for (int i = kDigitsPerField - 1; i >= 0; --i) {
-                    const int c = ff * kDigitsPerField + i;
-                    val = 3u * val + (c < cpt ? static_cast<uint32_t>(src[c]) >> a.m : 0u);
-                }
+        for (int q = kDigitsPerField - 1; q >= 0; --q) {
+            const int c = fi * kDigitsPerField + q;
+            val = 3u * val + (c < cpt ? static_cast<uint32_t>(src[c]) >> a.m : 0u);
+        }
+        fields[f] = val;
+    }
+    __syncthreads();
+
+    // step 3: every word of the block's groups
+    const int nfg = 1 << log2_nfg;
+    const int groups = static_cast<int>(min(static_cast<int64_t>(gpb), a.gps - g0));
+    uint32_t *dst = a.out + (slice * a.gps + g0) * a.gw;
+    for (int w = threadIdx.x; w < groups * a.gw; w += kPackExThreads) {
+        const int gi = static_cast<int>(__umul24(static_cast<uint32_t>(w), a.gw_magic) >> 24);
+        const int ww = w - gi * a.gw;
+        uint32_t v;
+        if (ww < lw) {
+            v = lows[gi * lw + ww];
+        } else {
+            const int b0 = 32 * (ww - lw);
+            const int f_hi = min(nfg - 1, (b0 + 31) / kFieldBits);
+            v = 0u;
+            for (int f = b0 / kFieldBits; f <= f_hi; ++f) {
+                const uint32_t val = fields[gi * nfg + f];
                 const int sft = f * kFieldBits - b0;   // -12 .. 31
                 v |= sft >= 0 ? (val << sft) : (val >> -sft);
             }
         }
-        a.out[(slice * a.gps + g0 + gi) * a.gw + ww] = v;
+        dst[w] = v;
+    }
+}
+
+// Exact-rate packing specialised for 32 chunks per row (head_dim 128) and a
+// fixed m (S = 8: m = 6, S = 32: m = 8): one thread per (group, plane, row)
+// stream of 32 codes, all in registers.  Threads 0-127 take the index streams
+// of the block's 32 groups (loading their whole-bit code rows), threads
+// 128-255 the norm streams (loading their binary16 half-norm rows), so no
+// wave runs both.  Each writes its row's m low-bit words straight to the
+// record and its 4 digit field values to LDS; the 13 digit words per group
+// are then gathered from the fields.
+template <int M>
+__global__ __launch_bounds__(kPackExThreads) void pack_exact32_kernel(PackExArgs a) {
+    constexpr int CPT = 32, B = M + 2, WL = M, FH = 4, NFG = 8 * FH, LW = 8 * WL;
+    constexpr int GW = LW + (kExactRows * 2 * FH * kFieldBits + 31) / 32;
+    constexpr int GPB = kPackExThreads / 8;   // groups per block
+    __shared__ uint32_t fields[GPB * NFG];
+    const int64_t slice = blockIdx.x / a.blocks_per_slice;
+    const int64_t g0 = (blockIdx.x - slice * a.blocks_per_slice) * GPB;
+    const int pl = threadIdx.x >> 7;
+    const int gi = (threadIdx.x & 127) >> 2, r = threadIdx.x & 3;
+    const int64_t g = g0 + gi;
+    const int64_t t = g * kExactRows + r;
+    const bool live = g < a.gps;
+    uint32_t code[CPT];
+    if (t < a.tokens) {
+        const int64_t rowi = slice * a.tokens + t;
+        if (pl == 0) {
+            uint32_t w[B];
+            const uint2 *src = reinterpret_cast<const uint2 *>(a.idx + rowi * B);
+#pragma unroll
+            for (int k = 0; k < B / 2; ++k) {
+                const uint2 v = src[k];
+                w[2 * k] = v.x;
+                w[2 * k + 1] = v.y;
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                constexpr uint32_t kmask = (1u << B) - 1u;
+                const int p = c * B, k = p >> 5, sft = p & 31;
+                code[c] = (sft + B <= 32 ? w[k] >> sft : __builtin_amdgcn_alignbit(w[k + 1], w[k], sft)) & kmask;
+            }
+        } else {
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.h16 + rowi * CPT);
+#pragma unroll
+            for (int k = 0; k < CPT / 8; ++k) {
+                const uint4 v = src[k];
+                const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    code[8 * k + e] = exact_norm_code((h[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, M, a.nmax, a.step);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) code[c] = 0u;   // rows past the slice's end
+    }
+    // low-bit words of the stream
+    uint32_t lw[WL];
+#pragma unroll
+    for (int q = 0; q < WL; ++q) lw[q] = 0u;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        constexpr uint32_t lmask = (1u << M) - 1u;
+        const int p = c * M, k = p >> 5, sft = p & 31;
+        const uint32_t low = code[c] & lmask;
+        lw[k] |= low << sft;
+        if (sft + M > 32) lw[k + 1] |= low >> (32 - sft);
+    }
+    uint32_t *dst = a.out + (slice * a.gps + g) * GW;
+    if (live) {
+        uint32_t *lp = dst + (pl * kExactRows + r) * WL;
+#pragma unroll
+        for (int q = 0; q < WL; ++q) lp[q] = lw[q];
+    }
+    // digit fields of the stream
+#pragma unroll
+    for (int f = 0; f < FH; ++f) {
+        uint32_t val = 0u;
+#pragma unroll
+        for (int q = kDigitsPerField - 1; q >= 0; --q) val = 3u * val + (code[f * kDigitsPerField + q] >> M);
+        fields[gi * NFG + r * 2 * FH + pl * FH + f] = val;
+    }
+    __syncthreads();
+    constexpr int DW = GW - LW;   // digit words per group
+    for (int w = threadIdx.x; w < GPB * DW; w += kPackExThreads) {
+        const int gj = w / DW, ww = w - gj * DW;
+        if (g0 + gj >= a.gps) break;
+        const int b0 = 32 * ww;
+        const int f_hi = min(NFG - 1, (b0 + 31) / kFieldBits);
+        uint32_t v = 0u;
+        for (int f = b0 / kFieldBits; f <= f_hi; ++f) {
+            const uint32_t val = fields[gj * NFG + f];
+            const int sft = f * kFieldBits - b0;
+            v |= sft >= 0 ? (val << sft) : (val >> -sft);
+        }
+        a.out[(slice * a.gps + g0 + gj) * GW + LW + ww] = v;
     }
 }
 
@@ -2144,6 +2300,17 @@ hipError_t launch_pack_exact(const Geometry &g, const uint32_t *idx32, const uin
     a.gw = g.egw;
     a.nmax = g.enmax;
     a.step = g.estep;
+    a.gw_magic = static_cast<uint32_t>(((int64_t{1} << 24) + g.egw - 1) / g.egw);
+    a.wl_magic = static_cast<uint32_t>(((int64_t{1} << 20) + g.ewl - 1) / g.ewl);
+    a.m_recip = static_cast<uint32_t>(((int64_t{1} << 16) + g.em - 1) / g.em);
+    a.log2_fh = __builtin_ctz(static_cast<unsigned>(g.efh));
+    if (g.cpt == 32 && (g.em == 6 || g.em == 8)) {
+        a.blocks_per_slice = ceil_div(g.egps, static_cast<int64_t>(kPackExThreads / 8));
+        const dim3 grid(static_cast<unsigned>(g.slices * a.blocks_per_slice));
+        if (g.em == 8) hipLaunchKernelGGL(pack_exact32_kernel<8>, grid, dim3(kPackExThreads), 0, st, a);
+        else hipLaunchKernelGGL(pack_exact32_kernel<6>, grid, dim3(kPackExThreads), 0, st, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(pack_exact_kernel, dim3(static_cast<unsigned>(g.slices * a.blocks_per_slice)),
                        dim3(kPackExThreads), 0, st, a);
     return hipGetLastError();
