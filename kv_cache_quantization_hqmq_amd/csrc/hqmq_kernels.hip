@@ -1658,8 +1658,11 @@ __device__ __forceinline__ void digit_pair(uint32_t v, uint32_t sel, uint32_t *d
     *d1 = q3 - 3u * div3_small(q3);
 }
 
+// (5 waves per SIMD where the registers allow it: the decode is bound by
+// memory latency and bandwidth, so it wants many waves in flight)
 template <bool F32OUT, bool TABLE, int NF>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(NF == 1 ? 4 : 5)))
+void decode_kernel(DecArgs a) {
     constexpr bool NPACK = NF == kNormPacked;
     constexpr bool EXACT = NF == kNormExact;
     // steps whose loads a thread issues together (an exact-rate step holds
@@ -1797,7 +1800,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
         return d;
     };
     constexpr int kWaveStep = 128;   // chunks per wave step
-    for (int64_t c0 = w0 + 2 * lane; c0 < w1; c0 += static_cast<int64_t>(kWaveStep) * kUnroll) {
+    // the loop runs on a wave-uniform base, so that every lane takes part in
+    // the exchange below (lanes past the range's end load and store nothing)
+    for (int64_t base = w0; base < w1; base += static_cast<int64_t>(kWaveStep) * kUnroll) {
+        const int64_t c0 = base + 2 * lane;
+        // the next 64 side-list entries (lane j: entry e_next + j), requested
+        // with the records: the iteration's flagged chunks take their values
+        // from this window by lane exchange instead of loads issued after
+        // their flags are known
+        const uint64_t wbase = e_next;
+        uint2 wv = make_uint2(0u, 0u);
+        if (wbase < e_end) {
+            const uint64_t e = wbase + static_cast<uint64_t>(lane);
+            wv = sval[e < e_end ? e : e_end - 1];
+        }
         DecPair pd[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -1853,8 +1869,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
             const uint64_t e1 = e0 + (f0 ? 1 : 0);
             oh[u][0] = f0 && e0 < e_end;
             oh[u][1] = f1 && e1 < e_end;
-            ov[u][0] = oh[u][0] ? sval[e0] : make_uint2(0u, 0u);
-            ov[u][1] = oh[u][1] ? sval[e1] : make_uint2(0u, 0u);
+            ov[u][0] = make_uint2(0u, 0u);
+            ov[u][1] = make_uint2(0u, 0u);
+            if ((m0 | m1) != 0u) {   // wave-uniform: every lane takes part in the exchange
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint64_t q = (i ? e1 : e0) - wbase;   // window lane of the entry
+                    const int src = q < 64u ? static_cast<int>(q) : 0;
+                    const uint2 v = make_uint2(static_cast<uint32_t>(__shfl(static_cast<int>(wv.x), src)),
+                                               static_cast<uint32_t>(__shfl(static_cast<int>(wv.y), src)));
+                    // entries past the window (more than 64 flags in one
+                    // iteration) are loaded on their own
+                    const bool far = oh[u][i] && q >= 64u;
+                    uint2 fv = make_uint2(0u, 0u);
+                    if (far) fv = sval[i ? e1 : e0];
+                    if (oh[u][i]) ov[u][i] = far ? fv : v;
+                }
+            }
             e_next += static_cast<uint64_t>(__popcll(m0) + __popcll(m1));
         }
 #pragma unroll

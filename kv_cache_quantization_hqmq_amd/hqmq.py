@@ -18,7 +18,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhqmq.so")
+# HQMQ_LIB selects another build of the same library (the host-sanitizer
+# build, or a build kept for a comparison run)
+LIB_PATH = os.environ.get("HQMQ_LIB") or os.path.join(_HERE, "libhqmq.so")
 
 HQMQ_OK, HQMQ_EINVAL, HQMQ_ENOTSUP, HQMQ_ECAPACITY, HQMQ_EHIP = 0, -1, -2, -3, -4
 HQMQ_F16, HQMQ_F32 = 0, 1
