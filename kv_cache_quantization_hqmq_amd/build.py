@@ -2,11 +2,14 @@
 
     python -m kv_cache_quantization_hqmq_amd.build
 
-compiles csrc/hqmq_kernels.hip, csrc/hqmq_attend.hip, csrc/hqmq_ceiling.hip,
-csrc/hqmq_noalloc.hip and csrc/hqmq_api.cpp with hipcc into
-kv_cache_quantization_hqmq_amd/libhqmq.so.  Every HIP translation unit is
+compiles csrc/hqmq_kernels.hip, csrc/hqmq_search.hip, csrc/hqmq_attend.hip,
+csrc/hqmq_ceiling.hip, csrc/hqmq_noalloc.hip and csrc/hqmq_api.cpp with hipcc
+into kv_cache_quantization_hqmq_amd/libhqmq.so.  Every HIP translation unit is
 built with packed FP32 disabled and fp contraction off (each fused
-multiply-add in the kernels is written out).
+multiply-add in the kernels is written out).  hqmq_search.hip (the fp16-input
+search) is also built with IEEE mode off and fp32 denormals flushed: the mode
+in which the hardware applies VOP3 output modifiers (its file comment shows
+why that mode changes none of its values).
 """
 import os
 import subprocess
@@ -34,6 +37,12 @@ KERNEL_FLAGS = [
     # MFMA results in arch VGPRs (no v_accvgpr_read per result)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# per-file additions
+FILE_FLAGS = {
+    "hqmq_search.hip": ["-fgpu-flush-denormals-to-zero", "-mno-amdgpu-ieee"],
+}
+SOURCES = ("hqmq_kernels.hip", "hqmq_search.hip", "hqmq_attend.hip", "hqmq_ceiling.hip", "hqmq_noalloc.hip",
+           "hqmq_api.cpp")
 
 
 def _run(cmd, verbose):
@@ -54,9 +63,9 @@ def build(verbose: bool = False) -> str:
     objs = []
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    for src in ("hqmq_kernels.hip", "hqmq_attend.hip", "hqmq_ceiling.hip", "hqmq_noalloc.hip", "hqmq_api.cpp"):
+    for src in SOURCES:
         obj = os.path.join(bdir, src + ".o")
-        extra = ["-x", "hip", *KERNEL_FLAGS] if src.endswith(".hip") else []
+        extra = ["-x", "hip", *KERNEL_FLAGS, *FILE_FLAGS.get(src, [])] if src.endswith(".hip") else []
         _run([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"

@@ -28,57 +28,17 @@
 #include <type_traits>
 
 #include "hqmq_device.h"
+#include "hqmq_encode.h"
 #include "hqmq_launch.h"
 
 namespace hqmq {
 namespace {
 
-constexpr int kEncThreads = 256;   // 4 waves; each wave encodes 64 chunks per step
 constexpr int kFlagThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kDecThreads = 256;   // each thread decodes 4 chunks per step
 constexpr int kDecUnroll = 8;      // steps whose loads a thread issues together
-constexpr int kMaxS = 1024;
 constexpr int kTableMaxS = 64;     // decode keeps the 24 S codewords in LDS up to here
-
-// Correctly rounded fp32 square root of a >= 0.  v_sqrt_f32 is within one
-// ulp; the result is then moved to the neighbour whose rounding interval
-// holds sqrt(a), decided exactly in fp64: the midpoints between y and its
-// neighbours have at most 25 significant bits, so their squares are exact.
-// Inputs below 2^-100 are scaled by 2^100 first (exact) to stay in the
-// normal range of v_sqrt_f32.
-__device__ __forceinline__ float sqrt_rn(float a) {
-    if (!(a > 0.0f)) return a;  // 0 (and the documented non-finite precondition)
-    const bool tiny = a < 0x1p-100f;
-    const float as = tiny ? a * 0x1p100f : a;
-    float y = __builtin_amdgcn_sqrtf(as);
-    const double ad = static_cast<double>(as);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const float yu = __uint_as_float(__float_as_uint(y) + 1u);
-        const float yd = __uint_as_float(__float_as_uint(y) - 1u);
-        const double hi = (static_cast<double>(y) + static_cast<double>(yu)) * 0.5;
-        const double lo = (static_cast<double>(y) + static_cast<double>(yd)) * 0.5;
-        if (ad > hi * hi) y = yu;
-        else if (ad < lo * lo) y = yd;
-    }
-    return tiny ? y * 0x1p-50f : y;
-}
-
-// binary16 half-norm code fp16_rn(sqrt_rn(s2) / 2).  v_sqrt_f32 is within one
-// ulp, so h = v_sqrt_f32(s2) / 2 and the exact half-root round to the same
-// binary16 unless a rounding midpoint lies within one fp32 ulp of h: in the
-// normal binary16 range [2^-14, 2^16) the midpoints are the fp32 values whose
-// low 13 mantissa bits are 0x1000, so h is safe unless those bits are
-// 0x0FFF..0x1001.  Only the others (about 3 in 8192 chunks, and any h outside
-// that range) take the correctly rounded root.
-__device__ __forceinline__ uint16_t half_norm_code(float s2) {
-    const float h = __builtin_amdgcn_sqrtf(s2) * 0.5f;
-    const uint32_t hb = __float_as_uint(h);
-    const bool safe = (hb - 0x38800000u) < (0x47800000u - 0x38800000u) && ((hb & 0x1FFFu) - 0x0FFFu) > 2u;
-    if (safe) return f32_to_f16_bits(h);
-    return f32_to_f16_bits(sqrt_rn(s2) * 0.5f);
-}
 
 // Score of the best 2T element for one s from t = (<x, e_m q_s>)_m:
 // max(|t|_inf, |t|_1 / 2) (a unit +-e_m scores +-t_m; a half-unit
@@ -122,74 +82,6 @@ __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
 // --------------------------------------------------------------------------
 // Encode search kernel.
 // --------------------------------------------------------------------------
-struct EncArgs {
-    const void *x;
-    const float *cb;
-    uint32_t *idx;
-    uint16_t *hnorm;
-    int64_t n_slice;
-    int64_t tiles_per_slice;
-    int64_t tokens;
-    int32_t tile_chunks;
-    int32_t S;
-    int32_t NT;     // ceil(S / 4) tiles of 4 secondary codewords
-    int32_t cpt;
-    int32_t log2_cpt;
-    int32_t bits;
-    int32_t words;
-    // Med3x (batch_chunks == 0: off).  Tiles are grouped by batch and
-    // accumulate the batch's histogram of half-norm codes.
-    int32_t tiles_per_batch;
-    int64_t batch_chunks;
-    int64_t bps;            // batches per slice
-    int64_t nbatch;         // slices * bps
-    int32_t xcd_map;        // 1: a batch's tiles are dispatched to one XCD
-    uint32_t *hist;         // [nbatch][2048] histograms of hnorm >> 4, zeroed
-};
-
-// Chunk range of this block.  Without Med3x: tiles_per_slice tiles per
-// slice.  With Med3x: tiles_per_batch tiles per batch, the last one partial
-// or empty; blocks are dispatched to the 8 XCDs round-robin, so with
-// xcd_map block b serves batch (b / 8 / tiles_per_batch) * 8 + b % 8 and the
-// histogram atomics of a batch stay within one XCD.
-struct TileCoords {
-    int64_t slice, c_begin, c_end;
-    int64_t batch, b_lo, b_n;   // Med3x: batch index, first chunk, chunk count
-};
-
-__device__ __forceinline__ TileCoords tile_coords(const EncArgs &a) {
-    TileCoords t;
-    const int64_t bid = blockIdx.x;
-    if (a.batch_chunks == 0) {
-        t.slice = bid / a.tiles_per_slice;
-        t.c_begin = (bid - t.slice * a.tiles_per_slice) * a.tile_chunks;
-        t.c_end = min(t.c_begin + static_cast<int64_t>(a.tile_chunks), a.n_slice);
-        t.batch = -1;
-        t.b_lo = 0;
-        t.b_n = 0;
-        return t;
-    }
-    const int64_t tpb = a.tiles_per_batch;
-    int64_t batch, tile;
-    if (a.xcd_map) {
-        const int64_t j = bid >> 3;
-        batch = (j / tpb) * 8 + (bid & 7);
-        tile = j - (j / tpb) * tpb;
-    } else {
-        batch = bid / tpb;
-        tile = bid - batch * tpb;
-    }
-    t.batch = batch;
-    t.slice = batch / a.bps;
-    t.b_lo = (batch - t.slice * a.bps) * a.batch_chunks;
-    t.b_n = min(a.batch_chunks, a.n_slice - t.b_lo);
-    t.c_begin = t.b_lo + tile * a.tile_chunks;
-    t.c_end = min(t.c_begin + static_cast<int64_t>(a.tile_chunks), t.b_lo + t.b_n);
-    return t;
-}
-
-__device__ void med3_after_tile(const EncArgs &a, const TileCoords &tc, uint32_t *shist, uint32_t *sh);
-
 // NT_REG > 0: S <= 4 NT_REG and the A operands live in registers.
 // NT_REG == 0: any S <= kMaxS, A read from the LDS copy of the codebook.
 template <int NT_REG, bool F32IN, bool MED>
@@ -368,194 +260,6 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_kernel(EncArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Encode search for fp16 inputs on the f16 matrix cores.
-//
-// v_mfma_f32_32x32x8_f16 computes 32 rows (8 secondary codewords x 4 basis
-// units e_m) against 32 chunks with K = 8: k = 0..3 multiply the chunk's four
-// fp16 components by the hi parts of the rows e_m q_s, k = 4..7 by the lo
-// parts.  Every product is exact in fp32 and D accumulates in fp32, so t is
-// the fp32 transform of the exact codebook value.  Lane l supplies A row
-// l % 32, k block l / 32, and B column l % 32 (the raw 8-byte chunk, the same
-// for both k blocks); D VGPR 4 a + r of lane l is row 8 a + 4 (l / 32) + r,
-// column l % 32: t_r of s = 8 tile + 2 a + l / 32 for chunk l % 32.
-// --------------------------------------------------------------------------
-template <int NT8, bool MED>
-__global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a) {
-    constexpr int kQ = NT8 > 0 ? 32 * NT8 : 4 * kMaxS;
-    __shared__ __attribute__((aligned(16))) float sq[kQ];
-    __shared__ uint32_t sword[4][64];   // the group's packed index words, per wave
-    __shared__ uint32_t shist[MED ? 2048 : 1];
-    __shared__ uint32_t sh[kEncThreads / 64 + 3];
-
-    const TileCoords tc = tile_coords(a);
-    const int64_t slice = tc.slice;
-    const int64_t c_begin = tc.c_begin;
-    const int64_t c_end = tc.c_end;
-    const int NT = NT8 > 0 ? NT8 : (a.S + 7) / 8;
-    {
-        const float *q = a.cb + slice * a.S * 4;
-        const int nq = 32 * NT;
-        for (int i = threadIdx.x; i < nq; i += kEncThreads) sq[i] = i < 4 * a.S ? double_f16(q[i]) : 0.0f;
-        if constexpr (MED)
-            for (int i = threadIdx.x; i < 2048; i += kEncThreads) shist[i] = 0;
-    }
-    __syncthreads();
-
-    const int lane = threadIdx.x & 63;
-    // wave-uniform (a scalar register), so the loop and the block-relative
-    // offsets below are scalar work
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int col = lane & 31;
-    const int hh = lane >> 5;            // K block: 0 = hi parts, 1 = lo parts
-    const int m_row = col & 3;
-    const int s_loc = col >> 2;
-
-    // A operand of tile t: row (s = 8 t + s_loc, m = m_row), k = 0..3 of the
-    // hi (hh = 0) or lo (hh = 1) part of (e_m q_s)[k] = sign(m, k) q_s[m ^ k]
-    auto a_operand = [&](int t) {
-        const float *qs = &sq[4 * (8 * t + s_loc)];
-        f16x4 r;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float v = qs[m_row ^ k];
-            const _Float16 hi = static_cast<_Float16>(v);
-            const _Float16 part = hh ? static_cast<_Float16>(v - static_cast<float>(hi)) : hi;
-            r[k] = ((kNegMask >> (4 * m_row + k)) & 1u) ? -part : part;
-        }
-        return r;
-    };
-    f16x4 A[NT8 > 0 ? NT8 : 1];
-    if constexpr (NT8 > 0) {
-#pragma unroll
-        for (int t = 0; t < NT8; ++t) A[t] = a_operand(t);
-    }
-
-    const f32x16 zero = {};
-    const int wpg = (64 >> a.log2_cpt) * a.words;
-    // buffer resources over the wave's current 64 chunks onward (rebuilt per
-    // step from uniform values, so scalar work): the block's chunks
-    // [c_begin, c_end) start on a token row and number at most 8192, so
-    // offsets are 32-bit and the resources' sizes do the range checks (loads
-    // past the end read 0, stores there are dropped)
-    const uint32_t n = c_end > c_begin ? static_cast<uint32_t>(c_end - c_begin) : 0u;
-    const uint32_t tok_lim = (n + static_cast<uint32_t>(a.cpt) - 1u) >> a.log2_cpt;   // token rows of the block
-    const uint2 *xb = static_cast<const uint2 *>(a.x) + slice * a.n_slice + c_begin;
-    uint16_t *hb = a.hnorm + slice * a.n_slice + c_begin;
-    uint32_t *wb = a.idx + (slice * a.tokens + (c_begin >> a.log2_cpt)) * a.words;
-
-    for (uint32_t o0 = 64u * wave; o0 < n; o0 += 64u * 4u) {
-        const uint32_t r0 = o0 >> a.log2_cpt;   // the step's first token row
-        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<void *>(static_cast<const void *>(xb + o0)), 0, static_cast<int>((n - o0) * 8u), kBufWord3);
-        const __amdgpu_buffer_rsrc_t hrs =
-            __builtin_amdgcn_make_buffer_rsrc(hb + o0, 0, static_cast<int>((n - o0) * 2u), kBufWord3);
-        const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-            wb + r0 * static_cast<uint32_t>(a.words), 0,
-            static_cast<int>((tok_lim - r0) * static_cast<uint32_t>(a.words) * 4u), kBufWord3);
-        // B operands: chunk o0 + 32 b + col of both column blocks
-        uint2 xr[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(xrs, static_cast<int>((32u * b + col) * 8u), 0, 0);
-            xr[b] = make_uint2(u[0], u[1]);
-        }
-        float bsc[2];
-        int bsi[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const f16x4 bv = __builtin_bit_cast(f16x4, xr[b]);
-            // running best over the MFMA tiles t: the best of a tile's four
-            // scores (s = 8 t + 2 g + hh, g = 0..3) replaces the running one
-            // when strictly larger, with the tile and its four scores; which g
-            // it was is resolved once at the end (first g reaching it), so the
-            // result is the sequential strict argmax in s order
-            float best = -1.0f;
-            int bt = 0;
-            f32x4 bs = {-1.0f, -1.0f, -1.0f, -1.0f};
-            auto tile = [&](int t, const f32x16 &d) {
-                f32x4 sc;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 tv = {d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]};
-                    sc[g] = best_primary(tv);
-                }
-                const float m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-                if (m > best) {
-                    best = m;
-                    bt = t;
-                    bs = sc;
-                }
-            };
-            if constexpr (NT8 > 0) {
-#pragma unroll
-                for (int t = 0; t < NT8; ++t) tile(t, __builtin_amdgcn_mfma_f32_32x32x8f16(A[t], bv, zero, 0, 0, 0));
-            } else {
-                for (int t = 0; t < NT; ++t)
-                    tile(t, __builtin_amdgcn_mfma_f32_32x32x8f16(a_operand(t), bv, zero, 0, 0, 0));
-            }
-            const int g = bs[0] == best ? 0 : (bs[1] == best ? 1 : (bs[2] == best ? 2 : 3));
-            bsc[b] = best;
-            bsi[b] = 8 * bt + 2 * g + hh;
-        }
-
-        // lane l < 32 holds parity 0 of chunks l and l + 32, lane l + 32
-        // parity 1 of the same chunks; swapping the upper half of block 0 with
-        // the lower half of block 1 leaves every lane l with both parities of
-        // chunk o0 + l (v_permlane32_swap)
-        int s_best;
-        {
-            const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(bsc[0]), __float_as_uint(bsc[1]), false, false);
-            const auto pi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(bsi[0]), static_cast<uint32_t>(bsi[1]),
-                                                             false, false);
-            const float s0 = __uint_as_float(ps[0]), s1 = __uint_as_float(ps[1]);
-            const int i0 = static_cast<int>(pi[0]), i1 = static_cast<int>(pi[1]);
-            const bool take1 = (s1 > s0) | ((s1 == s0) & (i1 < i0));
-            s_best = min(take1 ? i1 : i0, 8 * NT - 1);
-        }
-        const uint32_t o = o0 + lane;
-        const bool valid = o < n;
-        const uint2 own = hh ? xr[1] : xr[0];
-        const float v0 = f16_bits_to_f32(static_cast<uint16_t>(own.x));
-        const float v1 = f16_bits_to_f32(static_cast<uint16_t>(own.x >> 16));
-        const float v2 = f16_bits_to_f32(static_cast<uint16_t>(own.y));
-        const float v3 = f16_bits_to_f32(static_cast<uint16_t>(own.y >> 16));
-
-        // declared fp32 squared norm and its binary16 half-norm code
-        float s2 = v0 * v0;
-        s2 = __builtin_fmaf(v1, v1, s2);
-        s2 = __builtin_fmaf(v2, v2, s2);
-        s2 = __builtin_fmaf(v3, v3, s2);
-        const uint16_t hn = half_norm_code(s2);
-
-        const int pidx = primary_index(&sq[4 * s_best], v0, v1, v2, v3);
-        const uint32_t code = s2 > 0.0f ? __umul24(24u, static_cast<uint32_t>(s_best)) + static_cast<uint32_t>(pidx) : 0u;
-        __builtin_amdgcn_raw_buffer_store_b16(hn, hrs, lane * 2, 0, 0);
-        if constexpr (MED) {
-            if (valid) atomicAdd(&shist[hn >> 4], 1u);
-        }
-        // pack the group's codes into its token rows' words: every code is
-        // ORed into the one or two words it spans, then lane w < wpg stores
-        // word w (codes past the range are 0 and leave their words as they are)
-        if (lane < wpg) sword[wave][lane] = 0u;
-        wave_sync();
-        {
-            const int bit = (lane & (a.cpt - 1)) * a.bits;
-            uint32_t *wr = &sword[wave][(lane >> a.log2_cpt) * a.words + (bit >> 5)];
-            const int sft = bit & 31;
-            atomicOr(wr, code << sft);
-            if (sft + a.bits > 32) atomicOr(wr + 1, code >> (32 - sft));
-        }
-        wave_sync();
-        if (lane < wpg) {
-            // word lane % words of token row r0 + lane / words
-            __builtin_amdgcn_raw_buffer_store_b32(sword[wave][lane], wrs, lane * 4, 0, 0);
-        }
-        wave_sync();
-    }
-    if constexpr (MED) med3_after_tile(a, tc, shist, sh);
-}
-
-// --------------------------------------------------------------------------
 // Block-wide exclusive scan (all threads of the block must call it).
 // --------------------------------------------------------------------------
 template <typename T, int NTHREADS>
@@ -600,17 +304,6 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *total, T *sh) {
 // declared fp32 operations); a chunk is an outlier if h > h(thr), or if
 // h == h(thr) and its exact s2 > thr.
 // --------------------------------------------------------------------------
-
-// Called by every thread of a Med3x tile after its search loop: merge the
-// tile's code histogram into its batch's (read by the next kernel).
-__device__ void med3_after_tile(const EncArgs &a, const TileCoords &tc, uint32_t *shist, uint32_t *) {
-    __syncthreads();
-    uint32_t *gh = a.hist + tc.batch * 2048;
-    for (int i = threadIdx.x; i < 2048; i += kEncThreads) {
-        const uint32_t v = shist[i];
-        if (v) atomicAdd(&gh[i], v);
-    }
-}
 
 constexpr int kSelThreads = 512;
 constexpr int kCandCap = 4096;
@@ -2152,22 +1845,13 @@ hipError_t launch_encode_search(const Geometry &g, const void *x, const float *c
         if (m) HQMQ_ENC(NT, true, true);         \
         else HQMQ_ENC(NT, true, false);          \
     } while (0)
-#define HQMQ_ENC_H(NT8)                                                                            \
-    do {                                                                                           \
-        if (m) hipLaunchKernelGGL((encode_search_h_kernel<NT8, true>), grid, block, 0, st, a);    \
-        else hipLaunchKernelGGL((encode_search_h_kernel<NT8, false>), grid, block, 0, st, a);     \
-    } while (0)
     if (g.f32) {
         if (a.NT == 2) HQMQ_ENC_NT(2);
         else if (a.NT == 8) HQMQ_ENC_NT(8);
         else HQMQ_ENC_NT(0);
     } else {
-        const int nt8 = (g.S + 7) / 8;
-        if (nt8 == 1) HQMQ_ENC_H(1);
-        else if (nt8 == 4) HQMQ_ENC_H(4);
-        else HQMQ_ENC_H(0);
+        return launch_search_h(a, blocks, (g.S + 7) / 8, m, st);
     }
-#undef HQMQ_ENC_H
 #undef HQMQ_ENC_NT
 #undef HQMQ_ENC
     return hipGetLastError();

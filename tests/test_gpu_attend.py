@@ -208,8 +208,8 @@ def test_attend_full_size_decode_step():
             dec, near, bad = {}, 0, 0
             for role in (0, 1):
                 x = xs[role][l, h, b * Tc:(b + 1) * Tc].float().cpu().numpy()
-                r, dec[role] = A.oracle_slice(x, cbh[role][l, h], b * Tc, w.med_batch_tokens, w.med_C)
-                nr, br = A.record_mismatches(r, A.gpu_slice_records(desc, recs[role], l, h, b * Tc, Tc))
+                dec[role], nr, br = A.reference_slice(x, cbh[role][l, h], b * Tc, w.med_batch_tokens, w.med_C, desc,
+                                                      recs[role], l, h)
                 near, bad = near + nr, bad + br
             ref = A.O.attend(dec[0], dec[1], qn[b, h * group:(h + 1) * group], 1.0 / math.sqrt(D))
             ratio = A.compare_out(got[b, h * group:(h + 1) * group], ref, dec[1])
