@@ -19,7 +19,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libhqmq_oracle.so")
+# HQMQ_ORACLE_LIB: another build of the same source (the host sanitizer run)
+_LIB_PATH = os.environ.get("HQMQ_ORACLE_LIB") or os.path.join(_HERE, "libhqmq_oracle.so")
 _lib = None
 
 _f32p = ctypes.POINTER(ctypes.c_float)
