@@ -371,6 +371,30 @@ def test_single_token_and_tiny_batches():
         _check(desc, x, cb_host, cb)
 
 
+@pytest.mark.parametrize("case", ["inflated_rows", "some_rows_inflated", "crowded_outliers"])
+def test_med3_uneven_batches(case):
+    """Med3x batches of 32768 chunks whose outliers are spread unevenly: the
+    first 8 token rows of every 256 x 100 (a few huge rows, and the hot
+    channel's outliers everywhere else), the same in every third 256-row block
+    only, or the first 26 channels x 30 (22% of the chunks are outliers).  The
+    side list, flags and codes must be bit-exact with the oracle."""
+    L, H, T, D, S, B = 1, 2, 3000, 128, 32, 1024
+    x = _x((L, H, T, D), torch.float16, seed=17)
+    x[:, :, :, 5] *= 40
+    rows = torch.arange(T, device="cuda")
+    first_rows = (rows % 256) < 8
+    if case == "inflated_rows":
+        x[:, :, first_rows, :] *= 100
+    elif case == "some_rows_inflated":
+        x[:, :, first_rows & ((rows // 256) % 3 == 1), :] *= 100
+    else:
+        x[:, :, :, :26] *= 30
+    cb_host, cb = _cb(L, H, S)
+    desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F16, B, 3.0)
+    rep, _, _ = _check(desc, x, cb_host, cb)
+    assert rep["outliers"] > 0
+
+
 def test_zero_and_degenerate_batches():
     """All-zero slice (median 0, no outlier), half-zero batch (median 0: every
     nonzero chunk is an outlier), fp16 extremes."""
