@@ -39,10 +39,13 @@ PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense f16 matrix cores
 PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 NORM_FORMATS = {"f16": 0, "packed": 1, "exact": 2}   # hqmq_desc.norm_format
-KERNEL_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_kernels.hip")
+_CSRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc")
+# the sources a committed counter summary was taken from (codec; attention)
+KERNEL_SRC = [os.path.join(_CSRC, f) for f in ("hqmq_kernels.hip", "hqmq_search.hip", "hqmq_encode.h",
+                                                "hqmq_device.h")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_llama3-70b-kv-128k.json")
 COUNTERS5_FILE = os.path.join(ROOT, "profiles", "counters_llama3-8b-decode-32x32k.json")
-ATTEND_SRC = os.path.join(ROOT, "kv_cache_quantization_hqmq_amd", "csrc", "hqmq_attend.hip")
+ATTEND_SRC = [os.path.join(_CSRC, f) for f in ("hqmq_attend.hip", "hqmq_device.h")]
 
 
 def log(*a):
@@ -119,8 +122,15 @@ def measure_ceilings(src, dst, stream: int, ev) -> dict:
     return out
 
 
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    return source_hash(KERNEL_SRC)
 
 
 def _counters(path: str, hash_key: str, src: str):
@@ -129,7 +139,7 @@ def _counters(path: str, hash_key: str, src: str):
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get(hash_key) != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
+    if t.get(hash_key) != source_hash(src):
         return None
     return t
 
@@ -247,8 +257,9 @@ def _kernel_key(name: str) -> str:
 def summarize_counters(run_dir: str, workload: int):
     """Counter summary of one workload from the per-pass outputs of
     `bench.py --summarize-pmc` (files pA.jsonl: instruction counts, pB.jsonl:
-    busy metrics, pF.jsonl / pW.jsonl: FETCH_SIZE / WRITE_SIZE, pFc.jsonl /
-    pWc.jsonl: the same two counters on --copy-calibration) in run_dir.
+    busy metrics, pC.jsonl / pD.jsonl: optional SQ cycle counters, pF.jsonl /
+    pW.jsonl: FETCH_SIZE / WRITE_SIZE, pFc.jsonl / pWc.jsonl: the same two
+    counters on --copy-calibration) in run_dir.
     Prints the JSON kept under profiles/: per kernel the counters' average,
     minimum and maximum over its dispatches (the minimum and maximum of the
     codec kernels are its V and K launches), instructions per chunk, and
@@ -267,6 +278,7 @@ def summarize_counters(run_dir: str, workload: int):
         return out
 
     inst, busy, fetch, write = load("pA"), load("pB"), load("pF"), load("pW")
+    cycles, more = load("pC"), load("pD")   # optional SQ cycle-counter passes
     cal_f = load("pFc").get("__amd_rocclr_copyBuffer", {}).get("FETCH_SIZE")
     cal_w = load("pWc").get("__amd_rocclr_copyBuffer", {}).get("WRITE_SIZE")
     moved_kib = 4 * 1024 * 1024          # the calibration copies 4 GiB each way
@@ -279,7 +291,7 @@ def summarize_counters(run_dir: str, workload: int):
             continue
         k = _kernel_key(name)
         e = kernels.setdefault(k, {"kernel": name})
-        for src in (inst.get(name, {}), busy.get(name, {})):
+        for src in (inst.get(name, {}), busy.get(name, {}), cycles.get(name, {}), more.get(name, {})):
             for c, r in src.items():
                 e[c] = {"avg": r["avg"], "min": r["min"], "max": r["max"], "dispatches": r["dispatches"]}
         if name in fetch and fscale:
@@ -291,13 +303,19 @@ def summarize_counters(run_dir: str, workload: int):
             e["valu_insts_per_wave_step_64_chunks"] = 64 * e["SQ_INSTS_VALU"]["avg"] / chunks
             e["mfma_insts_per_chunk"] = e["SQ_INSTS_MFMA"]["avg"] / chunks
             e["salu_insts_per_chunk"] = e["SQ_INSTS_SALU"]["avg"] / chunks
+        if "SQ_ACTIVE_INST_VALU" in e and "SQ_ACTIVE_INST_VALU2" in e:
+            # VALU issue: at most two instructions per quad-cycle per SIMD
+            # (dual issue); quad-cycles with any = single + dual
+            v, v2 = e["SQ_ACTIVE_INST_VALU"]["avg"], e["SQ_ACTIVE_INST_VALU2"]["avg"]
+            e["valu_dual_issue_fraction"] = 2 * v2 / v if v else None
+            e["valu_issue_quad_cycles"] = v - v2
         if "VALUBusy" in e:
             e["valu_busy"] = e["VALUBusy"]["avg"] / 100.0
             e["source"] = "VALUBusy = 100 sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE) (rocprofv3's definition)"
     print(json.dumps({"workload": synth.describe(w), "chunks_per_role": chunks,
                       "fetch_scale": fscale, "write_scale": wscale,
                       "kernel_sha256_16": kernel_hash(),
-                      "attend_sha256_16": hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()[:16],
+                      "attend_sha256_16": source_hash(ATTEND_SRC),
                       "kernels": kernels}, indent=1))
 
 
