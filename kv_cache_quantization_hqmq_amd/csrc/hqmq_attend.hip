@@ -497,59 +497,63 @@ void attend_split_kernel(AttArgs a) {
     // exact-rate records: the lane's CPL full codes of one plane from its
     // low-bit window (words 0 .. NWL-1, chunk c0's bits first) and digit
     // window (words NWL, NWL+1): code = 2^m d + l
+    // (its body is compiled for exact-rate instantiations only: the others
+    // hold no digit window)
     auto extract_exact = [&](const Words &tw, uint32_t dsh, uint32_t (&out)[CPL]) {
         using TR = TileRegs<D, BITS, NF>;
-        constexpr int NWL = TR::NWL;
-        const uint32_t sh = static_cast<uint32_t>(c0 * em) & 31u;
-        const uint32_t lmask = (1u << em) - 1u;
-        if constexpr (BITS > 0) {
-            // the window from the lane's first bit, then fields at fixed places
-            uint32_t nw[NWL];
+        if constexpr (TR::EXACT) {
+            constexpr int NWL = TR::NWL;
+            const uint32_t sh = static_cast<uint32_t>(c0 * em) & 31u;
+            const uint32_t lmask = (1u << em) - 1u;
+            if constexpr (BITS > 0) {
+                // the window from the lane's first bit, then fields at fixed places
+                uint32_t nw[NWL];
 #pragma unroll
-            for (int k = 0; k + 1 < NWL; ++k) nw[k] = __builtin_amdgcn_alignbit(tw[k + 1], tw[k], sh);
-            nw[NWL - 1] = tw[NWL - 1] >> sh;
+                for (int k = 0; k + 1 < NWL; ++k) nw[k] = __builtin_amdgcn_alignbit(tw[k + 1], tw[k], sh);
+                nw[NWL - 1] = tw[NWL - 1] >> sh;
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const int p = j * BITS, k = p >> 5, sft = p & 31;
-                if (sft + BITS <= 32) out[j] = (nw[k] >> sft) & lmask;
-                else out[j] = __builtin_amdgcn_alignbit(nw[k + 1], nw[k], sft) & lmask;
-            }
-        } else {
-            // any m: each field's two words picked from the window
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const uint32_t p = sh + static_cast<uint32_t>(j * em);
-                const uint32_t k = p >> 5;
-                uint32_t wlo = tw[0], whi = NWL > 1 ? tw[1] : 0u;
-#pragma unroll
-                for (int q = 1; q < NWL; ++q) {
-                    wlo = k == static_cast<uint32_t>(q) ? tw[q] : wlo;
-                    whi = k + 1 == static_cast<uint32_t>(q) ? tw[q] : whi;
+                for (int j = 0; j < CPL; ++j) {
+                    const int p = j * BITS, k = p >> 5, sft = p & 31;
+                    if (sft + BITS <= 32) out[j] = (nw[k] >> sft) & lmask;
+                    else out[j] = __builtin_amdgcn_alignbit(nw[k + 1], nw[k], sft) & lmask;
                 }
-                out[j] = __builtin_amdgcn_alignbit(whi, wlo, p & 31u) & lmask;
+            } else {
+                // any m: each field's two words picked from the window
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    const uint32_t p = sh + static_cast<uint32_t>(j * em);
+                    const uint32_t k = p >> 5;
+                    uint32_t wlo = tw[0], whi = NWL > 1 ? tw[1] : 0u;
+#pragma unroll
+                    for (int q = 1; q < NWL; ++q) {
+                        wlo = k == static_cast<uint32_t>(q) ? tw[q] : wlo;
+                        whi = k + 1 == static_cast<uint32_t>(q) ? tw[q] : whi;
+                    }
+                    out[j] = __builtin_amdgcn_alignbit(whi, wlo, p & 31u) & lmask;
+                }
             }
-        }
-        // digit fields: CPL / 8 whole fields (CPL >= 8), or half of one
-        uint32_t v = __builtin_amdgcn_alignbit(tw[NWL + 1], tw[NWL], dsh);
-        if constexpr (CPL >= kDigitsPerField) {
+            // digit fields: CPL / 8 whole fields (CPL >= 8), or half of one
+            uint32_t v = __builtin_amdgcn_alignbit(tw[NWL + 1], tw[NWL], dsh);
+            if constexpr (CPL >= kDigitsPerField) {
 #pragma unroll
-            for (int f = 0; f < CPL / kDigitsPerField; ++f) {
-                uint32_t q = (v >> (kFieldBits * f)) & 0x1FFFu;
+                for (int f = 0; f < CPL / kDigitsPerField; ++f) {
+                    uint32_t q = (v >> (kFieldBits * f)) & 0x1FFFu;
 #pragma unroll
-                for (int i = 0; i < kDigitsPerField; ++i) {
+                    for (int i = 0; i < kDigitsPerField; ++i) {
+                        const uint32_t q3 = div3_small(q);
+                        out[f * kDigitsPerField + i] |= (q - 3u * q3) << em;
+                        q = q3;
+                    }
+                }
+            } else {
+                uint32_t q = v & 0x1FFFu;
+                if (c0 & 4) q = __umul24(q, 207127u) >> 24;   // skip digits 0..3: q / 81
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
                     const uint32_t q3 = div3_small(q);
-                    out[f * kDigitsPerField + i] |= (q - 3u * q3) << em;
+                    out[i] |= (q - 3u * q3) << em;
                     q = q3;
                 }
-            }
-        } else {
-            uint32_t q = v & 0x1FFFu;
-            if (c0 & 4) q = __umul24(q, 207127u) >> 24;   // skip digits 0..3: q / 81
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const uint32_t q3 = div3_small(q);
-                out[i] |= (q - 3u * q3) << em;
-                q = q3;
             }
         }
     };

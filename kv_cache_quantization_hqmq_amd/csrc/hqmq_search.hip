@@ -14,7 +14,10 @@
 // the fp32 transform of the exact codebook value.  Lane l supplies A row
 // l % 32, k block l / 32, and B column l % 32 (the raw 8-byte chunk, the same
 // for both k blocks); D VGPR 4 a + r of lane l is row 8 a + 4 (l / 32) + r,
-// column l % 32: t_r of s = 8 tile + 2 a + l / 32 for chunk l % 32.
+// column l % 32.  Row 8 a + 4 h + r of tile t holds m = r of
+// s = h H + 4 t + a, H = 4 x (tiles): lanes 0..31 score the first H secondary
+// codewords and lanes 32..63 the rest, so every candidate of the upper lanes
+// has the larger index.
 //
 // The scoring epilogue is VALU work, the kernel's bound.  This file is built
 // with IEEE mode off and fp32 denormals flushed so that the halving in
@@ -50,6 +53,14 @@ __device__ __forceinline__ float sqrt_half(float a) {
     return r;
 }
 
+// l - |t| as one v_sub_f32 with the abs source modifier (kept from being
+// folded back into a compare of |t|, which would need |t| in a register).
+__device__ __forceinline__ float abs_gap(float l, float t) {
+    float r;
+    asm("v_sub_f32_e64 %0, %1, |%2|" : "=v"(r) : "v"(l), "v"(t));
+    return r;
+}
+
 // Score of the best 2T element for one s from t = (<x, e_m q_s>)_m:
 // max(|t|_inf, |t|_1 / 2) (a unit +-e_m scores +-t_m, a half-unit
 // (s0..s3)/2 scores sum s_m t_m / 2, largest with s_m = sign t_m).
@@ -72,17 +83,19 @@ __device__ __forceinline__ uint32_t primary_index(const float *qs, float x0, flo
     const float t2 = __builtin_fmaf(-q1, x3, __builtin_fmaf(q0, x2, __builtin_fmaf(q3, x1, __builtin_fmaf(-q2, x0, 0.0f))));
     const float t3 = __builtin_fmaf(q0, x3, __builtin_fmaf(q1, x2, __builtin_fmaf(-q2, x1, __builtin_fmaf(-q3, x0, 0.0f))));
     const float e0 = fabsf(t0), e1 = fabsf(t1), e2 = fabsf(t2), e3 = fabsf(t3);
-    // first argmax of |t_m| as a pairwise tournament
-    const float m01 = fmaxf(e0, e1), m23 = fmaxf(e2, e3);
-    const float linf = fmaxf(m01, m23);
-    const uint32_t a01 = e0 >= e1 ? 0u : 1u;
-    const uint32_t a23 = e2 >= e3 ? 2u : 3u;
-    const uint32_t m = m01 >= m23 ? a01 : a23;
-    // top bytes of the four values side by side, then their sign bits moved
-    // to bits 28..31 by one multiply (no two partial products overlap)
-    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x0c0c0703u);
-    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t3), __float_as_uint(t2), 0x07030c0cu);
-    const uint32_t nib = (((lo | hi) & 0x80808080u) * 0x00204081u) >> 28;
+    // first argmax of |t_m|: the first m reaching the largest, from
+    // linf - |t_m| (zero exactly when equal: every t_m is a multiple of
+    // 2^-48, so a nonzero difference is far above the denormal range)
+    const float linf = fmaxf(fmaxf(e0, e1), fmaxf(e2, e3));
+    uint32_t m = abs_gap(linf, t2) == 0.0f ? 2u : 3u;
+    m = abs_gap(linf, t1) == 0.0f ? 1u : m;
+    m = abs_gap(linf, t0) == 0.0f ? 0u : m;
+    // sign bits: v_perm selectors 9 and 11 give 0xFF or 0x00 from the sign of
+    // the low and the high source word, one byte per value; masking byte m
+    // to 2^m and summing the bytes (v_sad_u8 against zero) gives the nibble
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x0c0c0b09u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t3), __float_as_uint(t2), 0x0b090c0cu);
+    const uint32_t nib = __builtin_amdgcn_sad_u8((lo | hi) & 0x08040201u, 0u, 0u);
     const uint32_t unit = 2u * m + __builtin_amdgcn_ubfe(nib, m, 1u);
     return linf >= half_sum(e0 + e1, e2 + e3) ? unit : 8u + nib;
 }
@@ -114,14 +127,18 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
     // offsets below are scalar work
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(thread_id() >> 6));
     const int col = lane & 31;
-    const int hh = lane >> 5;            // K block: 0 = hi parts, 1 = lo parts
+    // A: K block (0 = hi parts, 1 = lo parts); D: row half (0 = the first H
+    // secondary codewords, 1 = the rest)
+    const int hh = lane >> 5;
     const int m_row = col & 3;
-    const int s_loc = col >> 2;
+    const int half_q = 4 * NT;               // H
+    // the A row's s relative to 4 t
+    const int s_row = ((col >> 2) & 1) * half_q + (col >> 3);
 
-    // A operand of tile t: row (s = 8 t + s_loc, m = m_row), k = 0..3 of the
+    // A operand of tile t: row (s = s_row + 4 t, m = m_row), k = 0..3 of the
     // hi (hh = 0) or lo (hh = 1) part of (e_m q_s)[k] = sign(m, k) q_s[m ^ k]
     auto a_operand = [&](int t) {
-        const float *qs = &sq[4 * (8 * t + s_loc)];
+        const float *qs = &sq[4 * (s_row + 4 * t)];
         f16x4 r;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -193,13 +210,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
         for (int b = 0; b < 2; ++b) {
             const f16x4 bv = __builtin_bit_cast(f16x4, xr[b]);
             // Running best over the MFMA tiles t: the best of a tile's four
-            // scores (s = 8 t + 2 g + hh, g = 0..3) replaces the running one
+            // scores (s = hh H + 4 t + g, g = 0..3) replaces the running one
             // when strictly larger, with the tile and its first three scores;
             // which g it was is resolved once at the end (first g reaching
             // it), so the result is the sequential strict argmax in s order.
             // The first tile sets the running best unconditionally.
             float best = 0.0f;
-            uint32_t bt8 = 0;   // 8 t of the running best's tile
+            uint32_t bt4 = 0;   // 4 t of the running best's tile
             float bs0 = 0.0f, bs1 = 0.0f, bs2 = 0.0f;
             auto tile = [&](int t, const f32x16 &d) {
                 float sc[4];
@@ -208,7 +225,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
                 const float m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
                 if (t == 0 || m > best) {
                     best = m;
-                    bt8 = 8u * t;
+                    bt4 = 4u * t;
                     bs0 = sc[0];
                     bs1 = sc[1];
                     bs2 = sc[2];
@@ -223,25 +240,29 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
                     tile(t, __builtin_amdgcn_mfma_f32_32x32x8f16(a_operand(t), bv, zero, 0, 0, 0));
             }
             // first g reaching the best, as selects
-            uint32_t g2 = bs2 == best ? 4u : 6u;   // 2 g
-            g2 = bs1 == best ? 2u : g2;
-            g2 = bs0 == best ? 0u : g2;
+            uint32_t g = bs2 == best ? 2u : 3u;
+            g = bs1 == best ? 1u : g;
+            g = bs0 == best ? 0u : g;
             bsc[b] = best;
-            bsi[b] = bt8 + g2 + hh;
+            // (disjoint bit fields when H is a power of two: one v_or3)
+            constexpr bool kPow2 = NT8 > 0 && (NT8 & (NT8 - 1)) == 0;
+            const uint32_t hoff = static_cast<uint32_t>(hh * half_q);
+            bsi[b] = kPow2 ? (bt4 | g | hoff) : bt4 + g + hoff;
         }
 
-        // lane l < 32 holds parity 0 of chunks l and l + 32, lane l + 32
-        // parity 1 of the same chunks; swapping the upper half of block 0 with
-        // the lower half of block 1 leaves every lane l with both parities of
-        // chunk o0 + l (v_permlane32_swap)
+        // lane l < 32 holds the first half's best of chunks l and l + 32, lane
+        // l + 32 the second half's of the same chunks; swapping the upper half
+        // of block 0 with the lower half of block 1 leaves every lane l with
+        // both halves' of chunk o0 + l (v_permlane32_swap)
         uint32_t s_best;
         {
             const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(bsc[0]), __float_as_uint(bsc[1]), false, false);
             const auto pi = __builtin_amdgcn_permlane32_swap(bsi[0], bsi[1], false, false);
             const float s0 = __uint_as_float(ps[0]), s1 = __uint_as_float(ps[1]);
             const uint32_t i0 = pi[0], i1 = pi[1];
-            const bool take1 = (s1 > s0) | ((s1 == s0) & (i1 < i0));
-            // 8 bt + 2 g + hh < 8 NT <= kMaxS: inside the codebook copy sq
+            // i1 > i0 always: the first half wins ties
+            const bool take1 = s1 > s0;
+            // 4 bt + g + hh H < 8 NT <= kMaxS: inside the codebook copy sq
             s_best = take1 ? i1 : i0;
             __builtin_assume(s_best < static_cast<uint32_t>(kMaxS));
         }

@@ -230,6 +230,29 @@ def test_med3_other_multipliers_random(C):
         assert rep["outliers"] > 0
 
 
+@pytest.mark.parametrize("S", [8, 13, 32, 40])
+def test_repeated_codewords_take_the_first(S):
+    """Codebooks whose entries repeat, as copies or negated copies (q and -q
+    give the same 24 scores, 2T holding -1), before and after their source:
+    every chunk whose best codeword repeats has exact score ties across s,
+    among them ties between the two halves of the codebook that the fp16
+    search scores in different lanes.  The smallest s wins, as in the
+    oracle; zero chunks take s = 0."""
+    L, H, T, D = 1, 2, 600, 64
+    x = _x((L, H, T, D), torch.float16, seed=90 + S)
+    x[:, :, ::37, :] = 0
+    base, _ = _cb(L, H, S, seed=9)
+    cb_host = base.copy()
+    rng = np.random.default_rng(S)
+    for s in range(S):
+        if rng.random() < 0.6:
+            src = base[:, :, rng.integers(0, S), :]
+            cb_host[:, :, s, :] = -src if rng.random() < 0.3 else src
+    assert len({tuple(v) for v in cb_host[0, 0]}) < S
+    desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F16, 0, 3.0)
+    _check(desc, x, cb_host, torch.from_numpy(cb_host).cuda())
+
+
 def test_off_grid_codebook_encodes_like_its_rounded_copy():
     """The kernels use every codebook value on the double-binary16 grid
     (hi + lo binary16 parts): a codebook off the grid gives bit-identical
