@@ -1353,14 +1353,27 @@ __device__ __forceinline__ void digit_pair(uint32_t v, uint32_t sel, uint32_t *d
 
 // (5 waves per SIMD where the registers allow it: the decode is bound by
 // memory latency and bandwidth, so it wants many waves in flight)
-template <bool F32OUT, bool TABLE, int NF>
+//
+// EM > 0 (exact-rate records, head_dim 128, m = EM in {6, 8}): a wave step
+// of 128 chunks is one whole group of 4 token rows (8 EM + 13 words), so the
+// wave loads the group with one or two coalesced loads per lane (lane l
+// holds words l and 64 + l) and every lane takes the words its two chunks
+// need from the others by ds_bpermute, in place of eight loads of its own.
+template <bool F32OUT, bool TABLE, int NF, int EM = 0>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(NF == 1 ? 4 : 5)))
 void decode_kernel(DecArgs a) {
     constexpr bool NPACK = NF == kNormPacked;
     constexpr bool EXACT = NF == kNormExact;
+    constexpr bool GROUPED = EXACT && EM > 0;
+    static_assert(!GROUPED || EM == 6 || EM == 8, "grouped exact-rate decode: m = 6 or 8");
+    // words per group: 4 rows x 2 planes x EM words of low bits, 32 digit
+    // fields of 13 bits; EM = 8: low bits in words 0..63, digits 64..76;
+    // EM = 6: everything in words 0..60
+    constexpr int kGW = 8 * EM + (4 * 2 * 4 * kFieldBits + 31) / 32;
     // steps whose loads a thread issues together (an exact-rate step holds
-    // twice the record words, so half as many keep the register count)
-    constexpr int kUnroll = EXACT ? kDecUnroll / 2 : kDecUnroll;
+    // twice the record words, so half as many keep the register count;
+    // grouped steps hold at most two words)
+    constexpr int kUnroll = EXACT && !GROUPED ? kDecUnroll / 2 : kDecUnroll;
     extern __shared__ f32x4 tab[];   // TABLE: the 24 S codewords; else the S q_s
     const int64_t slice = blockIdx.x / a.wg_per_slice;
     const int64_t r0 = (blockIdx.x - slice * a.wg_per_slice) * a.wg_chunks;
@@ -1493,6 +1506,70 @@ void decode_kernel(DecArgs a) {
         return d;
     };
     constexpr int kWaveStep = 128;   // chunks per wave step
+    // grouped exact-rate records: the group of wave step base (a multiple of
+    // 128, as every wave's range starts on a group), words l and 64 + l
+    auto load_group = [&](int64_t sbase_) {
+        uint2 g = make_uint2(0u, 0u);
+        if (sbase_ < w1) {   // wave-uniform
+            const uint32_t *gp = idx_s + (sbase_ >> 7) * kGW;
+            if (lane < kGW) g.x = gp[lane];
+            if (64 + lane < kGW) g.y = gp[64 + lane];
+        }
+        return g;
+    };
+    // the lane's DecPair from the wave's group words (every lane runs it:
+    // the permutes read all lanes); row r = lane / 16, chunks 2 (lane % 16)
+    // and the next
+    auto from_group = [&](uint2 g) {
+        const int r = lane >> 4, q = lane & 15;
+        auto perm = [](uint32_t v, int src) {
+            return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(v)));
+        };
+        DecPair d;
+        const int ob = 2 * q * EM, w = r * EM + (ob >> 5);
+        d.w0 = perm(g.x, w);
+        d.n0 = perm(g.x, 4 * EM + w);
+        if constexpr (EM == 8) {
+            d.w1 = d.n1 = 0u;   // 16 bits at bit 0 or 16 of one word
+        } else {
+            d.w1 = perm(g.x, w + 1);   // (w + 1 stays inside the row when used)
+            d.n1 = perm(g.x, 4 * EM + w + 1);
+        }
+        d.sh = static_cast<uint32_t>(ob & 31);
+        const int fk = kFieldBits * (8 * r + (q >> 2));
+        const int fn = fk + kFieldBits * 4;
+        const uint32_t dg = EM == 8 ? g.y : g.x;
+        constexpr int kDig = EM == 8 ? 0 : 8 * EM;   // first digit word's lane in dg
+        d.dk0 = perm(dg, kDig + (fk >> 5));
+        d.dk1 = perm(dg, kDig + (fk >> 5) + 1);
+        d.dn0 = perm(dg, kDig + (fn >> 5));
+        d.dn1 = perm(dg, kDig + (fn >> 5) + 1);
+        d.dsh = static_cast<uint32_t>(fk & 31) | (static_cast<uint32_t>(fn & 31) << 8) |
+                (static_cast<uint32_t>(q & 3) << 16);
+        d.h = 0u;
+        return d;
+    };
+    // exact-rate records: full codes 2^m d + l of the two chunks as indices
+    // in w0 / w1 (read below with a zero shift), the norm codes as half-norm
+    // records
+    const int em = GROUPED ? EM : a.m;
+    auto finish_exact = [&](DecPair &p) {
+        const uint32_t lmask = (1u << em) - 1u;
+        const uint32_t flag = (3u << em) - 1u;
+        const uint32_t sel = (p.dsh >> 16) & 3u;
+        const uint32_t vk = static_cast<uint32_t>(((static_cast<uint64_t>(p.dk1) << 32) | p.dk0) >> (p.dsh & 31u)) & 0x1FFFu;
+        const uint32_t vn = static_cast<uint32_t>(((static_cast<uint64_t>(p.dn1) << 32) | p.dn0) >> ((p.dsh >> 8) & 31u)) & 0x1FFFu;
+        uint32_t ka, kb, na, nb;
+        digit_pair(vk, sel, &ka, &kb);
+        digit_pair(vn, sel, &na, &nb);
+        const uint32_t lk = static_cast<uint32_t>(((static_cast<uint64_t>(p.w1) << 32) | p.w0) >> p.sh);
+        const uint32_t ln = static_cast<uint32_t>(((static_cast<uint64_t>(p.n1) << 32) | p.n0) >> p.sh);
+        p.w0 = (ka << em) | (lk & lmask);
+        p.w1 = (kb << em) | ((lk >> em) & lmask);
+        p.sh = 0u;
+        const uint32_t n0 = (na << em) | (ln & lmask), n1 = (nb << em) | ((ln >> em) & lmask);
+        p.h = exact_norm_h16(n0, flag, a.step) | (exact_norm_h16(n1, flag, a.step) << 16);
+    };
     // the loop runs on a wave-uniform base, so that every lane takes part in
     // the exchange below (lanes past the range's end load and store nothing)
     for (int64_t base = w0; base < w1; base += static_cast<int64_t>(kWaveStep) * kUnroll) {
@@ -1507,52 +1584,11 @@ void decode_kernel(DecArgs a) {
             const uint64_t e = wbase + static_cast<uint64_t>(lane);
             wv = sval[e < e_end ? e : e_end - 1];
         }
-        DecPair pd[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
-            pd[u] = c < w1 ? load(c) : DecPair{};
-        }
-        if constexpr (NPACK) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const uint64_t nwin = ((static_cast<uint64_t>(pd[u].n1) << 32) | pd[u].n0) >> pd[u].sh;
-                const uint32_t k0 = static_cast<uint32_t>(nwin) & kmask;
-                const uint32_t k1 = static_cast<uint32_t>(nwin >> a.bits) & kmask;
-                pd[u].h = compact_norm_h16(k0, a.bits) | (compact_norm_h16(k1, a.bits) << 16);
-            }
-        }
-        if constexpr (EXACT) {
-            // full codes 2^m d + l of the two chunks: indices into w0 / w1
-            // (read below with a zero shift), norm codes to half-norm records
-            const uint32_t lmask = (1u << a.m) - 1u;
-            const uint32_t flag = (3u << a.m) - 1u;
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                DecPair &p = pd[u];
-                const uint32_t sel = (p.dsh >> 16) & 3u;
-                const uint32_t vk = static_cast<uint32_t>(((static_cast<uint64_t>(p.dk1) << 32) | p.dk0) >> (p.dsh & 31u)) & 0x1FFFu;
-                const uint32_t vn = static_cast<uint32_t>(((static_cast<uint64_t>(p.dn1) << 32) | p.dn0) >> ((p.dsh >> 8) & 31u)) & 0x1FFFu;
-                uint32_t ka, kb, na, nb;
-                digit_pair(vk, sel, &ka, &kb);
-                digit_pair(vn, sel, &na, &nb);
-                const uint32_t lk = static_cast<uint32_t>(((static_cast<uint64_t>(p.w1) << 32) | p.w0) >> p.sh);
-                const uint32_t ln = static_cast<uint32_t>(((static_cast<uint64_t>(p.n1) << 32) | p.n0) >> p.sh);
-                p.w0 = (ka << a.m) | (lk & lmask);
-                p.w1 = (kb << a.m) | ((lk >> a.m) & lmask);
-                p.sh = 0u;
-                const uint32_t n0 = (na << a.m) | (ln & lmask), n1 = (nb << a.m) | ((ln >> a.m) & lmask);
-                p.h = exact_norm_h16(n0, flag, a.step) | (exact_norm_h16(n1, flag, a.step) << 16);
-            }
-        }
-        // side-list values of this iteration's flagged chunks, in order (a
-        // chunk whose entry was dropped, past the capacity, keeps its bulk value)
-        uint2 ov[kUnroll][2];
-        bool oh[kUnroll][2];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const bool f0 = (pd[u].h & 0x8000u) != 0;
-            const bool f1 = (pd[u].h & 0x80000000u) != 0;
+        // side-list values of one step's flagged chunks, in order (a chunk
+        // whose entry was dropped, past the capacity, keeps its bulk value)
+        auto rank = [&](const DecPair &p, uint2 (&ov)[2], bool (&oh)[2]) {
+            const bool f0 = (p.h & 0x8000u) != 0;
+            const bool f1 = (p.h & 0x80000000u) != 0;
             const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
             const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m0 >> 32),
                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m0), 0u)) +
@@ -1560,10 +1596,10 @@ void decode_kernel(DecArgs a) {
                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m1), 0u));
             const uint64_t e0 = e_next + below;
             const uint64_t e1 = e0 + (f0 ? 1 : 0);
-            oh[u][0] = f0 && e0 < e_end;
-            oh[u][1] = f1 && e1 < e_end;
-            ov[u][0] = make_uint2(0u, 0u);
-            ov[u][1] = make_uint2(0u, 0u);
+            oh[0] = f0 && e0 < e_end;
+            oh[1] = f1 && e1 < e_end;
+            ov[0] = make_uint2(0u, 0u);
+            ov[1] = make_uint2(0u, 0u);
             if ((m0 | m1) != 0u) {   // wave-uniform: every lane takes part in the exchange
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
@@ -1573,19 +1609,16 @@ void decode_kernel(DecArgs a) {
                                                static_cast<uint32_t>(__shfl(static_cast<int>(wv.y), src)));
                     // entries past the window (more than 64 flags in one
                     // iteration) are loaded on their own
-                    const bool far = oh[u][i] && q >= 64u;
+                    const bool far = oh[i] && q >= 64u;
                     uint2 fv = make_uint2(0u, 0u);
                     if (far) fv = sval[i ? e1 : e0];
-                    if (oh[u][i]) ov[u][i] = far ? fv : v;
+                    if (oh[i]) ov[i] = far ? fv : v;
                 }
             }
             e_next += static_cast<uint64_t>(__popcll(m0) + __popcll(m1));
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
-            if (c >= w1) break;
-            const DecPair &cur = pd[u];
+        };
+        // the two decoded chunks c, c + 1 of a step, one 16-byte store
+        auto emit = [&](int64_t c, const DecPair &cur, const uint2 (&ov)[2], const bool (&oh)[2]) {
             const uint64_t win = ((static_cast<uint64_t>(cur.w1) << 32) | cur.w0) >> cur.sh;
             f32x4 out[2];
 #pragma unroll
@@ -1604,8 +1637,8 @@ void decode_kernel(DecArgs a) {
                     cw = codeword_f32(qa, static_cast<int>(k) - 24 * s);
                 }
                 out[i] = r * cw;
-                if (oh[u][i]) {
-                    const uint2 v = ov[u][i];
+                if (oh[i]) {
+                    const uint2 v = ov[i];
                     const f32x4 f = {f16_bits_to_f32(static_cast<uint16_t>(v.x)), f16_bits_to_f32(static_cast<uint16_t>(v.x >> 16)),
                                      f16_bits_to_f32(static_cast<uint16_t>(v.y)), f16_bits_to_f32(static_cast<uint16_t>(v.y >> 16))};
                     out[i] = f;
@@ -1627,6 +1660,54 @@ void decode_kernel(DecArgs a) {
                 }
                 __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.y) + 4 * gc));
             }
+        };
+        if constexpr (GROUPED) {
+            // the group loads of every step first, then each step whole: its
+            // pair from the group words, codes, ranking and store
+            uint2 gw[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) gw[u] = load_group(base + static_cast<int64_t>(u) * kWaveStep);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
+                DecPair p = from_group(gw[u]);
+                if (c >= w1) p = DecPair{};
+                finish_exact(p);
+                uint2 ov[2];
+                bool oh[2];
+                rank(p, ov, oh);
+                if (c < w1) emit(c, p, ov, oh);
+            }
+            continue;
+        }
+        DecPair pd[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
+            pd[u] = c < w1 ? load(c) : DecPair{};
+        }
+        if constexpr (NPACK) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const uint64_t nwin = ((static_cast<uint64_t>(pd[u].n1) << 32) | pd[u].n0) >> pd[u].sh;
+                const uint32_t k0 = static_cast<uint32_t>(nwin) & kmask;
+                const uint32_t k1 = static_cast<uint32_t>(nwin >> a.bits) & kmask;
+                pd[u].h = compact_norm_h16(k0, a.bits) | (compact_norm_h16(k1, a.bits) << 16);
+            }
+        }
+        if constexpr (EXACT) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) finish_exact(pd[u]);
+        }
+        uint2 ov[kUnroll][2];
+        bool oh[kUnroll][2];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) rank(pd[u], ov[u], oh[u]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
+            if (c >= w1) break;
+            emit(c, pd[u], ov[u], oh[u]);
         }
     }
 }
@@ -2072,9 +2153,16 @@ hipError_t launch_decode(const Geometry &g, const uint32_t *idx, const void *hno
     const size_t lds = (table ? 24 * static_cast<size_t>(g.S) : static_cast<size_t>(g.S)) * sizeof(f32x4);
     const int nf = g.exact ? kNormExact : (g.npack ? kNormPacked : kNormF16);
     const void *k = nullptr;
+    // exact-rate records of head_dim 128 at m = 6 or 8 (S = 8, 32): whole
+    // groups per wave step
+    const bool grouped = g.exact && g.cpt == 32 && (g.em == 6 || g.em == 8) && g.ewl == g.em && g.efh == 4 &&
+                         g.egw == 8 * g.em + 13;
     auto pick = [&](auto f32out) {
         constexpr bool F = decltype(f32out)::value;
-        if (nf == kNormExact)
+        if (nf == kNormExact && grouped && table)
+            k = g.em == 8 ? reinterpret_cast<const void *>(&decode_kernel<F, true, kNormExact, 8>)
+                          : reinterpret_cast<const void *>(&decode_kernel<F, true, kNormExact, 6>);
+        else if (nf == kNormExact)
             k = table ? reinterpret_cast<const void *>(&decode_kernel<F, true, kNormExact>)
                       : reinterpret_cast<const void *>(&decode_kernel<F, false, kNormExact>);
         else if (nf == kNormPacked)
