@@ -131,15 +131,19 @@ __device__ __forceinline__ uint32_t exact_norm_h16(uint32_t n, uint32_t flag_cod
 // record; otherwise the level with the nearest value (a tie to the even
 // level), at most nmax (the top finite level).  h lies between the patterns
 // of levels floor(3 h / 2^(15 - m)) and the next, so those two are compared
-// (differences of nearby binary16 values are exact in fp32).
+// (differences of nearby binary16 values are exact in fp32).  The flag and
+// the cap are applied last by selects (the comparison then runs on a
+// clamped level, whose result they discard).
 __device__ __forceinline__ uint32_t exact_norm_code(uint32_t h, int m, uint32_t nmax, float level_step) {
-    if (h & 0x8000u) return (3u << m) - 1u;
-    const uint32_t n0 = (3u * h) >> (15 - m);
-    if (n0 >= nmax) return nmax;
-    const float v = f16_bits_to_f32(static_cast<uint16_t>(h));
+    const uint32_t hv = h & 0x7FFFu;
+    const uint32_t nr = (3u * hv) >> (15 - m);
+    const uint32_t n0 = nr < nmax ? nr : nmax;
+    const float v = f16_bits_to_f32(static_cast<uint16_t>(hv));
     const float d0 = v - f16_bits_to_f32(static_cast<uint16_t>(exact_level_pattern(n0, level_step)));
     const float d1 = f16_bits_to_f32(static_cast<uint16_t>(exact_level_pattern(n0 + 1u, level_step))) - v;
-    return d0 < d1 ? n0 : (d1 < d0 ? n0 + 1u : n0 + (n0 & 1u));
+    uint32_t n = d0 < d1 ? n0 : (d1 < d0 ? n0 + 1u : n0 + (n0 & 1u));
+    n = nr >= nmax ? nmax : n;
+    return (h & 0x8000u) ? (3u << m) - 1u : n;
 }
 
 // floor(q / 3) for q < 2^13 with a full-rate 24-bit multiply:

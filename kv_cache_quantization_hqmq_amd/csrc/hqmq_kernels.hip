@@ -1188,90 +1188,103 @@ __global__ __launch_bounds__(kPackExThreads) void pack_exact_kernel(PackExArgs a
 }
 
 // Exact-rate packing specialised for 32 chunks per row (head_dim 128) and a
-// fixed m (S = 8: m = 6, S = 32: m = 8): one thread per (group, plane, row)
-// stream of 32 codes, all in registers.  Threads 0-127 take the index streams
-// of the block's 32 groups (loading their whole-bit code rows), threads
-// 128-255 the norm streams (loading their binary16 half-norm rows), so no
-// wave runs both.  Each writes its row's m low-bit words straight to the
-// record and its 4 digit field values to LDS; the 13 digit words per group
-// are then gathered from the fields.
+// fixed m (S = 8: m = 6, S = 32: m = 8).  A block packs 32 groups (128 token
+// rows) whose records are contiguous.  Its work items are (plane, row, digit
+// field): 8 codes each, whole-bit index codes (m + 2 bits) or binary16
+// half-norms turned into norm codes.  Consecutive threads take consecutive
+// items, so the loads are contiguous, and every thread takes two items of
+// each plane.  An item puts its 8 m-bit low parts into the group's low-bit
+// words and its digit field value (digit i weighing 3^i) into LDS; the 13
+// digit words per group are assembled there and the block's records are
+// written out word by word (coalesced stores).
 template <int M>
 __global__ __launch_bounds__(kPackExThreads) void pack_exact32_kernel(PackExArgs a) {
     constexpr int CPT = 32, B = M + 2, WL = M, FH = 4, NFG = 8 * FH, LW = 8 * WL;
     constexpr int GW = LW + (kExactRows * 2 * FH * kFieldBits + 31) / 32;
-    constexpr int GPB = kPackExThreads / 8;   // groups per block
+    constexpr int GPB = 32;                       // groups per block
+    constexpr int ROWS = GPB * kExactRows;        // token rows per block
+    constexpr int ITEMS = 2 * ROWS * FH;          // (plane, row, field)
+    static_assert(ITEMS % kPackExThreads == 0, "whole items per thread");
     __shared__ uint32_t fields[GPB * NFG];
+    __shared__ uint32_t stage[GPB * GW];
     const int64_t slice = blockIdx.x / a.blocks_per_slice;
     const int64_t g0 = (blockIdx.x - slice * a.blocks_per_slice) * GPB;
-    const int pl = threadIdx.x >> 7;
-    const int gi = (threadIdx.x & 127) >> 2, r = threadIdx.x & 3;
-    const int64_t g = g0 + gi;
-    const int64_t t = g * kExactRows + r;
-    const bool live = g < a.gps;
-    uint32_t code[CPT];
-    if (t < a.tokens) {
-        const int64_t rowi = slice * a.tokens + t;
-        if (pl == 0) {
-            uint32_t w[B];
-            const uint2 *src = reinterpret_cast<const uint2 *>(a.idx + rowi * B);
+    const int64_t t0 = g0 * kExactRows;   // the block's first token row
+    // low-bit words are ORed together from the items (with m = 6 an item's
+    // 48 bits share words with its neighbours')
+    for (int i = threadIdx.x; i < GPB * LW; i += kPackExThreads) stage[(i / LW) * GW + i % LW] = 0u;
+    __syncthreads();
 #pragma unroll
-            for (int k = 0; k < B / 2; ++k) {
-                const uint2 v = src[k];
-                w[2 * k] = v.x;
-                w[2 * k + 1] = v.y;
-            }
+    for (int j = 0; j < ITEMS / kPackExThreads; ++j) {
+        const int item = threadIdx.x + j * kPackExThreads;
+        const int pl = item / (ROWS * FH);
+        const int rb = (item % (ROWS * FH)) / FH, f = item % FH;   // row in the block, field
+        const int gi = rb / kExactRows, r = rb % kExactRows;
+        const int64_t t = t0 + rb;
+        uint32_t code[kDigitsPerField];
+        if (t < a.tokens) {
+            const int64_t rowi = slice * a.tokens + t;
+            if (pl == 0) {
+                constexpr int NWI = (8 * B + 31) / 32 + 1;
+                const int b0 = 8 * f * B, w0 = b0 >> 5, sh = b0 & 31;
+                const uint32_t *src = a.idx + rowi * B + w0;
+                uint32_t w[NWI];
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                constexpr uint32_t kmask = (1u << B) - 1u;
-                const int p = c * B, k = p >> 5, sft = p & 31;
-                code[c] = (sft + B <= 32 ? w[k] >> sft : __builtin_amdgcn_alignbit(w[k + 1], w[k], sft)) & kmask;
-            }
-        } else {
-            const uint4 *src = reinterpret_cast<const uint4 *>(a.h16 + rowi * CPT);
+                for (int k = 0; k < NWI; ++k) w[k] = w0 + k < B ? src[k] : 0u;
 #pragma unroll
-            for (int k = 0; k < CPT / 8; ++k) {
-                const uint4 v = src[k];
+                for (int c = 0; c < kDigitsPerField; ++c) {
+                    constexpr uint32_t kmask = (1u << B) - 1u;
+                    const int p = sh + c * B, k = p >> 5, sft = p & 31;
+                    code[c] = __builtin_amdgcn_alignbit(w[k + 1], w[k], sft) & kmask;
+                }
+            } else {
+                const uint4 v = reinterpret_cast<const uint4 *>(a.h16 + rowi * CPT)[f];
                 const uint32_t h[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    code[8 * k + e] = exact_norm_code((h[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, M, a.nmax, a.step);
+                for (int e = 0; e < kDigitsPerField; ++e)
+                    code[e] = exact_norm_code((h[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, M, a.nmax, a.step);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < kDigitsPerField; ++c) code[c] = 0u;
+        }
+        // low parts: 8 M bits at bit 8 f M of the (plane, row) low-bit words
+        {
+            constexpr uint32_t lmask = (1u << M) - 1u;
+            uint32_t lo0 = 0u, lo1 = 0u;   // the 8 M <= 64 bits from the item's first bit
+#pragma unroll
+            for (int c = 0; c < kDigitsPerField; ++c) {
+                const uint32_t low = code[c] & lmask;
+                const int p = c * M;
+                if (p < 32) {
+                    lo0 |= low << p;
+                    if (p + M > 32) lo1 |= low >> (32 - p);
+                } else {
+                    lo1 |= low << (p - 32);
+                }
+            }
+            uint32_t *lw = stage + gi * GW + (pl * kExactRows + r) * WL;
+            const int b0 = 8 * f * M, k = b0 >> 5, sh = b0 & 31;
+            if constexpr ((8 * M) % 32 == 0) {
+                lw[k] = lo0;            // whole words (m = 8)
+                lw[k + 1] = lo1;
+            } else {
+                atomicOr(&lw[k], lo0 << sh);
+                if (sh > 0) atomicOr(&lw[k + 1], (lo0 >> (32 - sh)) | (lo1 << sh));
+                else atomicOr(&lw[k + 1], lo1);
+                if (sh + 8 * M > 64) atomicOr(&lw[k + 2], lo1 >> (32 - sh));
             }
         }
-    } else {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) code[c] = 0u;   // rows past the slice's end
-    }
-    // low-bit words of the stream
-    uint32_t lw[WL];
-#pragma unroll
-    for (int q = 0; q < WL; ++q) lw[q] = 0u;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        constexpr uint32_t lmask = (1u << M) - 1u;
-        const int p = c * M, k = p >> 5, sft = p & 31;
-        const uint32_t low = code[c] & lmask;
-        lw[k] |= low << sft;
-        if (sft + M > 32) lw[k + 1] |= low >> (32 - sft);
-    }
-    uint32_t *dst = a.out + (slice * a.gps + g) * GW;
-    if (live) {
-        uint32_t *lp = dst + (pl * kExactRows + r) * WL;
-#pragma unroll
-        for (int q = 0; q < WL; ++q) lp[q] = lw[q];
-    }
-    // digit fields of the stream
-#pragma unroll
-    for (int f = 0; f < FH; ++f) {
+        // the digit field's value
         uint32_t val = 0u;
 #pragma unroll
-        for (int q = kDigitsPerField - 1; q >= 0; --q) val = 3u * val + (code[f * kDigitsPerField + q] >> M);
+        for (int q = kDigitsPerField - 1; q >= 0; --q) val = 3u * val + (code[q] >> M);
         fields[gi * NFG + r * 2 * FH + pl * FH + f] = val;
     }
     __syncthreads();
     constexpr int DW = GW - LW;   // digit words per group
     for (int w = threadIdx.x; w < GPB * DW; w += kPackExThreads) {
         const int gj = w / DW, ww = w - gj * DW;
-        if (g0 + gj >= a.gps) break;
         const int b0 = 32 * ww;
         const int f_hi = min(NFG - 1, (b0 + 31) / kFieldBits);
         uint32_t v = 0u;
@@ -1280,8 +1293,13 @@ __global__ __launch_bounds__(kPackExThreads) void pack_exact32_kernel(PackExArgs
             const int sft = f * kFieldBits - b0;
             v |= sft >= 0 ? (val << sft) : (val >> -sft);
         }
-        a.out[(slice * a.gps + g0 + gj) * GW + LW + ww] = v;
+        stage[gj * GW + LW + ww] = v;
     }
+    __syncthreads();
+    // the block's groups that exist, contiguous in the record
+    const int64_t ng = min(static_cast<int64_t>(GPB), a.gps - g0);
+    uint32_t *dst = a.out + (slice * a.gps + g0) * GW;
+    for (int i = threadIdx.x; i < ng * GW; i += kPackExThreads) dst[i] = stage[i];
 }
 
 // --------------------------------------------------------------------------
