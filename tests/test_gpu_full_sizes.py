@@ -30,11 +30,11 @@ def _picks(w: synth.Workload, n: int, seed: int, span: int):
     return out
 
 
-def _run_role(w: synth.Workload, role: int, n_picks: int, span: int = 2048):
-    print(f"workload {w.name} role {role}: {synth.describe(w)}", flush=True)
+def _run_role(w: synth.Workload, role: int, n_picks: int, span: int = 2048, norm_format: int = K.HQMQ_NORM_F16):
+    print(f"workload {w.name} role {role} norm format {norm_format}: {synth.describe(w)}", flush=True)
     x = synth.generate(w, role, "cuda")
     cb_host, cb = G.codebook(w, role)
-    d = G.desc_for(w)
+    d = G.desc_for(w, norm_format=norm_format)
     rec, y = G.run(d, x, cb)
     rep = G.compare(d, x, cb_host, rec, y, _picks(w, n_picks, 100 * w.wid + role, span))
     print(dict(rep), "outliers total", rec.n_outliers, flush=True)
@@ -58,6 +58,18 @@ def test_qwen_outlier_kv_32k_s32_med3(role):
 @pytest.mark.parametrize("role", [0, 1])
 def test_llama3_70b_kv_128k_s32_med3(role):
     rep = _run_role(synth.WORKLOADS[4], role, n_picks=4)
+    if role == 0:
+        assert rep["outliers"] > 0
+
+
+@pytest.mark.parametrize("role", [0, 1])
+@pytest.mark.parametrize("norm_format", [K.HQMQ_NORM_PACKED, K.HQMQ_NORM_EXACT])
+def test_llama3_70b_kv_128k_s32_med3_compact_norms(role, norm_format):
+    """The packed and the exact-rate records of the whole 128k cache (their
+    pack kernels and decoders at full size: the exact-rate decode takes one
+    group of 4 rows per wave step here), sampled whole Med3x batches against
+    the oracle."""
+    rep = _run_role(synth.WORKLOADS[4], role, n_picks=3, norm_format=norm_format)
     if role == 0:
         assert rep["outliers"] > 0
 
