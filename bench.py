@@ -762,12 +762,18 @@ def quality_report(args):
     print(json.dumps(rep), flush=True)
 
 
-def codec_bench(w, norm_format: str, xs, cbs, ev, sh, steps: int, warmup: int, ws=None, ys=None) -> dict:
+def codec_bench(w, norm_format: str, xs, cbs, ev, sh, steps: int, warmup: int, ws=None, ys=None,
+                overlap: int = 0) -> dict:
     """Time `steps` steps of the codec on workload w's resident inputs xs
     (dict role -> device tensor) in one norm format: per role hqmq_encode
     (search kernel bracketed by HIP events the library records on the launch
-    stream) then per role hqmq_decode.  Returns the figures and keeps the
-    records and decode outputs in the result ('_recs', '_ys')."""
+    stream) and hqmq_decode.  overlap = 0: every call on one stream, the
+    encodes then the decodes.  overlap = n > 0: each role's decode runs on a
+    second stream as soon as its encode is done, beside the next encode, with
+    the search capped at n blocks per CU (hqmq_set_search_blocks_per_cu) so
+    that the decode finds room; a role's encode waits for the previous decode
+    of its records.  Returns the figures and keeps the records and decode
+    outputs in the result ('_recs', '_ys')."""
     import torch
     import kv_cache_quantization_hqmq_amd as K
     desc = K.Desc.make(w.layers, w.heads, w.tokens, w.head_dim, w.S,
@@ -790,23 +796,43 @@ def codec_bench(w, norm_format: str, xs, cbs, ev, sh, steps: int, warmup: int, w
         log(f"{norm_format} norms, role {role}: {recs[role].n_outliers} outliers "
             f"({recs[role].n_outliers / sz.chunks:.4%})")
     torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if overlap else None   # default priority
+    enc_done = {r: torch.cuda.Event() for r in w.roles}
+    dec_done = {r: torch.cuda.Event() for r in w.roles}
+    K.hqmq_set_search_blocks_per_cu(overlap)
+
+    def encode(role, events):
+        e = events[("enc", role)] if events else None
+        if e:
+            ev.record(e[0], sh)
+        K.hqmq_encode_timed(desc, xs[role], cbs[role], recs[role], ws, sh,
+                            e[1] if e else None, e[2] if e else None)
+        if e:
+            ev.record(e[3], sh)
+
+    def decode(role, events, stream):
+        d = events[("dec", role)] if events else None
+        if d:
+            ev.record(d[0], stream)
+        K.hqmq_decode(desc, recs[role], cbs[role], ys[role], stream)
+        if d:
+            ev.record(d[1], stream)
 
     def step(events=None):
+        if not overlap:
+            for role in w.roles:
+                encode(role, events)
+            for role in w.roles:
+                decode(role, events, sh)
+            return
         for role in w.roles:
-            e = events[("enc", role)] if events else (None, None, None, None)
-            if events:
-                ev.record(e[0], sh)
-            K.hqmq_encode_timed(desc, xs[role], cbs[role], recs[role], ws, sh,
-                                e[1] if events else None, e[2] if events else None)
-            if events:
-                ev.record(e[3], sh)
-        for role in w.roles:
-            if events:
-                d = events[("dec", role)]
-                ev.record(d[0], sh)
-            K.hqmq_decode(desc, recs[role], cbs[role], ys[role], sh)
-            if events:
-                ev.record(d[1], sh)
+            main.wait_event(dec_done[role])     # the last decode of these records
+            encode(role, events)
+            enc_done[role].record(main)
+            side.wait_event(enc_done[role])
+            decode(role, events, side.cuda_stream)
+            dec_done[role].record(side)
 
     for _ in range(warmup):
         step()
@@ -821,6 +847,7 @@ def codec_bench(w, norm_format: str, xs, cbs, ev, sh, steps: int, warmup: int, w
         step(all_events[i])
     torch.cuda.synchronize()
     ms_step = 1000.0 * (time.perf_counter() - t0) / steps
+    K.hqmq_set_search_blocks_per_cu(0)
 
     search_ms = {r: [] for r in w.roles}
     enc_ms = {r: [] for r in w.roles}
@@ -837,6 +864,22 @@ def codec_bench(w, norm_format: str, xs, cbs, ev, sh, steps: int, warmup: int, w
                 ev.destroy(e)
     mean = lambda v: sum(v) / len(v)
     flat = lambda d: [x for r in w.roles for x in d[r]]
+    dec_in_step = dec_ms
+    if overlap:
+        # in the overlapped step a decode shares the chip with an encode; its
+        # kernel figures come from each role's decode run alone
+        dec_ms = {r: [] for r in w.roles}
+        for r in w.roles:
+            pairs = [(ev.create(), ev.create()) for _ in range(3)]
+            for a_, b_ in pairs:
+                ev.record(a_, sh)
+                K.hqmq_decode(desc, recs[r], cbs[r], ys[r], sh)
+                ev.record(b_, sh)
+            torch.cuda.synchronize()
+            dec_ms[r] = [ev.ms(a_, b_) for a_, b_ in pairs]
+            for a_, b_ in pairs:
+                ev.destroy(a_)
+                ev.destroy(b_)
 
     # every launch must still be valid after the timed steps
     n_out = {r: K.hqmq_encode_result(recs[r], sh) for r in w.roles}
@@ -853,6 +896,8 @@ def codec_bench(w, norm_format: str, xs, cbs, ev, sh, steps: int, warmup: int, w
         "encode_ms_per_role": {str(r): mean(enc_ms[r]) for r in w.roles},
         "med3_ms_per_role": {str(r): mean(enc_ms[r]) - mean(search_ms[r]) for r in w.roles},
         "decode_ms_per_role": {str(r): mean(dec_ms[r]) for r in w.roles},
+        **({"decode_in_step_ms_per_role": {str(r): mean(dec_in_step[r]) for r in w.roles},
+            "overlap_search_blocks_per_cu": overlap} if overlap else {}),
         "decode_GBps_per_role": {str(r): dec_bytes[r] / (mean(dec_ms[r]) * 1e-3) / 1e9 for r in w.roles},
         "decode_bytes_per_launch": mean([dec_bytes[r] for r in w.roles]),
         "decode_ms": mean(flat(dec_ms)),
@@ -881,6 +926,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--overlap", type=int, default=0, metavar="N",
+                    help="encode/decode workloads: run each role's decode on a second stream beside the next "
+                         "encode, the search capped at N blocks per CU (1..7; 0: one stream)")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="1..5 (see synth.WORKLOADS; 5 is the decode step)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -952,7 +1000,7 @@ def main():
         torch.cuda.synchronize()
         log(f"role {role}: input generated in {time.perf_counter() - t:.1f} s")
 
-    main_res = codec_bench(w, args.norm_format, xs, cbs, ev, sh, args.steps, args.warmup)
+    main_res = codec_bench(w, args.norm_format, xs, cbs, ev, sh, args.steps, args.warmup, overlap=args.overlap)
     sz = main_res["_sz"]
     chunks_role = sz.chunks
     total_chunks = chunks_role * len(w.roles)
@@ -1041,7 +1089,7 @@ def main():
             if fmt == args.norm_format:
                 continue
             torch.cuda.empty_cache()
-            r = codec_bench(w, fmt, xs, cbs, ev, sh, args.extra_steps, 1, ws=None, ys=ys)
+            r = codec_bench(w, fmt, xs, cbs, ev, sh, args.extra_steps, 1, ws=None, ys=ys, overlap=args.overlap)
             keep = ("ms_per_step", "search_ms", "med3_ms_per_role", "decode_ms_per_role", "decode_GBps_per_role",
                     "compression_ratio", "bits_per_element", "bulk_bits_per_element", "compressed_bytes")
             out["formats"][fmt] = {k: r[k] for k in keep}

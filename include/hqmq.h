@@ -249,6 +249,18 @@ int hqmq_encode_result(const hqmq_enc *enc, hipStream_t stream, uint64_t *n_outl
 int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, void *y,
                 hipStream_t stream);
 
+/* Scheduling, not part of the method: cap the blocks of the fp16 encode
+ * search resident on one compute unit at n (1..7; 0, the default, removes
+ * the cap).  Process-wide; it applies to the hqmq_encode, hqmq_encode_timed
+ * and hqmq_append calls issued after it, and changes no output.  For callers
+ * that run other work on a second stream during an encode (for example the
+ * decode of the role encoded before): uncapped, the search fills every CU
+ * and refills each slot a block frees, so the other stream's kernels wait
+ * for its tail; at n = 7 a CU keeps one block slot (4 waves, about 16 KB of
+ * LDS) for them.  The search blocks then reserve LDS they do not use.
+ * Errors: HQMQ_EINVAL for n outside 0..7. */
+int hqmq_set_search_blocks_per_cu(int32_t n);
+
 /* ------------------------------------------------------------------------
  * Decode-step attention read straight from the records (gist.science/nl
  * "Technische Samenvatting", "Memory en Latentie": a fused kernel decodes K

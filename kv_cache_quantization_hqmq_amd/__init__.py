@@ -11,7 +11,7 @@ from .hqmq import (AttnDesc, AttnSizes, CapacityError, Desc, HQMQError, PagedDes
                    attend_paged, decode, encode, hqmq_append, hqmq_attend, hqmq_attend_paged,
                    hqmq_attn_sizes, hqmq_decode, hqmq_paged_clear, hqmq_paged_sizes,
                    hqmq_encode, hqmq_encode_result, hqmq_encode_timed, hqmq_make_codebook, hqmq_sizes,
-                   hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_NORM_F16, HQMQ_NORM_PACKED, HQMQ_NORM_EXACT,
+                   hqmq_set_search_blocks_per_cu, hqmq_strerror, workspace, HQMQ_F16, HQMQ_F32, HQMQ_NORM_F16, HQMQ_NORM_PACKED, HQMQ_NORM_EXACT,
                    HQMQ_ROLE_K, HQMQ_ROLE_V, hqmq_ceiling_compute, hqmq_ceiling_stream, HQMQ_CEIL_READ,
                    HQMQ_CEIL_WRITE, HQMQ_CEIL_COPY, HQMQ_CEIL_FMA_F32, HQMQ_CEIL_MFMA_F32, HQMQ_CEIL_MFMA_F16)
 
@@ -20,7 +20,8 @@ __all__ = ["AttnDesc", "AttnSizes", "CapacityError", "Desc", "HQMQError", "Paged
            "append_workspace", "attend", "attend_paged", "decode", "encode", "hqmq_append", "hqmq_attend",
            "hqmq_attend_paged", "hqmq_attn_sizes", "hqmq_paged_clear", "hqmq_paged_sizes",
            "hqmq_decode", "hqmq_encode", "hqmq_encode_result", "hqmq_encode_timed",
-           "hqmq_make_codebook", "hqmq_sizes", "hqmq_strerror", "workspace", "HQMQ_F16",
+           "hqmq_make_codebook", "hqmq_sizes", "hqmq_set_search_blocks_per_cu", "hqmq_strerror", "workspace",
+           "HQMQ_F16",
            "HQMQ_F32", "HQMQ_NORM_F16", "HQMQ_NORM_PACKED", "HQMQ_NORM_EXACT", "HQMQ_ROLE_K", "HQMQ_ROLE_V",
            "hqmq_ceiling_compute", "hqmq_ceiling_stream", "HQMQ_CEIL_READ", "HQMQ_CEIL_WRITE", "HQMQ_CEIL_COPY",
            "HQMQ_CEIL_FMA_F32", "HQMQ_CEIL_MFMA_F32", "HQMQ_CEIL_MFMA_F16"]

@@ -462,6 +462,12 @@ int hqmq_decode(const hqmq_desc *d, const hqmq_enc *enc, const float *codebook, 
     return e == hipSuccess ? HQMQ_OK : HQMQ_EHIP;
 }
 
+int hqmq_set_search_blocks_per_cu(int32_t n) {
+    if (n < 0 || n > 7) return HQMQ_EINVAL;
+    hqmq::set_search_blocks_per_cu(n);
+    return HQMQ_OK;
+}
+
 int hqmq_attn_sizes(const hqmq_desc *d, const hqmq_attn_desc *a, hqmq_attn_sizes_t *out) {
     if (!out) return HQMQ_EINVAL;
     hqmq::Geometry g;

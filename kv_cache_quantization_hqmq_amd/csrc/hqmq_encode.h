@@ -38,8 +38,11 @@ struct EncArgs {
 };
 
 // fp16-input search launch (hqmq_search.hip): blocks of kEncThreads threads,
-// nt8 = ceil(S / 8) tiles of 8 secondary codewords.
-hipError_t launch_search_h(const EncArgs &a, int64_t blocks, int nt8, bool med, hipStream_t st);
+// nt8 = ceil(S / 8) tiles of 8 secondary codewords.  blocks_per_cu > 0 caps
+// the blocks resident per CU at that many (each block then reserves LDS it
+// does not use), leaving the rest of every CU to work on other streams.
+hipError_t launch_search_h(const EncArgs &a, int64_t blocks, int nt8, bool med, int blocks_per_cu,
+                           hipStream_t st);
 
 namespace {
 

@@ -25,6 +25,7 @@
 // scores differ by less than fp32 rounding (near ties).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "hqmq_device.h"
@@ -1893,6 +1894,13 @@ bool med3_single_pass(const Geometry &g) { return g.batch_chunks <= kSel1MaxChun
 // --------------------------------------------------------------------------
 // Launchers.
 // --------------------------------------------------------------------------
+namespace {
+std::atomic<int> g_search_blocks_per_cu{0};
+}  // namespace
+
+void set_search_blocks_per_cu(int n) { g_search_blocks_per_cu.store(n, std::memory_order_relaxed); }
+int search_blocks_per_cu() { return g_search_blocks_per_cu.load(std::memory_order_relaxed); }
+
 hipError_t launch_encode_search(const Geometry &g, const void *x, const float *codebook,
                                 uint32_t *idx, uint16_t *hnorm, const Med3Work *med, hipStream_t st) {
     const int64_t total = g.slices * g.n_slice;
@@ -1949,7 +1957,7 @@ hipError_t launch_encode_search(const Geometry &g, const void *x, const float *c
         else if (a.NT == 8) HQMQ_ENC_NT(8);
         else HQMQ_ENC_NT(0);
     } else {
-        return launch_search_h(a, blocks, (g.S + 7) / 8, m, st);
+        return launch_search_h(a, blocks, (g.S + 7) / 8, m, search_blocks_per_cu(), st);
     }
 #undef HQMQ_ENC_NT
 #undef HQMQ_ENC

@@ -47,9 +47,14 @@ struct Med3Work {
 
 // Encode: nearest codeword and norm code per chunk; with med != nullptr the
 // launch also accumulates each batch's code histogram (med->hist must be
-// zero).
+// zero).  The fp16 search keeps at most search_blocks_per_cu() blocks on a
+// CU when that is above 0.
 hipError_t launch_encode_search(const Geometry &g, const void *x, const float *codebook,
                                 uint32_t *idx, uint16_t *hnorm, const Med3Work *med, hipStream_t st);
+
+// The fp16 search's cap on resident blocks per CU (0: none), process-wide.
+void set_search_blocks_per_cu(int n);
+int search_blocks_per_cu();
 
 // Med3x: per batch, exact median, threshold, outlier count and bitmask (and,
 // for batches of at most 131072 chunks, the outlier flags in hnorm).  With

@@ -322,18 +322,32 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
 
 }  // namespace
 
-hipError_t launch_search_h(const EncArgs &a, int64_t blocks, int nt8, bool med, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(blocks));
-    const dim3 block(kEncThreads);
-#define HQMQ_ENC_H(NT8)                                                                            \
-    do {                                                                                           \
-        if (med) hipLaunchKernelGGL((encode_search_h_kernel<NT8, true>), grid, block, 0, st, a);  \
-        else hipLaunchKernelGGL((encode_search_h_kernel<NT8, false>), grid, block, 0, st, a);     \
-    } while (0)
+hipError_t launch_search_h(const EncArgs &a, int64_t blocks, int nt8, bool med, int blocks_per_cu,
+                           hipStream_t st) {
+    const void *k = nullptr;
+#define HQMQ_ENC_H(NT8)                                                                         \
+    k = med ? reinterpret_cast<const void *>(&encode_search_h_kernel<NT8, true>)                 \
+            : reinterpret_cast<const void *>(&encode_search_h_kernel<NT8, false>)
     if (nt8 == 1) HQMQ_ENC_H(1);
     else if (nt8 == 4) HQMQ_ENC_H(4);
     else HQMQ_ENC_H(0);
 #undef HQMQ_ENC_H
+    // an occupancy cap: the block's LDS (static + reserved) is sized so that
+    // blocks_per_cu fit in a CU's 160 KB and one more does not (allocation in
+    // 512-byte granules)
+    size_t lds = 0;
+    if (blocks_per_cu > 0) {
+        hipFuncAttributes fa;
+        const hipError_t e = hipFuncGetAttributes(&fa, k);
+        if (e != hipSuccess) return e;
+        constexpr size_t kLdsPerCu = 160 * 1024;
+        const size_t per_block = (kLdsPerCu / static_cast<size_t>(blocks_per_cu + 1) + 1 + 511) / 512 * 512;
+        lds = per_block > fa.sharedSizeBytes ? per_block - fa.sharedSizeBytes : 0;
+    }
+    EncArgs args = a;
+    void *argv[] = {&args};
+    const hipError_t e = hipLaunchKernel(k, dim3(static_cast<unsigned>(blocks)), dim3(kEncThreads), argv, lds, st);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ HQMQ_NORM_F16, HQMQ_NORM_PACKED, HQMQ_NORM_EXACT = 0, 1, 2
 EXPORTS = ("hqmq_strerror", "hqmq_sizes", "hqmq_make_codebook", "hqmq_encode",
            "hqmq_encode_timed", "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes",
            "hqmq_attend", "hqmq_attend_noalloc", "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append",
-           "hqmq_attend_paged",
+           "hqmq_attend_paged", "hqmq_set_search_blocks_per_cu",
            "hqmq_ceiling_stream", "hqmq_ceiling_compute")
 
 # include/hqmq_ceiling.h
@@ -175,6 +175,7 @@ def lib():
                                         ctypes.POINTER(Pages), ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.hqmq_set_search_blocks_per_cu.argtypes = [ctypes.c_int32]
         L.hqmq_ceiling_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p]
         L.hqmq_ceiling_compute.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -182,7 +183,7 @@ def lib():
         for f in ("hqmq_sizes", "hqmq_make_codebook", "hqmq_encode", "hqmq_encode_timed",
                   "hqmq_encode_result", "hqmq_decode", "hqmq_attn_sizes", "hqmq_attend", "hqmq_attend_noalloc",
                   "hqmq_paged_sizes", "hqmq_paged_clear", "hqmq_append", "hqmq_attend_paged",
-                  "hqmq_ceiling_stream", "hqmq_ceiling_compute"):
+                  "hqmq_set_search_blocks_per_cu", "hqmq_ceiling_stream", "hqmq_ceiling_compute"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -207,6 +208,11 @@ def _stream(stream) -> int:
 # ------------------------------------------------------------------ C calls
 def hqmq_strerror(code: int) -> str:
     return lib().hqmq_strerror(int(code)).decode()
+
+
+def hqmq_set_search_blocks_per_cu(n: int) -> None:
+    """Cap the fp16 encode search's resident blocks per compute unit (0: no cap)."""
+    _check(lib().hqmq_set_search_blocks_per_cu(int(n)), "hqmq_set_search_blocks_per_cu")
 
 
 def hqmq_ceiling_stream(kind: int, src, dst, nbytes: int, stream=None) -> None:

@@ -36,6 +36,21 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_search_blocks_per_cu_accepts_0_to_7_only():
+    """The scheduling setter takes 0 (no cap) to 7 and rejects anything else
+    with HQMQ_EINVAL, leaving the setting as it was (host only, no GPU)."""
+    lib = B.lib()
+    try:
+        for n in range(8):
+            assert lib.hqmq_set_search_blocks_per_cu(n) == B.HQMQ_OK
+        for n in (-1, 8, 64, -(2 ** 31)):
+            assert lib.hqmq_set_search_blocks_per_cu(n) == B.HQMQ_EINVAL
+        with pytest.raises(K.HQMQError):
+            K.hqmq_set_search_blocks_per_cu(9)
+    finally:
+        K.hqmq_set_search_blocks_per_cu(0)
+
+
 def test_struct_layouts_match_header(tmp_path):
     """Field offsets and sizes of the ctypes structs equal what a C compiler
     makes of include/hqmq.h."""

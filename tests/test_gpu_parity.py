@@ -253,6 +253,35 @@ def test_repeated_codewords_take_the_first(S):
     _check(desc, x, cb_host, torch.from_numpy(cb_host).cuda())
 
 
+@pytest.mark.parametrize("S", [32, 13])
+def test_search_occupancy_cap_changes_no_output(S):
+    """hqmq_set_search_blocks_per_cu only limits how many search blocks share
+    a CU (the blocks reserve LDS they do not use): records, side list and
+    decoded values are bit-identical at every cap."""
+    L, H, T, D = 2, 2, 1500, 128
+    x = _x((L, H, T, D), torch.float16, seed=31 + S)
+    x[:, :, :, 7] *= 30
+    cb_host, cb = _cb(L, H, S)
+    desc = K.Desc.make(L, H, T, D, S, K.HQMQ_F16, 512, 3.0)
+
+    def run():
+        rec, y = G.run(desc, x, cb)
+        torch.cuda.synchronize()
+        n = rec.n_outliers
+        return [t.cpu() for t in (rec.idx, rec.hnorm, rec.out_pos[:n], rec.out_val[:n], y)]
+
+    ref = run()
+    try:
+        for cap in (7, 3, 1):
+            K.hqmq_set_search_blocks_per_cu(cap)
+            got = run()
+            for a, b in zip(ref, got):
+                assert torch.equal(a, b), cap
+    finally:
+        K.hqmq_set_search_blocks_per_cu(0)
+    G.compare(desc, x, cb_host, *G.run(desc, x, cb))
+
+
 def test_off_grid_codebook_encodes_like_its_rounded_copy():
     """The kernels use every codebook value on the double-binary16 grid
     (hi + lo binary16 parts): a codebook off the grid gives bit-identical
