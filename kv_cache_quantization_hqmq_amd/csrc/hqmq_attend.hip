@@ -724,8 +724,15 @@ void attend_split_kernel(AttArgs a) {
             s[i] = 4 * g + i < nvalid ? s[i] * a.qscale : -INFINITY;
             tmax = fmaxf(tmax, s[i]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        // the max over the four lane groups: v_permlane16_swap pairs rows
+        // 0-1 and 2-3 of 16 lanes, v_permlane32_swap the two halves of the
+        // wave (VALU exchanges instead of two LDS-routed permutes)
+        {
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+        }
         if (__ballot(tmax > m_run + kLazy)) {
             const float m_new = tmax > m_run + kLazy ? tmax : m_run;
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 where unchanged, 0 from -inf
