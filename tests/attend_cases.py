@@ -151,12 +151,13 @@ def make_queries(batch: int, hq: int, D: int, seed: int, device="cuda"):
 
 
 def run_case(w: synth.Workload, seqs, group: int, scale: float, layers=None, max_len=None, seed=0,
-             norm_format: int = K.HQMQ_NORM_F16):
+             norm_format: int = K.HQMQ_NORM_F16, xform=None):
     """Encode w's K and V on the GPU, attend over seqs = [(start, len)], and
     compare every (layer, sequence, query head) with the oracle.  Returns a
     report with the worst error / tolerance ratio, the near-tie codes the two
     encoders chose differently (allowed) and every other record difference
-    (must be 0)."""
+    (must be 0).  xform(role, x), if given, changes the generated input of a
+    role in place before both sides encode it."""
     desc = GC.desc_for(w, norm_format=norm_format)
     npack = norm_format == K.HQMQ_NORM_PACKED
     exact = norm_format == K.HQMQ_NORM_EXACT
@@ -164,6 +165,8 @@ def run_case(w: synth.Workload, seqs, group: int, scale: float, layers=None, max
     xs, cbh, cbd, recs = {}, {}, {}, {}
     for role in (0, 1):
         xs[role] = synth.generate(w, role, "cuda")
+        if xform is not None:
+            xform(role, xs[role])
         cbh[role], cbd[role] = GC.codebook(w, role)
         recs[role] = K.encode(desc, xs[role], cbd[role])
     nb = len(seqs)

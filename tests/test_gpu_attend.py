@@ -40,6 +40,19 @@ def test_attend_sharp_scores():
     _check(A.run_case(BASE, SEQS, 4, 8.0 / math.sqrt(128), seed=7), "sharp")
 
 
+def test_attend_tiles_with_more_than_64_outliers():
+    """Whole token rows 40 times the rest, so that every chunk of them is a
+    Med3x outlier: K rows 100-110 and V rows 2000-2039 put up to 512 side-list
+    entries in a 16-token tile, which the kernel reads in several 64-entry
+    windows."""
+    def boost(role, x):
+        if role == 0:
+            x[:, :, 100:111] *= 40
+        else:
+            x[:, :, 2000:2040] *= 40
+    _check(A.run_case(BASE, SEQS, 4, 1.0 / math.sqrt(128), xform=boost), "dense outlier rows")
+
+
 def test_attend_d64_s8_without_med3():
     w = synth.WORKLOADS[2].scaled(layers=1, heads=2, tokens=3000, data_seed=2302)
     _check(A.run_case(w, [(0, 3000), (17, 1500), (2990, 10)], 4, 0.125), "D=64")

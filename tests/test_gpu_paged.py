@@ -48,6 +48,20 @@ def test_append_drops_entries_past_page_capacity():
     assert sum(st[0][1] + st[1][1] for st in rp.statuses) > 0, "no entry was dropped"
 
 
+def test_attend_paged_over_pages_cut_at_capacity():
+    """Attention over pools whose page lists were cut at a capacity of 3
+    entries: the kept entries are read, the dropped chunks take their records'
+    bulk values (as the model decodes them), for one and four query heads per
+    KV head."""
+    rp = PC.replay(PC.Scenario(page_capacity=3, seed=1, outlier_channels=2))
+    _records_ok(rp, "capacity 3")
+    assert sum(st[0][1] + st[1][1] for st in rp.statuses) > 0, "no entry was dropped"
+    for group in (4, 1):
+        ratio = PC.attend_case(rp, group, 1.0 / math.sqrt(128))
+        print("attend paged, capacity 3", group, ratio, flush=True)
+        assert ratio <= 1.0
+
+
 def test_append_packed_norms_and_med3_batches_inside_a_call():
     sc = PC.Scenario(norm_format=K.HQMQ_NORM_PACKED, med_batch_tokens=48, seed=2)
     _records_ok(PC.replay(sc), "packed, B=48")
