@@ -1605,6 +1605,11 @@ void decode_kernel(DecArgs a) {
             const uint64_t e = wbase + static_cast<uint64_t>(lane);
             wv = sval[e < e_end ? e : e_end - 1];
         }
+        // entries are counted from wbase in 32 bits: wlim entries are left in
+        // the list (saturated), wused have gone to earlier steps
+        const uint64_t left = e_end - wbase;   // e_end >= wbase
+        const uint32_t wlim = left > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(left);
+        uint32_t wused = 0u;
         // side-list values of one step's flagged chunks, in order (a chunk
         // whose entry was dropped, past the capacity, keeps its bulk value)
         auto rank = [&](const DecPair &p, uint2 (&ov)[2], bool (&oh)[2]) {
@@ -1615,16 +1620,14 @@ void decode_kernel(DecArgs a) {
                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m0), 0u)) +
                                    __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m1 >> 32),
                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m1), 0u));
-            const uint64_t e0 = e_next + below;
-            const uint64_t e1 = e0 + (f0 ? 1 : 0);
-            oh[0] = f0 && e0 < e_end;
-            oh[1] = f1 && e1 < e_end;
-            ov[0] = make_uint2(0u, 0u);
-            ov[1] = make_uint2(0u, 0u);
+            const uint32_t q0 = wused + below;            // window lanes of the entries
+            const uint32_t q1 = q0 + (f0 ? 1u : 0u);
+            oh[0] = f0 && q0 < wlim;
+            oh[1] = f1 && q1 < wlim;
             if ((m0 | m1) != 0u) {   // wave-uniform: every lane takes part in the exchange
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const uint64_t q = (i ? e1 : e0) - wbase;   // window lane of the entry
+                    const uint32_t q = i ? q1 : q0;
                     const int src = q < 64u ? static_cast<int>(q) : 0;
                     const uint2 v = make_uint2(static_cast<uint32_t>(__shfl(static_cast<int>(wv.x), src)),
                                                static_cast<uint32_t>(__shfl(static_cast<int>(wv.y), src)));
@@ -1632,16 +1635,19 @@ void decode_kernel(DecArgs a) {
                     // iteration) are loaded on their own
                     const bool far = oh[i] && q >= 64u;
                     uint2 fv = make_uint2(0u, 0u);
-                    if (far) fv = sval[i ? e1 : e0];
-                    if (oh[i]) ov[i] = far ? fv : v;
+                    if (far) fv = sval[wbase + q];
+                    ov[i] = far ? fv : v;
                 }
             }
-            e_next += static_cast<uint64_t>(__popcll(m0) + __popcll(m1));
+            wused += static_cast<uint32_t>(__popcll(m0) + __popcll(m1));
         };
         // the two decoded chunks c, c + 1 of a step, one 16-byte store
+        // (binary16 output: the bulk values rounded in pairs, an outlier's
+        // side value taken as its binary16 words)
         auto emit = [&](int64_t c, const DecPair &cur, const uint2 (&ov)[2], const bool (&oh)[2]) {
             const uint64_t win = ((static_cast<uint64_t>(cur.w1) << 32) | cur.w0) >> cur.sh;
             f32x4 out[2];
+            u32x4 o;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 uint32_t k = EXACT ? (i ? cur.w1 : cur.w0) : static_cast<uint32_t>(win >> (i * a.bits)) & kmask;
@@ -1658,28 +1664,31 @@ void decode_kernel(DecArgs a) {
                     cw = codeword_f32(qa, static_cast<int>(k) - 24 * s);
                 }
                 out[i] = r * cw;
-                if (oh[i]) {
-                    const uint2 v = ov[i];
-                    const f32x4 f = {f16_bits_to_f32(static_cast<uint16_t>(v.x)), f16_bits_to_f32(static_cast<uint16_t>(v.x >> 16)),
-                                     f16_bits_to_f32(static_cast<uint16_t>(v.y)), f16_bits_to_f32(static_cast<uint16_t>(v.y >> 16))};
-                    out[i] = f;
+                if constexpr (F32OUT) {
+                    if (oh[i]) {
+                        const uint2 v = ov[i];
+                        const f32x4 f = {f16_bits_to_f32(static_cast<uint16_t>(v.x)), f16_bits_to_f32(static_cast<uint16_t>(v.x >> 16)),
+                                         f16_bits_to_f32(static_cast<uint16_t>(v.y)), f16_bits_to_f32(static_cast<uint16_t>(v.y >> 16))};
+                        out[i] = f;
+                    }
+                } else {
+                    const f16x4 hy = {static_cast<_Float16>(out[i][0]), static_cast<_Float16>(out[i][1]),
+                                      static_cast<_Float16>(out[i][2]), static_cast<_Float16>(out[i][3])};
+                    uint2 w = __builtin_bit_cast(uint2, hy);
+                    if (oh[i]) w = ov[i];
+                    o[2 * i] = w.x;
+                    o[2 * i + 1] = w.y;
                 }
             }
-            const int64_t gc = sbase + c;
+            // the iteration's wave-uniform output base plus a 32-bit lane offset
+            const uint32_t rel = static_cast<uint32_t>(c - base);
             if constexpr (F32OUT) {
-                f32x4 *yp = reinterpret_cast<f32x4 *>(a.y) + gc;
+                f32x4 *yp = reinterpret_cast<f32x4 *>(a.y) + (sbase + base) + rel;
                 __builtin_nontemporal_store(out[0], yp);
                 __builtin_nontemporal_store(out[1], yp + 1);
             } else {
-                u32x4 o;
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    o[2 * i] = static_cast<uint32_t>(f32_to_f16_bits(out[i][0])) |
-                               (static_cast<uint32_t>(f32_to_f16_bits(out[i][1])) << 16);
-                    o[2 * i + 1] = static_cast<uint32_t>(f32_to_f16_bits(out[i][2])) |
-                                   (static_cast<uint32_t>(f32_to_f16_bits(out[i][3])) << 16);
-                }
-                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.y) + 4 * gc));
+                uint16_t *yw = static_cast<uint16_t *>(a.y) + 4 * (sbase + base);
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(yw + 4 * rel));
             }
         };
         if constexpr (GROUPED) {
@@ -1699,13 +1708,20 @@ void decode_kernel(DecArgs a) {
                 rank(p, ov, oh);
                 if (c < w1) emit(c, p, ov, oh);
             }
+            e_next = wbase + wused;
             continue;
         }
+        // binary16 and packed norms: every step's loads are issued
+        // unconditionally (lanes past the range's end read its last pair, w1
+        // being even), so that the compiler waits for each step's loads
+        // alone, not for all of them (exact-rate records: conditional loads,
+        // which keep the register count)
         DecPair pd[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
-            pd[u] = c < w1 ? load(c) : DecPair{};
+            if constexpr (EXACT) pd[u] = c < w1 ? load(c) : DecPair{};
+            else pd[u] = load(c < w1 ? c : w1 - 2);
         }
         if constexpr (NPACK) {
 #pragma unroll
@@ -1720,10 +1736,15 @@ void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) finish_exact(pd[u]);
         }
+        // chunks past the range carry no flags
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (c0 + static_cast<int64_t>(u) * kWaveStep >= w1) pd[u].h = 0u;
         uint2 ov[kUnroll][2];
         bool oh[kUnroll][2];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) rank(pd[u], ov[u], oh[u]);
+        e_next = wbase + wused;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t c = c0 + static_cast<int64_t>(u) * kWaveStep;
