@@ -1528,15 +1528,13 @@ void decode_kernel(DecArgs a) {
     };
     constexpr int kWaveStep = 128;   // chunks per wave step
     // grouped exact-rate records: the group of wave step base (a multiple of
-    // 128, as every wave's range starts on a group), words l and 64 + l
+    // 128, as every wave's range starts and ends on a group), words l and
+    // 64 + l.  The loads are unconditional (steps past the range read its
+    // last group, lanes past the group's words its last word; the permutes
+    // read neither), so that each step waits for its own loads only.
     auto load_group = [&](int64_t sbase_) {
-        uint2 g = make_uint2(0u, 0u);
-        if (sbase_ < w1) {   // wave-uniform
-            const uint32_t *gp = idx_s + (sbase_ >> 7) * kGW;
-            if (lane < kGW) g.x = gp[lane];
-            if (64 + lane < kGW) g.y = gp[64 + lane];
-        }
-        return g;
+        const uint32_t *gp = idx_s + ((sbase_ < w1 ? sbase_ : w1 - kWaveStep) >> 7) * kGW;
+        return make_uint2(gp[lane < kGW ? lane : kGW - 1], gp[64 + lane < kGW ? 64 + lane : kGW - 1]);
     };
     // the lane's DecPair from the wave's group words (every lane runs it:
     // the permutes read all lanes); row r = lane / 16, chunks 2 (lane % 16)
@@ -1632,11 +1630,19 @@ void decode_kernel(DecArgs a) {
                     const uint2 v = make_uint2(static_cast<uint32_t>(__shfl(static_cast<int>(wv.x), src)),
                                                static_cast<uint32_t>(__shfl(static_cast<int>(wv.y), src)));
                     // entries past the window (more than 64 flags in one
-                    // iteration) are loaded on their own
+                    // iteration) are loaded on their own; the empty asm
+                    // takes the wait for that load inside this rare branch,
+                    // so that the common path does not wait for every load
+                    // in flight
                     const bool far = oh[i] && q >= 64u;
-                    uint2 fv = make_uint2(0u, 0u);
-                    if (far) fv = sval[wbase + q];
-                    ov[i] = far ? fv : v;
+                    uint32_t vx = v.x, vy = v.y;
+                    if (far) {
+                        const uint2 t = sval[wbase + q];
+                        vx = t.x;
+                        vy = t.y;
+                        asm volatile("" : "+v"(vx), "+v"(vy));
+                    }
+                    ov[i] = make_uint2(vx, vy);
                 }
             }
             wused += static_cast<uint32_t>(__popcll(m0) + __popcll(m1));
