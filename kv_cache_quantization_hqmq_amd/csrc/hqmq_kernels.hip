@@ -642,16 +642,25 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
         const uint32_t wshift = 4u * static_cast<uint32_t>(lane & 7);
         constexpr int U = 8;
         for (int i0 = threadIdx.x; i0 - lane < n4; i0 += kSelThreads * U) {
+            // loads issued unconditionally (lanes past the batch read its
+            // last word and then hold zeros); the empty asm consumes each
+            // word where it is first used, so that the loads stay
+            // unconditional and each u waits for its own load only
             uint2 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int q = i0 + kSelThreads * u;
-                v[u] = q < n4 ? c4[q] : make_uint2(0u, 0u);
+                v[u] = c4[q < n4 ? q : n4 - 1];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int q = i0 + kSelThreads * u;
                 const bool valid = q < n4;
+                {
+                    uint32_t vx = v[u].x, vy = v[u].y;
+                    asm volatile("" : "+v"(vx), "+v"(vy));
+                    v[u] = valid ? make_uint2(vx, vy) : make_uint2(0u, 0u);
+                }
                 const u16x2 wx = __builtin_bit_cast(u16x2, v[u].x);
                 const u16x2 wy = __builtin_bit_cast(u16x2, v[u].y);
                 // bit 15 of each halfword set iff its code exceeds hhi
