@@ -847,32 +847,45 @@ __global__ __launch_bounds__(kSelThreads) void med3_select1_kernel(SelArgs a) {
     if (threadIdx.x == 0) a.counts[bid] = tot + *nout;
 
     // packed norm format: the batch's codes are final now (flags included),
-    // so pack them into the record's norm words here, 2048 chunks (whole
-    // token rows) per round with the words ORed together in LDS
+    // so pack them into the record's norm words here, in rounds of up to
+    // 3 x 2048 chunks (whole token rows; as many as the LDS word buffer
+    // holds, at least two: 2048 chunks take at most 2048 * 15 / 32 + 512
+    // words) with the words ORed together in LDS; a thread's loads of a round
+    // are issued together, before the round's first barrier
     if (a.pwords != nullptr) {
         __syncthreads();   // every decision has been written to codes[]
-        uint32_t *sw = cand;   // rows * words <= 2048 * 15 / 32 + 32 <= kCand1Cap
+        uint32_t *sw = cand;
         const int cpt = 1 << a.log2_cpt;
         const int W = a.words;
         uint32_t *out = a.pwords + (slice * a.tokens + (lo >> a.log2_cpt)) * W;
-        constexpr int kRound = 4 * kSelThreads;
-        for (int r0 = 0; r0 < n; r0 += kRound) {
-            const int rows = min(kRound, n - r0) >> a.log2_cpt;
+        constexpr int kSub = 4 * kSelThreads;   // chunks per sub-round, one load per thread
+        const int nsub = min(3, kCand1Cap / ((kSub >> a.log2_cpt) * W));
+        const int round = nsub * kSub;
+        for (int r0 = 0; r0 < n; r0 += round) {
+            const int rows = min(round, n - r0) >> a.log2_cpt;
             for (int i = threadIdx.x; i < rows * W; i += kSelThreads) sw[i] = 0u;
-            __syncthreads();
-            const int c = r0 + 4 * static_cast<int>(threadIdx.x);
-            if (c < n) {   // n and c are multiples of 4
-                const uint2 u = *reinterpret_cast<const uint2 *>(codes + c);
-                const uint32_t h[4] = {u.x & 0xFFFFu, u.x >> 16, u.y & 0xFFFFu, u.y >> 16};
+            uint2 u[3];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int lc = 4 * static_cast<int>(threadIdx.x) + j;
-                    const uint32_t code = compact_norm_code(h[j], a.bits);
-                    const int bit = (lc & (cpt - 1)) * a.bits;
-                    uint32_t *wr = &sw[(lc >> a.log2_cpt) * W + (bit >> 5)];
-                    const int sft = bit & 31;
-                    atomicOr(wr, code << sft);
-                    if (sft + a.bits > 32) atomicOr(wr + 1, code >> (32 - sft));
+            for (int j = 0; j < 3; ++j) {
+                const int c = r0 + kSub * j + 4 * static_cast<int>(threadIdx.x);
+                u[j] = j < nsub && c < n ? *reinterpret_cast<const uint2 *>(codes + c) : make_uint2(0u, 0u);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int c = r0 + kSub * j + 4 * static_cast<int>(threadIdx.x);
+                if (j < nsub && c < n) {   // n and c are multiples of 4
+                    const uint32_t h[4] = {u[j].x & 0xFFFFu, u[j].x >> 16, u[j].y & 0xFFFFu, u[j].y >> 16};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int lc = c - r0 + e;
+                        const uint32_t code = compact_norm_code(h[e], a.bits);
+                        const int bit = (lc & (cpt - 1)) * a.bits;
+                        uint32_t *wr = &sw[(lc >> a.log2_cpt) * W + (bit >> 5)];
+                        const int sft = bit & 31;
+                        atomicOr(wr, code << sft);
+                        if (sft + a.bits > 32) atomicOr(wr + 1, code >> (32 - sft));
+                    }
                 }
             }
             __syncthreads();
@@ -1599,7 +1612,8 @@ void decode_kernel(DecArgs a) {
         p.h = exact_norm_h16(n0, flag, a.step) | (exact_norm_h16(n1, flag, a.step) << 16);
     };
     // the loop runs on a wave-uniform base, so that every lane takes part in
-    // the exchange below (lanes past the range's end load and store nothing)
+    // the exchange below (lanes past the range's end carry no flags and store
+    // nothing)
     for (int64_t base = w0; base < w1; base += static_cast<int64_t>(kWaveStep) * kUnroll) {
         const int64_t c0 = base + 2 * lane;
         // the next 64 side-list entries (lane j: entry e_next + j), requested
