@@ -61,6 +61,17 @@ __device__ __forceinline__ float abs_gap(float l, float t) {
     return r;
 }
 
+// Index of the first zero among gaps g0, g1, g2 (3 when none is zero), for
+// gaps that are +0 or at least 2^-48: as bit patterns they order like their
+// values, so the keys g0, g1 | 1 and med3(g2, 2, 3) are 0, 1 and 2 for a zero
+// gap and above 3 otherwise, and their minimum is the index (one bitwise op,
+// v_med3_u32 and v_min3_u32 instead of three compares and three selects).
+__device__ __forceinline__ uint32_t first_zero_gap(float g0, float g1, float g2) {
+    uint32_t k2;
+    asm("v_med3_u32 %0, %1, 2, 3" : "=v"(k2) : "v"(__float_as_uint(g2)));
+    return min(min(__float_as_uint(g0), __float_as_uint(g1) | 1u), k2);
+}
+
 // Score of the best 2T element for one s from t = (<x, e_m q_s>)_m:
 // max(|t|_inf, |t|_1 / 2) (a unit +-e_m scores +-t_m, a half-unit
 // (s0..s3)/2 scores sum s_m t_m / 2, largest with s_m = sign t_m).
@@ -83,13 +94,11 @@ __device__ __forceinline__ uint32_t primary_index(const float *qs, float x0, flo
     const float t2 = __builtin_fmaf(-q1, x3, __builtin_fmaf(q0, x2, __builtin_fmaf(q3, x1, __builtin_fmaf(-q2, x0, 0.0f))));
     const float t3 = __builtin_fmaf(q0, x3, __builtin_fmaf(q1, x2, __builtin_fmaf(-q2, x1, __builtin_fmaf(-q3, x0, 0.0f))));
     const float e0 = fabsf(t0), e1 = fabsf(t1), e2 = fabsf(t2), e3 = fabsf(t3);
-    // first argmax of |t_m|: the first m reaching the largest, from
+    // first argmax of |t_m|: the first m reaching the largest, from the gaps
     // linf - |t_m| (zero exactly when equal: every t_m is a multiple of
     // 2^-48, so a nonzero difference is far above the denormal range)
     const float linf = fmaxf(fmaxf(e0, e1), fmaxf(e2, e3));
-    uint32_t m = abs_gap(linf, t2) == 0.0f ? 2u : 3u;
-    m = abs_gap(linf, t1) == 0.0f ? 1u : m;
-    m = abs_gap(linf, t0) == 0.0f ? 0u : m;
+    const uint32_t m = first_zero_gap(abs_gap(linf, t0), abs_gap(linf, t1), abs_gap(linf, t2));
     // sign bits: v_perm selectors 9 and 11 give 0xFF or 0x00 from the sign of
     // the low and the high source word, one byte per value; masking byte m
     // to 2^m and summing the bytes (v_sad_u8 against zero) gives the nibble
@@ -239,10 +248,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_search_h_kernel(EncArgs a)
                 for (int t = 1; t < NT; ++t)
                     tile(t, __builtin_amdgcn_mfma_f32_32x32x8f16(a_operand(t), bv, zero, 0, 0, 0));
             }
-            // first g reaching the best, as selects
-            uint32_t g = bs2 == best ? 2u : 3u;
-            g = bs1 == best ? 1u : g;
-            g = bs0 == best ? 0u : g;
+            // first g reaching the best: the gaps best - bs_g are >= 0, zero
+            // only when equal (multiples of 2^-48), and g = 3 when none is
+            const uint32_t g = first_zero_gap(best - bs0, best - bs1, best - bs2);
             bsc[b] = best;
             // (disjoint bit fields when H is a power of two: one v_or3)
             constexpr bool kPow2 = NT8 > 0 && (NT8 & (NT8 - 1)) == 0;
