@@ -347,3 +347,31 @@ def test_paged_calls_reject_before_enqueueing():
                                  ctypes.c_void_p(256), 1 << 20, None) == B.HQMQ_EINVAL
     assert lib.hqmq_paged_clear(ctypes.byref(d), ctypes.byref(p), ctypes.byref(pool), None, 3,
                                 None) == B.HQMQ_EINVAL
+
+
+def _first_zero_keys(g0, g1, g2):
+    """The search kernel's first-index choice on fp32 gaps (bit patterns):
+    min3(g0, g1 | 1, med3(g2, 2, 3))."""
+    b = [np.asarray(g, dtype=np.float32).view(np.uint32).astype(np.int64) for g in (g0, g1, g2)]
+    k2 = np.clip(b[2], 2, 3)   # med3(x, 2, 3) = clamp to [2, 3]
+    return np.minimum(np.minimum(b[0], b[1] | 1), k2)
+
+
+def test_first_zero_gap_keys_give_the_first_zero_index():
+    # Gaps max - value are +0 or multiples of 2^-48 of at least 2^-48 (scores
+    # and transform components are multiples of 2^-48); as bit patterns the
+    # keys are 0, 1, 2 for a zero gap and above 3 otherwise, so their minimum
+    # is the index of the first zero gap, 3 when there is none.  Every zero /
+    # nonzero pattern, with nonzero gaps from 2^-48 up to 2^40.
+    rng = np.random.default_rng(7)
+    n = 4096
+    for pat in range(8):
+        gaps = []
+        for i in range(3):
+            mag = np.ldexp(rng.integers(1, 1 << 20, n).astype(np.float64), rng.integers(-48, 21, n))
+            mag = np.maximum(mag, 2.0 ** -48).astype(np.float32)
+            gaps.append(np.where((pat >> i) & 1, np.float32(0.0), mag))
+        want = np.where(gaps[0] == 0, 0, np.where(gaps[1] == 0, 1, np.where(gaps[2] == 0, 2, 3)))
+        assert np.array_equal(_first_zero_keys(*gaps), want), pat
+    # the smallest nonzero gap is far above the keys' range
+    assert _first_zero_keys(np.float32(2.0 ** -48), np.float32(2.0 ** -48), np.float32(2.0 ** -48)) == 3
